@@ -1,0 +1,441 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each test checks one oracle function against something other than itself:
+a closed form, a hand-worked case, a brute-force enumeration written
+differently, a library routine, or a number printed on the pages.
+"""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def facts():
+    with open(os.path.join(GOLDEN, "page_facts.json")) as f:
+        return {k: v["value"] for k, v in json.load(f).items() if not k.startswith("_")}
+
+
+# --------------------------------------------------------------------------
+# storage rounding
+# --------------------------------------------------------------------------
+
+def test_round_bf16_matches_torch_cast():
+    """For fp32 inputs, one RNE step to bf16 equals torch's fp32->bf16 cast."""
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(20000) * s for s in (1e-3, 1.0, 37.0, 1e4)]).astype(np.float32)
+    # exact halfway cases (low 16 bits = 0x8000) in both parities
+    bits = rng.integers(0x3F000000, 0x43000000, 4000, dtype=np.uint32)
+    halfway = ((bits & 0xFFFF0000) | 0x8000).view(np.float32)
+    x = np.concatenate([x, halfway, -halfway])
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.round_bf16(x.astype(np.float64)), ref)
+
+
+def test_round_bf16_hand_cases():
+    # bf16 keeps 8 significant bits: the spacing just above 1.0 is 2^-7
+    assert O.round_bf16(1.0 + 2.0 ** -8) == 1.0                    # tie -> even (1.0)
+    assert O.round_bf16(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6     # tie -> even (up)
+    assert O.round_bf16(1.0 + 2.0 ** -8 + 2.0 ** -30) == 1.0 + 2.0 ** -7  # just above the tie
+    assert O.round_bf16(-3.0) == -3.0
+    assert O.round_bf16(0.0) == 0.0
+    # a value whose fp32 rounding would land on a bf16 tie: one step from fp64 is not two
+    x = 1.0 + 2.0 ** -8 + 2.0 ** -40
+    assert O.round_bf16(x) == 1.0 + 2.0 ** -7
+    assert O.round_bf16(O.round_f32(x)) == 1.0   # the double rounding the oracle avoids
+
+
+def test_f64_reads_bf16_bits_exactly():
+    t = torch.randn(1000).to(torch.bfloat16)
+    bits = t.view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(O.f64(bits), t.to(torch.float64).numpy())
+
+
+def test_round_f32_is_numpy_cast():
+    assert O.round_f32(1.0 + 2.0 ** -24) == 1.0
+    assert O.round_f32(1.0 + 3 * 2.0 ** -24) == 1.0 + 2.0 ** -22
+
+
+# --------------------------------------------------------------------------
+# RMSNorm
+# --------------------------------------------------------------------------
+
+def test_rmsnorm_constant_vector_closed_form():
+    # h = c * ones(H): mean(h^2) = c^2, so xn = c / sqrt(c^2 + eps)
+    for c, eps in [(3.0, 0.5), (-2.0, 1e-6), (0.25, 0.1)]:
+        xn = O.rmsnorm(np.full((1, 7), c), eps)
+        np.testing.assert_allclose(xn, c / math.sqrt(c * c + eps), rtol=1e-15)
+
+
+def test_rmsnorm_loops_and_scale_invariance():
+    rng = np.random.default_rng(1)
+    h = rng.standard_normal((3, 5))
+    eps = 0.3
+    for t in range(3):
+        ms = sum(v * v for v in h[t]) / 5
+        for i in range(5):
+            assert math.isclose(O.rmsnorm(h, eps)[t, i], h[t, i] / math.sqrt(ms + eps), rel_tol=1e-14)
+    # eps -> 0: RMSNorm ignores a positive scale, and mean(xn^2) = 1
+    np.testing.assert_allclose(O.rmsnorm(4.0 * h, 0.0), O.rmsnorm(h, 0.0), rtol=1e-14)
+    np.testing.assert_allclose((O.rmsnorm(h, 0.0) ** 2).mean(-1), 1.0, rtol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# router
+# --------------------------------------------------------------------------
+
+def test_router_logits_loops():
+    rng = np.random.default_rng(2)
+    xn, W, b = rng.standard_normal((2, 5)), rng.standard_normal((3, 5)), rng.standard_normal(3)
+    lg = O.router_logits(xn, W, b)
+    for t in range(2):
+        for e in range(3):
+            assert math.isclose(lg[t, e], sum(xn[t, h] * W[e, h] for h in range(5)) + b[e], rel_tol=1e-13)
+
+
+def _brute_topk(row, k):
+    """Subset with the largest logit sum, lexicographically smallest ids on ties,
+    listed by descending logit (ties by ascending id)."""
+    best, best_key = None, None
+    for sub in itertools.combinations(range(len(row)), k):
+        key = (sum(row[i] for i in sub), [-i for i in sub])
+        if best_key is None or key > best_key:
+            best, best_key = sub, key
+    return sorted(best, key=lambda i: (-row[i], i))
+
+
+def test_topk_bruteforce_all_subsets():
+    """All C(8,2) = 28 subsets per token at the tiny shape, plus k = 3 and ties."""
+    rng = np.random.default_rng(3)
+    rows = [rng.standard_normal(8) for _ in range(200)]
+    rows += [np.round(rng.standard_normal(8) * 2) / 2 for _ in range(200)]   # many exact ties
+    rows += [np.zeros(8), np.ones(8)]
+    for k in (1, 2, 3, 6):
+        got = O.topk_ids(np.asarray(rows), k)
+        for r, g in zip(rows, got):
+            assert list(g) == _brute_topk(list(r), k)
+
+
+def test_topk_weights_identities():
+    # hand-worked: logits log(1..4), top-2 = ids 3,2 with weights 4/7, 3/7
+    lg = np.log(np.array([[1.0, 2.0, 3.0, 4.0]]))
+    ids = O.topk_ids(lg, 2)
+    assert list(ids[0]) == [3, 2]
+    np.testing.assert_allclose(O.topk_weights(lg, ids, True), [[4 / 7, 3 / 7]], rtol=1e-15)
+    np.testing.assert_allclose(O.topk_weights(lg, ids, False), [[4 / 10, 3 / 10]], rtol=1e-15)
+    # renormalised full softmax == softmax over the selected logits; sum is 1
+    rng = np.random.default_rng(4)
+    lg = rng.standard_normal((50, 64)) * 3
+    ids = O.topk_ids(lg, 6)
+    full = O.topk_weights(lg, ids, False)
+    np.testing.assert_allclose(full / full.sum(-1, keepdims=True), O.topk_weights(lg, ids, True), rtol=1e-13)
+    np.testing.assert_allclose(O.topk_weights(lg, ids, True).sum(-1), 1.0, rtol=1e-14)
+    assert np.all(np.diff(O.topk_weights(lg, ids, True), axis=-1) <= 0)   # descending order
+
+
+def test_zero_router_picks_lowest_ids_uniformly():
+    wts = {"w_router": np.zeros((8, 16)), "bias": np.zeros(8)}
+    r = O.route(np.random.default_rng(5).standard_normal((4, 16)), wts["w_router"], wts["bias"], 2, 1e-6, "exact")
+    assert (r["ids"] == [[0, 1]] * 4).all()
+    np.testing.assert_allclose(r["w"], 0.5)
+    assert (r["gap"] == 0).all()
+
+
+def test_topk_gap():
+    lg = np.array([[5.0, 1.0, 4.0, 4.5, 0.0]])
+    # sorted 5, 4.5, 4, 1, 0; k=2: gaps 0.5 (5-4.5), 0.5 (4.5-4) -> 0.5
+    assert O.topk_gap(lg, 2)[0] == 0.5
+    assert O.topk_gap(lg, 3)[0] == 0.5
+    lg = np.array([[5.0, 4.999, 1.0]])
+    assert math.isclose(O.topk_gap(lg, 1)[0], 0.001, rel_tol=1e-9)
+
+
+# --------------------------------------------------------------------------
+# permutation
+# --------------------------------------------------------------------------
+
+def test_permute_hand_case():
+    ids = np.array([[2, 0], [0, 1], [2, 1]])     # T=3, k=2, E=3
+    off, gat, inv = O.permute(ids, 3, S=1)
+    # expert 0: slots 1 (t0), 2 (t1); expert 1: slots 3 (t1), 5 (t2); expert 2: slots 0 (t0), 4 (t2)
+    assert list(off) == [0, 2, 4, 6, 9]
+    assert list(gat) == [0, 1, 1, 2, 0, 2, 0, 1, 2]
+    assert list(inv) == [4, 0, 1, 2, 5, 3]
+
+
+def test_permute_invariants():
+    rng = np.random.default_rng(6)
+    for T, k, E, S in [(16, 2, 8, 2), (128, 6, 64, 2), (5, 6, 64, 0), (1, 1, 1, 0)]:
+        ids = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+        off, gat, inv = O.permute(ids, E, S)
+        assert off[0] == 0 and np.all(np.diff(off) >= 0) and off[-1] == T * k + S * T
+        assert off[E] == T * k
+        assert np.array_equal(np.diff(off[:E + 1]), np.bincount(ids.ravel(), minlength=E))
+        assert sorted(inv) == list(range(T * k))                       # bijection
+        for slot in range(T * k):
+            t, j = divmod(slot, k)
+            r = inv[slot]
+            assert gat[r] == t and off[ids[t, j]] <= r < off[ids[t, j] + 1]
+        for e in range(E):
+            rows = gat[off[e]:off[e + 1]]
+            assert np.all(np.diff(rows) > 0)                            # stable: ascending tokens
+        for s in range(S):
+            assert np.array_equal(gat[off[E + s]:off[E + s + 1]], np.arange(T))
+
+
+# --------------------------------------------------------------------------
+# experts and the block
+# --------------------------------------------------------------------------
+
+def test_silu_closed_forms():
+    assert O.silu(0.0) == 0.0
+    assert math.isclose(float(O.silu(1.0)), 1.0 / (1.0 + math.exp(-1.0)), rel_tol=1e-15)
+    z = np.linspace(-8, 8, 101)
+    np.testing.assert_allclose(O.silu(-z), O.silu(z) - z, atol=1e-14)   # silu(-z) = silu(z) - z
+    assert math.isclose(float(O.silu(50.0)), 50.0, rel_tol=1e-15)
+
+
+def _dense_swiglu_loops(x, wg, wu, wd):
+    H, I = len(x), len(wg)
+    g = [sum(wg[i][h] * x[h] for h in range(H)) for i in range(I)]
+    u = [sum(wu[i][h] * x[h] for h in range(H)) for i in range(I)]
+    a = [g[i] / (1 + math.exp(-g[i])) * u[i] for i in range(I)]
+    return [sum(wd[o][i] * a[i] for i in range(I)) for o in range(H)]
+
+
+def test_single_expert_block_is_dense_swiglu():
+    """E=1, k=1, S=0: the block reduces to h + W_d(silu(W_g xn) * W_u xn)."""
+    rng = np.random.default_rng(7)
+    H, I, eps = 6, 4, 1e-6
+    h = rng.standard_normal((3, H))
+    wts = {"w_router": rng.standard_normal((1, H)), "bias": np.zeros(1),
+           "w_gate_up": rng.standard_normal((1, 2 * I, H)) * 0.5,
+           "w_down": rng.standard_normal((1, H, I)) * 0.5}
+    out = O.moe_layer(h, wts, 1, eps, "exact")
+    for t in range(3):
+        ms = sum(v * v for v in h[t]) / H
+        xn = [v / math.sqrt(ms + eps) for v in h[t]]
+        y = _dense_swiglu_loops(xn, wts["w_gate_up"][0][:I], wts["w_gate_up"][0][I:], wts["w_down"][0])
+        np.testing.assert_allclose(out["h_out"][t], h[t] + np.array(y), rtol=1e-12, atol=1e-13)
+        assert out["route"]["w"][t, 0] == 1.0
+
+
+def test_block_with_shared_expert_loops():
+    """E=3, k=2, S=1 at tiny size: h + sum_j w_j y_j + y_shared, written as loops."""
+    rng = np.random.default_rng(8)
+    H, I, E, k, eps = 5, 3, 3, 2, 1e-6
+    h = rng.standard_normal((4, H))
+    wts = {"w_router": rng.standard_normal((E, H)), "bias": rng.standard_normal(E),
+           "w_gate_up": rng.standard_normal((E + 1, 2 * I, H)) * 0.5,
+           "w_down": rng.standard_normal((E + 1, H, I)) * 0.5}
+    out = O.moe_layer(h, wts, k, eps, "exact")
+    for t in range(4):
+        ms = sum(v * v for v in h[t]) / H
+        xn = [v / math.sqrt(ms + eps) for v in h[t]]
+        lg = [sum(xn[j] * wts["w_router"][e][j] for j in range(H)) + wts["bias"][e] for e in range(E)]
+        sel = sorted(range(E), key=lambda e: (-lg[e], e))[:k]
+        z = [math.exp(lg[e] - lg[sel[0]]) for e in sel]
+        w = [v / sum(z) for v in z]
+        acc = np.zeros(H)
+        for wj, e in zip(w, sel):
+            acc += wj * np.array(_dense_swiglu_loops(xn, wts["w_gate_up"][e][:I], wts["w_gate_up"][e][I:], wts["w_down"][e]))
+        acc += np.array(_dense_swiglu_loops(xn, wts["w_gate_up"][E][:I], wts["w_gate_up"][E][I:], wts["w_down"][E]))
+        np.testing.assert_allclose(out["h_out"][t], h[t] + acc, rtol=1e-12, atol=1e-13)
+        assert list(out["route"]["ids"][t]) == sel
+
+
+def test_identical_experts_make_routing_irrelevant():
+    rng = np.random.default_rng(9)
+    H, I, E, k = 16, 8, 8, 2
+    h = rng.standard_normal((10, H))
+    one_gu, one_d = rng.standard_normal((2 * I, H)) * 0.3, rng.standard_normal((H, I)) * 0.3
+    wts = {"w_router": rng.standard_normal((E, H)), "bias": np.zeros(E),
+           "w_gate_up": np.broadcast_to(one_gu, (E, 2 * I, H)).copy(),
+           "w_down": np.broadcast_to(one_d, (E, H, I)).copy()}
+    out = O.moe_layer(h, wts, k, 1e-6, "exact")
+    y = O.swiglu(O.rmsnorm(h, 1e-6), one_gu, one_d, "exact")
+    np.testing.assert_allclose(out["combined"], y, rtol=1e-12, atol=1e-14)
+
+
+def test_bf16_mode_rounds_at_storage_points():
+    rng = np.random.default_rng(10)
+    H, I, E = 32, 16, 4
+    tb = lambda a: torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    wts = {"w_router": rng.standard_normal((E, H)).astype(np.float32) * 0.02, "bias": np.zeros(E, np.float32),
+           "w_gate_up": tb(rng.standard_normal((E + 2, 2 * I, H)) * 0.02), "w_down": tb(rng.standard_normal((E + 2, H, I)) * 0.02)}
+    h = tb(rng.standard_normal((8, H)))
+    out = O.moe_layer(h, wts, 2, 1e-6, "bf16")
+    for a in (out["route"]["xn"], out["y"], out["ys"], out["h_out"]):
+        np.testing.assert_array_equal(O.round_bf16(a), a)
+    ex = O.moe_layer(h, wts, 2, 1e-6, "exact")
+    # storage rounding moves the block output by at most a few bf16 ulps
+    assert np.max(np.abs(out["h_out"] - ex["h_out"])) < 0.05
+
+
+# --------------------------------------------------------------------------
+# LM head
+# --------------------------------------------------------------------------
+
+def test_lm_argmax_bruteforce_with_ties_across_chunks():
+    rng = np.random.default_rng(11)
+    T, H, V = 6, 5, 50
+    h = rng.standard_normal((T, H))
+    W = rng.standard_normal((V, H))
+    W[37] = W[12]              # exact tie between ids 12 and 37 (different chunks of 7)
+    h[0] = W[12] * 10          # row 0 very likely peaks at the tied pair
+    ids, mx, gap = O.lm_argmax(h, W, chunk=7)
+    for t in range(T):
+        lg = [sum(h[t, j] * W[v, j] for j in range(H)) for v in range(V)]
+        best = 0
+        for v in range(1, V):
+            if lg[v] > lg[best]:
+                best = v
+        assert ids[t] == best
+        assert math.isclose(mx[t], lg[best], rel_tol=1e-12)
+        s = sorted(lg, reverse=True)
+        assert math.isclose(gap[t], s[0] - s[1], abs_tol=1e-12)
+    assert ids[0] == 12 and gap[0] == 0.0
+
+
+def test_lm_argmax_one_hot_selects_weight_column():
+    rng = np.random.default_rng(12)
+    V, H = 300, 16
+    W = rng.standard_normal((V, H))
+    h = np.eye(H)
+    ids, _, _ = O.lm_argmax(h, W, chunk=64)
+    np.testing.assert_array_equal(ids, np.argmax(W, axis=0))
+
+
+# --------------------------------------------------------------------------
+# acceptance
+# --------------------------------------------------------------------------
+
+def test_spec_verify_bruteforce_v3_k3():
+    """All 3^3 drafts x 3^4 verifier outputs (2,187 cases) against a prefix-slice
+    formulation: the accepted count is the longest m with d[:m] == g[:m]."""
+    cases = list(itertools.product(itertools.product(range(3), repeat=3), itertools.product(range(3), repeat=4)))
+    assert len(cases) == 2187
+    D = np.array([c[0] for c in cases])
+    G = np.array([c[1] for c in cases])
+    acc, com, nc = O.spec_verify(D, G)
+    for i, (d, g) in enumerate(cases):
+        m = max(m for m in range(4) if list(d[:m]) == list(g[:m]))
+        assert acc[i] == m and nc[i] == m + 1 <= 4
+        assert list(com[i]) == list(d[:m]) + [g[m]] + [-1] * (3 - m)
+
+
+def test_spec_verify_k0_is_greedy():
+    g = np.array([[5], [7], [0]])
+    acc, com, nc = O.spec_verify(np.zeros((3, 0), np.int64), g)
+    assert list(acc) == [0, 0, 0] and list(nc) == [1, 1, 1] and list(com[:, 0]) == [5, 7, 0]
+
+
+def test_plant_drafts_leading_keeps():
+    rng = np.random.default_rng(13)
+    V, B, K = 97, 2000, 3
+    g = rng.integers(0, V, (B, K + 1))
+    keep = rng.random((B, K)) < 0.576
+    repl = rng.integers(0, V - 1, (B, K))
+    d = O.plant_drafts(g, keep, repl)
+    assert np.all((d == g[:, :K]) == keep)             # a replaced draft never matches
+    assert d.min() >= 0 and d.max() < V
+    acc, _, nc = O.spec_verify(d, g)
+    lead = np.array([next((i for i in range(K) if not keep[b, i]), K) for b in range(B)])
+    np.testing.assert_array_equal(acc, lead)
+
+
+def test_planted_tau_closed_form():
+    """n+1 with independent keeps has mean 1+p+p^2+p^3; the pages' tau = 1 + K*alpha
+    relation holds for their printed acceptance 57.6% and tau 2.73."""
+    f = facts()
+    p, K = f["acceptance_rate_K3"], f["draft_tokens_K"]
+    rng = np.random.default_rng(14)
+    n_s = 200000
+    keep = rng.random((n_s, K)) < p
+    g = np.zeros((n_s, K + 1), np.int64)
+    d = O.plant_drafts(g, keep, rng.integers(0, 10, (n_s, K)))
+    _, _, nc = O.spec_verify(d, g)
+    expect = 1 + p + p ** 2 + p ** 3
+    se = nc.std() / math.sqrt(n_s)
+    assert abs(nc.mean() - expect) < 4 * se
+    assert abs((1 + K * p) - f["tau_eager_K3"]) < 0.005            # 2.728 vs 2.73
+    assert abs(f["tau_eager_K3"] / f["speedup_eager_K3"] - f["cost_eager"]) < 0.005   # c = tau / speedup
+    assert abs(f["spec_tok_s_eager"] / f["ar_tok_s_eager"] - f["speedup_eager_K3"]) < 0.01
+
+
+# --------------------------------------------------------------------------
+# speculative decoding is token-identical to greedy decoding
+# --------------------------------------------------------------------------
+
+def _tiny_token_model(seed=0):
+    """Token-driven tiny model: embedding 512x128 -> one tiny MoE block -> LM head 512."""
+    rng = np.random.default_rng(seed)
+    V, H, I, E, k = 512, 128, 64, 8, 2
+    emb = rng.standard_normal((V, H))
+    wts = {"w_router": rng.standard_normal((E, H)) * 0.02, "bias": np.zeros(E),
+           "w_gate_up": rng.standard_normal((E + 2, 2 * I, H)) * 0.02,
+           "w_down": rng.standard_normal((E + 2, H, I)) * 0.02}
+    w_lm = rng.standard_normal((V, H)) * 0.02
+    cache = {}
+
+    def next_tokens(tokens):
+        out = []
+        for t in tokens:
+            if t not in cache:
+                hout = O.moe_layer(emb[[t]], wts, k, 1e-6, "exact")["h_out"]
+                cache[t] = int(O.lm_argmax(hout, w_lm)[0][0])
+            out.append(cache[t])
+        return out
+    return next_tokens, V
+
+
+@pytest.mark.parametrize("K", [0, 1, 2, 3])
+def test_speculative_equals_greedy(K):
+    next_tokens, V = _tiny_token_model()
+    rng = np.random.default_rng(100 + K)
+    n = 60
+    ref = O.greedy_decode(7, n, next_tokens)
+    # random proposals
+    seq, passes, commits = O.speculative_decode(7, n, next_tokens, lambda s, K: rng.integers(0, V, K), K)
+    assert seq == ref and all(1 <= c <= K + 1 for c in commits)
+    # planted proposals (keep the true continuation with probability 0.576)
+    def planted(s, K):
+        pos = len(s) - 1
+        truth = ref[pos + 1:pos + 1 + K] + [0] * K
+        return [truth[i] if rng.random() < 0.576 else int(rng.integers(0, V)) for i in range(K)]
+    seq, passes, commits = O.speculative_decode(7, n, next_tokens, planted, K)
+    assert seq == ref
+    # perfect proposals commit K+1 per pass
+    seq, passes, commits = O.speculative_decode(
+        7, n, next_tokens, lambda s, K: (ref[len(s):len(s) + K] + [0] * K)[:K], K)
+    assert seq == ref and all(c == K + 1 for c in commits[:-1])
+
+
+# --------------------------------------------------------------------------
+# parameter accounting against the pages
+# --------------------------------------------------------------------------
+
+def test_active_and_total_params_match_pages():
+    f = facts()
+    H, E, k, S, V, L = f["hidden"], f["routed_experts"], f["top_k"], f["shared_experts"], f["vocab"], f["decoder_layers"]
+    I = 896          # synthetic intermediate size (the pages do not give it)
+    attn = 4 * H * H  # attention projections q,k,v,o, omitted from the hot path
+    moe_only = O.active_params(H, E, k, S, I, V, L)
+    assert moe_only == 496_762_880
+    act = O.active_params(H, E, k, S, I, V, L, attn_per_layer=attn)
+    assert abs(act / f["active_params_approx"] - 1) < 0.015           # 575.4M vs ~570M
+    tot = O.total_params(H, E, S, I, V, L, attn_per_layer=attn, encoder=f["encoder_params_approx"])
+    assert abs(tot / f["total_params_approx"] - 1) < 0.03              # 3.35B vs 3.4B
+    assert abs(f["total_params_approx"] * 2 / 1e9 - f["weights_bf16_gb_approx"]) < 0.05
+    # visual token budget: 256 base + 9 tiles x 100
+    assert f["visual_tokens_base"] + f["visual_tiles_max"] * f["visual_tokens_per_tile"] == f["visual_tokens_max"]
+    # throughput arithmetic on the A100 run
+    assert abs(f["pages_per_s_a100"] * f["tokens_per_page"] / f["tokens_per_s_a100"] - 1) < 0.005
