@@ -1,0 +1,192 @@
+"""Benchmark of the MoE speculative verify step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Default workload: one full verify pass at concurrency 32 -- 32 sequences x 4
+positions (1 committed + K=3 drafts) = 128 tokens through 12 MoE layers
+(hidden 1280, 64 routed + 2 shared SwiGLU experts with intermediate 896, top-6),
+the 1280 x 129,280 LM-head argmax and greedy acceptance.  Weights and inputs
+are seeded synthetic data (N(0, 0.02) bf16 weights, N(0, 1) hidden states),
+resident in HBM before the timed region.  Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="step128", choices=["step128", "batch1", "layer128"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-layers", type=int, default=6, help="layers of the oracle sample")
+    ap.add_argument("--cpu-vocab", type=int, default=65536, help="LM-head rows of the oracle sample")
+    return ap.parse_args()
+
+
+def expert_bytes(sh) -> int:
+    return 3 * sh.H * sh.I * 2
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(the step is sharded by design only; see the sharding notes).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import moe_decoder_step_amd as m
+    import synth
+
+    m.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sh = synth.SHAPES[args.workload]
+    T = sh.T
+    log(f"workload {sh.name}: T={T} L={sh.L} V={sh.V}; generating weights on {dev}")
+    t0 = time.time()
+    layers = [synth.layer_weights(0, l, sh, dev) for l in range(sh.L)]
+    w_lm = synth.lm_weight(0, sh, dev) if sh.V else None
+    h_in = synth.hidden(0, T, sh.H, torch.bfloat16, dev, name="step_hidden")
+    drafts = synth.uniform_ids(0, (sh.B, sh.K), sh.V or 2).to(dev)
+    torch.cuda.synchronize()
+    log(f"weights ready in {time.time() - t0:.1f}s")
+
+    st = m.VerifyStack(layers, w_lm, sh.E, sh.k, sh.S, max_tokens=T, max_seqs=sh.B, K=sh.K)
+
+    def step():
+        st.forward(h_in)
+        if w_lm is not None:
+            st.head(T)
+            st.verify(drafts)
+
+    # routed experts touched per layer (weights the step must read)
+    rec = []
+    st.forward(h_in, rec)
+    touched = [int(np.unique(r["ids"].cpu().numpy()).size) for r in rec]
+    layer_bytes = [(t + sh.S) * expert_bytes(sh) + sh.E * sh.H * 4 + 2 * T * sh.H * 2 for t in touched]
+    step_bytes = sum(layer_bytes) + (sh.V * sh.H * 2 if sh.V else 0)
+    ffn_bytes = [(t + sh.S) * expert_bytes(sh) + T * sh.H * 2 + (T * sh.k + sh.S * T) * sh.H * 2 for t in touched]
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done; timing {args.steps} steps")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    log(f"{ms:.3f} ms/step")
+
+    # dominant op (grouped SwiGLU, routed + shared experts): HIP events around
+    # each launch on the stream it runs on, over a second timed pass
+    st.ffn_events = ev = []
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    st.ffn_events = None
+    ffn_ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
+    ffn_b = float(np.mean(ffn_bytes))
+    achieved = ffn_b / (ffn_ms * 1e-3) / 1e9
+    log(f"grouped SwiGLU: {ffn_ms * 1e3:.1f} us/launch, {achieved:.0f} GB/s")
+
+    out = {
+        "metric": "MoE verify-step tokens/s (32 seq x 4 tok, 12 layers)" if sh.name == "step128"
+        else f"MoE verify tokens/s ({sh.name})",
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"verify pass, {sh.B} seq x {sh.P} positions = {T} tokens, {sh.L} MoE layers"
+                   + (f" + LM head {sh.H}x{sh.V} argmax + greedy acceptance" if sh.V else ""),
+                   "hidden": sh.H, "experts": f"{sh.E} routed + {sh.S} shared, top-{sh.k}",
+                   "expert_intermediate": sh.I, "global_batch": T},
+        "step_hbm": {"algorithmic_bytes": step_bytes, "achieved_GBs": step_bytes / (ms * 1e-3) / 1e9,
+                     "frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "touched_experts_per_layer": touched},
+        "roofline": {"kernel": "moe_grouped_swiglu (gate/up + down launches)", "bound": "hbm",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "us_per_launch": ffn_ms * 1e3, "algorithmic_bytes_per_launch": ffn_b},
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args, sh, layers, w_lm, h_in, T)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def cpu_baseline(args, sh, layers, w_lm, h_in, T) -> dict:
+    """The fp64 oracle on the host cores over a bounded sample of the same step:
+    `cpu_layers` MoE layers on all T tokens plus the LM head over `cpu_vocab`
+    vocabulary rows, scaled to the full 12 layers and vocabulary."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+
+    def host(t):
+        t = t.detach().cpu().contiguous()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+    nl = min(args.cpu_layers, sh.L)
+    log(f"cpu baseline: oracle on {nl} layer(s) + {args.cpu_vocab} LM rows")
+    hw = [{k: host(v) for k, v in layers[l].items()} for l in range(nl)]
+    x = host(h_in)
+    t0 = time.perf_counter()
+    cur = x
+    for l in range(nl):
+        cur = O.moe_layer(cur, hw[l], sh.k, sh.eps, "bf16")["h_out"]
+    t_layers = time.perf_counter() - t0
+    t_lm = 0.0
+    vs = 0
+    if w_lm is not None:
+        vs = min(args.cpu_vocab, sh.V)
+        wl = host(w_lm[:vs])
+        t1 = time.perf_counter()
+        O.lm_argmax(cur, wl)
+        t_lm = time.perf_counter() - t1
+    t_step = t_layers * sh.L / nl + (t_lm * sh.V / vs if vs else 0.0)
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    return {"value": T / t_step, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{nl} of {sh.L} MoE layers on all {T} tokens ({t_layers:.1f}s) + LM head over "
+                      f"{vs} of {sh.V} vocabulary rows ({t_lm:.1f}s), scaled to the full step "
+                      f"({t_step:.1f}s per step)"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

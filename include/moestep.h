@@ -1,0 +1,230 @@
+/*
+ * moestep.h -- C ABI of the MoE speculative verify step on MI355X (gfx950).
+ *
+ * The step is the verifier pass of the jina-ocr-v1 decoder (DeepSeek-3B-MoE:
+ * hidden 1280, 64 routed + 2 shared experts, top-6 routing, vocabulary
+ * 129,280 -- jina.ai/ko model card "jina-ocr-v1", architecture paragraph),
+ * which checks K drafted tokens greedily and commits the longest agreeing
+ * prefix plus one bonus token (jina.ai/de "jina-ocr-v1: Schnellere
+ * Dokumentenanalyse auf kostenguenstigen GPUs", sections "Modell und
+ * Training" and "Spekulatives Decoding auf einer L4").  Per layer:
+ *
+ *   moe_route -> moe_permute -> moe_grouped_swiglu -> moe_combine
+ *
+ * and once per verify pass: lmhead_argmax -> spec_verify.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All tensor pointers are device memory owned by the caller.  The library
+ *   never allocates, frees or synchronises; every call enqueues its kernels on
+ *   `stream` (a hipStream_t passed as void*, NULL = the default stream) and
+ *   returns at once.  Calls on one stream run in order.
+ * - Layouts are row-major and contiguous.  Ids are int32.  `dtype` selects
+ *   the storage type of activations and expert / LM-head weights (MOE_BF16 or
+ *   MOE_F32); router weights, router bias and routing weights are always fp32.
+ *   Arithmetic accumulates in fp32 (the RMSNorm scale in fp64).
+ * - Activation and weight pointers must be 16-byte aligned (MOE_ERR_ALIGN).
+ * - A size of 0 tokens (or sequences) is a no-op that returns MOE_OK.
+ * - The return value is a moe_status.  Host-side argument checks run before
+ *   anything is enqueued; a failed launch returns MOE_ERR_HIP.  Device-side
+ *   data is never trusted for memory addressing: out-of-range ids and offsets
+ *   are clamped into range (memory-safe, the mistake is not reported).
+ * - Outputs are fully overwritten.  The only aliasing allowed is
+ *   out == residual in moe_combine.
+ * - No global mutable state: calls on different streams may run concurrently
+ *   as long as they do not share output or workspace buffers.
+ */
+#ifndef MOESTEP_H
+#define MOESTEP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,         /* a required pointer is NULL */
+  MOE_ERR_SHAPE = 2,        /* a size is negative or inconsistent */
+  MOE_ERR_UNSUPPORTED = 3,  /* a valid shape this build does not handle (e.g. E > 64) */
+  MOE_ERR_ALIGN = 4,        /* a tensor pointer is not 16-byte aligned */
+  MOE_ERR_WORKSPACE = 5,    /* workspace missing or smaller than the query says */
+  MOE_ERR_HIP = 6           /* the HIP runtime reported an error at launch */
+} moe_status;
+
+typedef enum { MOE_BF16 = 0, MOE_F32 = 1 } moe_dtype;
+
+/* moe_route flags */
+#define MOE_ROUTE_NORM 1    /* apply RMSNorm before the router (else xn = h) */
+#define MOE_ROUTE_RENORM 2  /* softmax over the k selected logits (else full-softmax probabilities) */
+
+/* Version of this ABI (MOE_ABI_VERSION). */
+int moe_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* moe_status_str(int status);
+
+/* ---------------------------------------------------------------------------
+ * moe_route -- pre-norm, router logits, top-k selection and routing weights.
+ *
+ * Per token t (the pages give top-6 of 64 routed experts -- alphasignal.ai
+ * "Jina AI's 3.4B OCR model targets faster page parsing", section "A
+ * compressed visual front end"; the norm and the routing function are not on
+ * the pages, the readings are):
+ *   xn[t]  = h[t] / sqrt(mean(h[t]^2) + eps) * gain     (if MOE_ROUTE_NORM)
+ *            stored once, rounded to nearest-even from an fp64 scale
+ *   l[t,e] = sum_h xn[t,h] * w_router[e,h] + bias[e]     fp32
+ *   ids    = the k largest l[t,:], descending; equal logits -> lower expert id
+ *   w[t,j] = exp(l[t,ids_j]) / sum_{i<k} exp(l[t,ids_i])  (MOE_ROUTE_RENORM)
+ *            exp(l[t,ids_j]) / sum_e exp(l[t,e])          (otherwise)
+ *
+ * h        [T,H] dtype             in
+ * gain     [H] fp32 or NULL (= 1)  in
+ * w_router [E,H] fp32, bias [E] fp32 or NULL   in
+ * xn       [T,H] dtype             out (the normed input the experts read)
+ * topk_ids [T,k] int32, topk_w [T,k] fp32      out
+ * logits   [T,E] fp32 or NULL      out (optional, for near-tie diagnostics)
+ * Limits: 1 <= k <= E <= 64, 8 <= H <= 2048, H % 8 == 0.
+ * ------------------------------------------------------------------------- */
+int moe_route(const void* h, const float* gain, float eps,
+              const float* w_router, const float* bias,
+              int T, int H, int E, int k, int flags, int dtype,
+              void* xn, int32_t* topk_ids, float* topk_w, float* logits,
+              void* stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_permute -- group the T*k (token, slot) pairs by expert.
+ *
+ * Slot s = t*k + j.  Routed expert e owns rows offsets[e] .. offsets[e+1]-1,
+ * holding its slots in ascending token order (a stable counting sort).
+ * When S > 0, shared expert s is appended as group E+s owning the T rows
+ * T*k + s*T .. T*k + (s+1)*T - 1, one per token in order, so one grouped
+ * SwiGLU call covers routed and shared experts.
+ *
+ * topk_ids [T,k] int32     in  (ids outside [0,E) are clamped into it)
+ * offsets  [E+S+1] int32   out (offsets[E+s] = T*k + s*T)
+ * gather   [T*k + S*T] int32 out: token read by each row
+ * inv      [T*k] int32     out: row of each slot
+ * ws / ws_bytes            scratch of at least moe_permute_workspace_bytes()
+ *                          bytes (may be NULL when that is 0)
+ * Limits: 1 <= E <= 64, 1 <= k <= E, 0 <= S <= 8.
+ * ------------------------------------------------------------------------- */
+size_t moe_permute_workspace_bytes(int T, int k, int E);
+int moe_permute(const int32_t* topk_ids, int T, int k, int E, int S,
+                int32_t* offsets, int32_t* gather, int32_t* inv,
+                void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_grouped_swiglu -- SwiGLU expert FFN over groups of gathered rows.
+ *
+ * For each group g and each row r in offsets[g] .. offsets[g+1]-1, with
+ * token t = gather[r] (or t = r - offsets[g] when gather is NULL):
+ *   a[r] = silu(W_g[g] x[t]) * (W_u[g] x[t])    fp32 accumulate, stored in dtype
+ *   y[r] = W_d[g] a[r]                          fp32 accumulate, stored in dtype
+ * with silu(z) = z / (1 + exp(-z)).  Routed and shared experts are the same
+ * operation (64 routed + 2 shared experts: jina.ai/ko model card, architecture
+ * paragraph; the SwiGLU form is a reading, the pages do not give it).
+ *
+ * x         [T,H] dtype                 in
+ * gather    [n_rows] int32 or NULL      in  (clamped into [0,T))
+ * offsets   [G+1] int32 (device)        in  (nondecreasing, offsets[G] <= n_rows;
+ *                                            clamped into [0,n_rows])
+ * w_gate_up [G, 2I, H] dtype            in  rows 0..I-1 = W_g, I..2I-1 = W_u
+ * w_down    [G, H, I] dtype             in
+ * max_rows  host-side upper bound on any group's row count (e.g. T); it only
+ *           selects the kernel shape -- any count is computed correctly
+ * y         [n_rows, H] dtype           out (rows outside every group untouched)
+ * ws        scratch of at least moe_grouped_swiglu_workspace_bytes() bytes
+ * Limits: H % 32 == 0 and I % 32 == 0 for MOE_BF16, H % 4 == 0 and
+ *         I % 4 == 0 for MOE_F32; 1 <= G.
+ * ------------------------------------------------------------------------- */
+size_t moe_grouped_swiglu_workspace_bytes(int n_rows, int I, int dtype);
+int moe_grouped_swiglu(const void* x, const int32_t* gather, const int32_t* offsets,
+                       int G, int n_rows, const void* w_gate_up, const void* w_down,
+                       int T, int H, int I, int max_rows, int dtype,
+                       void* y, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_combine -- weighted sum of the expert outputs plus the residual.
+ *
+ *   c[t]   = sum_{j<k} topk_w[t,j] * y[inv[t*k+j]] + sum_{s<S} y_shared[s*T+t]
+ *   out[t] = residual[t] + c[t]          (out = c[t] when residual is NULL)
+ * fp32, summed in that fixed order, then stored in dtype.  Shared experts
+ * carry weight 1.
+ *
+ * y        [n_rows, H] dtype (rows in permuted order)   in
+ * inv      [T*k] int32  (clamped into [0,n_rows))        in
+ * topk_w   [T,k] fp32                                    in
+ * y_shared [S*T, H] dtype or NULL (then S must be 0)     in
+ * residual [T,H] dtype or NULL                           in
+ * out      [T,H] dtype, may alias residual               out
+ * combined [T,H] dtype or NULL: c[t] before the residual out
+ * ------------------------------------------------------------------------- */
+int moe_combine(const void* y, const int32_t* inv, const float* topk_w,
+                const void* y_shared, int S, const void* residual,
+                int T, int H, int k, int n_rows, int dtype,
+                void* out, void* combined, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * lmhead_argmax -- greedy next token of every row: argmax_v (h W_lm^T)[v].
+ *
+ * The logits (vocabulary 129,280: jina.ai/ko model card, architecture
+ * paragraph) are never written out; each row gets the index of its largest
+ * fp32 logit, equal logits going to the lowest index, and that logit.
+ *
+ * h          [T,H] dtype       in
+ * w_lm       [V,H] dtype       in
+ * argmax_ids [T] int32         out
+ * max_logit  [T] fp32 or NULL  out
+ * ws         scratch of at least lmhead_argmax_workspace_bytes() bytes
+ * Limits: H % 32 == 0 (MOE_BF16) or H % 4 == 0 (MOE_F32); 1 <= V < 2^31.
+ * ------------------------------------------------------------------------- */
+size_t lmhead_argmax_workspace_bytes(int T, int V, int dtype);
+int lmhead_argmax(const void* h, const void* w_lm, int T, int H, int V, int dtype,
+                  int32_t* argmax_ids, float* max_logit,
+                  void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * spec_verify -- greedy longest-prefix acceptance plus the bonus token.
+ *
+ * Sequence b verified K+1 positions: its last committed token and K drafts.
+ * argmax_ids[b,i] is the verifier's greedy token after position i, so
+ * draft i is accepted while drafts[b,i'] == argmax_ids[b,i'] for every
+ * i' <= i.  With n accepted drafts the step commits drafts[b,0..n-1] and
+ * argmax_ids[b,n]: n+1 tokens, at most K+1 (jina.ai/de page, sections
+ * "Modell und Training" and "Spekulatives Decoding auf einer L4").  K = 0
+ * is plain greedy decoding.  A draft id outside the vocabulary is simply a
+ * mismatch.
+ *
+ * drafts     [B,K] int32     in
+ * argmax_ids [B,K+1] int32   in
+ * accepted   [B] int32       out  n
+ * committed  [B,K+1] int32   out  committed tokens, -1 padded
+ * n_commit   [B] int32       out  n+1
+ * Limits: 0 <= K <= 15.
+ * ------------------------------------------------------------------------- */
+int spec_verify(const int32_t* drafts, const int32_t* argmax_ids, int B, int K,
+                int32_t* accepted, int32_t* committed, int32_t* n_commit,
+                void* stream);
+
+/* ---------------------------------------------------------------------------
+ * spec_plant_drafts -- benchmark-harness stand-in for a draft head (not part
+ * of the verify step).  Draft i of sequence b is argmax_ids[b,i] when
+ * keep[b,i] != 0, else u + (u >= argmax_ids[b,i]) with u = repl[b,i] in
+ * [0, V-1): a uniform draw over the other V-1 ids, so it never matches.
+ *
+ * argmax_ids [B,K+1] int32, keep [B,K] uint8, repl [B,K] int32   in
+ * drafts     [B,K] int32                                          out
+ * ------------------------------------------------------------------------- */
+int spec_plant_drafts(const int32_t* argmax_ids, const uint8_t* keep, const int32_t* repl,
+                      int B, int K, int V, int32_t* drafts, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOESTEP_H */

@@ -1,0 +1,98 @@
+// extern "C" entry points of libmoestep: host checks, then the launchers.
+#include <hip/hip_runtime.h>
+
+#include "../../include/moestep.h"
+#include "kernels.hpp"
+#include "validate.hpp"
+
+namespace {
+
+inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "a size is negative or inconsistent";
+    case MOE_ERR_UNSUPPORTED: return "shape or dtype not supported by this build";
+    case MOE_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+size_t moe_permute_workspace_bytes(int T, int k, int E) { return moe::permute_ws_bytes(T, k, E); }
+
+size_t moe_grouped_swiglu_workspace_bytes(int n_rows, int I, int dtype) {
+  return moe::swiglu_ws_bytes(n_rows, I, dtype);
+}
+
+size_t lmhead_argmax_workspace_bytes(int T, int V, int dtype) { return moe::lmhead_ws_bytes(T, V, dtype); }
+
+int moe_route(const void* h, const float* gain, float eps, const float* w_router, const float* bias,
+              int T, int H, int E, int k, int flags, int dtype, void* xn, int32_t* topk_ids,
+              float* topk_w, float* logits, void* stream) {
+  int st = moe::check_route(h, w_router, T, H, E, k, dtype, xn, topk_ids, topk_w);
+  if (st != MOE_OK || T == 0) return st;
+  return hip_status(moe::launch_route(h, gain, eps, w_router, bias, T, H, E, k, flags, dtype, xn, topk_ids,
+                                      topk_w, logits, as_stream(stream)));
+}
+
+int moe_permute(const int32_t* topk_ids, int T, int k, int E, int S, int32_t* offsets, int32_t* gather,
+                int32_t* inv, void* ws, size_t ws_bytes, void* stream) {
+  int st = moe::check_permute(topk_ids, T, k, E, S, offsets, gather, inv, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  // T == 0 still writes offsets (all groups empty) with a kernel, not a memset
+  return hip_status(moe::launch_permute(topk_ids, T, k, E, S, offsets, gather, inv, ws, as_stream(stream)));
+}
+
+int moe_grouped_swiglu(const void* x, const int32_t* gather, const int32_t* offsets, int G, int n_rows,
+                       const void* w_gate_up, const void* w_down, int T, int H, int I, int max_rows,
+                       int dtype, void* y, void* ws, size_t ws_bytes, void* stream) {
+  int st = moe::check_swiglu(x, offsets, G, n_rows, w_gate_up, w_down, T, H, I, max_rows, dtype, y, ws,
+                             ws_bytes);
+  if (st != MOE_OK || n_rows == 0 || T == 0) return st;
+  return hip_status(moe::launch_swiglu(x, gather, offsets, G, n_rows, w_gate_up, w_down, T, H, I, max_rows,
+                                       dtype, y, ws, as_stream(stream)));
+}
+
+int moe_combine(const void* y, const int32_t* inv, const float* topk_w, const void* y_shared, int S,
+                const void* residual, int T, int H, int k, int n_rows, int dtype, void* out, void* combined,
+                void* stream) {
+  int st = moe::check_combine(y, inv, topk_w, y_shared, S, residual, T, H, k, n_rows, dtype, out, combined);
+  if (st != MOE_OK || T == 0) return st;
+  return hip_status(moe::launch_combine(y, inv, topk_w, y_shared, S, residual, T, H, k, n_rows, dtype, out,
+                                        combined, as_stream(stream)));
+}
+
+int lmhead_argmax(const void* h, const void* w_lm, int T, int H, int V, int dtype, int32_t* argmax_ids,
+                  float* max_logit, void* ws, size_t ws_bytes, void* stream) {
+  int st = moe::check_lmhead(h, w_lm, T, H, V, dtype, argmax_ids, ws, ws_bytes);
+  if (st != MOE_OK || T == 0) return st;
+  return hip_status(moe::launch_lmhead(h, w_lm, T, H, V, dtype, argmax_ids, max_logit, ws, as_stream(stream)));
+}
+
+int spec_verify(const int32_t* drafts, const int32_t* argmax_ids, int B, int K, int32_t* accepted,
+                int32_t* committed, int32_t* n_commit, void* stream) {
+  int st = moe::check_verify(drafts, argmax_ids, B, K, accepted, committed, n_commit);
+  if (st != MOE_OK || B == 0) return st;
+  return hip_status(moe::launch_verify(drafts, argmax_ids, B, K, accepted, committed, n_commit,
+                                       as_stream(stream)));
+}
+
+int spec_plant_drafts(const int32_t* argmax_ids, const uint8_t* keep, const int32_t* repl, int B, int K, int V,
+                      int32_t* drafts, void* stream) {
+  int st = moe::check_plant(argmax_ids, keep, repl, B, K, V, drafts);
+  if (st != MOE_OK || B == 0 || K == 0) return st;
+  return hip_status(moe::launch_plant(argmax_ids, keep, repl, B, K, V, drafts, as_stream(stream)));
+}
+
+}  // extern "C"

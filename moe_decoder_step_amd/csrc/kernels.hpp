@@ -1,0 +1,34 @@
+// Internal launchers of the gfx950 kernels (C++ linkage, not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_route(const void* h, const float* gain, float eps, const float* w_router,
+                        const float* bias, int T, int H, int E, int k, int flags, int dtype,
+                        void* xn, int32_t* ids, float* w, float* logits, hipStream_t s);
+
+hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int S, int32_t* offsets,
+                          int32_t* gather, int32_t* inv, void* ws, hipStream_t s);
+
+hipError_t launch_swiglu(const void* x, const int32_t* gather, const int32_t* offsets, int G,
+                         int n_rows, const void* w_gate_up, const void* w_down, int T, int H, int I,
+                         int max_rows, int dtype, void* y, void* ws, hipStream_t s);
+
+hipError_t launch_combine(const void* y, const int32_t* inv, const float* topk_w,
+                          const void* y_shared, int S, const void* residual, int T, int H, int k,
+                          int n_rows, int dtype, void* out, void* combined, hipStream_t s);
+
+hipError_t launch_lmhead(const void* h, const void* w_lm, int T, int H, int V, int dtype,
+                         int32_t* ids, float* max_logit, void* ws, hipStream_t s);
+
+hipError_t launch_verify(const int32_t* drafts, const int32_t* argmax_ids, int B, int K,
+                         int32_t* accepted, int32_t* committed, int32_t* n_commit, hipStream_t s);
+
+hipError_t launch_plant(const int32_t* argmax_ids, const uint8_t* keep, const int32_t* repl, int B,
+                        int K, int V, int32_t* drafts, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,222 @@
+// lmhead_argmax: argmax_v (h W_lm^T)[t, v] per row, ties to the lowest v.
+//
+// The 129,280 x 1280 bf16 LM head (331 MB) is streamed from HBM exactly once
+// per call and the logits never leave registers:
+//   * a block of 4 wavefronts owns 128 vocabulary rows; wavefront w streams 32
+//     of them (two 16-row MFMA blocks) as the A operand of
+//     v_mfma_f32_16x16x32_bf16, two 128-element chunks in flight;
+//   * the h rows (all T rows, up to 128 per pass) are the B operand, staged
+//     through LDS in 128-element chunks and shared by the four wavefronts;
+//   * each logit becomes a 64-bit key (order-preserving float bits, then
+//     0xffffffff - v) so "largest logit, then lowest index" is a plain max;
+//     keys are reduced over the block's rows with shuffles and LDS and one key
+//     per (row, block) goes to the workspace;
+//   * a second kernel takes the max over blocks for each row.
+// Max is exact, so the result does not depend on reduction order.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "validate.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kNB = 2;               // 16-row vocabulary blocks per wavefront
+constexpr int kKC = 128;             // K elements per LDS chunk
+constexpr int kSteps = kKC / 32;
+constexpr int kLdsRow = kKC + 8;
+static_assert(kLmRowsPerBlock == 4 * kNB * 16, "block rows");
+
+__device__ __forceinline__ unsigned long long make_key(float v, int idx) {
+  return ((unsigned long long)float_key(v) << 32) | (uint32_t)(0xffffffffu - (uint32_t)idx);
+}
+
+template <int MB>
+__global__ __launch_bounds__(kThreads) void lm_bf16_kernel(const bf16_t* __restrict__ h,
+                                                           const bf16_t* __restrict__ W, int T, int H, int V,
+                                                           unsigned long long* __restrict__ part, int nblk) {
+  constexpr int MROWS = MB * 16;
+  __shared__ __align__(16) bf16_t xl[2][MROWS][kLdsRow];
+  __shared__ unsigned long long red[4][MROWS];
+
+  const int blk = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int vbase = blk * kLmRowsPerBlock + wave * kNB * 16;
+  const bf16_t* wp[kNB];
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    const int v = min(vbase + nb * 16 + (lane & 15), V - 1);
+    wp[nb] = W + (size_t)v * H + (lane >> 4) * 8;
+  }
+  const int nK = H / 32;
+  const int nC = (H + kKC - 1) / kKC;
+  const int srow = threadIdx.x >> 4, sseg = (threadIdx.x & 15) * 8;
+
+  for (int mstart = 0; mstart < T; mstart += MROWS) {
+    const int mr = min(MROWS, T - mstart);
+    const bf16_t* src[MB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const int row = srow + 16 * i;
+      src[i] = row < mr ? h + (size_t)(mstart + row) * H + sseg : nullptr;
+    }
+    f32x4_t acc[kNB][MB];
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+      for (int i = 0; i < MB; ++i) acc[nb][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    uint4 w0[kNB][kSteps], w1[kNB][kSteps], xst[MB];
+    auto load_w = [&](int c, uint4 (*d)[kSteps]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+          const int kk = c * kSteps + s;
+          d[nb][s] = kk < nK ? ldg16_stream(wp[nb] + kk * 32) : make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    auto load_x = [&](int c) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const int kofs = c * kKC + sseg;
+        xst[i] = (src[i] && kofs < H) ? ldg16(src[i] + c * kKC) : make_uint4(0u, 0u, 0u, 0u);
+      }
+    };
+    auto store_x = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < MB; ++i) *reinterpret_cast<uint4*>(&xl[buf][srow + 16 * i][sseg]) = xst[i];
+    };
+    auto chunk = [&](int c, uint4 (*cw)[kSteps], uint4 (*nw)[kSteps]) __attribute__((always_inline)) {
+      const bool more = c + 1 < nC;
+      if (more) {
+        load_x(c + 1);
+        load_w(c + 1, nw);
+      }
+      const int buf = c & 1;
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) {
+        if (c * kSteps + s < nK) {
+#pragma unroll
+          for (int i = 0; i < MB; ++i) {
+            if (i * 16 < mr) {
+              const bf16x8_t bx = as_bf16x8(*reinterpret_cast<const uint4*>(
+                  &xl[buf][i * 16 + (lane & 15)][s * 32 + (lane >> 4) * 8]));
+#pragma unroll
+              for (int nb = 0; nb < kNB; ++nb) acc[nb][i] = mfma16x16x32(as_bf16x8(cw[nb][s]), bx, acc[nb][i]);
+            }
+          }
+        }
+      }
+      if (more) store_x(buf ^ 1);
+      __syncthreads();
+    };
+
+    load_x(0);
+    load_w(0, w0);
+    store_x(0);
+    __syncthreads();
+    for (int c = 0; c < nC; c += 2) {
+      chunk(c, w0, w1);
+      if (c + 1 < nC) chunk(c + 1, w1, w0);
+    }
+
+    // lane holds D[vocab 4*(lane/16)+v][row lane%16] of each (nb, i) block
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      if (i * 16 < mr) {
+        unsigned long long best = 0ull;
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int vocab = vbase + nb * 16 + 4 * (lane >> 4) + v;
+            const unsigned long long key = vocab < V ? make_key(acc[nb][i][v], vocab) : 0ull;
+            best = key > best ? key : best;
+          }
+        unsigned long long o = __shfl_xor(best, 16, kWave);
+        best = o > best ? o : best;
+        o = __shfl_xor(best, 32, kWave);
+        best = o > best ? o : best;
+        if (lane < 16) red[wave][i * 16 + lane] = best;
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < mr) {
+      unsigned long long best = red[0][threadIdx.x];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) best = red[w][threadIdx.x] > best ? red[w][threadIdx.x] : best;
+      part[(size_t)(mstart + threadIdx.x) * nblk + blk] = best;
+    }
+    __syncthreads();
+  }
+}
+
+// fp32 path: one thread per vocabulary row, plain sequential dot products.
+__global__ __launch_bounds__(256) void lm_f32_kernel(const float* __restrict__ h, const float* __restrict__ W,
+                                                     int T, int H, int V, unsigned long long* __restrict__ part,
+                                                     int nblk) {
+  __shared__ unsigned long long red[4];
+  const int v = blockIdx.x * kLmF32RowsPerBlock + threadIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const float* w = W + (size_t)min(v, V - 1) * H;
+  for (int t = 0; t < T; ++t) {
+    const float* x = h + (size_t)t * H;
+    float acc = 0.f;
+    for (int j = 0; j < H; ++j) acc = fmaf(w[j], x[j], acc);
+    unsigned long long key = v < V ? make_key(acc, v) : 0ull;
+    key = wave_max_u64(key);
+    if (lane == 0) red[wave] = key;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      unsigned long long best = red[0];
+      for (int i = 1; i < 4; ++i) best = red[i] > best ? red[i] : best;
+      part[(size_t)t * nblk + blockIdx.x] = best;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(64) void lm_reduce_kernel(const unsigned long long* __restrict__ part, int nblk,
+                                                       int32_t* __restrict__ ids, float* __restrict__ max_logit) {
+  const int t = blockIdx.x;
+  unsigned long long best = 0ull;
+  for (int i = threadIdx.x; i < nblk; i += kWave) {
+    const unsigned long long k = part[(size_t)t * nblk + i];
+    best = k > best ? k : best;
+  }
+  best = wave_max_u64(best);
+  if (threadIdx.x == 0) {
+    ids[t] = (int32_t)(0xffffffffu - (uint32_t)(best & 0xffffffffull));
+    if (max_logit) max_logit[t] = key_float((uint32_t)(best >> 32));
+  }
+}
+
+template <int MB>
+void launch_mb(const bf16_t* h, const bf16_t* W, int T, int H, int V, unsigned long long* part, int nblk,
+               hipStream_t s) {
+  hipLaunchKernelGGL((lm_bf16_kernel<MB>), dim3(nblk), dim3(kThreads), 0, s, h, W, T, H, V, part, nblk);
+}
+
+}  // namespace
+
+hipError_t launch_lmhead(const void* h, const void* w_lm, int T, int H, int V, int dtype,
+                         int32_t* ids, float* max_logit, void* ws, hipStream_t s) {
+  unsigned long long* part = static_cast<unsigned long long*>(ws);
+  const int nblk = lmhead_blocks(V, dtype);
+  if (dtype == kF32) {
+    hipLaunchKernelGGL(lm_f32_kernel, dim3(nblk), dim3(256), 0, s, static_cast<const float*>(h),
+                       static_cast<const float*>(w_lm), T, H, V, part, nblk);
+  } else {
+    const bf16_t* hb = static_cast<const bf16_t*>(h);
+    const bf16_t* wb = static_cast<const bf16_t*>(w_lm);
+    if (T <= 16) launch_mb<1>(hb, wb, T, H, V, part, nblk, s);
+    else if (T <= 32) launch_mb<2>(hb, wb, T, H, V, part, nblk, s);
+    else if (T <= 64) launch_mb<4>(hb, wb, T, H, V, part, nblk, s);
+    else launch_mb<8>(hb, wb, T, H, V, part, nblk, s);
+  }
+  hipLaunchKernelGGL(lm_reduce_kernel, dim3(T), dim3(64), 0, s, part, nblk, ids, max_logit);
+  return hipGetLastError();
+}
+
+}  // namespace moe

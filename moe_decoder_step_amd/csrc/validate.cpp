@@ -1,0 +1,129 @@
+// Host-side argument checks and workspace sizes of the C ABI (no HIP).
+#include "validate.hpp"
+
+namespace moe {
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool valid_dtype(int dt) { return dt == kBf16 || dt == kF32; }
+size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+}  // namespace
+
+size_t permute_ws_bytes(int T, int k, int E) {
+  if (T <= 0 || k <= 0 || E <= 0) return 0;
+  long long slots = (long long)T * k;
+  long long chunks = (slots + kPermuteChunk - 1) / kPermuteChunk;
+  if (chunks <= 1) return 0;
+  // per-chunk expert counts and per-chunk scatter bases
+  return align256((size_t)(2 * chunks * E) * sizeof(int32_t));
+}
+
+size_t swiglu_ws_bytes(int n_rows, int I, int dtype) {
+  if (n_rows <= 0 || I <= 0) return 0;
+  size_t elem = dtype == kF32 ? 4 : 2;
+  return align256((size_t)n_rows * (size_t)I * elem);  // SwiGLU activation rows
+}
+
+int lmhead_blocks(int V, int dtype) {
+  int rows = dtype == kF32 ? kLmF32RowsPerBlock : kLmRowsPerBlock;
+  return (int)(((long long)V + rows - 1) / rows);
+}
+
+size_t lmhead_ws_bytes(int T, int V, int dtype) {
+  if (T <= 0 || V <= 0) return 0;
+  // one (max logit, index) pair per row and vocabulary block
+  return align256((size_t)T * (size_t)lmhead_blocks(V, dtype) * 8);
+}
+
+int check_route(const void* h, const float* w_router, int T, int H, int E, int k, int dtype,
+                const void* xn, const int32_t* ids, const float* w) {
+  if (!valid_dtype(dtype)) return kErrUnsupported;
+  if (T < 0 || H <= 0 || E <= 0 || k <= 0 || k > E) return kErrShape;
+  if (E > kMaxExperts || H > kMaxHidden || H % 8 != 0) return kErrUnsupported;
+  if (T == 0) return kOk;
+  if (!h || !w_router || !xn || !ids || !w) return kErrNull;
+  if (!aligned16(h) || !aligned16(xn) || !aligned16(w_router)) return kErrAlign;
+  return kOk;
+}
+
+int check_permute(const int32_t* ids, int T, int k, int E, int S, const int32_t* offsets,
+                  const int32_t* gather, const int32_t* inv, const void* ws, size_t ws_bytes) {
+  if (T < 0 || k <= 0 || E <= 0 || k > E || S < 0) return kErrShape;
+  if (E > kMaxExperts || S > kMaxShared) return kErrUnsupported;
+  if ((long long)T * (k + S) > 0x7fffffffLL) return kErrUnsupported;
+  if (!offsets) return kErrNull;   // offsets are written even for T == 0
+  if (T == 0) return kOk;
+  if (!ids || !gather || !inv) return kErrNull;
+  size_t need = permute_ws_bytes(T, k, E);
+  if (need && (!ws || ws_bytes < need)) return kErrWorkspace;
+  return kOk;
+}
+
+int check_swiglu(const void* x, const int32_t* offsets, int G, int n_rows, const void* w_gate_up,
+                 const void* w_down, int T, int H, int I, int max_rows, int dtype, const void* y,
+                 const void* ws, size_t ws_bytes) {
+  if (!valid_dtype(dtype)) return kErrUnsupported;
+  if (G <= 0 || n_rows < 0 || T < 0 || H <= 0 || I <= 0 || max_rows < 0) return kErrShape;
+  if (dtype == kBf16 && (H % 32 != 0 || I % 32 != 0)) return kErrUnsupported;
+  if (dtype == kF32 && (H % 4 != 0 || I % 4 != 0)) return kErrUnsupported;
+  if (n_rows == 0 || T == 0) return kOk;
+  if (!x || !offsets || !w_gate_up || !w_down || !y) return kErrNull;
+  if (!aligned16(x) || !aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(y)) return kErrAlign;
+  size_t need = swiglu_ws_bytes(n_rows, I, dtype);
+  if (!ws || ws_bytes < need) return kErrWorkspace;
+  if (!aligned16(ws)) return kErrAlign;
+  return kOk;
+}
+
+int check_combine(const void* y, const int32_t* inv, const float* topk_w, const void* y_shared,
+                  int S, const void* residual, int T, int H, int k, int n_rows, int dtype,
+                  const void* out, const void* combined) {
+  if (!valid_dtype(dtype)) return kErrUnsupported;
+  if (T < 0 || H <= 0 || k < 0 || S < 0 || n_rows < 0) return kErrShape;
+  if (H % 8 != 0) return kErrUnsupported;
+  if (k > 0 && n_rows <= 0 && T > 0) return kErrShape;
+  if (S > 0 && !y_shared) return kErrNull;
+  if (T == 0) return kOk;
+  if (!out || (k > 0 && (!y || !inv || !topk_w))) return kErrNull;
+  if ((y && !aligned16(y)) || (y_shared && !aligned16(y_shared)) || (residual && !aligned16(residual)) ||
+      !aligned16(out) || (combined && !aligned16(combined)))
+    return kErrAlign;
+  return kOk;
+}
+
+int check_lmhead(const void* h, const void* w_lm, int T, int H, int V, int dtype,
+                 const int32_t* ids, const void* ws, size_t ws_bytes) {
+  if (!valid_dtype(dtype)) return kErrUnsupported;
+  if (T < 0 || H <= 0 || V <= 0) return kErrShape;
+  if (dtype == kBf16 && H % 32 != 0) return kErrUnsupported;
+  if (dtype == kF32 && H % 4 != 0) return kErrUnsupported;
+  if (T == 0) return kOk;
+  if (!h || !w_lm || !ids) return kErrNull;
+  if (!aligned16(h) || !aligned16(w_lm)) return kErrAlign;
+  size_t need = lmhead_ws_bytes(T, V, dtype);
+  if (!ws || ws_bytes < need) return kErrWorkspace;
+  if (!aligned16(ws)) return kErrAlign;
+  return kOk;
+}
+
+int check_verify(const int32_t* drafts, const int32_t* argmax_ids, int B, int K,
+                 const int32_t* accepted, const int32_t* committed, const int32_t* n_commit) {
+  if (B < 0 || K < 0) return kErrShape;
+  if (K > kMaxDrafts) return kErrUnsupported;
+  if (B == 0) return kOk;
+  if ((K > 0 && !drafts) || !argmax_ids || !accepted || !committed || !n_commit) return kErrNull;
+  return kOk;
+}
+
+int check_plant(const int32_t* argmax_ids, const uint8_t* keep, const int32_t* repl, int B, int K,
+                int V, const int32_t* drafts) {
+  if (B < 0 || K < 0 || V <= 1) return kErrShape;
+  if (K > kMaxDrafts) return kErrUnsupported;
+  if (B == 0 || K == 0) return kOk;
+  if (!argmax_ids || !keep || !repl || !drafts) return kErrNull;
+  return kOk;
+}
+
+}  // namespace moe

@@ -1,0 +1,44 @@
+// Host-side argument checks and workspace sizes of the C ABI.
+// Pure C++ (no HIP): these run before anything is enqueued.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+enum Status { kOk = 0, kErrNull = 1, kErrShape = 2, kErrUnsupported = 3, kErrAlign = 4,
+              kErrWorkspace = 5, kErrHip = 6 };
+enum Dtype { kBf16 = 0, kF32 = 1 };
+
+constexpr int kMaxExperts = 64;      // one router lane per expert in a wavefront
+constexpr int kMaxHidden = 2048;     // route kernel keeps a block's normed rows in LDS
+constexpr int kMaxShared = 8;
+constexpr int kMaxDrafts = 15;
+constexpr int kPermuteChunk = 4096;  // slots per block of the permutation kernels
+constexpr int kLmRowsPerBlock = 128; // vocabulary rows per LM-head block (bf16 path)
+constexpr int kLmF32RowsPerBlock = 256;
+
+size_t permute_ws_bytes(int T, int k, int E);
+size_t swiglu_ws_bytes(int n_rows, int I, int dtype);
+size_t lmhead_ws_bytes(int T, int V, int dtype);
+int lmhead_blocks(int V, int dtype);
+
+int check_route(const void* h, const float* w_router, int T, int H, int E, int k, int dtype,
+                const void* xn, const int32_t* ids, const float* w);
+int check_permute(const int32_t* ids, int T, int k, int E, int S, const int32_t* offsets,
+                  const int32_t* gather, const int32_t* inv, const void* ws, size_t ws_bytes);
+int check_swiglu(const void* x, const int32_t* offsets, int G, int n_rows, const void* w_gate_up,
+                 const void* w_down, int T, int H, int I, int max_rows, int dtype, const void* y,
+                 const void* ws, size_t ws_bytes);
+int check_combine(const void* y, const int32_t* inv, const float* topk_w, const void* y_shared,
+                  int S, const void* residual, int T, int H, int k, int n_rows, int dtype,
+                  const void* out, const void* combined);
+int check_lmhead(const void* h, const void* w_lm, int T, int H, int V, int dtype,
+                 const int32_t* ids, const void* ws, size_t ws_bytes);
+int check_verify(const int32_t* drafts, const int32_t* argmax_ids, int B, int K,
+                 const int32_t* accepted, const int32_t* committed, const int32_t* n_commit);
+int check_plant(const int32_t* argmax_ids, const uint8_t* keep, const int32_t* repl, int B, int K,
+                int V, const int32_t* drafts);
+
+}  // namespace moe

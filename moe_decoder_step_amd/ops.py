@@ -1,0 +1,208 @@
+"""Python names of the C-ABI calls, taking torch tensors.
+
+Argument marshalling only: every wrapper checks dtypes and devices, passes
+data pointers and the current HIP stream to libmoestep, and raises MoeError on
+a non-zero status.  Output tensors are passed in by the caller (the `*_alloc`
+helpers allocate them with torch first, for tests and one-off calls).
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib as L
+
+__all__ = [
+    "moe_route", "moe_permute", "moe_grouped_swiglu", "moe_combine", "lmhead_argmax",
+    "spec_verify", "spec_plant_drafts", "permute_workspace_bytes", "swiglu_workspace_bytes",
+    "lmhead_workspace_bytes", "dtype_code", "route_alloc", "permute_alloc", "swiglu_alloc",
+    "combine_alloc", "lmhead_alloc", "verify_alloc",
+]
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return L.BF16
+    if t.dtype == torch.float32:
+        return L.F32
+    raise TypeError(f"unsupported storage dtype {t.dtype}")
+
+
+def _need(t, dtype, name):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def permute_workspace_bytes(T: int, k: int, E: int) -> int:
+    return int(L.load().moe_permute_workspace_bytes(T, k, E))
+
+
+def swiglu_workspace_bytes(n_rows: int, I: int, dtype: torch.dtype) -> int:
+    return int(L.load().moe_grouped_swiglu_workspace_bytes(n_rows, I, L.BF16 if dtype == torch.bfloat16 else L.F32))
+
+
+def lmhead_workspace_bytes(T: int, V: int, dtype: torch.dtype) -> int:
+    return int(L.load().lmhead_argmax_workspace_bytes(T, V, L.BF16 if dtype == torch.bfloat16 else L.F32))
+
+
+def moe_route(h, w_router, bias, k, xn, topk_ids, topk_w, logits=None, gain=None, eps=1e-6,
+              norm=True, renormalize=True):
+    """RMSNorm + router logits + top-k + routing weights (see moe_route in moestep.h)."""
+    T, H = h.shape
+    E = w_router.shape[0]
+    for t, d, n in ((h, None, "h"), (xn, h.dtype, "xn"), (w_router, torch.float32, "w_router"),
+                    (bias, torch.float32, "bias"), (gain, torch.float32, "gain"),
+                    (topk_ids, torch.int32, "topk_ids"), (topk_w, torch.float32, "topk_w"),
+                    (logits, torch.float32, "logits")):
+        _need(t, d, n)
+    flags = (L.ROUTE_NORM if norm else 0) | (L.ROUTE_RENORM if renormalize else 0)
+    L.check("moe_route", L.load().moe_route(
+        _p(h), _p(gain), float(eps), _p(w_router), _p(bias), T, H, E, k, flags, dtype_code(h),
+        _p(xn), _p(topk_ids), _p(topk_w), _p(logits), _stream(h)))
+
+
+def moe_permute(topk_ids, E, S, offsets, gather, inv, ws=None):
+    """Stable counting sort of the (token, slot) pairs by expert (+ shared groups)."""
+    T, k = topk_ids.shape
+    for t, n in ((topk_ids, "topk_ids"), (offsets, "offsets"), (gather, "gather"), (inv, "inv")):
+        _need(t, torch.int32, n)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    L.check("moe_permute", L.load().moe_permute(
+        _p(topk_ids), T, k, E, S, _p(offsets), _p(gather), _p(inv), _p(ws), nbytes, _stream(topk_ids)))
+
+
+def moe_grouped_swiglu(x, gather, offsets, w_gate_up, w_down, y, ws, max_rows=None):
+    """SwiGLU expert FFN over the rows of each group (routed and shared alike)."""
+    T, H = x.shape
+    G, I2, _ = w_gate_up.shape
+    n_rows = y.shape[0]
+    for t, d, n in ((x, None, "x"), (gather, torch.int32, "gather"), (offsets, torch.int32, "offsets"),
+                    (w_gate_up, x.dtype, "w_gate_up"), (w_down, x.dtype, "w_down"), (y, x.dtype, "y"), (ws, None, "ws")):
+        _need(t, d, n)
+    L.check("moe_grouped_swiglu", L.load().moe_grouped_swiglu(
+        _p(x), _p(gather), _p(offsets), G, n_rows, _p(w_gate_up), _p(w_down), T, H, I2 // 2,
+        T if max_rows is None else int(max_rows), dtype_code(x), _p(y), _p(ws),
+        ws.numel() * ws.element_size(), _stream(x)))
+
+
+def moe_combine(y, inv, topk_w, y_shared, S, residual, out, combined=None):
+    """out = residual + sum_j w_j y[inv] + sum_s y_shared (fixed order, fp32)."""
+    T, k = topk_w.shape
+    H = out.shape[1]
+    for t, d, n in ((y, out.dtype, "y"), (inv, torch.int32, "inv"), (topk_w, torch.float32, "topk_w"),
+                    (y_shared, out.dtype, "y_shared"), (residual, out.dtype, "residual"), (out, None, "out"),
+                    (combined, out.dtype, "combined")):
+        _need(t, d, n)
+    L.check("moe_combine", L.load().moe_combine(
+        _p(y), _p(inv), _p(topk_w), _p(y_shared), S, _p(residual), T, H, k, y.shape[0], dtype_code(out),
+        _p(out), _p(combined), _stream(out)))
+
+
+def lmhead_argmax(h, w_lm, argmax_ids, max_logit, ws):
+    """Greedy token per row: argmax of h @ W_lm^T, ties to the lowest id."""
+    T, H = h.shape
+    V = w_lm.shape[0]
+    for t, d, n in ((h, None, "h"), (w_lm, h.dtype, "w_lm"), (argmax_ids, torch.int32, "argmax_ids"),
+                    (max_logit, torch.float32, "max_logit"), (ws, None, "ws")):
+        _need(t, d, n)
+    L.check("lmhead_argmax", L.load().lmhead_argmax(
+        _p(h), _p(w_lm), T, H, V, dtype_code(h), _p(argmax_ids), _p(max_logit), _p(ws),
+        ws.numel() * ws.element_size(), _stream(h)))
+
+
+def spec_verify(drafts, argmax_ids, accepted, committed, n_commit):
+    """Greedy longest-prefix acceptance + bonus token per sequence."""
+    B, K = drafts.shape
+    for t, n in ((drafts, "drafts"), (argmax_ids, "argmax_ids"), (accepted, "accepted"),
+                 (committed, "committed"), (n_commit, "n_commit")):
+        _need(t, torch.int32, n)
+    L.check("spec_verify", L.load().spec_verify(
+        _p(drafts), _p(argmax_ids), B, K, _p(accepted), _p(committed), _p(n_commit), _stream(argmax_ids)))
+
+
+def spec_plant_drafts(argmax_ids, keep, repl, V, drafts):
+    """Benchmark harness: drafts equal to the verifier's tokens where `keep`, else a different id."""
+    B, K = keep.shape
+    _need(argmax_ids, torch.int32, "argmax_ids")
+    _need(keep, torch.uint8, "keep")
+    _need(repl, torch.int32, "repl")
+    _need(drafts, torch.int32, "drafts")
+    L.check("spec_plant_drafts", L.load().spec_plant_drafts(
+        _p(argmax_ids), _p(keep), _p(repl), B, K, V, _p(drafts), _stream(argmax_ids)))
+
+
+# ------------------------------------------------------------------ allocating helpers
+
+def route_alloc(h, w_router, bias, k, with_logits=True, **kw):
+    T, H = h.shape
+    E = w_router.shape[0]
+    xn = torch.empty_like(h)
+    ids = torch.empty((T, k), dtype=torch.int32, device=h.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=h.device)
+    lg = torch.empty((T, E), dtype=torch.float32, device=h.device) if with_logits else None
+    moe_route(h, w_router, bias, k, xn, ids, w, lg, **kw)
+    return xn, ids, w, lg
+
+
+def permute_alloc(topk_ids, E, S):
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    offsets = torch.empty(E + S + 1, dtype=torch.int32, device=dev)
+    gather = torch.empty(T * k + S * T, dtype=torch.int32, device=dev)
+    inv = torch.empty(T * k, dtype=torch.int32, device=dev)
+    nb = permute_workspace_bytes(T, k, E)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev) if nb else None
+    moe_permute(topk_ids, E, S, offsets, gather, inv, ws)
+    return offsets, gather, inv
+
+
+def swiglu_alloc(x, gather, offsets, w_gate_up, w_down, n_rows, max_rows=None):
+    I = w_down.shape[2]
+    y = torch.zeros((n_rows, x.shape[1]), dtype=x.dtype, device=x.device)
+    ws = torch.empty(max(swiglu_workspace_bytes(n_rows, I, x.dtype), 16), dtype=torch.uint8, device=x.device)
+    moe_grouped_swiglu(x, gather, offsets, w_gate_up, w_down, y, ws, max_rows)
+    return y
+
+
+def combine_alloc(y, inv, topk_w, y_shared, S, residual, with_combined=True):
+    T = topk_w.shape[0]
+    H = y.shape[1]
+    out = torch.empty((T, H), dtype=y.dtype, device=y.device)
+    comb = torch.empty_like(out) if with_combined else None
+    moe_combine(y, inv, topk_w, y_shared, S, residual, out, comb)
+    return out, comb
+
+
+def lmhead_alloc(h, w_lm):
+    T = h.shape[0]
+    ids = torch.empty(T, dtype=torch.int32, device=h.device)
+    mx = torch.empty(T, dtype=torch.float32, device=h.device)
+    ws = torch.empty(max(lmhead_workspace_bytes(T, w_lm.shape[0], h.dtype), 16), dtype=torch.uint8, device=h.device)
+    lmhead_argmax(h, w_lm, ids, mx, ws)
+    return ids, mx
+
+
+def verify_alloc(drafts, argmax_ids):
+    B, K = drafts.shape
+    dev = drafts.device
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    com = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    nc = torch.empty(B, dtype=torch.int32, device=dev)
+    spec_verify(drafts, argmax_ids, acc, com, nc)
+    return acc, com, nc

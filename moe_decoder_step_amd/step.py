@@ -1,0 +1,112 @@
+"""The speculative verify step, driven through the C-ABI calls.
+
+A VerifyStack holds one model's device-resident weights and the buffers of
+one batch (allocated once, for the largest batch it will see).  A verify
+pass of T = B*(K+1) positions runs, per MoE layer,
+
+    moe_route -> moe_permute -> moe_grouped_swiglu -> moe_combine
+
+(the residual add is fused into the combine, in place on the hidden state),
+then lmhead_argmax over all positions and spec_verify per sequence.  Every
+step runs in libmoestep's HIP kernels; torch only owns memory and streams.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import ops
+
+
+class VerifyStack:
+    def __init__(self, layers: list[dict], w_lm: torch.Tensor | None, E: int, k: int, S: int,
+                 max_tokens: int, max_seqs: int = 0, K: int = 0, eps: float = 1e-6,
+                 keep_logits: bool = False):
+        self.layers = layers
+        self.w_lm = w_lm
+        # when a list: (start, end) torch.cuda.Event pairs around every grouped
+        # SwiGLU launch, recorded on the stream the kernels run on
+        self.ffn_events = None
+        self.E, self.k, self.S, self.eps = E, k, S, eps
+        wgu = layers[0]["w_gate_up"]
+        self.dtype = wgu.dtype
+        self.device = wgu.device
+        self.H = wgu.shape[2]
+        self.I = wgu.shape[1] // 2
+        self.max_tokens = T = max_tokens
+        dev, H = self.device, self.H
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.h = torch.empty((T, H), dtype=self.dtype, device=dev)
+        self.xn = torch.empty((T, H), dtype=self.dtype, device=dev)
+        self.ids = torch.empty((T, k), **i32)
+        self.tw = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.logits = torch.empty((T, E), dtype=torch.float32, device=dev) if keep_logits else None
+        self.offsets = torch.empty(E + S + 1, **i32)
+        self.gather = torch.empty(T * k + S * T, **i32)
+        self.inv = torch.empty(T * k, **i32)
+        nb = ops.permute_workspace_bytes(T, k, E)
+        self.pws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+        self.n_rows = T * k + S * T
+        self.y = torch.empty((self.n_rows, H), dtype=self.dtype, device=dev)
+        self.sws = torch.empty(max(ops.swiglu_workspace_bytes(self.n_rows, self.I, self.dtype), 16),
+                               dtype=torch.uint8, device=dev)
+        if w_lm is not None:
+            V = w_lm.shape[0]
+            self.argmax = torch.empty(T, **i32)
+            self.max_logit = torch.empty(T, dtype=torch.float32, device=dev)
+            self.lws = torch.empty(max(ops.lmhead_workspace_bytes(T, V, self.dtype), 16), dtype=torch.uint8,
+                                   device=dev)
+        if max_seqs:
+            self.accepted = torch.empty(max_seqs, **i32)
+            self.committed = torch.empty((max_seqs, K + 1), **i32)
+            self.n_commit = torch.empty(max_seqs, **i32)
+
+    def layer(self, li: int, T: int) -> None:
+        """One MoE block in place on self.h[:T]."""
+        E, k, S = self.E, self.k, self.S
+        w = self.layers[li]
+        h = self.h[:T]
+        ops.moe_route(h, w["w_router"], w.get("bias"), k, self.xn[:T], self.ids[:T], self.tw[:T],
+                      None if self.logits is None else self.logits[:T], eps=self.eps)
+        ops.moe_permute(self.ids[:T], E, S, self.offsets, self.gather[:T * k + S * T], self.inv[:T * k], self.pws)
+        n_rows = T * k + S * T
+        y = self.y[:n_rows]
+        if self.ffn_events is not None:
+            ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            ev[0].record()
+        ops.moe_grouped_swiglu(self.xn[:T], self.gather[:n_rows], self.offsets, w["w_gate_up"], w["w_down"], y,
+                               self.sws, max_rows=T)
+        if self.ffn_events is not None:
+            ev[1].record()
+            self.ffn_events.append(ev)
+        ops.moe_combine(y[:T * k], self.inv[:T * k], self.tw[:T], y[T * k:] if S else None, S, h, h)
+
+    def forward(self, h_in: torch.Tensor, record: list | None = None) -> torch.Tensor:
+        """All MoE blocks on a copy of h_in; returns the final hidden state (a view).
+
+        With `record` (a list), a copy of every block's input, expert ids and
+        routing weights is appended to it (for teacher-forced comparison)."""
+        T = h_in.shape[0]
+        self.h[:T].copy_(h_in)
+        for li in range(len(self.layers)):
+            inp = self.h[:T].clone() if record is not None else None
+            self.layer(li, T)
+            if record is not None:
+                record.append({"input": inp, "ids": self.ids[:T].clone(), "w": self.tw[:T].clone(),
+                               "output": self.h[:T].clone()})
+        return self.h[:T]
+
+    def head(self, T: int) -> None:
+        ops.lmhead_argmax(self.h[:T], self.w_lm, self.argmax[:T], self.max_logit[:T], self.lws)
+
+    def verify(self, drafts: torch.Tensor) -> None:
+        B, K = drafts.shape
+        ops.spec_verify(drafts, self.argmax[:B * (K + 1)].view(B, K + 1), self.accepted[:B],
+                        self.committed[:B], self.n_commit[:B])
+
+    def step(self, h_in: torch.Tensor, drafts: torch.Tensor, record: list | None = None) -> None:
+        """One verify pass: blocks, LM-head argmax, acceptance (results in self.*)."""
+        T = h_in.shape[0]
+        self.forward(h_in, record)
+        self.head(T)
+        self.verify(drafts)

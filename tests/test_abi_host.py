@@ -1,0 +1,123 @@
+"""The C-ABI library on the host: it loads, exports every function the header
+declares, and its argument checks return the documented status codes before
+anything reaches the GPU (no compute calls here)."""
+
+import ctypes
+
+import pytest
+
+import moe_decoder_step_amd as m
+from moe_decoder_step_amd import _lib as L
+
+P = ctypes.c_void_p
+A = P(0x100000)        # aligned, never dereferenced: checks fail before any use
+MIS = P(0x100004)      # misaligned
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return L.load()
+
+
+def test_exports_every_declared_function(lib):
+    names = L.header_functions()
+    assert len(names) == 12
+    assert set(names) == set(L.SIGNATURES)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.moe_abi_version() == 1
+    for s in range(7):
+        assert lib.moe_status_str(s)
+    assert lib.moe_status_str(99) == b"unknown status"
+
+
+def test_workspace_queries(lib):
+    assert lib.moe_permute_workspace_bytes(128, 6, 64) == 0            # one chunk: no scratch
+    n_chunks = (36992 * 6 + 4095) // 4096
+    assert lib.moe_permute_workspace_bytes(36992, 6, 64) >= 2 * n_chunks * 64 * 4
+    assert lib.moe_grouped_swiglu_workspace_bytes(1024, 896, m.BF16) >= 1024 * 896 * 2
+    assert lib.moe_grouped_swiglu_workspace_bytes(1024, 896, m.F32) >= 1024 * 896 * 4
+    assert lib.lmhead_argmax_workspace_bytes(128, 129280, m.BF16) >= 128 * 1010 * 8
+    assert lib.lmhead_argmax_workspace_bytes(0, 129280, m.BF16) == 0
+
+
+def test_route_checks(lib):
+    f = lib.moe_route
+    base = dict(h=A, gain=None, eps=1e-6, w=A, b=None, T=4, H=128, E=8, k=2, flags=3, dt=m.BF16,
+                xn=A, ids=A, tw=A, lg=None, s=None)
+
+    def call(**kw):
+        a = {**base, **kw}
+        return f(a["h"], a["gain"], a["eps"], a["w"], a["b"], a["T"], a["H"], a["E"], a["k"], a["flags"],
+                 a["dt"], a["xn"], a["ids"], a["tw"], a["lg"], a["s"])
+    assert call(h=None) == L.ERR_NULL
+    assert call(ids=None) == L.ERR_NULL
+    assert call(T=-1) == L.ERR_SHAPE
+    assert call(k=9) == L.ERR_SHAPE
+    assert call(k=0) == L.ERR_SHAPE
+    assert call(E=65, k=6) == L.ERR_UNSUPPORTED
+    assert call(H=100) == L.ERR_UNSUPPORTED
+    assert call(H=4096) == L.ERR_UNSUPPORTED
+    assert call(dt=7) == L.ERR_UNSUPPORTED
+    assert call(h=MIS) == L.ERR_ALIGN
+    assert call(T=0, h=None) == L.OK        # empty batch: no-op
+
+
+def test_permute_checks(lib):
+    f = lib.moe_permute
+    assert f(A, 4, 2, 8, 2, None, A, A, None, 0, None) == L.ERR_NULL
+    assert f(None, 4, 2, 8, 2, A, A, A, None, 0, None) == L.ERR_NULL
+    assert f(A, 4, 9, 8, 2, A, A, A, None, 0, None) == L.ERR_SHAPE
+    assert f(A, 4, 2, 8, -1, A, A, A, None, 0, None) == L.ERR_SHAPE
+    assert f(A, 4, 2, 80, 2, A, A, A, None, 0, None) == L.ERR_UNSUPPORTED
+    assert f(A, 4, 2, 8, 9, A, A, A, None, 0, None) == L.ERR_UNSUPPORTED
+    # multi-chunk sizes need a workspace
+    assert f(A, 36992, 6, 64, 2, A, A, A, None, 0, None) == L.ERR_WORKSPACE
+    assert f(A, 36992, 6, 64, 2, A, A, A, A, 16, None) == L.ERR_WORKSPACE
+
+
+def test_swiglu_checks(lib):
+    f = lib.moe_grouped_swiglu
+    need = lib.moe_grouped_swiglu_workspace_bytes(40, 896, m.BF16)
+
+    def call(x=A, off=A, G=66, n=40, wgu=A, wd=A, T=4, H=1280, I=896, mr=4, dt=m.BF16, y=A, ws=A, wsb=need):
+        return f(x, None, off, G, n, wgu, wd, T, H, I, mr, dt, y, ws, wsb, None)
+    assert call(off=None) == L.ERR_NULL
+    assert call(y=None) == L.ERR_NULL
+    assert call(G=0) == L.ERR_SHAPE
+    assert call(n=-1) == L.ERR_SHAPE
+    assert call(H=1288) == L.ERR_UNSUPPORTED          # bf16 needs H % 32 == 0
+    assert call(I=900) == L.ERR_UNSUPPORTED
+    assert call(wgu=MIS) == L.ERR_ALIGN
+    assert call(ws=None) == L.ERR_WORKSPACE
+    assert call(wsb=need - 1) == L.ERR_WORKSPACE
+    assert call(n=0, x=None) == L.OK
+
+
+def test_combine_lmhead_verify_plant_checks(lib):
+    assert lib.moe_combine(A, A, A, None, 2, A, 4, 1280, 6, 40, m.BF16, A, None, None) == L.ERR_NULL
+    assert lib.moe_combine(A, None, A, A, 2, A, 4, 1280, 6, 40, m.BF16, A, None, None) == L.ERR_NULL
+    assert lib.moe_combine(A, A, A, A, 2, A, 4, 1284, 6, 40, m.BF16, A, None, None) == L.ERR_UNSUPPORTED
+    assert lib.moe_combine(A, A, A, A, 2, A, 4, 1280, 6, 40, m.BF16, MIS, None, None) == L.ERR_ALIGN
+    assert lib.moe_combine(A, A, A, A, 2, A, 0, 1280, 6, 40, m.BF16, A, None, None) == L.OK
+    need = lib.lmhead_argmax_workspace_bytes(4, 129280, m.BF16)
+    assert lib.lmhead_argmax(A, A, 4, 1280, 129280, m.BF16, A, None, A, need - 8, None) == L.ERR_WORKSPACE
+    assert lib.lmhead_argmax(A, None, 4, 1280, 129280, m.BF16, A, None, A, need, None) == L.ERR_NULL
+    assert lib.lmhead_argmax(A, A, 4, 1280, 0, m.BF16, A, None, A, need, None) == L.ERR_SHAPE
+    assert lib.spec_verify(A, A, 4, 16, A, A, A, None) == L.ERR_UNSUPPORTED
+    assert lib.spec_verify(A, A, 4, -1, A, A, A, None) == L.ERR_SHAPE
+    assert lib.spec_verify(None, A, 4, 3, A, A, A, None) == L.ERR_NULL
+    assert lib.spec_verify(None, A, 0, 3, None, None, None, None) == L.OK
+    assert lib.spec_plant_drafts(A, A, A, 4, 3, 1, A, None) == L.ERR_SHAPE
+    assert lib.spec_plant_drafts(A, None, A, 4, 3, 10, A, None) == L.ERR_NULL
+
+
+def test_binding_raises_without_gpu_tensors():
+    import torch
+    h = torch.zeros(4, 128)
+    with pytest.raises(ValueError):
+        m.moe_route(h, torch.zeros(8, 128), None, 2, torch.zeros_like(h), torch.zeros(4, 2, dtype=torch.int32),
+                    torch.zeros(4, 2))

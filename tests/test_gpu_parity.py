@@ -1,0 +1,237 @@
+"""Per-op and per-layer parity of the HIP path against the fp64 oracle.
+
+Every call goes through the C ABI (via the Python binding) on seeded
+synthetic inputs and is compared element by element with the oracle in the
+rounding mode of its storage dtype: ids, permutations and accepted lengths
+bit-exact (oracle near-ties below 1e-6 flagged), floating-point outputs within
+max|d|/max(1,|ref|) <= 2e-2 (bf16) or 1e-4 (fp32).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from tests._util import BF16_TOL, F32_TOL, as_f64, assert_close, compare_ids, host
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def m():
+    import moe_decoder_step_amd as mod
+    mod.load()
+    assert torch.cuda.is_available(), "GPU tests need a device"
+    return mod
+
+
+def _layer(sh, seed, device=DEV):
+    return synth.layer_weights(seed, 0, sh, device)
+
+
+def _host_layer(w):
+    return {k: host(v) for k, v in w.items()}
+
+
+# --------------------------------------------------------------------------- route
+
+@pytest.mark.parametrize("shape,T", [("tiny", 16), ("layer128", 128), ("layer128", 1), ("layer128", 37),
+                                     ("layer128", 300)])
+def test_route(m, shape, T):
+    sh = synth.SHAPES[shape]
+    w = _layer(sh, 1)
+    h = synth.hidden(2, T, sh.H, sh.torch_dtype, DEV)
+    bias = synth.normal(5, (sh.E,), 0.01, torch.float32, "cpu").to(DEV)   # non-zero bias exercises the add
+    xn, ids, tw, lg = m.route_alloc(h, w["w_router"], bias, sh.k)
+    torch.cuda.synchronize()
+    mode = sh.dtype
+    ref = O.route(host(h), host(w["w_router"]), host(bias), sh.k, sh.eps, mode)
+    # xn is the correctly rounded RMSNorm: bit-exact against the oracle's rounding
+    np.testing.assert_array_equal(as_f64(xn), ref["xn"])
+    # logits: fp32 accumulation of the same inputs
+    lref = O.router_logits(ref["xn"], O.f64(host(w["w_router"])), O.f64(host(bias)))
+    assert_close(as_f64(lg), lref, F32_TOL, "logits")
+    nflag, flagged = compare_ids(ids.cpu().numpy(), ref["ids"], ref["gap"], "topk ids")
+    ok = ~flagged
+    assert_close(tw.cpu().numpy()[ok], ref["w"][ok], F32_TOL, "topk weights")
+
+
+def test_route_full_softmax_and_no_norm(m):
+    sh = synth.SHAPES["layer128"]
+    w = _layer(sh, 1)
+    h = synth.hidden(3, 64, sh.H, torch.bfloat16, DEV)
+    xn, ids, tw, _ = m.route_alloc(h, w["w_router"], None, 6, renormalize=False)
+    ref = O.route(host(h), host(w["w_router"]), None, 6, sh.eps, "bf16", renormalize=False)
+    _, flagged = compare_ids(ids.cpu().numpy(), ref["ids"], ref["gap"], "ids")
+    assert_close(tw.cpu().numpy()[~flagged], ref["w"][~flagged], F32_TOL, "full-softmax weights")
+    xn2, ids2, tw2, _ = m.route_alloc(h, w["w_router"], None, 6, norm=False)
+    torch.cuda.synchronize()
+    assert torch.equal(xn2, h)
+    ref2 = O.route(host(h), host(w["w_router"]), None, 6, sh.eps, "bf16", norm=False)
+    compare_ids(ids2.cpu().numpy(), ref2["ids"], ref2["gap"], "ids without norm")
+
+
+def test_route_zero_router_tie_rule(m):
+    """All logits equal: experts 0..k-1, weights 1/k (the lower-id tie rule)."""
+    h = synth.hidden(4, 9, 1280, torch.bfloat16, DEV)
+    wr = torch.zeros(64, 1280, device=DEV)
+    _, ids, tw, _ = m.route_alloc(h, wr, None, 6)
+    assert (ids.cpu() == torch.arange(6, dtype=torch.int32)).all()
+    assert torch.allclose(tw.cpu(), torch.full((9, 6), 1 / 6))
+
+
+# --------------------------------------------------------------------------- permute
+
+@pytest.mark.parametrize("T,k,E,S", [(16, 2, 8, 2), (128, 6, 64, 2), (1, 6, 64, 2), (37, 6, 64, 0),
+                                     (700, 6, 64, 2), (4096, 6, 64, 2), (5000, 3, 17, 1)])
+def test_permute(m, T, k, E, S):
+    g = torch.Generator().manual_seed(T * 131 + E)
+    ids = torch.stack([torch.randperm(E, generator=g)[:k] for _ in range(T)]).to(torch.int32)
+    if T > 64:   # skewed load: a few hot experts
+        hot = torch.randint(0, 3, (T,), generator=g)
+        ids[:, 0] = torch.where(hot == 0, ids[:, 0], ids[:, 0] % 4)   # may repeat an id within a token
+    off, gat, inv = m.permute_alloc(ids.to(DEV), E, S)
+    roff, rgat, rinv = O.permute(ids.numpy(), E, S)
+    np.testing.assert_array_equal(off.cpu().numpy(), roff)
+    np.testing.assert_array_equal(gat.cpu().numpy(), rgat)
+    np.testing.assert_array_equal(inv.cpu().numpy(), rinv)
+
+
+# --------------------------------------------------------------------------- grouped SwiGLU
+
+@pytest.mark.parametrize("shape,T", [("tiny", 16), ("layer128", 128), ("layer128", 4), ("layer128", 37),
+                                     ("layer128", 200)])
+def test_grouped_swiglu(m, shape, T):
+    sh = synth.SHAPES[shape]
+    w = _layer(sh, 1)
+    h = synth.hidden(2, T, sh.H, sh.torch_dtype, DEV)
+    xn, ids, tw, _ = m.route_alloc(h, w["w_router"], None, sh.k)
+    off, gat, inv = m.permute_alloc(ids, sh.E, sh.S)
+    n_rows = T * sh.k + sh.S * T
+    y = m.swiglu_alloc(xn, gat, off, w["w_gate_up"], w["w_down"], n_rows, max_rows=T)
+    torch.cuda.synchronize()
+    # oracle: every group on the GPU's own xn and permutation
+    xh = O.f64(host(xn))
+    offh, gath = off.cpu().numpy(), gat.cpu().numpy()
+    wgu, wd = host(w["w_gate_up"]), host(w["w_down"])
+    yg = as_f64(y)
+    for g in range(sh.E + sh.S):
+        a, b = offh[g], offh[g + 1]
+        if a == b:
+            continue
+        ref = O.swiglu(xh[gath[a:b]], wgu[g], wd[g], sh.dtype)
+        assert_close(yg[a:b], ref, BF16_TOL if sh.dtype == "bf16" else F32_TOL, f"group {g}")
+
+
+def test_grouped_swiglu_identity_gather_and_skewed_groups(m):
+    """gather = NULL (row r of a group reads token r - offsets[g]); groups of
+    0, 1, 15, 16, 17, 33, 100 rows (ragged M-blocks, several row blocks)."""
+    H, I, T = 1280, 896, 100
+    counts = [0, 1, 15, 16, 17, 33, 100, 0]
+    G = len(counts)
+    gen = torch.Generator(device=DEV).manual_seed(7)
+    x = (torch.randn(T, H, generator=gen, device=DEV)).to(torch.bfloat16)
+    wgu = (torch.randn(G, 2 * I, H, generator=gen, device=DEV) * 0.02).to(torch.bfloat16)
+    wd = (torch.randn(G, H, I, generator=gen, device=DEV) * 0.02).to(torch.bfloat16)
+    off = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32, device=DEV)
+    n_rows = int(sum(counts))
+    for max_rows in (16, 100):
+        y = m.swiglu_alloc(x, None, off, wgu, wd, n_rows, max_rows=max_rows)
+        torch.cuda.synchronize()
+        xh, yg = O.f64(host(x)), as_f64(y)
+        for g, c in enumerate(counts):
+            a = int(off[g])
+            if c:
+                ref = O.swiglu(xh[:c], host(wgu[g]), host(wd[g]), "bf16")
+                assert_close(yg[a:a + c], ref, BF16_TOL, f"group {g} ({c} rows, max_rows {max_rows})")
+
+
+# --------------------------------------------------------------------------- combine
+
+@pytest.mark.parametrize("dtype,T,k,S", [(torch.bfloat16, 128, 6, 2), (torch.float32, 16, 2, 2),
+                                         (torch.bfloat16, 5, 6, 0), (torch.bfloat16, 3, 1, 1)])
+def test_combine(m, dtype, T, k, S):
+    H = 1280 if dtype == torch.bfloat16 else 128
+    gen = torch.Generator(device=DEV).manual_seed(11)
+    n_rows = T * k + S * T
+    y = torch.randn(n_rows, H, generator=gen, device=DEV).to(dtype)
+    inv = torch.randperm(T * k, generator=gen, device=DEV).to(torch.int32)
+    tw = torch.rand(T, k, generator=gen, device=DEV)
+    res = torch.randn(T, H, generator=gen, device=DEV).to(dtype)
+    out, comb = m.combine_alloc(y[:T * k], inv, tw, y[T * k:] if S else None, S, res)
+    torch.cuda.synchronize()
+    yh, rh = O.f64(host(y)), O.f64(host(res))
+    invh, twh = inv.cpu().numpy(), tw.cpu().numpy().astype(np.float64)
+    c = np.zeros((T, H))
+    for t in range(T):
+        for j in range(k):
+            c[t] += twh[t, j] * yh[invh[t * k + j]]
+        for s in range(S):
+            c[t] += yh[T * k + s * T + t]
+    mode = "bf16" if dtype == torch.bfloat16 else "f32"
+    tol = BF16_TOL if dtype == torch.bfloat16 else F32_TOL
+    assert_close(as_f64(comb), O.store(c, mode), tol, "combined")
+    assert_close(as_f64(out), O.store(rh + c, mode), tol, "out")
+    # in place: out aliases residual
+    res2 = res.clone()
+    m.moe_combine(y[:T * k], inv, tw, y[T * k:] if S else None, S, res2, res2)
+    torch.cuda.synchronize()
+    assert torch.equal(res2, out)
+
+
+# --------------------------------------------------------------------------- LM head
+
+@pytest.mark.parametrize("dtype,T,H,V", [(torch.float32, 16, 128, 512), (torch.bfloat16, 4, 1280, 129280),
+                                         (torch.bfloat16, 128, 1280, 20000), (torch.bfloat16, 37, 1280, 1003),
+                                         (torch.bfloat16, 1, 64, 77), (torch.bfloat16, 200, 256, 5000)])
+def test_lmhead_argmax(m, dtype, T, H, V):
+    gen = torch.Generator(device=DEV).manual_seed(T + V)
+    h = torch.randn(T, H, generator=gen, device=DEV).to(dtype)
+    W = (torch.randn(V, H, generator=gen, device=DEV) * 0.02).to(dtype)
+    ids, mx = m.lmhead_alloc(h, W)
+    torch.cuda.synchronize()
+    rid, rmx, gap = O.lm_argmax(host(h), host(W))
+    nflag, flagged = compare_ids(ids.cpu().numpy(), rid, gap, "argmax")
+    assert_close(mx.cpu().numpy()[~flagged], rmx[~flagged], F32_TOL, "max logit")
+
+
+def test_lmhead_ties_go_to_lowest_id(m):
+    H, V = 256, 3000
+    gen = torch.Generator(device=DEV).manual_seed(3)
+    W = (torch.randn(V, H, generator=gen, device=DEV) * 0.02).to(torch.bfloat16)
+    W[2900] = W[17]
+    W[1500] = W[17]
+    h = (W[17:18].float() * 50).to(torch.bfloat16).repeat(3, 1)
+    ids, _ = m.lmhead_alloc(h, W)
+    assert (ids.cpu() == 17).all()
+
+
+# --------------------------------------------------------------------------- verify / plant
+
+@pytest.mark.parametrize("B,K", [(32, 3), (1, 3), (7, 0), (100, 1), (3, 15)])
+def test_spec_verify_and_plant(m, B, K):
+    g = torch.Generator().manual_seed(B * 17 + K)
+    V = 5
+    argmax = torch.randint(0, V, (B, K + 1), generator=g, dtype=torch.int32)
+    drafts = torch.randint(0, V, (B, K), generator=g, dtype=torch.int32)
+    acc, com, nc = m.verify_alloc(drafts.to(DEV), argmax.to(DEV))
+    racc, rcom, rnc = O.spec_verify(drafts.numpy(), argmax.numpy())
+    np.testing.assert_array_equal(acc.cpu().numpy(), racc)
+    np.testing.assert_array_equal(com.cpu().numpy(), rcom)
+    np.testing.assert_array_equal(nc.cpu().numpy(), rnc)
+    if K:
+        keep = (torch.rand(B, K, generator=g) < 0.576).to(torch.uint8)
+        repl = torch.randint(0, V - 1, (B, K), generator=g, dtype=torch.int32)
+        d = torch.empty(B, K, dtype=torch.int32, device=DEV)
+        m.spec_plant_drafts(argmax.to(DEV), keep.to(DEV), repl.to(DEV), V, d)
+        np.testing.assert_array_equal(d.cpu().numpy(), O.plant_drafts(argmax.numpy(), keep.numpy(), repl.numpy()))
+
+
+def test_out_of_vocab_draft_is_a_mismatch(m):
+    argmax = torch.tensor([[5, 6, 7, 8]], dtype=torch.int32, device=DEV)
+    drafts = torch.tensor([[5, 2 ** 31 - 1, 7]], dtype=torch.int32, device=DEV)
+    acc, com, nc = m.verify_alloc(drafts, argmax)
+    assert acc.item() == 1 and nc.item() == 2 and com.cpu().tolist() == [[5, 6, -1, -1]]

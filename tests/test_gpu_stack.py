@@ -1,0 +1,155 @@
+"""Whole verify passes through the C ABI against the fp64 oracle.
+
+Layer outputs are compared with the oracle run from the GPU's own stored
+layer input (teacher forcing: a bf16 rounding difference in one layer would
+otherwise be amplified by the next and make an exact-id comparison
+meaningless), and the LM head from the GPU's final hidden state.  Expert ids,
+argmax tokens and accepted lengths are bit-exact outside oracle near-ties.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from tests._util import BF16_TOL, F32_TOL, as_f64, assert_close, compare_ids, host
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def m():
+    import moe_decoder_step_amd as mod
+    mod.load()
+    return mod
+
+
+def _stack(m, sh, seed, T, device=DEV, L=None):
+    layers = [synth.layer_weights(seed, l, sh, device) for l in range(L or sh.L)]
+    w_lm = synth.lm_weight(seed, sh, device) if sh.V else None
+    st = m.VerifyStack(layers, w_lm, sh.E, sh.k, sh.S, max_tokens=T, max_seqs=max(T // sh.P, 1), K=sh.K)
+    return st, layers, w_lm
+
+
+def _check_layers(record, layers, sh, mode):
+    """Teacher-forced per-layer comparison; returns total near-tie flags."""
+    tol = BF16_TOL if mode == "bf16" else F32_TOL
+    flags = 0
+    for li, (rec, w) in enumerate(zip(record, layers)):
+        hw = {k: host(v) for k, v in w.items()}
+        ref = O.moe_layer(host(rec["input"]), hw, sh.k, sh.eps, mode)
+        n, flagged = compare_ids(rec["ids"].cpu().numpy(), ref["route"]["ids"], ref["route"]["gap"], f"layer {li} ids")
+        flags += n
+        ok = ~flagged
+        assert_close(rec["w"].cpu().numpy()[ok], ref["route"]["w"][ok], F32_TOL, f"layer {li} weights")
+        assert_close(as_f64(rec["output"])[ok], ref["h_out"][ok], tol, f"layer {li} output")
+    return flags
+
+
+def test_tiny_verify_pass(m):
+    """1 layer, hidden 128, 8+2 experts (I=64), top-2, vocab 512, 4 x 4 tokens,
+    fp32; drafts uniform from seed 0."""
+    sh = synth.SHAPES["tiny"]
+    st, layers, w_lm = _stack(m, sh, 0, sh.T)
+    h = synth.hidden(0, sh.T, sh.H, torch.float32, DEV)
+    drafts = synth.uniform_ids(0, (sh.B, sh.K), sh.V).to(DEV)
+    rec = []
+    st.step(h, drafts, rec)
+    torch.cuda.synchronize()
+    _check_layers(rec, layers, sh, "f32")
+    rid, rmx, gap = O.lm_argmax(host(st.h[:sh.T]), host(w_lm))
+    _, flagged = compare_ids(st.argmax[:sh.T].cpu().numpy(), rid, gap, "argmax")
+    assert not flagged.any()
+    racc, rcom, rnc = O.spec_verify(drafts.cpu().numpy(), rid.reshape(sh.B, sh.P))
+    np.testing.assert_array_equal(st.accepted[:sh.B].cpu().numpy(), racc)
+    np.testing.assert_array_equal(st.committed[:sh.B].cpu().numpy(), rcom)
+    np.testing.assert_array_equal(st.n_commit[:sh.B].cpu().numpy(), rnc)
+    # free-running oracle (no teacher forcing) agrees too at fp32
+    full = O.verify_step(host(h), [{k: host(v) for k, v in w.items()} for w in layers], host(w_lm),
+                         drafts.cpu().numpy(), sh.k, sh.eps, "f32")
+    np.testing.assert_array_equal(full["argmax"], rid)
+    assert_close(as_f64(st.h[:sh.T]), full["layers"][-1]["h_out"], F32_TOL, "final hidden (free-running)")
+
+
+def test_real_shape_layer_128_tokens(m):
+    """One real-shape layer (hidden 1280, 64+2 experts, I=896, top-6) at 32 x 4 tokens."""
+    sh = synth.SHAPES["layer128"]
+    st, layers, _ = _stack(m, sh, 1, sh.T)
+    h = synth.hidden(2, sh.T, sh.H, torch.bfloat16, DEV)
+    rec = []
+    st.forward(h, rec)
+    torch.cuda.synchronize()
+    _check_layers(rec, layers, sh, "bf16")
+    # every expert touched at least once at this batch size (the weight-bound regime)
+    assert len(np.unique(rec[0]["ids"].cpu().numpy())) >= 60
+
+
+@pytest.mark.parametrize("steps", [3])
+def test_batch1_stack_teacher_forced(m, steps):
+    """12 layers + LM head 1280 x 129,280 + acceptance at 1 x 4 tokens, drafts
+    planted from the oracle's own argmax with keep probability 0.576."""
+    sh = synth.SHAPES["batch1"]
+    st, layers, w_lm = _stack(m, sh, 0, sh.T)
+    keep, repl = synth.plant_schedule(0, steps, sh.B, sh.K, sh.V, 0.576)
+    for s in range(steps):
+        h = synth.hidden(s, sh.T, sh.H, torch.bfloat16, DEV, name="step_hidden")
+        rec = []
+        st.forward(h, rec)
+        st.head(sh.T)
+        torch.cuda.synchronize()
+        _check_layers(rec, layers, sh, "bf16")
+        rid, rmx, gap = O.lm_argmax(host(st.h[:sh.T]), host(w_lm))
+        _, flagged = compare_ids(st.argmax[:sh.T].cpu().numpy(), rid, gap, "argmax")
+        g = rid.reshape(sh.B, sh.P)
+        drafts = O.plant_drafts(g, keep[s].numpy(), repl[s].numpy())
+        st.verify(torch.from_numpy(drafts.astype(np.int32)).to(DEV))
+        racc, rcom, rnc = O.spec_verify(drafts, g)
+        if not flagged.any():
+            np.testing.assert_array_equal(st.accepted[:1].cpu().numpy(), racc)
+            np.testing.assert_array_equal(st.committed[:1].cpu().numpy(), rcom)
+            # planted drafts: accepted = leading keeps (the model does not matter)
+            lead = next((i for i in range(sh.K) if not keep[s, 0, i]), sh.K)
+            assert racc[0] == lead
+
+
+def test_full_step_128_tokens(m):
+    """The benchmarked workload: 12 layers + LM head + acceptance at 32 x 4 tokens."""
+    sh = synth.SHAPES["step128"]
+    st, layers, w_lm = _stack(m, sh, 0, sh.T)
+    h = synth.hidden(0, sh.T, sh.H, torch.bfloat16, DEV, name="step_hidden")
+    drafts = synth.uniform_ids(0, (sh.B, sh.K), sh.V).to(DEV)
+    rec = []
+    st.step(h, drafts, rec)
+    torch.cuda.synchronize()
+    _check_layers(rec, layers, sh, "bf16")
+    rid, rmx, gap = O.lm_argmax(host(st.h[:sh.T]), host(w_lm))
+    _, flagged = compare_ids(st.argmax[:sh.T].cpu().numpy(), rid, gap, "argmax")
+    assert_close(st.max_logit[:sh.T].cpu().numpy()[~flagged], rmx[~flagged], F32_TOL, "max logit")
+    racc, rcom, rnc = O.spec_verify(drafts.cpu().numpy(), st.argmax[:sh.T].cpu().numpy().reshape(sh.B, sh.P))
+    np.testing.assert_array_equal(st.accepted[:sh.B].cpu().numpy(), racc)
+    np.testing.assert_array_equal(st.n_commit[:sh.B].cpu().numpy(), rnc)
+
+
+def test_determinism_and_batch_invariance(m):
+    """Two runs are bit-identical, and a token's result does not depend on the
+    other tokens of its batch (needed for speculative == greedy on the GPU)."""
+    sh = synth.SHAPES["step128"]
+    st, layers, w_lm = _stack(m, sh, 0, sh.T, L=3)
+    h = synth.hidden(9, sh.T, sh.H, torch.bfloat16, DEV)
+    st.forward(h)
+    st.head(sh.T)
+    out1, ids1 = st.h[:sh.T].clone(), st.argmax[:sh.T].clone()
+    st.forward(h)
+    st.head(sh.T)
+    assert torch.equal(out1, st.h[:sh.T]) and torch.equal(ids1, st.argmax[:sh.T])
+    for sub in (slice(0, 4), slice(60, 61), slice(100, 128)):
+        hs = h[sub].contiguous()
+        n = hs.shape[0]
+        st.forward(hs)
+        st.head(n)
+        torch.cuda.synchronize()
+        assert torch.equal(st.h[:n], out1[sub]), f"hidden of rows {sub} depends on the batch"
+        assert torch.equal(st.argmax[:n], ids1[sub])
