@@ -163,6 +163,7 @@ int moe_grouped_swiglu(const void* x, const int32_t* gather, const int32_t* offs
  * residual [T,H] dtype or NULL                           in
  * out      [T,H] dtype, may alias residual               out
  * combined [T,H] dtype or NULL: c[t] before the residual out
+ * Limits: H % 8 == 0, 0 <= k <= 64.
  * ------------------------------------------------------------------------- */
 int moe_combine(const void* y, const int32_t* inv, const float* topk_w,
                 const void* y_shared, int S, const void* residual,

@@ -3,6 +3,7 @@
 // One block per token row; each thread owns 8 consecutive hidden elements
 // (one 16-byte vector for bf16) and sums its k routed rows and S shared rows
 // in a fixed order in fp32, so a token's result never depends on the batch.
+// The k row indices and weights are read once per block into LDS.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "validate.hpp"
@@ -10,7 +11,7 @@
 namespace moe {
 namespace {
 
-constexpr int kThreads = 128;
+constexpr int kThreads = 256;  // one thread per 8 elements of the row (H <= 2048 in one pass)
 
 __device__ __forceinline__ void load8(const bf16_t* p, float* f) { unpack8(ldg16(p), f); }
 __device__ __forceinline__ void load8(const float* p, float* f) {
@@ -36,14 +37,20 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
     const St* __restrict__ ys, int S, const St* res, int T, int H, int k, int n_rows, St* out,
     St* __restrict__ combined) {
   const int t = blockIdx.x;
+  __shared__ int rows[kMaxExperts];
+  __shared__ float wk[kMaxExperts];
+  if (threadIdx.x < k) {
+    rows[threadIdx.x] = clampi(inv[(size_t)t * k + threadIdx.x], 0, n_rows - 1);
+    wk[threadIdx.x] = w[(size_t)t * k + threadIdx.x];
+  }
+  __syncthreads();
   for (int c = threadIdx.x * 8; c < H; c += kThreads * 8) {
     float acc[8], f[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
     for (int j = 0; j < k; ++j) {
-      const int r = clampi(inv[(size_t)t * k + j], 0, n_rows - 1);
-      const float wj = w[(size_t)t * k + j];
-      load8(y + (size_t)r * H + c, f);
+      const float wj = wk[j];
+      load8(y + (size_t)rows[j] * H + c, f);
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, f[i], acc[i]);
     }

@@ -104,4 +104,14 @@ __device__ __forceinline__ uint4 ldg16_stream(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Block barrier for data exchanged through LDS only.  __syncthreads() carries
+// a workgroup-scope fence over all memory, which waits for every outstanding
+// global load; restricting the fence to LDS keeps a weight stream in flight
+// across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 }  // namespace moe

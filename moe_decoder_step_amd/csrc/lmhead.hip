@@ -54,11 +54,15 @@ __global__ __launch_bounds__(kThreads) void lm_bf16_kernel(const bf16_t* __restr
 
   for (int mstart = 0; mstart < T; mstart += MROWS) {
     const int mr = min(MROWS, T - mstart);
+    // rows past T point at a valid row and are zeroed after the load: no
+    // load is conditional, so the compiler can keep the weight stream in flight
     const bf16_t* src[MB];
+    bool xvalid[MB];
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
       const int row = srow + 16 * i;
-      src[i] = row < mr ? h + (size_t)(mstart + row) * H + sseg : nullptr;
+      xvalid[i] = row < mr;
+      src[i] = h + (size_t)(mstart + min(row, mr - 1)) * H;
     }
     f32x4_t acc[kNB][MB];
 #pragma unroll
@@ -67,58 +71,67 @@ __global__ __launch_bounds__(kThreads) void lm_bf16_kernel(const bf16_t* __restr
       for (int i = 0; i < MB; ++i) acc[nb][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     uint4 w0[kNB][kSteps], w1[kNB][kSteps], xst[MB];
+    bool xok[MB];
     auto load_w = [&](int c, uint4 (*d)[kSteps]) __attribute__((always_inline)) {
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
-        for (int s = 0; s < kSteps; ++s) {
-          const int kk = c * kSteps + s;
-          d[nb][s] = kk < nK ? ldg16_stream(wp[nb] + kk * 32) : make_uint4(0u, 0u, 0u, 0u);
-        }
+        for (int s = 0; s < kSteps; ++s) d[nb][s] = ldg16_stream(wp[nb] + min(c * kSteps + s, nK - 1) * 32);
     };
     auto load_x = [&](int c) __attribute__((always_inline)) {
+      const int kofs = c * kKC + sseg;
+      const bool kin = kofs < H;
+      const int kc = min(kofs, H - 8);
 #pragma unroll
       for (int i = 0; i < MB; ++i) {
-        const int kofs = c * kKC + sseg;
-        xst[i] = (src[i] && kofs < H) ? ldg16(src[i] + c * kKC) : make_uint4(0u, 0u, 0u, 0u);
+        xst[i] = ldg16(src[i] + kc);
+        xok[i] = kin && xvalid[i];
       }
     };
     auto store_x = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < MB; ++i) *reinterpret_cast<uint4*>(&xl[buf][srow + 16 * i][sseg]) = xst[i];
+      for (int i = 0; i < MB; ++i) {
+        const uint4 v = xst[i];
+        const bool ok = xok[i];  // masked here, after the MFMAs, not at the load
+        *reinterpret_cast<uint4*>(&xl[buf][srow + 16 * i][sseg]) =
+            make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+      }
     };
-    auto chunk = [&](int c, uint4 (*cw)[kSteps], uint4 (*nw)[kSteps]) __attribute__((always_inline)) {
-      const bool more = c + 1 < nC;
-      if (more) {
-        load_x(c + 1);
-        load_w(c + 1, nw);
-      }
-      const int buf = c & 1;
+    auto mma = [&](int buf, uint4 (*cw)[kSteps]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int s = 0; s < kSteps; ++s) {
-        if (c * kSteps + s < nK) {
+      for (int s = 0; s < kSteps; ++s)
 #pragma unroll
-          for (int i = 0; i < MB; ++i) {
-            if (i * 16 < mr) {
-              const bf16x8_t bx = as_bf16x8(*reinterpret_cast<const uint4*>(
-                  &xl[buf][i * 16 + (lane & 15)][s * 32 + (lane >> 4) * 8]));
+        for (int i = 0; i < MB; ++i) {
+          const bf16x8_t bx = as_bf16x8(*reinterpret_cast<const uint4*>(
+              &xl[buf][i * 16 + (lane & 15)][s * 32 + (lane >> 4) * 8]));
 #pragma unroll
-              for (int nb = 0; nb < kNB; ++nb) acc[nb][i] = mfma16x16x32(as_bf16x8(cw[nb][s]), bx, acc[nb][i]);
-            }
-          }
+          for (int nb = 0; nb < kNB; ++nb) acc[nb][i] = mfma16x16x32(as_bf16x8(cw[nb][s]), bx, acc[nb][i]);
         }
-      }
-      if (more) store_x(buf ^ 1);
-      __syncthreads();
+    };
+    auto step_pf = [&](int c, uint4 (*cw)[kSteps], uint4 (*nw)[kSteps]) __attribute__((always_inline)) {
+      load_x(c + 1);
+      load_w(c + 1, nw);
+      __builtin_amdgcn_sched_barrier(0);  // issue the whole prefetch before any MFMA
+      mma(c & 1, cw);
+      __builtin_amdgcn_sched_barrier(0);
+      store_x((c + 1) & 1);
+      lds_barrier();
     };
 
     load_x(0);
     load_w(0, w0);
     store_x(0);
-    __syncthreads();
-    for (int c = 0; c < nC; c += 2) {
-      chunk(c, w0, w1);
-      if (c + 1 < nC) chunk(c + 1, w1, w0);
+    lds_barrier();
+    int c = 0;
+    for (; c + 2 < nC; c += 2) {
+      step_pf(c, w0, w1);
+      step_pf(c + 1, w1, w0);
+    }
+    if (nC - c == 2) {
+      step_pf(c, w0, w1);
+      mma((c + 1) & 1, w1);
+    } else {
+      mma(c & 1, w0);
     }
 
     // lane holds D[vocab 4*(lane/16)+v][row lane%16] of each (nb, i) block
@@ -141,14 +154,14 @@ __global__ __launch_bounds__(kThreads) void lm_bf16_kernel(const bf16_t* __restr
         if (lane < 16) red[wave][i * 16 + lane] = best;
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (threadIdx.x < mr) {
       unsigned long long best = red[0][threadIdx.x];
 #pragma unroll
       for (int w = 1; w < 4; ++w) best = red[w][threadIdx.x] > best ? red[w][threadIdx.x] : best;
       part[(size_t)(mstart + threadIdx.x) * nblk + blk] = best;
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 

@@ -1,12 +1,15 @@
 // moe_permute: stable counting sort of the T*k (token, slot) pairs by expert.
 //
-// Slots are cut into chunks of 4096.  Within a chunk, wavefront w owns the
-// experts e = w, w+16, ...; it walks the chunk 64 slots at a time and ranks the
-// slots of its expert with a ballot and a popcount, which keeps ascending
-// slot (= token) order without atomics, so the result is deterministic.
-// One chunk (T*k <= 4096, every decode batch) is a single block; larger
-// inputs take a histogram pass, a one-block scan over (chunk, expert) and a
-// scatter pass.
+// Slots are cut into chunks of 4096 = 64 pieces of 64 slots, one piece per
+// wavefront pass.  For a piece, the wavefront takes one ballot per expert:
+// the popcount of the lanes below a slot in its expert's ballot is the slot's
+// rank inside the piece, and the ballot's popcount is the expert's count in
+// the piece.  A scan of the counts over pieces (per expert) and over experts
+// turns ranks into rows.  Ranks follow slot order, so the sort is stable
+// (ascending token inside an expert) and deterministic, with no atomics.
+// One chunk (every decode batch) is a single block; larger inputs take a
+// count pass, a one-block scan over (chunk, expert) and a scatter pass that
+// re-ranks its chunk.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "validate.hpp"
@@ -15,27 +18,61 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / kWave;
+constexpr int kWaves = kThreads / kWave;                // 16
+constexpr int kPieces = kPermuteChunk / kWave;          // 64 pieces per chunk
+constexpr int kPiecesPerWave = kPieces / kWaves;        // 4
 
-// Rank and scatter the slots of one chunk.  sid: the chunk's expert ids (LDS),
-// base[e]: first row of expert e for this chunk.
-__device__ void scatter_chunk(const int* sid, int n, int slot0, int k, int E, const int* base,
-                              int32_t* __restrict__ gather, int32_t* __restrict__ inv) {
+// Rank the slots of one chunk.  Fills pcount[p][e] (count of expert e in
+// piece p; lanes >= E write nothing) and, per pass pi, the lane's expert and
+// rank inside its piece.
+__device__ __forceinline__ void rank_chunk(const int32_t* __restrict__ ids, int s0, int n, int E,
+                                           int (*pcount)[kMaxExperts], int* my_e, int* my_rank) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const unsigned long long below = (1ull << lane) - 1ull;
-  for (int e = wave; e < E; e += kWaves) {
-    int run = base[e];
-    for (int p = 0; p < n; p += kWave) {
-      const int s = p + lane;
-      const bool mine = s < n && sid[s] == e;
-      const unsigned long long mask = __ballot(mine);
-      if (mine) {
-        const int pos = run + __popcll(mask & below);
-        const int slot = slot0 + s;
-        gather[pos] = slot / k;
-        inv[slot] = pos;
+#pragma unroll
+  for (int pi = 0; pi < kPiecesPerWave; ++pi) {
+    const int p = wave + kWaves * pi;
+    const int s = p * kWave + lane;
+    const int e = s < n ? clampi(ids[s0 + s], 0, E - 1) : -1;
+    int rank = 0, cnt = 0;
+    if (p * kWave < n) {
+      for (int ee = 0; ee < E; ++ee) {
+        const unsigned long long b = __ballot(e == ee);
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0));
+        if (e == ee) rank = below;
+        if (lane == ee) cnt = __popcll(b);
       }
-      run += __popcll(mask);
+      if (lane < E) pcount[p][lane] = cnt;
+    }
+    my_e[pi] = e;
+    my_rank[pi] = rank;
+  }
+}
+
+// Exclusive scan of pcount[.][e] over the pieces of a chunk, in place; returns
+// the chunk total of expert e (threads e < E only).
+__device__ __forceinline__ int scan_pieces(int (*pcount)[kMaxExperts], int n_pieces, int e) {
+  int run = 0;
+  for (int p = 0; p < n_pieces; ++p) {
+    const int c = pcount[p][e];
+    pcount[p][e] = run;
+    run += c;
+  }
+  return run;
+}
+
+__device__ __forceinline__ void scatter_chunk(int s0, int n, int k, const int* base,
+                                              int (*pcount)[kMaxExperts], const int* my_e, const int* my_rank,
+                                              int32_t* __restrict__ gather, int32_t* __restrict__ inv) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int pi = 0; pi < kPiecesPerWave; ++pi) {
+    const int p = wave + kWaves * pi;
+    const int s = p * kWave + lane;
+    if (s < n) {
+      const int e = my_e[pi];
+      const int pos = base[e] + pcount[p][e] + my_rank[pi];
+      gather[pos] = (s0 + s) / k;
+      inv[s0 + s] = pos;
     }
   }
 }
@@ -45,51 +82,64 @@ __device__ void fill_shared_rows(int T, int k, int S, int32_t* __restrict__ gath
   for (long long i = start; i < n; i += stride) gather[base + i] = (int32_t)(i % T);
 }
 
+// exclusive scan over experts by one wavefront: base[e], offsets[0..E], shared offsets
+__device__ __forceinline__ void scan_experts(const int* tot, int E, int S, int T, int* base,
+                                             int32_t* __restrict__ offsets) {
+  const int e = threadIdx.x;
+  const int c = e < E ? tot[e] : 0;
+  int incl = c;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int v = __shfl_up(incl, o, kWave);
+    if (e >= o) incl += v;
+  }
+  const int total = __shfl(incl, kWave - 1, kWave);
+  if (e < E) {
+    base[e] = incl - c;
+    offsets[e] = incl - c;
+  }
+  if (e == 0) offsets[E] = total;
+  if (e < S) offsets[E + 1 + e] = total + (e + 1) * T;
+}
+
 __global__ __launch_bounds__(kThreads) void permute_one_block(const int32_t* __restrict__ ids, int T, int k,
                                                               int E, int S, int32_t* __restrict__ offsets,
                                                               int32_t* __restrict__ gather,
                                                               int32_t* __restrict__ inv) {
-  __shared__ int sid[kPermuteChunk];
-  __shared__ int cnt[kMaxExperts];
+  __shared__ int pcount[kPieces][kMaxExperts];
+  __shared__ int tot[kMaxExperts];
   __shared__ int base[kMaxExperts];
   const int n = T * k;
-  if (threadIdx.x < kMaxExperts) cnt[threadIdx.x] = 0;
-  for (int i = threadIdx.x; i < n; i += kThreads) sid[i] = clampi(ids[i], 0, E - 1);
+  const int n_pieces = (n + kWave - 1) / kWave;
+  int my_e[kPiecesPerWave], my_rank[kPiecesPerWave];
+  rank_chunk(ids, 0, n, E, pcount, my_e, my_rank);
   __syncthreads();
-  for (int i = threadIdx.x; i < n; i += kThreads) atomicAdd(&cnt[sid[i]], 1);
+  if (threadIdx.x < E) tot[threadIdx.x] = scan_pieces(pcount, n_pieces, threadIdx.x);
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int e = 0; e < E; ++e) {
-      base[e] = acc;
-      offsets[e] = acc;
-      acc += cnt[e];
-    }
-    offsets[E] = acc;
-    for (int s = 0; s < S; ++s) offsets[E + 1 + s] = acc + (s + 1) * T;
-  }
+  if (threadIdx.x < kWave) scan_experts(tot, E, S, T, base, offsets);
   __syncthreads();
-  scatter_chunk(sid, n, 0, k, E, base, gather, inv);
+  scatter_chunk(0, n, k, base, pcount, my_e, my_rank, gather, inv);
   fill_shared_rows(T, k, S, gather, threadIdx.x, kThreads);
 }
 
-__global__ __launch_bounds__(kThreads) void permute_hist(const int32_t* __restrict__ ids, int n_slots, int E,
-                                                         int32_t* __restrict__ counts) {
-  __shared__ int cnt[kMaxExperts];
-  if (threadIdx.x < kMaxExperts) cnt[threadIdx.x] = 0;
-  __syncthreads();
+// count pass: per-chunk expert totals
+__global__ __launch_bounds__(kThreads) void permute_count(const int32_t* __restrict__ ids, int n_slots, int E,
+                                                          int32_t* __restrict__ counts) {
+  __shared__ int pcount[kPieces][kMaxExperts];
   const int s0 = blockIdx.x * kPermuteChunk;
   const int n = min(kPermuteChunk, n_slots - s0);
-  for (int i = threadIdx.x; i < n; i += kThreads) atomicAdd(&cnt[clampi(ids[s0 + i], 0, E - 1)], 1);
+  const int n_pieces = (n + kWave - 1) / kWave;
+  int my_e[kPiecesPerWave], my_rank[kPiecesPerWave];
+  rank_chunk(ids, s0, n, E, pcount, my_e, my_rank);
   __syncthreads();
-  if (threadIdx.x < E) counts[blockIdx.x * E + threadIdx.x] = cnt[threadIdx.x];
+  if (threadIdx.x < E) counts[blockIdx.x * E + threadIdx.x] = scan_pieces(pcount, n_pieces, threadIdx.x);
 }
 
 // One block of 64 threads: thread e walks the chunks in order.
 __global__ __launch_bounds__(64) void permute_scan(const int32_t* __restrict__ counts, int n_chunks, int E,
                                                    int S, int T, int32_t* __restrict__ bases,
                                                    int32_t* __restrict__ offsets) {
-  __shared__ int total[kMaxExperts];
+  __shared__ int tot[kMaxExperts];
   __shared__ int first[kMaxExperts];
   const int e = threadIdx.x;
   if (e < E) {
@@ -98,19 +148,10 @@ __global__ __launch_bounds__(64) void permute_scan(const int32_t* __restrict__ c
       bases[c * E + e] = run;
       run += counts[c * E + e];
     }
-    total[e] = run;
+    tot[e] = run;
   }
   __syncthreads();
-  if (e == 0) {
-    int acc = 0;
-    for (int i = 0; i < E; ++i) {
-      first[i] = acc;
-      offsets[i] = acc;
-      acc += total[i];
-    }
-    offsets[E] = acc;
-    for (int s = 0; s < S; ++s) offsets[E + 1 + s] = acc + (s + 1) * T;
-  }
+  scan_experts(tot, E, S, T, first, offsets);
   __syncthreads();
   if (e < E)
     for (int c = 0; c < n_chunks; ++c) bases[c * E + e] += first[e];
@@ -120,15 +161,19 @@ __global__ __launch_bounds__(kThreads) void permute_scatter(const int32_t* __res
                                                             int E, int S, const int32_t* __restrict__ bases,
                                                             int32_t* __restrict__ gather,
                                                             int32_t* __restrict__ inv) {
-  __shared__ int sid[kPermuteChunk];
+  __shared__ int pcount[kPieces][kMaxExperts];
   __shared__ int base[kMaxExperts];
   const int n_slots = T * k;
   const int s0 = blockIdx.x * kPermuteChunk;
   const int n = min(kPermuteChunk, n_slots - s0);
-  for (int i = threadIdx.x; i < n; i += kThreads) sid[i] = clampi(ids[s0 + i], 0, E - 1);
+  const int n_pieces = (n + kWave - 1) / kWave;
+  int my_e[kPiecesPerWave], my_rank[kPiecesPerWave];
+  rank_chunk(ids, s0, n, E, pcount, my_e, my_rank);
   if (threadIdx.x < E) base[threadIdx.x] = bases[blockIdx.x * E + threadIdx.x];
   __syncthreads();
-  scatter_chunk(sid, n, s0, k, E, base, gather, inv);
+  if (threadIdx.x < E) scan_pieces(pcount, n_pieces, threadIdx.x);
+  __syncthreads();
+  scatter_chunk(s0, n, k, base, pcount, my_e, my_rank, gather, inv);
   fill_shared_rows(T, k, S, gather, blockIdx.x * kThreads + threadIdx.x, gridDim.x * kThreads);
 }
 
@@ -144,7 +189,7 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int S, int32_
   }
   int32_t* counts = static_cast<int32_t*>(ws);
   int32_t* bases = counts + (size_t)n_chunks * E;
-  hipLaunchKernelGGL(permute_hist, dim3(n_chunks), dim3(kThreads), 0, s, ids, n_slots, E, counts);
+  hipLaunchKernelGGL(permute_count, dim3(n_chunks), dim3(kThreads), 0, s, ids, n_slots, E, counts);
   hipLaunchKernelGGL(permute_scan, dim3(1), dim3(64), 0, s, counts, n_chunks, E, S, T, bases, offsets);
   hipLaunchKernelGGL(permute_scatter, dim3(n_chunks), dim3(kThreads), 0, s, ids, T, k, E, S, bases, gather, inv);
   return hipGetLastError();

@@ -1,13 +1,18 @@
 // moe_route: pre-RMSNorm, fp32 router logits and top-k routing of each token.
 //
-// One block of 4 wavefronts handles 4*TPW tokens; each wavefront owns TPW
-// tokens from the norm to the top-k, so the only block-wide traffic is the
-// router weight, staged through LDS 64 hidden elements at a time and shared
-// by all of the block's tokens.  In the logit and top-k phases lane e is
-// expert e (E <= 64 routed experts), so the top-k is k rounds of a
-// wavefront-wide max over (logit, lower id) keys and needs no sort.
-#include <type_traits>
-
+// A block of 8 wavefronts owns TPB tokens:
+//   1. norm: wavefront w normalises tokens w, w+8, ... (fp64 scale, one
+//      rounding to the storage type) into LDS and to xn;
+//   2. logits: the hidden dimension is split in eight slices, one per
+//      wavefront; lane e (= expert e, E <= 64) accumulates its slice of
+//      l[t,e] for all TPB tokens in fp32, reading its router row with 16-byte
+//      loads and the normed tokens from LDS (broadcast);
+//   3. top-k: wavefront w sums the eight slices in order (a fixed order that
+//      does not depend on the batch), adds the bias and runs k rounds of a
+//      wavefront-wide max over 64-bit (logit, lower id) keys, then the
+//      softmax weights.
+// Decode batches use 2 tokens per block so that a 128-token batch spreads
+// over 64 blocks; large batches use up to 16 to amortise the router reads.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "validate.hpp"
@@ -15,21 +20,14 @@
 namespace moe {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kChunk = 64;        // hidden elements of the router weight per LDS pass
-constexpr int kWtStride = 65;     // padded LDS row (conflict-free transpose)
+constexpr int kWaves = 8;      // wavefronts per block (hidden split in 8 slices)
+constexpr int kThreads = kWaves * 64;
 
-template <typename St> struct Vec8;
-template <> struct Vec8<bf16_t> {
-  static __device__ __forceinline__ void load(const bf16_t* p, float* f) { unpack8(ldg16(p), f); }
-};
-template <> struct Vec8<float> {
-  static __device__ __forceinline__ void load(const float* p, float* f) {
-    float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
-    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
-  }
-};
-
+__device__ __forceinline__ void load8(const bf16_t* p, float* f) { unpack8(ldg16(p), f); }
+__device__ __forceinline__ void load8(const float* p, float* f) {
+  float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
 __device__ __forceinline__ void store8(bf16_t* p, const bf16_t* v) {
   uint4 o;
   o.x = pack2(v[0], v[1]); o.y = pack2(v[2], v[3]); o.z = pack2(v[4], v[5]); o.w = pack2(v[6], v[7]);
@@ -39,40 +37,43 @@ __device__ __forceinline__ void store8(float* p, const float* v) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
   *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
-
 __device__ __forceinline__ bf16_t round_store(double v, bf16_t*) { return f64_to_bf16(v); }
 __device__ __forceinline__ float round_store(double v, float*) { return (float)v; }
 
-__device__ __forceinline__ float lds_val(const bf16_t* p) { return bf16_to_f32(*p); }
-__device__ __forceinline__ float lds_val(const float* p) { return *p; }
+// four consecutive normed values of a token from LDS
+__device__ __forceinline__ float4 lds4(const bf16_t* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+}
+__device__ __forceinline__ float4 lds4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 
-template <typename St, int TPW>
-__global__ __launch_bounds__(256) void route_kernel(
+template <typename St, int TPB>
+__global__ __launch_bounds__(kThreads) void route_kernel(
     const St* __restrict__ h, const float* __restrict__ gain, float eps,
     const float* __restrict__ wr, const float* __restrict__ bias, int T, int H, int E, int k,
     int flags, St* __restrict__ xn, int32_t* __restrict__ ids, float* __restrict__ wts,
     float* __restrict__ logits) {
-  constexpr int TPB = TPW * kWaves;
   extern __shared__ __align__(16) char smem[];
   St* xs = reinterpret_cast<St*>(smem);
-  float* wt = reinterpret_cast<float*>(smem + ((TPB * H * (int)sizeof(St) + 15) & ~15));
+  float* part = reinterpret_cast<float*>(smem + ((TPB * H * (int)sizeof(St) + 15) & ~15));  // [kWaves][TPB][64]
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int tbase = blockIdx.x * TPB + wave * TPW;
+  const int t0 = blockIdx.x * TPB;
 
-  // ---- RMSNorm: xn = h / sqrt(mean(h^2) + eps) * gain, scale in fp64, one rounding ----
-  for (int i = 0; i < TPW; ++i) {
-    const int t = tbase + i;
+  // ---- 1. RMSNorm: xn = h / sqrt(mean(h^2) + eps) * gain, scale in fp64, one rounding ----
+  const bool norm = (flags & 1) != 0;
+  for (int i = wave; i < TPB; i += kWaves) {
+    const int t = t0 + i;
     if (t >= T) break;
     const St* hrow = h + (size_t)t * H;
-    St* xrow = xs + (wave * TPW + i) * H;
+    St* xrow = xs + i * H;
     double scale = 1.0;
-    const bool norm = (flags & 1) != 0;
     if (norm) {
       double ss = 0.0;
       for (int c = lane * 8; c < H; c += 8 * kWave) {
         float f[8];
-        Vec8<St>::load(hrow + c, f);
+        load8(hrow + c, f);
 #pragma unroll
         for (int j = 0; j < 8; ++j) ss += (double)f[j] * (double)f[j];
       }
@@ -82,7 +83,7 @@ __global__ __launch_bounds__(256) void route_kernel(
     for (int c = lane * 8; c < H; c += 8 * kWave) {
       float f[8];
       St o[8];
-      Vec8<St>::load(hrow + c, f);
+      load8(hrow + c, f);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         double v = (double)f[j];
@@ -96,35 +97,56 @@ __global__ __launch_bounds__(256) void route_kernel(
       store8(xrow + c, o);
     }
   }
+  __syncthreads();
 
-  // ---- router logits: lane e accumulates l[t,e] over h in order, fp32 ----
-  float acc[TPW];
-#pragma unroll
-  for (int i = 0; i < TPW; ++i) acc[i] = 0.f;
+  // ---- 2. partial logits over this wavefront's slice of the hidden dim ----
+  const int hq = ((H / kWaves + 3) / 4) * 4;
+  const int h_lo = min(H, wave * hq), h_hi = min(H, h_lo + hq);
   const int e = lane;
-  for (int h0 = 0; h0 < H; h0 += kChunk) {
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < kChunk * kWave; idx += 256) {
-      const int ee = idx / kChunk, hh = idx % kChunk;
-      float v = 0.f;
-      if (ee < E && h0 + hh < H) v = wr[(size_t)ee * H + h0 + hh];
-      wt[hh * kWtStride + ee] = v;
-    }
-    __syncthreads();
-    const int hn = min(kChunk, H - h0);
-    for (int hh = 0; hh < hn; ++hh) {
-      const float wv = wt[hh * kWtStride + e];
+  const float* wrow = wr + (size_t)min(e, E - 1) * H;
+  float acc[TPB];
 #pragma unroll
-      for (int i = 0; i < TPW; ++i) acc[i] = fmaf(lds_val(xs + (wave * TPW + i) * H + h0 + hh), wv, acc[i]);
+  for (int i = 0; i < TPB; ++i) acc[i] = 0.f;
+  int hh = h_lo;
+  for (; hh + 32 <= h_hi; hh += 32) {
+    float4 w4[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) w4[u] = *reinterpret_cast<const float4*>(wrow + hh + 4 * u);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int i = 0; i < TPB; ++i) {
+        const float4 x = lds4(xs + i * H + hh + 4 * u);
+        acc[i] = fmaf(x.x, w4[u].x, acc[i]);
+        acc[i] = fmaf(x.y, w4[u].y, acc[i]);
+        acc[i] = fmaf(x.z, w4[u].z, acc[i]);
+        acc[i] = fmaf(x.w, w4[u].w, acc[i]);
+      }
+  }
+  for (; hh < h_hi; hh += 4) {
+    const float4 w = *reinterpret_cast<const float4*>(wrow + hh);
+#pragma unroll
+    for (int i = 0; i < TPB; ++i) {
+      const float4 x = lds4(xs + i * H + hh);
+      acc[i] = fmaf(x.x, w.x, acc[i]);
+      acc[i] = fmaf(x.y, w.y, acc[i]);
+      acc[i] = fmaf(x.z, w.z, acc[i]);
+      acc[i] = fmaf(x.w, w.w, acc[i]);
     }
   }
+#pragma unroll
+  for (int i = 0; i < TPB; ++i) part[(wave * TPB + i) * kWave + e] = acc[i];
+  __syncthreads();
 
-  // ---- top-k by (logit desc, expert id asc), then softmax weights ----
-  for (int i = 0; i < TPW; ++i) {
-    const int t = tbase + i;
+  // ---- 3. top-k by (logit desc, expert id asc), then softmax weights ----
+  for (int i = wave; i < TPB; i += kWaves) {
+    const int t = t0 + i;
     if (t >= T) break;
     const bool valid = e < E;
-    const float l = valid ? acc[i] + (bias ? bias[e] : 0.f) : 0.f;
+    float l = part[i * kWave + e];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) l += part[(w * TPB + i) * kWave + e];
+    if (bias && valid) l += bias[e];
     if (logits && valid) logits[(size_t)t * E + e] = l;
     const unsigned long long key = valid ? (((unsigned long long)float_key(l) << 32) | (uint32_t)(255 - e)) : 0ull;
     int rank = -1;
@@ -146,14 +168,18 @@ __global__ __launch_bounds__(256) void route_kernel(
   }
 }
 
-template <typename St, int TPW>
-hipError_t launch_tpw(const void* h, const float* gain, float eps, const float* wr, const float* bias,
+template <typename St, int TPB>
+size_t lds_bytes(int H) {
+  return ((TPB * H * sizeof(St) + 15) & ~size_t(15)) + (size_t)kWaves * TPB * kWave * sizeof(float);
+}
+
+template <typename St, int TPB>
+hipError_t launch_tpb(const void* h, const float* gain, float eps, const float* wr, const float* bias,
                       int T, int H, int E, int k, int flags, void* xn, int32_t* ids, float* w,
                       float* logits, hipStream_t s) {
-  constexpr int TPB = TPW * kWaves;
-  const size_t lds = ((TPB * H * sizeof(St) + 15) & ~size_t(15)) + kChunk * kWtStride * sizeof(float);
   const int grid = (T + TPB - 1) / TPB;
-  hipLaunchKernelGGL((route_kernel<St, TPW>), dim3(grid), dim3(256), lds, s,
+  const size_t lds = lds_bytes<St, TPB>(H);
+  hipLaunchKernelGGL((route_kernel<St, TPB>), dim3(grid), dim3(kThreads), lds, s,
                      static_cast<const St*>(h), gain, eps, wr, bias, T, H, E, k, flags,
                      static_cast<St*>(xn), ids, w, logits);
   return hipGetLastError();
@@ -163,13 +189,12 @@ template <typename St>
 hipError_t launch_st(const void* h, const float* gain, float eps, const float* wr, const float* bias,
                      int T, int H, int E, int k, int flags, void* xn, int32_t* ids, float* w,
                      float* logits, hipStream_t s) {
-  // keep the block's normed rows within 40 KB of LDS
-  const size_t row = (size_t)H * sizeof(St);
-  if (16 * row <= 40 * 1024)
-    return launch_tpw<St, 4>(h, gain, eps, wr, bias, T, H, E, k, flags, xn, ids, w, logits, s);
-  if (8 * row <= 40 * 1024)
-    return launch_tpw<St, 2>(h, gain, eps, wr, bias, T, H, E, k, flags, xn, ids, w, logits, s);
-  return launch_tpw<St, 1>(h, gain, eps, wr, bias, T, H, E, k, flags, xn, ids, w, logits, s);
+  constexpr size_t kLds = 64 * 1024;
+  if (T > 256 && lds_bytes<St, 16>(H) <= kLds)
+    return launch_tpb<St, 16>(h, gain, eps, wr, bias, T, H, E, k, flags, xn, ids, w, logits, s);
+  if (T > 256 && lds_bytes<St, 8>(H) <= kLds)
+    return launch_tpb<St, 8>(h, gain, eps, wr, bias, T, H, E, k, flags, xn, ids, w, logits, s);
+  return launch_tpb<St, 2>(h, gain, eps, wr, bias, T, H, E, k, flags, xn, ids, w, logits, s);
 }
 
 }  // namespace

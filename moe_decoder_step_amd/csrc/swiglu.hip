@@ -6,14 +6,12 @@
 //   * a block of 4 wavefronts owns 64 output columns of one group; wavefront w
 //     owns 16 of them (for the gated stage, its 16 gate rows and the matching
 //     16 up rows) and streams those weight rows straight into registers as the
-//     A operand of v_mfma_f32_16x16x32_bf16, two 128-element chunks in flight;
-//   * the group's activation rows (gathered tokens) are the B operand; they
-//     are staged through LDS in 128-element chunks (double-buffered) and
-//     shared by the block's four wavefronts;
+//     A operand of v_mfma_f32_16x16x32_bf16, three or four 32-wide k-steps in flight;
+//   * the group's activation rows (gathered tokens, a few hundred KB that stay
+//     in L2) are the B operand, loaded by each wavefront alongside its
+//     weights -- no LDS and no barrier, so every wavefront streams on its own;
 //   * a block covers up to 32 rows; larger groups are split over several
-//     blocks, and the row blocks of one (group, column tile) are placed on the
-//     same XCD (consecutive blocks of that XCD) so they share its L2 copy of
-//     the weights;
+//     blocks on the same XCD, so they share its L2 copy of the weights;
 //   * groups with no rows cost one early exit, so untouched experts are
 //     never read.
 // The fp32 reduction order along K is fixed (chunk by chunk, 32 per MFMA)
@@ -30,174 +28,157 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kColsPerBlock = 64;
-constexpr int kKC = 128;             // K elements per LDS chunk
-constexpr int kSteps = kKC / 32;     // MFMA k-steps per chunk
-constexpr int kLdsRow = kKC + 8;     // padded LDS row (bf16 elements)
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// One wavefront's stream: 16 weight rows (with TWO, a second set of 16: the
+// matching up rows, or the next 16 output rows) over the full reduction length K, against NM
+// 16-row activation blocks.  Lane l supplies weight row l%16 and activation
+// row l%16 at k-offset 8*(l/16) of every 32-wide MFMA step.  D steps of
+// loads are kept in flight in rotating registers; the loop body has no
+// conditional load (a conditional load makes the compiler drain every
+// outstanding load), so the weight stream never stalls on a full drain.
+template <int NM, int D, bool TWO>
+__device__ __forceinline__ void stream_rows(const bf16_t* wa, const bf16_t* wb, const bf16_t* const* xp, int nK,
+                                            f32x4_t* acc_a, f32x4_t* acc_b) {
+  uint4 ra[D], rb[D], rx[D][NM];
+  auto load = [&](int d, int kk) __attribute__((always_inline)) {
+    ra[d] = ldg16(wa + kk * 32);
+    if (TWO) rb[d] = ldg16(wb + kk * 32);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) rx[d][i] = ldg16(xp[i] + kk * 32);
+  };
+  auto mma = [&](int d) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      const bf16x8_t bx = as_bf16x8(rx[d][i]);
+      acc_a[i] = mfma16x16x32(as_bf16x8(ra[d]), bx, acc_a[i]);
+      if (TWO) acc_b[i] = mfma16x16x32(as_bf16x8(rb[d]), bx, acc_b[i]);
+    }
+  };
+#pragma unroll
+  for (int d = 0; d < D; ++d) load(d, min(d, nK - 1));
+  const int nfull = nK / D;
+  for (int g = 0; g < nfull; ++g) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      mma(d);
+      load(d, min((g + 1) * D + d, nK - 1));  // past the end: a repeat of the last step, never used
+    }
+  }
+  const int rem = nK - nfull * D;
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (d < rem) mma(d);
+}
+
 // GATED: x = token rows [T,K] read through gather, W = [G, 2N, K] (gate rows
-//        0..N-1, up rows N..2N-1), out = a [n_rows, N].
+//        0..N-1, up rows N..2N-1), out = a [n_rows, N]; wavefront w owns output
+//        columns 16w..16w+15 of a 64-column block tile (its 16 gate rows and
+//        16 up rows are the two streamed row sets).
 // plain: x = activation rows [n_rows, K] read directly, W = [G, N, K],
-//        out = y [n_rows, N].
-template <int MB, bool GATED>
-__global__ __launch_bounds__(kThreads) void skinny_kernel(
+//        out = y [n_rows, N]; wavefront w owns output columns 32w..32w+31 of a
+//        128-column block tile (two 16-row sets), so that every wavefront
+//        streams as many bytes per k-step as in the gated stage.
+// A block of 4 independent wavefronts owns one column tile of one group and
+// one range of up to 32 rows.
+template <bool GATED>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void skinny_kernel(
     const bf16_t* __restrict__ x, const int32_t* __restrict__ gather,
     const int32_t* __restrict__ offsets, int G, int n_rows, int T,
     const bf16_t* __restrict__ W, int K, int N, int n_ctiles, int n_mranges,
     bf16_t* __restrict__ out) {
-  constexpr int MROWS = MB * 16;
-  __shared__ __align__(16) bf16_t xl[2][MROWS][kLdsRow];
-
-  // (group, column tile) pair p lives on XCD p % 8; its row ranges are
-  // consecutive blocks of that XCD (block b runs on XCD b % 8).
+  constexpr int MROWS = 32;
+  constexpr int D = 3;               // k-steps in flight: fits 4 wavefronts per SIMD without spills
+  constexpr int WCOLS = GATED ? 16 : 32;  // output columns per wavefront
+  // Block b runs on XCD b % 8.  (group, column tile) pair p lives on XCD
+  // p % 8, so the row ranges of one pair share that XCD's L2 copy of the
+  // weights.  The row range is the slowest-varying index: the first range of
+  // every pair (the only non-empty one for a decode-sized group) comes first
+  // and is dealt over all CUs of the XCD; later ranges, mostly empty, follow.
   const int b = blockIdx.x;
   const int xcd = b & 7, local = b >> 3;
-  const int q = local / n_mranges, mr_idx = local % n_mranges;
+  const int per_xcd = (G * n_ctiles + 7) / 8;
+  const int mr_idx = local / per_xcd, q = local % per_xcd;
   const int p = xcd + 8 * q;
   if (p >= G * n_ctiles) return;
   const int g = p / n_ctiles, ct = p % n_ctiles;
   const int r_begin = clampi(offsets[g], 0, n_rows);
   const int r_end = clampi(offsets[g + 1], r_begin, n_rows);
-  if (r_begin + mr_idx * MROWS >= r_end) return;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int col0 = ct * kColsPerBlock + wave * 16;
-  const bool active = col0 < N;
+  const int col0 = ct * (4 * WCOLS) + wave * WCOLS;
+  if (col0 >= N) return;  // waves are independent: no block-wide sync below
   const size_t gstride = (GATED ? (size_t)2 * N : (size_t)N) * K;
-  const int wrow = min(col0 + (lane & 15), N - 1);
-  const bf16_t* wa = W + g * gstride + (size_t)wrow * K + (lane >> 4) * 8;
-  const bf16_t* wb = wa + (size_t)N * K;  // up rows (gated stage only)
+  const bf16_t* wa = W + g * gstride + (size_t)(col0 + (lane & 15)) * K + (lane >> 4) * 8;
+  // second row set: the up rows (gated) or the next 16 output columns (plain;
+  // clamped to a valid row when N is not a multiple of 32 -- never stored)
+  const bf16_t* wb = GATED ? wa + (size_t)N * K
+                           : W + g * gstride + (size_t)min(col0 + 16 + (lane & 15), N - 1) * K + (lane >> 4) * 8;
   const int nK = K / 32;
-  const int nC = (K + kKC - 1) / kKC;
-
-  // LDS staging role of this thread: rows srow + 16 i, 8 elements at sseg
-  const int srow = threadIdx.x >> 4, sseg = (threadIdx.x & 15) * 8;
 
   for (int mstart = r_begin + mr_idx * MROWS; mstart < r_end; mstart += n_mranges * MROWS) {
     const int mr = min(MROWS, r_end - mstart);
-    const bf16_t* src[MB];
+    // activation row of this lane in each 16-row block (rows past the group
+    // read a valid row; their results are never stored)
+    const bf16_t* xp[2];
 #pragma unroll
-    for (int i = 0; i < MB; ++i) {
-      const int row = srow + 16 * i;
-      src[i] = nullptr;
-      if (row < mr) {
-        const int r = mstart + row;
-        int s;
-        if (GATED) s = gather ? clampi(gather[r], 0, T - 1) : clampi(r - r_begin, 0, T - 1);
-        else s = r;
-        src[i] = x + (size_t)s * K + sseg;
-      }
+    for (int i = 0; i < 2; ++i) {
+      const int r = mstart + min(i * 16 + (lane & 15), mr - 1);
+      int s;
+      if (GATED) s = gather ? clampi(gather[r], 0, T - 1) : clampi(r - r_begin, 0, T - 1);
+      else s = r;
+      xp[i] = x + (size_t)s * K + (lane >> 4) * 8;
     }
-
-    f32x4_t acc_a[MB], acc_b[MB];
+    f32x4_t acc_a[2], acc_b[2];
 #pragma unroll
-    for (int i = 0; i < MB; ++i) {
+    for (int i = 0; i < 2; ++i) {
       acc_a[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       acc_b[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
+    if (mr <= 16) stream_rows<1, D, true>(wa, wb, xp, nK, acc_a, acc_b);
+    else stream_rows<2, D, true>(wa, wb, xp, nK, acc_a, acc_b);
 
-    uint4 w0a[kSteps], w0b[kSteps], w1a[kSteps], w1b[kSteps], xst[MB];
-
-    auto load_w = [&](int c, uint4* da, uint4* db) __attribute__((always_inline)) {
+    // lane holds D[col 4*(lane/16)+v][row lane%16]: 4 consecutive output columns of one row
 #pragma unroll
-      for (int s = 0; s < kSteps; ++s) {
-        const int kk = c * kSteps + s;
-        if (active && kk < nK) {
-          da[s] = ldg16_stream(wa + kk * 32);
-          if (GATED) db[s] = ldg16_stream(wb + kk * 32);
-        } else {
-          da[s] = make_uint4(0u, 0u, 0u, 0u);
-          if (GATED) db[s] = make_uint4(0u, 0u, 0u, 0u);
-        }
-      }
-    };
-    auto load_x = [&](int c) __attribute__((always_inline)) {
-#pragma unroll
-      for (int i = 0; i < MB; ++i) {
-        const int kofs = c * kKC + sseg;
-        xst[i] = (src[i] && kofs < K) ? ldg16(src[i] + c * kKC) : make_uint4(0u, 0u, 0u, 0u);
-      }
-    };
-    auto store_x = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-      for (int i = 0; i < MB; ++i) *reinterpret_cast<uint4*>(&xl[buf][srow + 16 * i][sseg]) = xst[i];
-    };
-    // One chunk: prefetch chunk c+1 (activations first, so that waiting for
-    // them before the LDS store leaves the weight loads in flight), run the
-    // MFMAs of chunk c on (ca, cb), stage chunk c+1 into the other buffer.
-    auto chunk = [&](int c, const uint4* ca, const uint4* cb, uint4* na, uint4* nb) __attribute__((always_inline)) {
-      const bool more = c + 1 < nC;
-      if (more) {
-        load_x(c + 1);
-        load_w(c + 1, na, nb);
-      }
-      const int buf = c & 1;
-#pragma unroll
-      for (int s = 0; s < kSteps; ++s) {
-        if (c * kSteps + s < nK) {
-#pragma unroll
-          for (int i = 0; i < MB; ++i) {
-            if (i * 16 < mr) {
-              const bf16x8_t bx = as_bf16x8(*reinterpret_cast<const uint4*>(
-                  &xl[buf][i * 16 + (lane & 15)][s * 32 + (lane >> 4) * 8]));
-              acc_a[i] = mfma16x16x32(as_bf16x8(ca[s]), bx, acc_a[i]);
-              if (GATED) acc_b[i] = mfma16x16x32(as_bf16x8(cb[s]), bx, acc_b[i]);
-            }
-          }
-        }
-      }
-      if (more) store_x(buf ^ 1);
-      __syncthreads();
-    };
-
-    load_x(0);
-    load_w(0, w0a, w0b);
-    store_x(0);
-    __syncthreads();
-    for (int c = 0; c < nC; c += 2) {
-      chunk(c, w0a, w0b, w1a, w1b);
-      if (c + 1 < nC) chunk(c + 1, w1a, w1b, w0a, w0b);
-    }
-
-    // D[col 4*(lane/16)+v][row lane%16] -> 4 consecutive output columns of one row
-    if (active) {
-#pragma unroll
-      for (int i = 0; i < MB; ++i) {
-        const int row = i * 16 + (lane & 15);
-        if (i * 16 < mr && row < mr) {
-          float o[4];
-#pragma unroll
-          for (int v = 0; v < 4; ++v) o[v] = GATED ? silu(acc_a[i][v]) * acc_b[i][v] : acc_a[i][v];
+    for (int i = 0; i < 2; ++i) {
+      const int row = i * 16 + (lane & 15);
+      if (row < mr) {
+        bf16_t* orow = out + (size_t)(mstart + row) * N + col0 + 4 * (lane >> 4);
+        if (GATED) {
           uint2 pk;
-          pk.x = pack2(f32_to_bf16(o[0]), f32_to_bf16(o[1]));
-          pk.y = pack2(f32_to_bf16(o[2]), f32_to_bf16(o[3]));
-          *reinterpret_cast<uint2*>(out + (size_t)(mstart + row) * N + col0 + 4 * (lane >> 4)) = pk;
+          pk.x = pack2(f32_to_bf16(silu(acc_a[i][0]) * acc_b[i][0]), f32_to_bf16(silu(acc_a[i][1]) * acc_b[i][1]));
+          pk.y = pack2(f32_to_bf16(silu(acc_a[i][2]) * acc_b[i][2]), f32_to_bf16(silu(acc_a[i][3]) * acc_b[i][3]));
+          *reinterpret_cast<uint2*>(orow) = pk;
+        } else {
+          uint2 pa, pb;
+          pa.x = pack2(f32_to_bf16(acc_a[i][0]), f32_to_bf16(acc_a[i][1]));
+          pa.y = pack2(f32_to_bf16(acc_a[i][2]), f32_to_bf16(acc_a[i][3]));
+          pb.x = pack2(f32_to_bf16(acc_b[i][0]), f32_to_bf16(acc_b[i][1]));
+          pb.y = pack2(f32_to_bf16(acc_b[i][2]), f32_to_bf16(acc_b[i][3]));
+          *reinterpret_cast<uint2*>(orow) = pa;
+          if (col0 + 16 < N) *reinterpret_cast<uint2*>(orow + 16) = pb;
         }
       }
     }
   }
 }
 
-template <int MB>
 hipError_t launch_bf16(const bf16_t* x, const int32_t* gather, const int32_t* offsets, int G, int n_rows,
                        const bf16_t* wgu, const bf16_t* wd, int T, int H, int I, int max_rows, bf16_t* act,
                        bf16_t* y, hipStream_t s) {
-  const int mrows = MB * 16;
-  const int n_mranges = max(1, (max_rows + mrows - 1) / mrows);
+  const int n_mranges = max(1, (max_rows + 31) / 32);
   {
     const int n_ctiles = (I + kColsPerBlock - 1) / kColsPerBlock;
-    const int pairs = G * n_ctiles;
-    const int blocks = 8 * ((pairs + 7) / 8) * n_mranges;
-    hipLaunchKernelGGL((skinny_kernel<MB, true>), dim3(blocks), dim3(kThreads), 0, s, x, gather, offsets, G,
-                       n_rows, T, wgu, H, I, n_ctiles, n_mranges, act);
+    const int blocks = 8 * ((G * n_ctiles + 7) / 8) * n_mranges;
+    hipLaunchKernelGGL((skinny_kernel<true>), dim3(blocks), dim3(kThreads), 0, s, x, gather, offsets, G, n_rows,
+                       T, wgu, H, I, n_ctiles, n_mranges, act);
   }
   {
-    const int n_ctiles = (H + kColsPerBlock - 1) / kColsPerBlock;
-    const int pairs = G * n_ctiles;
-    const int blocks = 8 * ((pairs + 7) / 8) * n_mranges;
-    hipLaunchKernelGGL((skinny_kernel<MB, false>), dim3(blocks), dim3(kThreads), 0, s, act, nullptr, offsets,
-                       G, n_rows, T, wd, I, H, n_ctiles, n_mranges, y);
+    const int n_ctiles = (H + 2 * kColsPerBlock - 1) / (2 * kColsPerBlock);
+    const int blocks = 8 * ((G * n_ctiles + 7) / 8) * n_mranges;
+    hipLaunchKernelGGL((skinny_kernel<false>), dim3(blocks), dim3(kThreads), 0, s, act, nullptr, offsets, G,
+                       n_rows, T, wd, I, H, n_ctiles, n_mranges, y);
   }
   return hipGetLastError();
 }
@@ -273,9 +254,7 @@ hipError_t launch_swiglu(const void* x, const int32_t* gather, const int32_t* of
   const bf16_t* wd = static_cast<const bf16_t*>(w_down);
   bf16_t* act = static_cast<bf16_t*>(ws);
   bf16_t* yb = static_cast<bf16_t*>(y);
-  if (max_rows <= 16)
-    return launch_bf16<1>(xb, gather, offsets, G, n_rows, wgu, wd, T, H, I, max_rows, act, yb, s);
-  return launch_bf16<2>(xb, gather, offsets, G, n_rows, wgu, wd, T, H, I, max_rows, act, yb, s);
+  return launch_bf16(xb, gather, offsets, G, n_rows, wgu, wd, T, H, I, max_rows, act, yb, s);
 }
 
 }  // namespace moe

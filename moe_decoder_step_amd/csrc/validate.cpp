@@ -82,7 +82,7 @@ int check_combine(const void* y, const int32_t* inv, const float* topk_w, const 
                   const void* out, const void* combined) {
   if (!valid_dtype(dtype)) return kErrUnsupported;
   if (T < 0 || H <= 0 || k < 0 || S < 0 || n_rows < 0) return kErrShape;
-  if (H % 8 != 0) return kErrUnsupported;
+  if (H % 8 != 0 || k > kMaxExperts) return kErrUnsupported;
   if (k > 0 && n_rows <= 0 && T > 0) return kErrShape;
   if (S > 0 && !y_shared) return kErrNull;
   if (T == 0) return kOk;

@@ -102,6 +102,7 @@ def test_combine_lmhead_verify_plant_checks(lib):
     assert lib.moe_combine(A, None, A, A, 2, A, 4, 1280, 6, 40, m.BF16, A, None, None) == L.ERR_NULL
     assert lib.moe_combine(A, A, A, A, 2, A, 4, 1284, 6, 40, m.BF16, A, None, None) == L.ERR_UNSUPPORTED
     assert lib.moe_combine(A, A, A, A, 2, A, 4, 1280, 6, 40, m.BF16, MIS, None, None) == L.ERR_ALIGN
+    assert lib.moe_combine(A, A, A, A, 2, A, 4, 1280, 65, 40, m.BF16, A, None, None) == L.ERR_UNSUPPORTED
     assert lib.moe_combine(A, A, A, A, 2, A, 0, 1280, 6, 40, m.BF16, A, None, None) == L.OK
     need = lib.lmhead_argmax_workspace_bytes(4, 129280, m.BF16)
     assert lib.lmhead_argmax(A, A, 4, 1280, 129280, m.BF16, A, None, A, need - 8, None) == L.ERR_WORKSPACE
