@@ -135,12 +135,13 @@ int moe_permute(const int32_t* topk_ids, int T, int k, int E, int S,
  *                                            clamped into [0,n_rows])
  * w_gate_up [G, 2I, H] dtype            in  rows 0..I-1 = W_g, I..2I-1 = W_u
  * w_down    [G, H, I] dtype             in
- * max_rows  host-side upper bound on any group's row count (e.g. T); it only
- *           selects the kernel shape -- any count is computed correctly
+ * max_rows  host-side upper bound on any group's row count (e.g. T): a
+ *           hint for choosing the kernel shape; any count is computed correctly
  * y         [n_rows, H] dtype           out (rows outside every group untouched)
  * ws        scratch of at least moe_grouped_swiglu_workspace_bytes() bytes
- * Limits: H % 32 == 0 and I % 32 == 0 for MOE_BF16, H % 4 == 0 and
- *         I % 4 == 0 for MOE_F32; 1 <= G.
+ * Limits: H % 32 == 0, I % 32 == 0, H <= 4096, I <= 4096 and G <= 128 for
+ *         MOE_BF16 (a block keeps 16 activation rows of the full reduction
+ *         length in LDS); H % 4 == 0 and I % 4 == 0 for MOE_F32; 1 <= G.
  * ------------------------------------------------------------------------- */
 size_t moe_grouped_swiglu_workspace_bytes(int n_rows, int I, int dtype);
 int moe_grouped_swiglu(const void* x, const int32_t* gather, const int32_t* offsets,

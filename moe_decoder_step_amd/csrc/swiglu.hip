@@ -3,17 +3,18 @@
 // bf16 path (decode-sized groups): the expert weights are the bytes that
 // matter -- each row of W is read once from HBM and used for every token of
 // its group -- so the kernel is a weight stream feeding MFMA:
-//   * a block of 4 wavefronts owns 64 output columns of one group; wavefront w
-//     owns 16 of them (for the gated stage, its 16 gate rows and the matching
-//     16 up rows) and streams those weight rows straight into registers as the
-//     A operand of v_mfma_f32_16x16x32_bf16, three or four 32-wide k-steps in flight;
-//   * the group's activation rows (gathered tokens, a few hundred KB that stay
-//     in L2) are the B operand, loaded by each wavefront alongside its
-//     weights -- no LDS and no barrier, so every wavefront streams on its own;
-//   * a block covers up to 32 rows; larger groups are split over several
-//     blocks on the same XCD, so they share its L2 copy of the weights;
-//   * groups with no rows cost one early exit, so untouched experts are
-//     never read.
+//   * a block of 8 wavefronts owns a tile of output columns of one group;
+//     wavefront w owns 16 of them (for the gated stage, its 16 gate rows and
+//     the matching 16 up rows; for the down projection two 16-row blocks) and
+//     streams those weight rows straight into registers as the A operand of
+//     v_mfma_f32_16x16x32_bf16, three 32-wide k-steps in flight;
+//   * the block's activation rows (up to 16 gathered tokens, the B operand)
+//     are staged once into LDS for the whole reduction length: one barrier,
+//     then every wavefront streams on its own with no activation traffic;
+//   * each block finds its (group, column tile, 16-row range) from the group
+//     offsets on the device, so untouched experts are never read and the
+//     launch holds few empty blocks; the ranges of one group and tile run
+//     back to back on one XCD and share its L2 copy of the weights;
 // The fp32 reduction order along K is fixed (chunk by chunk, 32 per MFMA)
 // and does not depend on how many rows a group has.
 //
@@ -26,136 +27,186 @@
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kColsPerBlock = 64;
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
-// One wavefront's stream: 16 weight rows (with TWO, a second set of 16: the
-// matching up rows, or the next 16 output rows) over the full reduction length K, against NM
-// 16-row activation blocks.  Lane l supplies weight row l%16 and activation
-// row l%16 at k-offset 8*(l/16) of every 32-wide MFMA step.  D steps of
-// loads are kept in flight in rotating registers; the loop body has no
-// conditional load (a conditional load makes the compiler drain every
-// outstanding load), so the weight stream never stalls on a full drain.
-template <int NM, int D, bool TWO>
-__device__ __forceinline__ void stream_rows(const bf16_t* wa, const bf16_t* wb, const bf16_t* const* xp, int nK,
-                                            f32x4_t* acc_a, f32x4_t* acc_b) {
-  uint4 ra[D], rb[D], rx[D][NM];
-  auto load = [&](int d, int kk) __attribute__((always_inline)) {
-    ra[d] = ldg16(wa + kk * 32);
-    if (TWO) rb[d] = ldg16(wb + kk * 32);
-#pragma unroll
-    for (int i = 0; i < NM; ++i) rx[d][i] = ldg16(xp[i] + kk * 32);
+constexpr int kWaves = 8;                 // wavefronts per block
+constexpr int kBlockThreads = kWaves * 64;
+constexpr int kRows = 16;                 // activation rows per block (one MFMA block)
+
+__host__ __device__ constexpr int lds_row(int K) { return K + 8; }  // padded LDS row (bf16): conflict-free
+
+// One wavefront's stream: two sets of 16 weight rows (the gate rows and the
+// matching up rows, or two neighbouring 16-row output blocks) over the full
+// reduction length K, against the block's 16 activation rows in LDS.  Lane
+// l supplies weight row l%16 and activation row l%16 at k-offset 8*(l/16) of
+// every 32-wide MFMA step.  D steps of weight loads stay in flight in
+// rotating registers; the loop body has no conditional load (a conditional
+// load makes the compiler drain every outstanding load).
+template <int D>
+__device__ __forceinline__ void stream_rows(const bf16_t* wa, const bf16_t* wb, const bf16_t* xs, int nK,
+                                            uint4* ra, uint4* rb, f32x4_t& acc_a, f32x4_t& acc_b) {
+  auto mma = [&](int d, int kk) __attribute__((always_inline)) {
+    const bf16x8_t bx = as_bf16x8(*reinterpret_cast<const uint4*>(xs + kk * 32));
+    acc_a = mfma16x16x32(as_bf16x8(ra[d]), bx, acc_a);
+    acc_b = mfma16x16x32(as_bf16x8(rb[d]), bx, acc_b);
   };
-  auto mma = [&](int d) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < NM; ++i) {
-      const bf16x8_t bx = as_bf16x8(rx[d][i]);
-      acc_a[i] = mfma16x16x32(as_bf16x8(ra[d]), bx, acc_a[i]);
-      if (TWO) acc_b[i] = mfma16x16x32(as_bf16x8(rb[d]), bx, acc_b[i]);
-    }
-  };
-#pragma unroll
-  for (int d = 0; d < D; ++d) load(d, min(d, nK - 1));
   const int nfull = nK / D;
   for (int g = 0; g < nfull; ++g) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      mma(d);
-      load(d, min((g + 1) * D + d, nK - 1));  // past the end: a repeat of the last step, never used
+      mma(d, g * D + d);
+      const int kk = min((g + 1) * D + d, nK - 1);  // past the end: a repeat of the last step, never used
+      ra[d] = ldg16(wa + kk * 32);
+      rb[d] = ldg16(wb + kk * 32);
     }
   }
   const int rem = nK - nfull * D;
 #pragma unroll
   for (int d = 0; d < D; ++d)
-    if (d < rem) mma(d);
+    if (d < rem) mma(d, nfull * D + d);
 }
 
 // GATED: x = token rows [T,K] read through gather, W = [G, 2N, K] (gate rows
 //        0..N-1, up rows N..2N-1), out = a [n_rows, N]; wavefront w owns output
-//        columns 16w..16w+15 of a 64-column block tile (its 16 gate rows and
+//        columns 16w..16w+15 of a 128-column block tile (its 16 gate rows and
 //        16 up rows are the two streamed row sets).
 // plain: x = activation rows [n_rows, K] read directly, W = [G, N, K],
 //        out = y [n_rows, N]; wavefront w owns output columns 32w..32w+31 of a
-//        128-column block tile (two 16-row sets), so that every wavefront
+//        256-column block tile (two 16-row sets), so that every wavefront
 //        streams as many bytes per k-step as in the gated stage.
-// A block of 4 independent wavefronts owns one column tile of one group and
-// one range of up to 32 rows.
+// A block of 8 wavefronts owns one column tile of one group and one range of
+// up to 16 rows, staged once into LDS (one barrier) and shared by its waves.
 template <bool GATED>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void skinny_kernel(
+__global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
     const bf16_t* __restrict__ x, const int32_t* __restrict__ gather,
     const int32_t* __restrict__ offsets, int G, int n_rows, int T,
-    const bf16_t* __restrict__ W, int K, int N, int n_ctiles, int n_mranges,
-    bf16_t* __restrict__ out) {
-  constexpr int MROWS = 32;
-  constexpr int D = 3;               // k-steps in flight: fits 4 wavefronts per SIMD without spills
+    const bf16_t* __restrict__ W, int K, int N, int n_ctiles, bf16_t* __restrict__ out) {
+  constexpr int D = 3;                    // k-steps of weights in flight per wavefront
   constexpr int WCOLS = GATED ? 16 : 32;  // output columns per wavefront
-  // Block b runs on XCD b % 8.  (group, column tile) pair p lives on XCD
-  // p % 8, so the row ranges of one pair share that XCD's L2 copy of the
-  // weights.  The row range is the slowest-varying index: the first range of
-  // every pair (the only non-empty one for a decode-sized group) comes first
-  // and is dealt over all CUs of the XCD; later ranges, mostly empty, follow.
-  const int b = blockIdx.x;
-  const int xcd = b & 7, local = b >> 3;
-  const int per_xcd = (G * n_ctiles + 7) / 8;
-  const int mr_idx = local / per_xcd, q = local % per_xcd;
-  const int p = xcd + 8 * q;
-  if (p >= G * n_ctiles) return;
-  const int g = p / n_ctiles, ct = p % n_ctiles;
+  extern __shared__ __align__(16) bf16_t xl[];   // [kRows][lds_row(K)]
+
+  // Work items are (group g, column tile ct, 16-row range) for the non-empty
+  // ranges.  Pair (g, ct) belongs to XCD (g*n_ctiles + ct) % 8 (block b runs
+  // on XCD b % 8); on each XCD the items are ordered by group, tile, range,
+  // so the ranges of one large group (a shared expert sees every token) run
+  // back to back on one XCD and share its L2 copy of the weights.  Block b
+  // takes the (b/8)-th item of XCD b%8; the launch holds an upper bound of
+  // items per XCD and the surplus blocks, last in every XCD's list, exit.
+  // Wavefront 0 finds the item: lane l handles groups l and l+64 (G <= 128),
+  // counts its items on this XCD, and a wavefront prefix sum places them.
+  __shared__ int item_g, item_ct, item_r0, item_r1;
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  if (threadIdx.x < kWave) {
+    const int l = threadIdx.x;
+    int r0[2], r1[2], nr[2], nc[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int g = l + h * kWave;
+      r0[h] = g < G ? clampi(offsets[g], 0, n_rows) : 0;
+      r1[h] = g < G ? clampi(offsets[g + 1], r0[h], n_rows) : 0;
+      nr[h] = (r1[h] - r0[h] + kRows - 1) / kRows;
+      // tiles of group g on this XCD: ct = c0, c0+8, ... < n_ctiles
+      const int c0 = ((xcd - g * n_ctiles) % 8 + 8) % 8;
+      nc[h] = g < G && c0 < n_ctiles ? (n_ctiles - c0 + 7) / 8 : 0;
+    }
+    int cnt[2] = {nr[0] * nc[0], nr[1] * nc[1]};
+    int incl[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      incl[h] = cnt[h];
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int v = __shfl_up(incl[h], o, kWave);
+        if (l >= o) incl[h] += v;
+      }
+    }
+    incl[1] += __shfl(incl[0], kWave - 1, kWave);
+    if (l == 0) item_g = -1;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int first = incl[h] - cnt[h];
+      if (j >= first && j < incl[h]) {
+        const int g = l + h * kWave;
+        const int li = j - first;              // ordered by tile, then range
+        const int c0 = ((xcd - g * n_ctiles) % 8 + 8) % 8;
+        item_g = g;
+        item_ct = c0 + 8 * (li / nr[h]);
+        item_r0 = r0[h] + (li % nr[h]) * kRows;
+        item_r1 = r1[h];
+      }
+    }
+  }
+  __syncthreads();
+  const int g = item_g;
+  if (g < 0) return;
+  const int ct = item_ct;
+  const int mstart = item_r0;
+  const int mr = min(kRows, item_r1 - mstart);
   const int r_begin = clampi(offsets[g], 0, n_rows);
-  const int r_end = clampi(offsets[g + 1], r_begin, n_rows);
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int col0 = ct * (4 * WCOLS) + wave * WCOLS;
-  if (col0 >= N) return;  // waves are independent: no block-wide sync below
+  const int col0 = ct * (kWaves * WCOLS) + wave * WCOLS;
+  const bool active = col0 < N;
   const size_t gstride = (GATED ? (size_t)2 * N : (size_t)N) * K;
-  const bf16_t* wa = W + g * gstride + (size_t)(col0 + (lane & 15)) * K + (lane >> 4) * 8;
+  const int wrow = min(col0 + (lane & 15), N - 1);
+  const bf16_t* wa = W + g * gstride + (size_t)wrow * K + (lane >> 4) * 8;
   // second row set: the up rows (gated) or the next 16 output columns (plain;
-  // clamped to a valid row when N is not a multiple of 32 -- never stored)
+  // clamped to a valid row past N -- never stored)
   const bf16_t* wb = GATED ? wa + (size_t)N * K
                            : W + g * gstride + (size_t)min(col0 + 16 + (lane & 15), N - 1) * K + (lane >> 4) * 8;
   const int nK = K / 32;
+  const int ldr = lds_row(K);
+  const int nseg = K / 8;                 // 16-byte segments per activation row
 
-  for (int mstart = r_begin + mr_idx * MROWS; mstart < r_end; mstart += n_mranges * MROWS) {
-    const int mr = min(MROWS, r_end - mstart);
-    // activation row of this lane in each 16-row block (rows past the group
-    // read a valid row; their results are never stored)
-    const bf16_t* xp[2];
+  {
+    // weights of the first D steps go out before the activation staging
+    uint4 ra[D], rb[D];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = mstart + min(i * 16 + (lane & 15), mr - 1);
-      int s;
-      if (GATED) s = gather ? clampi(gather[r], 0, T - 1) : clampi(r - r_begin, 0, T - 1);
-      else s = r;
-      xp[i] = x + (size_t)s * K + (lane >> 4) * 8;
+    for (int d = 0; d < D; ++d) {
+      const int kk = min(d, nK - 1);
+      ra[d] = ldg16(wa + kk * 32);
+      rb[d] = ldg16(wb + kk * 32);
     }
-    f32x4_t acc_a[2], acc_b[2];
+    // stage the range's activation rows (rows past the group repeat a valid row)
+    for (int i = threadIdx.x; i < kRows * nseg; i += kBlockThreads * 4) {
+      uint4 v[4];
+      int dst[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      acc_a[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      acc_b[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < 4; ++u) {
+        const int idx = min(i + u * kBlockThreads, kRows * nseg - 1);
+        const int row = idx / nseg, seg = idx % nseg;
+        const int r = mstart + min(row, mr - 1);
+        int s;
+        if (GATED) s = gather ? clampi(gather[r], 0, T - 1) : clampi(r - r_begin, 0, T - 1);
+        else s = r;
+        v[u] = ldg16(x + (size_t)s * K + seg * 8);
+        dst[u] = row * ldr + seg * 8;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (i + u * kBlockThreads < kRows * nseg) *reinterpret_cast<uint4*>(xl + dst[u]) = v[u];
     }
-    if (mr <= 16) stream_rows<1, D, true>(wa, wb, xp, nK, acc_a, acc_b);
-    else stream_rows<2, D, true>(wa, wb, xp, nK, acc_a, acc_b);
+    lds_barrier();
 
-    // lane holds D[col 4*(lane/16)+v][row lane%16]: 4 consecutive output columns of one row
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = i * 16 + (lane & 15);
+    if (active) {
+      f32x4_t acc_a = f32x4_t{0.f, 0.f, 0.f, 0.f}, acc_b = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      stream_rows<D>(wa, wb, xl + (lane & 15) * ldr + (lane >> 4) * 8, nK, ra, rb, acc_a, acc_b);
+      // lane holds D[col 4*(lane/16)+v][row lane%16]: 4 consecutive output columns of one row
+      const int row = lane & 15;
       if (row < mr) {
         bf16_t* orow = out + (size_t)(mstart + row) * N + col0 + 4 * (lane >> 4);
         if (GATED) {
           uint2 pk;
-          pk.x = pack2(f32_to_bf16(silu(acc_a[i][0]) * acc_b[i][0]), f32_to_bf16(silu(acc_a[i][1]) * acc_b[i][1]));
-          pk.y = pack2(f32_to_bf16(silu(acc_a[i][2]) * acc_b[i][2]), f32_to_bf16(silu(acc_a[i][3]) * acc_b[i][3]));
+          pk.x = pack2(f32_to_bf16(silu(acc_a[0]) * acc_b[0]), f32_to_bf16(silu(acc_a[1]) * acc_b[1]));
+          pk.y = pack2(f32_to_bf16(silu(acc_a[2]) * acc_b[2]), f32_to_bf16(silu(acc_a[3]) * acc_b[3]));
           *reinterpret_cast<uint2*>(orow) = pk;
         } else {
           uint2 pa, pb;
-          pa.x = pack2(f32_to_bf16(acc_a[i][0]), f32_to_bf16(acc_a[i][1]));
-          pa.y = pack2(f32_to_bf16(acc_a[i][2]), f32_to_bf16(acc_a[i][3]));
-          pb.x = pack2(f32_to_bf16(acc_b[i][0]), f32_to_bf16(acc_b[i][1]));
-          pb.y = pack2(f32_to_bf16(acc_b[i][2]), f32_to_bf16(acc_b[i][3]));
+          pa.x = pack2(f32_to_bf16(acc_a[0]), f32_to_bf16(acc_a[1]));
+          pa.y = pack2(f32_to_bf16(acc_a[2]), f32_to_bf16(acc_a[3]));
+          pb.x = pack2(f32_to_bf16(acc_b[0]), f32_to_bf16(acc_b[1]));
+          pb.y = pack2(f32_to_bf16(acc_b[2]), f32_to_bf16(acc_b[3]));
           *reinterpret_cast<uint2*>(orow) = pa;
           if (col0 + 16 < N) *reinterpret_cast<uint2*>(orow + 16) = pb;
         }
@@ -164,23 +215,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   }
 }
 
+template <bool GATED>
+hipError_t launch_skinny(const bf16_t* x, const int32_t* gather, const int32_t* offsets, int G, int n_rows, int T,
+                         const bf16_t* W, int K, int N, bf16_t* out, hipStream_t s) {
+  constexpr int tile = kWaves * (GATED ? 16 : 32);
+  const int n_ctiles = (N + tile - 1) / tile;
+  // items on one XCD <= ceil(n_ctiles / 8) * sum over groups of ceil(rows / 16)
+  //                  <= ceil(n_ctiles / 8) * (n_rows / 16 + G)
+  const int per_xcd = (n_ctiles + 7) / 8 * ((n_rows + kRows - 1) / kRows + G);
+  const int blocks = 8 * per_xcd;
+  const size_t lds = (size_t)kRows * lds_row(K) * sizeof(bf16_t);
+  if (lds > 64 * 1024) {  // K > 2040: allow up to the CU's 160 KB of LDS
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&skinny_kernel<GATED>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((skinny_kernel<GATED>), dim3(blocks), dim3(kBlockThreads), lds, s, x, gather, offsets, G,
+                     n_rows, T, W, K, N, n_ctiles, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_bf16(const bf16_t* x, const int32_t* gather, const int32_t* offsets, int G, int n_rows,
                        const bf16_t* wgu, const bf16_t* wd, int T, int H, int I, int max_rows, bf16_t* act,
                        bf16_t* y, hipStream_t s) {
-  const int n_mranges = max(1, (max_rows + 31) / 32);
-  {
-    const int n_ctiles = (I + kColsPerBlock - 1) / kColsPerBlock;
-    const int blocks = 8 * ((G * n_ctiles + 7) / 8) * n_mranges;
-    hipLaunchKernelGGL((skinny_kernel<true>), dim3(blocks), dim3(kThreads), 0, s, x, gather, offsets, G, n_rows,
-                       T, wgu, H, I, n_ctiles, n_mranges, act);
-  }
-  {
-    const int n_ctiles = (H + 2 * kColsPerBlock - 1) / (2 * kColsPerBlock);
-    const int blocks = 8 * ((G * n_ctiles + 7) / 8) * n_mranges;
-    hipLaunchKernelGGL((skinny_kernel<false>), dim3(blocks), dim3(kThreads), 0, s, act, nullptr, offsets, G,
-                       n_rows, T, wd, I, H, n_ctiles, n_mranges, y);
-  }
-  return hipGetLastError();
+  (void)max_rows;
+  hipError_t e = launch_skinny<true>(x, gather, offsets, G, n_rows, T, wgu, H, I, act, s);
+  if (e != hipSuccess) return e;
+  return launch_skinny<false>(act, nullptr, offsets, G, n_rows, T, wd, I, H, y, s);
 }
 
 // ---------------------------------------------------------------- fp32 path

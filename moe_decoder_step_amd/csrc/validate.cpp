@@ -66,7 +66,7 @@ int check_swiglu(const void* x, const int32_t* offsets, int G, int n_rows, const
                  const void* ws, size_t ws_bytes) {
   if (!valid_dtype(dtype)) return kErrUnsupported;
   if (G <= 0 || n_rows < 0 || T < 0 || H <= 0 || I <= 0 || max_rows < 0) return kErrShape;
-  if (dtype == kBf16 && (H % 32 != 0 || I % 32 != 0)) return kErrUnsupported;
+  if (dtype == kBf16 && (H % 32 != 0 || I % 32 != 0 || H > 4096 || I > 4096 || G > 128)) return kErrUnsupported;
   if (dtype == kF32 && (H % 4 != 0 || I % 4 != 0)) return kErrUnsupported;
   if (n_rows == 0 || T == 0) return kOk;
   if (!x || !offsets || !w_gate_up || !w_down || !y) return kErrNull;

@@ -91,6 +91,8 @@ def test_swiglu_checks(lib):
     assert call(n=-1) == L.ERR_SHAPE
     assert call(H=1288) == L.ERR_UNSUPPORTED          # bf16 needs H % 32 == 0
     assert call(I=900) == L.ERR_UNSUPPORTED
+    assert call(I=4128) == L.ERR_UNSUPPORTED          # LDS holds 16 rows of the reduction length
+    assert call(G=129) == L.ERR_UNSUPPORTED
     assert call(wgu=MIS) == L.ERR_ALIGN
     assert call(ws=None) == L.ERR_WORKSPACE
     assert call(wsb=need - 1) == L.ERR_WORKSPACE
