@@ -58,6 +58,10 @@ typedef enum {
 
 typedef enum { MOE_BF16 = 0, MOE_F32 = 1 } moe_dtype;
 
+/* moe_pack_weights kinds */
+#define MOE_PACK_GATE_UP 0  /* [G, 2N, K]: gate rows 0..N-1, up rows N..2N-1 */
+#define MOE_PACK_ROWS 1     /* [G, N, K]: plain rows (down projection, LM head) */
+
 /* moe_route flags */
 #define MOE_ROUTE_NORM 1    /* apply RMSNorm before the router (else xn = h) */
 #define MOE_ROUTE_RENORM 2  /* softmax over the k selected logits (else full-softmax probabilities) */
@@ -67,6 +71,28 @@ int moe_abi_version(void);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* moe_status_str(int status);
+
+/* ---------------------------------------------------------------------------
+ * moe_pack_weights -- convert row-major bf16 weights to the fragment layout
+ * the weight-streaming kernels read (done once, when a model is loaded).
+ *
+ * The expert FFN and the LM head read weight rows as matrix-core A operands:
+ * lane l of a wavefront takes row l%16, elements 8*(l/16)..+7 of each 32-wide
+ * k-step.  The packed layout stores each such 16-row x 32 fragment as 1 KB
+ * in lane order, two row sets side by side, so every load is 1 KB of
+ * consecutive bytes:
+ *   dst[g][p][s][h][l][j] = src[g][row][32*s + 8*(l/16) + j]
+ *   MOE_PACK_GATE_UP: src [G, 2N, K]; row = h*N + 16p + l%16  (p < N/16)
+ *   MOE_PACK_ROWS:    src [G, N, K];  row = 32p + 16h + l%16 (p < ceil(N/32));
+ *                     rows at or past N are zero
+ * src and dst: bf16, 16-byte aligned, not overlapping; dst holds
+ * moe_packed_weights_bytes(G, N, K, kind) bytes.  MOE_F32 weights are used
+ * row-major and are not packed (MOE_ERR_UNSUPPORTED).
+ * Limits: K % 32 == 0; N % 16 == 0 for MOE_PACK_GATE_UP.
+ * ------------------------------------------------------------------------- */
+size_t moe_packed_weights_bytes(int G, int N, int K, int kind);
+int moe_pack_weights(const void* src, void* dst, int G, int N, int K, int kind, int dtype,
+                     void* stream);
 
 /* ---------------------------------------------------------------------------
  * moe_route -- pre-norm, router logits, top-k selection and routing weights.
@@ -133,8 +159,9 @@ int moe_permute(const int32_t* topk_ids, int T, int k, int E, int S,
  * gather    [n_rows] int32 or NULL      in  (clamped into [0,T))
  * offsets   [G+1] int32 (device)        in  (nondecreasing, offsets[G] <= n_rows;
  *                                            clamped into [0,n_rows])
- * w_gate_up [G, 2I, H] dtype            in  rows 0..I-1 = W_g, I..2I-1 = W_u
- * w_down    [G, H, I] dtype             in
+ * w_gate_up [G, 2I, H] dtype            in  rows 0..I-1 = W_g, I..2I-1 = W_u;
+ *                                            MOE_BF16: packed (MOE_PACK_GATE_UP, N = I)
+ * w_down    [G, H, I] dtype             in  MOE_BF16: packed (MOE_PACK_ROWS, N = H)
  * max_rows  host-side upper bound on any group's row count (e.g. T): a
  *           hint for choosing the kernel shape; any count is computed correctly
  * y         [n_rows, H] dtype           out (rows outside every group untouched)
@@ -179,7 +206,7 @@ int moe_combine(const void* y, const int32_t* inv, const float* topk_w,
  * fp32 logit, equal logits going to the lowest index, and that logit.
  *
  * h          [T,H] dtype       in
- * w_lm       [V,H] dtype       in
+ * w_lm       [V,H] dtype       in  MOE_BF16: packed (MOE_PACK_ROWS, G = 1, N = V)
  * argmax_ids [T] int32         out
  * max_logit  [T] fp32 or NULL  out
  * ws         scratch of at least lmhead_argmax_workspace_bytes() bytes

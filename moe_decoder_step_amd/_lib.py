@@ -16,6 +16,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "moestep.h")
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP = range(7)
 BF16, F32 = 0, 1
 ROUTE_NORM, ROUTE_RENORM = 1, 2
+PACK_GATE_UP, PACK_ROWS = 0, 1
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -26,6 +27,8 @@ _Z = ctypes.c_size_t
 SIGNATURES = {
     "moe_abi_version": (_I, []),
     "moe_status_str": (ctypes.c_char_p, [_I]),
+    "moe_packed_weights_bytes": (_Z, [_I, _I, _I, _I]),
+    "moe_pack_weights": (_I, [_P, _P, _I, _I, _I, _I, _I, _P]),
     "moe_permute_workspace_bytes": (_Z, [_I, _I, _I]),
     "moe_grouped_swiglu_workspace_bytes": (_Z, [_I, _I, _I]),
     "lmhead_argmax_workspace_bytes": (_Z, [_I, _I, _I]),

@@ -29,6 +29,14 @@ const char* moe_status_str(int status) {
   }
 }
 
+size_t moe_packed_weights_bytes(int G, int N, int K, int kind) { return moe::packed_bytes(G, N, K, kind); }
+
+int moe_pack_weights(const void* src, void* dst, int G, int N, int K, int kind, int dtype, void* stream) {
+  int st = moe::check_pack(src, dst, G, N, K, kind, dtype);
+  if (st != MOE_OK || G == 0) return st;
+  return hip_status(moe::launch_pack(src, dst, G, N, K, kind, as_stream(stream)));
+}
+
 size_t moe_permute_workspace_bytes(int T, int k, int E) { return moe::permute_ws_bytes(T, k, E); }
 
 size_t moe_grouped_swiglu_workspace_bytes(int n_rows, int I, int dtype) {

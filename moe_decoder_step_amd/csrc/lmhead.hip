@@ -1,6 +1,7 @@
 // lmhead_argmax: argmax_v (h W_lm^T)[t, v] per row, ties to the lowest v.
 //
-// The 129,280 x 1280 bf16 LM head (331 MB) is streamed from HBM exactly once
+// The 129,280 x 1280 bf16 LM head (331 MB, packed by moe_pack_weights so
+// every load is 1 KB of consecutive bytes) is streamed from HBM exactly once
 // per call and the logits never leave registers:
 //   * a block of 4 wavefronts owns 128 vocabulary rows; wavefront w streams 32
 //     of them (two 16-row MFMA blocks) as the A operand of
@@ -42,13 +43,14 @@ __global__ __launch_bounds__(kThreads) void lm_bf16_kernel(const bf16_t* __restr
   const int blk = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int vbase = blk * kLmRowsPerBlock + wave * kNB * 16;
+  // packed LM head: [pair of 32 rows][k-step][set][lane][8]; this wavefront's
+  // 32 rows are one pair, each (pair, k-step) 2 KB of consecutive bytes
+  const int nK = H / 32;
+  const int n_pairs = (V + 31) / 32;
+  const int pair = min(blk * 4 + wave, n_pairs - 1);  // past the vocabulary: a valid pair, masked below
   const bf16_t* wp[kNB];
 #pragma unroll
-  for (int nb = 0; nb < kNB; ++nb) {
-    const int v = min(vbase + nb * 16 + (lane & 15), V - 1);
-    wp[nb] = W + (size_t)v * H + (lane >> 4) * 8;
-  }
-  const int nK = H / 32;
+  for (int nb = 0; nb < kNB; ++nb) wp[nb] = W + (size_t)pair * nK * 1024 + nb * 512 + lane * 8;
   const int nC = (H + kKC - 1) / kKC;
   const int srow = threadIdx.x >> 4, sseg = (threadIdx.x & 15) * 8;
 
@@ -76,7 +78,7 @@ __global__ __launch_bounds__(kThreads) void lm_bf16_kernel(const bf16_t* __restr
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
-        for (int s = 0; s < kSteps; ++s) d[nb][s] = ldg16_stream(wp[nb] + min(c * kSteps + s, nK - 1) * 32);
+        for (int s = 0; s < kSteps; ++s) d[nb][s] = ldg16(wp[nb] + min(c * kSteps + s, nK - 1) * 1024);
     };
     auto load_x = [&](int c) __attribute__((always_inline)) {
       const int kofs = c * kKC + sseg;

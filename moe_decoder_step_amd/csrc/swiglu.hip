@@ -7,7 +7,10 @@
 //     wavefront w owns 16 of them (for the gated stage, its 16 gate rows and
 //     the matching 16 up rows; for the down projection two 16-row blocks) and
 //     streams those weight rows straight into registers as the A operand of
-//     v_mfma_f32_16x16x32_bf16, three 32-wide k-steps in flight;
+//     v_mfma_f32_16x16x32_bf16, three 32-wide k-steps in flight; the weights
+//     are packed (moe_pack_weights) so every load is 1 KB of consecutive
+//     bytes -- row-major rows would give 64-byte half-line requests and
+//     halve the cache's request throughput;
 //   * the block's activation rows (up to 16 gathered tokens, the B operand)
 //     are staged once into LDS for the whole reduction length: one barrier,
 //     then every wavefront streams on its own with no activation traffic;
@@ -52,13 +55,26 @@ __device__ __forceinline__ void stream_rows(const bf16_t* wa, const bf16_t* wb, 
     acc_b = mfma16x16x32(as_bf16x8(rb[d]), bx, acc_b);
   };
   const int nfull = nK / D;
+  // Enter the loop with no load outstanding (the staging before it already
+  // waited on younger loads), so the wait at the loop head needs to cover
+  // only the slot it consumes.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   for (int g = 0; g < nfull; ++g) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       mma(d, g * D + d);
       const int kk = min((g + 1) * D + d, nK - 1);  // past the end: a repeat of the last step, never used
-      ra[d] = ldg16(wa + kk * 32);
-      rb[d] = ldg16(wb + kk * 32);
+      ra[d] = ldg16(wa + kk * 1024);
+      rb[d] = ldg16(wb + kk * 1024);
+    }
+    // keep each step's order -- LDS read, its two MFMAs, then the two loads
+    // that refill the same slot -- so loads leave in step order and the wait
+    // before a step covers only its own slot, not the whole pipeline
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // VMEM read
     }
   }
   const int rem = nK - nfull * D;
@@ -67,12 +83,12 @@ __device__ __forceinline__ void stream_rows(const bf16_t* wa, const bf16_t* wb, 
     if (d < rem) mma(d, nfull * D + d);
 }
 
-// GATED: x = token rows [T,K] read through gather, W = [G, 2N, K] (gate rows
-//        0..N-1, up rows N..2N-1), out = a [n_rows, N]; wavefront w owns output
+// GATED: x = token rows [T,K] read through gather, W = [G, 2N, K] packed as
+//        gate/up pairs (gate rows 16p.., up rows N+16p..), out = a [n_rows, N]; wavefront w owns output
 //        columns 16w..16w+15 of a 128-column block tile (its 16 gate rows and
 //        16 up rows are the two streamed row sets).
-// plain: x = activation rows [n_rows, K] read directly, W = [G, N, K],
-//        out = y [n_rows, N]; wavefront w owns output columns 32w..32w+31 of a
+// plain: x = activation rows [n_rows, K] read directly, W = [G, N, K] packed
+//        as row pairs, out = y [n_rows, N]; wavefront w owns output columns 32w..32w+31 of a
 //        256-column block tile (two 16-row sets), so that every wavefront
 //        streams as many bytes per k-step as in the gated stage.
 // A block of 8 wavefronts owns one column tile of one group and one range of
@@ -148,14 +164,13 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col0 = ct * (kWaves * WCOLS) + wave * WCOLS;
   const bool active = col0 < N;
-  const size_t gstride = (GATED ? (size_t)2 * N : (size_t)N) * K;
-  const int wrow = min(col0 + (lane & 15), N - 1);
-  const bf16_t* wa = W + g * gstride + (size_t)wrow * K + (lane >> 4) * 8;
-  // second row set: the up rows (gated) or the next 16 output columns (plain;
-  // clamped to a valid row past N -- never stored)
-  const bf16_t* wb = GATED ? wa + (size_t)N * K
-                           : W + g * gstride + (size_t)min(col0 + 16 + (lane & 15), N - 1) * K + (lane >> 4) * 8;
+  // packed weights: [group][pair][k-step][set][lane][8]; a pair is this
+  // wavefront's two 16-row sets, a (pair, k-step) is 2 KB of consecutive bytes
   const int nK = K / 32;
+  const int n_pairs = GATED ? N / 16 : (N + 31) / 32;
+  const int pair = min(col0 / WCOLS, n_pairs - 1);  // inactive wavefronts load a valid pair, store nothing
+  const bf16_t* wa = W + ((size_t)g * n_pairs + pair) * nK * 1024 + lane * 8;
+  const bf16_t* wb = wa + 512;
   const int ldr = lds_row(K);
   const int nseg = K / 8;                 // 16-byte segments per activation row
 
@@ -165,8 +180,8 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       const int kk = min(d, nK - 1);
-      ra[d] = ldg16(wa + kk * 32);
-      rb[d] = ldg16(wb + kk * 32);
+      ra[d] = ldg16(wa + kk * 1024);
+      rb[d] = ldg16(wb + kk * 1024);
     }
     // stage the range's activation rows (rows past the group repeat a valid row)
     for (int i = threadIdx.x; i < kRows * nseg; i += kBlockThreads * 4) {

@@ -11,6 +11,24 @@ size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 }  // namespace
 
+int pack_pairs(int N, int kind) { return kind == 0 ? N / 16 : (N + 31) / 32; }
+
+size_t packed_bytes(int G, int N, int K, int kind) {
+  if (G <= 0 || N <= 0 || K <= 0 || (kind != 0 && kind != 1)) return 0;
+  // per pair: K/32 steps x 2 sets x 1 KB fragment
+  return (size_t)G * (size_t)pack_pairs(N, kind) * (size_t)(K / 32) * 2 * 1024;
+}
+
+int check_pack(const void* src, const void* dst, int G, int N, int K, int kind, int dtype) {
+  if (dtype != kBf16) return kErrUnsupported;  // fp32 weights stay row-major
+  if (kind != 0 && kind != 1) return kErrUnsupported;
+  if (G < 0 || N <= 0 || K <= 0 || K % 32 != 0 || (kind == 0 && N % 16 != 0)) return kErrShape;
+  if (G == 0) return kOk;
+  if (!src || !dst) return kErrNull;
+  if (!aligned16(src) || !aligned16(dst)) return kErrAlign;
+  return kOk;
+}
+
 size_t permute_ws_bytes(int T, int k, int E) {
   if (T <= 0 || k <= 0 || E <= 0) return 0;
   long long slots = (long long)T * k;

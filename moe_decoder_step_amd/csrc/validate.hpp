@@ -19,6 +19,10 @@ constexpr int kPermuteChunk = 4096;  // slots per block of the permutation kerne
 constexpr int kLmRowsPerBlock = 128; // vocabulary rows per LM-head block (bf16 path)
 constexpr int kLmF32RowsPerBlock = 256;
 
+int pack_pairs(int N, int kind);
+size_t packed_bytes(int G, int N, int K, int kind);
+int check_pack(const void* src, const void* dst, int G, int N, int K, int kind, int dtype);
+
 size_t permute_ws_bytes(int T, int k, int E);
 size_t swiglu_ws_bytes(int n_rows, int I, int dtype);
 size_t lmhead_ws_bytes(int T, int V, int dtype);

@@ -15,9 +15,9 @@ import torch
 from . import _lib as L
 
 __all__ = [
-    "moe_route", "moe_permute", "moe_grouped_swiglu", "moe_combine", "lmhead_argmax",
+    "Packed", "pack_weights", "packed_weights_bytes", "moe_route", "moe_permute", "moe_grouped_swiglu", "moe_combine", "lmhead_argmax",
     "spec_verify", "spec_plant_drafts", "permute_workspace_bytes", "swiglu_workspace_bytes",
-    "lmhead_workspace_bytes", "dtype_code", "route_alloc", "permute_alloc", "swiglu_alloc",
+    "lmhead_workspace_bytes", "dtype_code", "expert_weights", "lm_weights", "route_alloc", "permute_alloc", "swiglu_alloc",
     "combine_alloc", "lmhead_alloc", "verify_alloc",
 ]
 
@@ -47,6 +47,55 @@ def _need(t, dtype, name):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+class Packed:
+    """bf16 weights in the fragment layout the streaming kernels read
+    (moe_pack_weights).  `shape` is the logical row-major shape."""
+
+    def __init__(self, data: torch.Tensor, shape, kind: int):
+        self.data = data
+        self.shape = tuple(int(v) for v in shape)
+        self.kind = kind
+        self.dtype = torch.bfloat16
+        self.device = data.device
+        self.is_cuda = data.is_cuda
+
+    def data_ptr(self) -> int:
+        return self.data.data_ptr()
+
+    def is_contiguous(self) -> bool:
+        return True
+
+
+def packed_weights_bytes(G: int, N: int, K: int, kind: int) -> int:
+    return int(L.load().moe_packed_weights_bytes(G, N, K, kind))
+
+
+def pack_weights(w: torch.Tensor, kind: int) -> Packed:
+    """Pack row-major bf16 weights: [G, 2N, K] (gate/up, kind PACK_GATE_UP),
+    [G, N, K] or [N, K] (kind PACK_ROWS)."""
+    _need(w, torch.bfloat16, "w")
+    shape = tuple(w.shape)
+    G, R, K = (1, *shape) if w.dim() == 2 else shape
+    N = R // 2 if kind == L.PACK_GATE_UP else R
+    nbytes = packed_weights_bytes(G, N, K, kind)
+    out = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=w.device)
+    L.check("moe_pack_weights", L.load().moe_pack_weights(
+        _p(w), _p(out), G, N, K, kind, L.BF16, _stream(w)))
+    return Packed(out, shape, kind)
+
+
+def expert_weights(w_gate_up: torch.Tensor, w_down: torch.Tensor):
+    """The weights the grouped SwiGLU reads: packed for bf16, as they are for fp32."""
+    if w_gate_up.dtype == torch.bfloat16:
+        return pack_weights(w_gate_up, L.PACK_GATE_UP), pack_weights(w_down, L.PACK_ROWS)
+    return w_gate_up, w_down
+
+
+def lm_weights(w_lm: torch.Tensor):
+    """The LM-head weight lmhead_argmax reads: packed for bf16, as it is for fp32."""
+    return pack_weights(w_lm, L.PACK_ROWS) if w_lm.dtype == torch.bfloat16 else w_lm
 
 
 def permute_workspace_bytes(T: int, k: int, E: int) -> int:
@@ -92,6 +141,9 @@ def moe_grouped_swiglu(x, gather, offsets, w_gate_up, w_down, y, ws, max_rows=No
     T, H = x.shape
     G, I2, _ = w_gate_up.shape
     n_rows = y.shape[0]
+    if x.dtype == torch.bfloat16 and not (isinstance(w_gate_up, Packed) and w_gate_up.kind == L.PACK_GATE_UP
+                                          and isinstance(w_down, Packed) and w_down.kind == L.PACK_ROWS):
+        raise TypeError("bf16 expert weights must be packed (expert_weights / pack_weights)")
     for t, d, n in ((x, None, "x"), (gather, torch.int32, "gather"), (offsets, torch.int32, "offsets"),
                     (w_gate_up, x.dtype, "w_gate_up"), (w_down, x.dtype, "w_down"), (y, x.dtype, "y"), (ws, None, "ws")):
         _need(t, d, n)
@@ -118,6 +170,8 @@ def lmhead_argmax(h, w_lm, argmax_ids, max_logit, ws):
     """Greedy token per row: argmax of h @ W_lm^T, ties to the lowest id."""
     T, H = h.shape
     V = w_lm.shape[0]
+    if h.dtype == torch.bfloat16 and not (isinstance(w_lm, Packed) and w_lm.kind == L.PACK_ROWS):
+        raise TypeError("a bf16 LM head must be packed (lm_weights / pack_weights)")
     for t, d, n in ((h, None, "h"), (w_lm, h.dtype, "w_lm"), (argmax_ids, torch.int32, "argmax_ids"),
                     (max_logit, torch.float32, "max_logit"), (ws, None, "ws")):
         _need(t, d, n)

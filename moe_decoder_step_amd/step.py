@@ -22,8 +22,15 @@ class VerifyStack:
     def __init__(self, layers: list[dict], w_lm: torch.Tensor | None, E: int, k: int, S: int,
                  max_tokens: int, max_seqs: int = 0, K: int = 0, eps: float = 1e-6,
                  keep_logits: bool = False):
-        self.layers = layers
-        self.w_lm = w_lm
+        """layers: per layer w_router [E,H] fp32, bias [E] fp32 (or absent),
+        w_gate_up [E+S, 2I, H], w_down [E+S, H, I] row-major; w_lm [V, H].
+        bf16 expert and LM-head weights are packed here (moe_pack_weights)
+        into the stack's own copies; the caller may drop its tensors."""
+        self.layers = []
+        for w in layers:
+            gu, dn = ops.expert_weights(w["w_gate_up"], w["w_down"])
+            self.layers.append({"w_router": w["w_router"], "bias": w.get("bias"), "w_gate_up": gu, "w_down": dn})
+        self.w_lm = None if w_lm is None else ops.lm_weights(w_lm)
         # when a list: (start, end) torch.cuda.Event pairs around every grouped
         # SwiGLU launch, recorded on the stream the kernels run on
         self.ffn_events = None

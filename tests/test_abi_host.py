@@ -21,7 +21,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = L.header_functions()
-    assert len(names) == 12
+    assert len(names) == 14
     assert set(names) == set(L.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
@@ -42,6 +42,19 @@ def test_workspace_queries(lib):
     assert lib.moe_grouped_swiglu_workspace_bytes(1024, 896, m.F32) >= 1024 * 896 * 4
     assert lib.lmhead_argmax_workspace_bytes(128, 129280, m.BF16) >= 128 * 1010 * 8
     assert lib.lmhead_argmax_workspace_bytes(0, 129280, m.BF16) == 0
+
+
+def test_pack_checks(lib):
+    f = lib.moe_pack_weights
+    assert lib.moe_packed_weights_bytes(66, 896, 1280, 0) == 66 * 2 * 896 * 1280 * 2
+    assert lib.moe_packed_weights_bytes(1, 77, 64, 1) == 3 * 2 * 2 * 1024   # rows padded to pairs of 32
+    assert f(A, A, 66, 896, 1280, 0, m.F32, None) == L.ERR_UNSUPPORTED       # fp32 weights stay row-major
+    assert f(A, A, 66, 896, 1280, 2, m.BF16, None) == L.ERR_UNSUPPORTED
+    assert f(A, A, 66, 896, 1290, 0, m.BF16, None) == L.ERR_SHAPE
+    assert f(A, A, 66, 900, 1280, 0, m.BF16, None) == L.ERR_SHAPE
+    assert f(None, A, 66, 896, 1280, 0, m.BF16, None) == L.ERR_NULL
+    assert f(MIS, A, 66, 896, 1280, 0, m.BF16, None) == L.ERR_ALIGN
+    assert f(None, None, 0, 896, 1280, 0, m.BF16, None) == L.OK
 
 
 def test_route_checks(lib):

@@ -36,6 +36,37 @@ def _host_layer(w):
     return {k: host(v) for k, v in w.items()}
 
 
+# --------------------------------------------------------------------------- weight packing
+
+def _pack_reference(w, kind):
+    """The packed layout written out with numpy index arithmetic (test side)."""
+    w = np.asarray(w)
+    if w.ndim == 2:
+        w = w[None]
+    G, R, K = w.shape
+    N = R // 2 if kind == 0 else R
+    P = N // 16 if kind == 0 else (N + 31) // 32
+    out = np.zeros((G, P, K // 32, 2, 64, 8), dtype=w.dtype)
+    for p in range(P):
+        for h in range(2):
+            for l in range(64):
+                row = h * N + 16 * p + l % 16 if kind == 0 else 32 * p + 16 * h + l % 16
+                if kind == 1 and row >= N:
+                    continue
+                for s in range(K // 32):
+                    c = 32 * s + 8 * (l // 16)
+                    out[:, p, s, h, l, :] = w[:, row, c:c + 8]
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("kind,shape", [(0, (3, 64, 96)), (1, (2, 96, 64)), (1, (77, 64)), (0, (1, 32, 32))])
+def test_pack_weights_layout(m, kind, shape):
+    w = (torch.randn(shape, device=DEV) * 0.02).to(torch.bfloat16)
+    pk = m.pack_weights(w, kind)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(pk.data), _pack_reference(host(w), kind))
+
+
 # --------------------------------------------------------------------------- route
 
 @pytest.mark.parametrize("shape,T", [("tiny", 16), ("layer128", 128), ("layer128", 1), ("layer128", 37),
@@ -111,7 +142,8 @@ def test_grouped_swiglu(m, shape, T):
     xn, ids, tw, _ = m.route_alloc(h, w["w_router"], None, sh.k)
     off, gat, inv = m.permute_alloc(ids, sh.E, sh.S)
     n_rows = T * sh.k + sh.S * T
-    y = m.swiglu_alloc(xn, gat, off, w["w_gate_up"], w["w_down"], n_rows, max_rows=T)
+    wgu_p, wd_p = m.expert_weights(w["w_gate_up"], w["w_down"])
+    y = m.swiglu_alloc(xn, gat, off, wgu_p, wd_p, n_rows, max_rows=T)
     torch.cuda.synchronize()
     # oracle: every group on the GPU's own xn and permutation
     xh = O.f64(host(xn))
@@ -138,8 +170,9 @@ def test_grouped_swiglu_identity_gather_and_skewed_groups(m):
     wd = (torch.randn(G, H, I, generator=gen, device=DEV) * 0.02).to(torch.bfloat16)
     off = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32, device=DEV)
     n_rows = int(sum(counts))
+    wgu_p, wd_p = m.expert_weights(wgu, wd)
     for max_rows in (16, 100):
-        y = m.swiglu_alloc(x, None, off, wgu, wd, n_rows, max_rows=max_rows)
+        y = m.swiglu_alloc(x, None, off, wgu_p, wd_p, n_rows, max_rows=max_rows)
         torch.cuda.synchronize()
         xh, yg = O.f64(host(x)), as_f64(y)
         for g, c in enumerate(counts):
@@ -191,7 +224,7 @@ def test_lmhead_argmax(m, dtype, T, H, V):
     gen = torch.Generator(device=DEV).manual_seed(T + V)
     h = torch.randn(T, H, generator=gen, device=DEV).to(dtype)
     W = (torch.randn(V, H, generator=gen, device=DEV) * 0.02).to(dtype)
-    ids, mx = m.lmhead_alloc(h, W)
+    ids, mx = m.lmhead_alloc(h, m.lm_weights(W))
     torch.cuda.synchronize()
     rid, rmx, gap = O.lm_argmax(host(h), host(W))
     nflag, flagged = compare_ids(ids.cpu().numpy(), rid, gap, "argmax")
@@ -205,7 +238,7 @@ def test_lmhead_ties_go_to_lowest_id(m):
     W[2900] = W[17]
     W[1500] = W[17]
     h = (W[17:18].float() * 50).to(torch.bfloat16).repeat(3, 1)
-    ids, _ = m.lmhead_alloc(h, W)
+    ids, _ = m.lmhead_alloc(h, m.lm_weights(W))
     assert (ids.cpu() == 17).all()
 
 
