@@ -61,10 +61,12 @@ typedef enum { MOE_BF16 = 0, MOE_F32 = 1 } moe_dtype;
 /* moe_pack_weights kinds */
 #define MOE_PACK_GATE_UP 0  /* [G, 2N, K]: gate rows 0..N-1, up rows N..2N-1 */
 #define MOE_PACK_ROWS 1     /* [G, N, K]: plain rows (down projection, LM head) */
+#define MOE_PACK_ROUTER 2   /* fp32 router weight [G, E, K], E <= 64 */
 
 /* moe_route flags */
 #define MOE_ROUTE_NORM 1    /* apply RMSNorm before the router (else xn = h) */
 #define MOE_ROUTE_RENORM 2  /* softmax over the k selected logits (else full-softmax probabilities) */
+#define MOE_ROUTE_WPACKED 4 /* w_router is in the MOE_PACK_ROUTER layout (else row-major [E,H]) */
 
 /* Version of this ABI (MOE_ABI_VERSION). */
 int moe_abi_version(void);
@@ -86,9 +88,15 @@ const char* moe_status_str(int status);
  *   MOE_PACK_ROWS:    src [G, N, K];  row = 32p + 16h + l%16 (p < ceil(N/32));
  *                     rows at or past N are zero
  * src and dst: bf16, 16-byte aligned, not overlapping; dst holds
- * moe_packed_weights_bytes(G, N, K, kind) bytes.  MOE_F32 weights are used
- * row-major and are not packed (MOE_ERR_UNSUPPORTED).
+ * moe_packed_weights_bytes(G, N, K, kind) bytes.  MOE_F32 expert and LM-head
+ * weights are used row-major and are not packed (MOE_ERR_UNSUPPORTED).
  * Limits: K % 32 == 0; N % 16 == 0 for MOE_PACK_GATE_UP.
+ *
+ * MOE_PACK_ROUTER (dtype MOE_F32): src is the router weight [G, E, K] with
+ * E <= 64 experts (N = E) and K % 4 == 0; dst[g][q][e][j] = src[g][e][4q + j]
+ * for e < E and 0 for E <= e < 64 (G * K/4 * 64 * 4 floats), the layout
+ * moe_route reads with MOE_ROUTE_WPACKED: one expert per lane, four hidden
+ * elements per 16-byte load, 1 KB per wavefront load.
  * ------------------------------------------------------------------------- */
 size_t moe_packed_weights_bytes(int G, int N, int K, int kind);
 int moe_pack_weights(const void* src, void* dst, int G, int N, int K, int kind, int dtype,
@@ -110,7 +118,8 @@ int moe_pack_weights(const void* src, void* dst, int G, int N, int K, int kind, 
  *
  * h        [T,H] dtype             in
  * gain     [H] fp32 or NULL (= 1)  in
- * w_router [E,H] fp32, bias [E] fp32 or NULL   in
+ * w_router [E,H] fp32 row-major, or packed (MOE_PACK_ROUTER) with
+ *          MOE_ROUTE_WPACKED;  bias [E] fp32 or NULL   in
  * xn       [T,H] dtype             out (the normed input the experts read)
  * topk_ids [T,k] int32, topk_w [T,k] fp32      out
  * logits   [T,E] fp32 or NULL      out (optional, for near-tie diagnostics)

@@ -15,8 +15,8 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "moestep.h")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP = range(7)
 BF16, F32 = 0, 1
-ROUTE_NORM, ROUTE_RENORM = 1, 2
-PACK_GATE_UP, PACK_ROWS = 0, 1
+ROUTE_NORM, ROUTE_RENORM, ROUTE_WPACKED = 1, 2, 4
+PACK_GATE_UP, PACK_ROWS, PACK_ROUTER = 0, 1, 2
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int

@@ -34,6 +34,7 @@ size_t moe_packed_weights_bytes(int G, int N, int K, int kind) { return moe::pac
 int moe_pack_weights(const void* src, void* dst, int G, int N, int K, int kind, int dtype, void* stream) {
   int st = moe::check_pack(src, dst, G, N, K, kind, dtype);
   if (st != MOE_OK || G == 0) return st;
+  if (kind == MOE_PACK_ROUTER) return hip_status(moe::launch_pack_router(src, dst, G, N, K, as_stream(stream)));
   return hip_status(moe::launch_pack(src, dst, G, N, K, kind, as_stream(stream)));
 }
 

@@ -71,6 +71,34 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
   return v;
 }
 
+// Wavefront-wide max / sum with DPP lane moves (no LDS round trip): quad
+// swaps, half-row and row mirrors, then row broadcasts carry the result to
+// lane 63, which every lane reads back.  The sum adds in a fixed tree order.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));        // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f32<0x4E>(v));        // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f32<0x141>(v));       // row_half_mirror
+  v = fmaxf(v, dpp_f32<0x140>(v));       // row_mirror
+  v = fmaxf(v, dpp_f32<0x142, 0xA>(v));  // row_bcast:15
+  v = fmaxf(v, dpp_f32<0x143, 0xC>(v));  // row_bcast:31
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x141>(v);
+  v += dpp_f32<0x140>(v);
+  v += dpp_f32<0x142, 0xA>(v);
+  v += dpp_f32<0x143, 0xC>(v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 // Order-preserving map of a float onto uint32 (larger float -> larger key).
 __device__ __forceinline__ uint32_t float_key(float f) {
   uint32_t u = __float_as_uint(f);

@@ -8,6 +8,7 @@
 namespace moe {
 
 hipError_t launch_pack(const void* src, void* dst, int G, int N, int K, int kind, hipStream_t s);
+hipError_t launch_pack_router(const void* src, void* dst, int G, int E, int K, hipStream_t s);
 
 hipError_t launch_route(const void* h, const float* gain, float eps, const float* w_router,
                         const float* bias, int T, int H, int E, int k, int flags, int dtype,

@@ -15,6 +15,11 @@
 //                     gate rows 16p.. (set 0) and up rows N + 16p.. (set 1);
 //   MOE_PACK_ROWS:    W is [G, N, K]; pair p holds rows 32p + 16h + (0..15);
 //                     rows at or past N are zero.
+//
+// The fp32 router weight [G, E, K] (E <= 64 experts, one per lane) is packed
+// as packed[g][q][e][j] = W[g][e][4q + j] (MOE_PACK_ROUTER; experts past E
+// are zero), so a wavefront's 16-byte loads of four hidden elements for its
+// 64 expert lanes are 1 KB of consecutive bytes.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "validate.hpp"
@@ -50,7 +55,27 @@ __global__ __launch_bounds__(256) void pack_kernel(const bf16_t* __restrict__ sr
   *reinterpret_cast<uint4*>(dst + idx * 8) = v;
 }
 
+__global__ __launch_bounds__(256) void pack_router_kernel(const float* __restrict__ src, float* __restrict__ dst,
+                                                          int E, int K, long long total) {
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;  // one float4
+  if (idx >= total) return;
+  const int e = (int)(idx % 64);
+  const long long r = idx / 64;
+  const int q = (int)(r % (K / 4));
+  const int g = (int)(r / (K / 4));
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (e < E) v = *reinterpret_cast<const float4*>(src + ((size_t)g * E + e) * K + 4 * q);
+  *reinterpret_cast<float4*>(dst + idx * 4) = v;
+}
+
 }  // namespace
+
+hipError_t launch_pack_router(const void* src, void* dst, int G, int E, int K, hipStream_t s) {
+  const long long total = (long long)G * (K / 4) * 64;
+  hipLaunchKernelGGL(pack_router_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                     static_cast<const float*>(src), static_cast<float*>(dst), E, K, total);
+  return hipGetLastError();
+}
 
 hipError_t launch_pack(const void* src, void* dst, int G, int N, int K, int kind, hipStream_t s) {
   const int n_pairs = pack_pairs(N, kind);

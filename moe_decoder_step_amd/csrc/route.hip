@@ -1,15 +1,17 @@
 // moe_route: pre-RMSNorm, fp32 router logits and top-k routing of each token.
 //
-// A block of 8 wavefronts owns TPB tokens:
-//   1. norm: wavefront w normalises tokens w, w+8, ... (fp64 scale, one
+// A block of 16 wavefronts owns TPB tokens:
+//   1. norm: wavefront w normalises tokens w, w+16, ... (fp64 scale, one
 //      rounding to the storage type) into LDS and to xn;
-//   2. logits: the hidden dimension is split in eight slices, one per
+//   2. logits: the hidden dimension is split in sixteen slices, one per
 //      wavefront; lane e (= expert e, E <= 64) accumulates its slice of
-//      l[t,e] for all TPB tokens in fp32, reading its router row with 16-byte
-//      loads and the normed tokens from LDS (broadcast);
-//   3. top-k: wavefront w sums the eight slices in order (a fixed order that
+//      l[t,e] for all TPB tokens in fp32, its router row slice having been
+//      loaded into registers at kernel entry (it does not depend on the norm),
+//      the normed tokens read from LDS (broadcast);
+//   3. top-k: wavefront w sums the sixteen slices in order (a fixed order that
 //      does not depend on the batch), adds the bias and runs k rounds of a
-//      wavefront-wide max over 64-bit (logit, lower id) keys, then the
+//      DPP wavefront max followed by a ballot: the lowest lane holding the
+//      maximum wins, which is the lower-id rule for equal logits; then the
 //      softmax weights.
 // Decode batches use 2 tokens per block so that a 128-token batch spreads
 // over 64 blocks; large batches use up to 16 to amortise the router reads.
@@ -20,7 +22,8 @@
 namespace moe {
 namespace {
 
-constexpr int kWaves = 8;      // wavefronts per block (hidden split in 8 slices)
+constexpr int kWaves = 16;     // wavefronts per block (hidden split in 16 slices)
+constexpr int kPre = 20;       // router-weight float4 per lane loaded at kernel entry
 constexpr int kThreads = kWaves * 64;
 
 __device__ __forceinline__ void load8(const bf16_t* p, float* f) { unpack8(ldg16(p), f); }
@@ -48,7 +51,7 @@ __device__ __forceinline__ float4 lds4(const bf16_t* p) {
 }
 __device__ __forceinline__ float4 lds4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 
-template <typename St, int TPB>
+template <typename St, int TPB, bool PACKED>
 __global__ __launch_bounds__(kThreads) void route_kernel(
     const St* __restrict__ h, const float* __restrict__ gain, float eps,
     const float* __restrict__ wr, const float* __restrict__ bias, int T, int H, int E, int k,
@@ -60,6 +63,21 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t0 = blockIdx.x * TPB;
+  const int e = lane;
+
+  // this wavefront's slice of the hidden dim; its router weights go out first
+  // (they do not depend on the norm) and land while the norm runs
+  const int hq = ((H / kWaves + 3) / 4) * 4;
+  const int h_lo = min(H, wave * hq), h_hi = min(H, h_lo + hq);
+  // router weights of hidden elements hh..hh+3 for this lane's expert: packed,
+  // a wavefront load is 1 KB of consecutive bytes; row-major, it touches 64 rows
+  auto wload = [&](int hh) __attribute__((always_inline)) -> float4 {
+    if (PACKED) return *reinterpret_cast<const float4*>(wr + ((size_t)(hh >> 2) * kWave + e) * 4);
+    return *reinterpret_cast<const float4*>(wr + (size_t)min(e, E - 1) * H + hh);
+  };
+  float4 wpre[kPre];
+#pragma unroll
+  for (int u = 0; u < kPre; ++u) wpre[u] = wload(min(h_lo + 4 * u, H - 4));
 
   // ---- 1. RMSNorm: xn = h / sqrt(mean(h^2) + eps) * gain, scale in fp64, one rounding ----
   const bool norm = (flags & 1) != 0;
@@ -99,32 +117,11 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   }
   __syncthreads();
 
-  // ---- 2. partial logits over this wavefront's slice of the hidden dim ----
-  const int hq = ((H / kWaves + 3) / 4) * 4;
-  const int h_lo = min(H, wave * hq), h_hi = min(H, h_lo + hq);
-  const int e = lane;
-  const float* wrow = wr + (size_t)min(e, E - 1) * H;
+  // ---- 2. partial logits over this wavefront's slice, fp32, ascending h ----
   float acc[TPB];
 #pragma unroll
   for (int i = 0; i < TPB; ++i) acc[i] = 0.f;
-  int hh = h_lo;
-  for (; hh + 32 <= h_hi; hh += 32) {
-    float4 w4[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) w4[u] = *reinterpret_cast<const float4*>(wrow + hh + 4 * u);
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-#pragma unroll
-      for (int i = 0; i < TPB; ++i) {
-        const float4 x = lds4(xs + i * H + hh + 4 * u);
-        acc[i] = fmaf(x.x, w4[u].x, acc[i]);
-        acc[i] = fmaf(x.y, w4[u].y, acc[i]);
-        acc[i] = fmaf(x.z, w4[u].z, acc[i]);
-        acc[i] = fmaf(x.w, w4[u].w, acc[i]);
-      }
-  }
-  for (; hh < h_hi; hh += 4) {
-    const float4 w = *reinterpret_cast<const float4*>(wrow + hh);
+  auto fma4 = [&](const float4& w, int hh) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < TPB; ++i) {
       const float4 x = lds4(xs + i * H + hh);
@@ -133,7 +130,11 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
       acc[i] = fmaf(x.z, w.z, acc[i]);
       acc[i] = fmaf(x.w, w.w, acc[i]);
     }
-  }
+  };
+#pragma unroll
+  for (int u = 0; u < kPre; ++u)
+    if (h_lo + 4 * u < h_hi) fma4(wpre[u], h_lo + 4 * u);
+  for (int hh = h_lo + 4 * kPre; hh < h_hi; hh += 4) fma4(wload(hh), hh);
 #pragma unroll
   for (int i = 0; i < TPB; ++i) part[(wave * TPB + i) * kWave + e] = acc[i];
   __syncthreads();
@@ -148,19 +149,22 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     for (int w = 1; w < kWaves; ++w) l += part[(w * TPB + i) * kWave + e];
     if (bias && valid) l += bias[e];
     if (logits && valid) logits[(size_t)t * E + e] = l;
-    const unsigned long long key = valid ? (((unsigned long long)float_key(l) << 32) | (uint32_t)(255 - e)) : 0ull;
+    // k rounds: the largest remaining logit, then the lowest lane holding it
+    float cur = valid ? l : -INFINITY;
     int rank = -1;
     float lmax = 0.f;
     for (int j = 0; j < k; ++j) {
-      const unsigned long long best = wave_max_u64(rank < 0 ? key : 0ull);
-      if (j == 0) lmax = key_float((uint32_t)(best >> 32));
-      if (e == 255 - (int)(best & 0xffu)) rank = j;
+      const float m = wave_max_dpp(cur);
+      const unsigned long long hit = __ballot(cur == m);
+      const int win = (int)__builtin_ctzll(hit);
+      if (j == 0) lmax = m;
+      if (e == win) {
+        rank = j;
+        cur = -INFINITY;
+      }
     }
     const float z = rank >= 0 ? expf(l - lmax) : 0.f;
-    float den;
-    if (flags & 2) den = wave_sum_f32(z);
-    else den = wave_sum_f32(valid ? expf(l - lmax) : 0.f);
-    den = __shfl(den, 0, kWave);
+    const float den = (flags & 2) ? wave_sum_dpp(z) : wave_sum_dpp(valid ? expf(l - lmax) : 0.f);
     if (rank >= 0) {
       ids[(size_t)t * k + rank] = e;
       wts[(size_t)t * k + rank] = z / den;
@@ -179,9 +183,14 @@ hipError_t launch_tpb(const void* h, const float* gain, float eps, const float* 
                       float* logits, hipStream_t s) {
   const int grid = (T + TPB - 1) / TPB;
   const size_t lds = lds_bytes<St, TPB>(H);
-  hipLaunchKernelGGL((route_kernel<St, TPB>), dim3(grid), dim3(kThreads), lds, s,
-                     static_cast<const St*>(h), gain, eps, wr, bias, T, H, E, k, flags,
-                     static_cast<St*>(xn), ids, w, logits);
+  if (flags & 4)
+    hipLaunchKernelGGL((route_kernel<St, TPB, true>), dim3(grid), dim3(kThreads), lds, s,
+                       static_cast<const St*>(h), gain, eps, wr, bias, T, H, E, k, flags,
+                       static_cast<St*>(xn), ids, w, logits);
+  else
+    hipLaunchKernelGGL((route_kernel<St, TPB, false>), dim3(grid), dim3(kThreads), lds, s,
+                       static_cast<const St*>(h), gain, eps, wr, bias, T, H, E, k, flags,
+                       static_cast<St*>(xn), ids, w, logits);
   return hipGetLastError();
 }
 

@@ -14,14 +14,24 @@ size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 int pack_pairs(int N, int kind) { return kind == 0 ? N / 16 : (N + 31) / 32; }
 
 size_t packed_bytes(int G, int N, int K, int kind) {
-  if (G <= 0 || N <= 0 || K <= 0 || (kind != 0 && kind != 1)) return 0;
+  if (G <= 0 || N <= 0 || K <= 0 || kind < 0 || kind > 2) return 0;
+  if (kind == 2) return (size_t)G * (size_t)(K / 4) * kMaxExperts * 4 * sizeof(float);
   // per pair: K/32 steps x 2 sets x 1 KB fragment
   return (size_t)G * (size_t)pack_pairs(N, kind) * (size_t)(K / 32) * 2 * 1024;
 }
 
 int check_pack(const void* src, const void* dst, int G, int N, int K, int kind, int dtype) {
-  if (dtype != kBf16) return kErrUnsupported;  // fp32 weights stay row-major
-  if (kind != 0 && kind != 1) return kErrUnsupported;
+  if (kind < 0 || kind > 2) return kErrUnsupported;
+  if (kind == 2) {  // router: fp32 [G, E, K], E <= 64
+    if (dtype != kF32) return kErrUnsupported;
+    if (G < 0 || N <= 0 || K <= 0 || K % 4 != 0) return kErrShape;
+    if (N > kMaxExperts) return kErrUnsupported;
+    if (G == 0) return kOk;
+    if (!src || !dst) return kErrNull;
+    if (!aligned16(src) || !aligned16(dst)) return kErrAlign;
+    return kOk;
+  }
+  if (dtype != kBf16) return kErrUnsupported;  // fp32 expert weights stay row-major
   if (G < 0 || N <= 0 || K <= 0 || K % 32 != 0 || (kind == 0 && N % 16 != 0)) return kErrShape;
   if (G == 0) return kOk;
   if (!src || !dst) return kErrNull;

@@ -17,7 +17,7 @@ from . import _lib as L
 __all__ = [
     "Packed", "pack_weights", "packed_weights_bytes", "moe_route", "moe_permute", "moe_grouped_swiglu", "moe_combine", "lmhead_argmax",
     "spec_verify", "spec_plant_drafts", "permute_workspace_bytes", "swiglu_workspace_bytes",
-    "lmhead_workspace_bytes", "dtype_code", "expert_weights", "lm_weights", "route_alloc", "permute_alloc", "swiglu_alloc",
+    "lmhead_workspace_bytes", "dtype_code", "expert_weights", "lm_weights", "router_weights", "route_alloc", "permute_alloc", "swiglu_alloc",
     "combine_alloc", "lmhead_alloc", "verify_alloc",
 ]
 
@@ -50,14 +50,15 @@ def _need(t, dtype, name):
 
 
 class Packed:
-    """bf16 weights in the fragment layout the streaming kernels read
-    (moe_pack_weights).  `shape` is the logical row-major shape."""
+    """Weights in the layout the streaming kernels read (moe_pack_weights):
+    bf16 expert / LM-head fragments, or the fp32 router layout.  `shape` is
+    the logical row-major shape."""
 
     def __init__(self, data: torch.Tensor, shape, kind: int):
         self.data = data
         self.shape = tuple(int(v) for v in shape)
         self.kind = kind
-        self.dtype = torch.bfloat16
+        self.dtype = data.dtype
         self.device = data.device
         self.is_cuda = data.is_cuda
 
@@ -86,6 +87,17 @@ def pack_weights(w: torch.Tensor, kind: int) -> Packed:
     return Packed(out, shape, kind)
 
 
+def router_weights(w_router: torch.Tensor) -> Packed:
+    """Pack an fp32 router weight [E, H] (E <= 64) for moe_route."""
+    _need(w_router, torch.float32, "w_router")
+    E, H = w_router.shape
+    nbytes = packed_weights_bytes(1, E, H, L.PACK_ROUTER)
+    out = torch.empty(nbytes // 4, dtype=torch.float32, device=w_router.device)
+    L.check("moe_pack_weights", L.load().moe_pack_weights(
+        _p(w_router), _p(out), 1, E, H, L.PACK_ROUTER, L.F32, _stream(w_router)))
+    return Packed(out, (E, H), L.PACK_ROUTER)
+
+
 def expert_weights(w_gate_up: torch.Tensor, w_down: torch.Tensor):
     """The weights the grouped SwiGLU reads: packed for bf16, as they are for fp32."""
     if w_gate_up.dtype == torch.bfloat16:
@@ -112,15 +124,20 @@ def lmhead_workspace_bytes(T: int, V: int, dtype: torch.dtype) -> int:
 
 def moe_route(h, w_router, bias, k, xn, topk_ids, topk_w, logits=None, gain=None, eps=1e-6,
               norm=True, renormalize=True):
-    """RMSNorm + router logits + top-k + routing weights (see moe_route in moestep.h)."""
+    """RMSNorm + router logits + top-k + routing weights (see moe_route in moestep.h).
+    `w_router` is the fp32 [E, H] weight, row-major or packed (router_weights)."""
     T, H = h.shape
     E = w_router.shape[0]
+    packed = isinstance(w_router, Packed)
+    if packed and w_router.kind != L.PACK_ROUTER:
+        raise TypeError("w_router must be packed with router_weights")
     for t, d, n in ((h, None, "h"), (xn, h.dtype, "xn"), (w_router, torch.float32, "w_router"),
                     (bias, torch.float32, "bias"), (gain, torch.float32, "gain"),
                     (topk_ids, torch.int32, "topk_ids"), (topk_w, torch.float32, "topk_w"),
                     (logits, torch.float32, "logits")):
         _need(t, d, n)
-    flags = (L.ROUTE_NORM if norm else 0) | (L.ROUTE_RENORM if renormalize else 0)
+    flags = ((L.ROUTE_NORM if norm else 0) | (L.ROUTE_RENORM if renormalize else 0)
+             | (L.ROUTE_WPACKED if packed else 0))
     L.check("moe_route", L.load().moe_route(
         _p(h), _p(gain), float(eps), _p(w_router), _p(bias), T, H, E, k, flags, dtype_code(h),
         _p(xn), _p(topk_ids), _p(topk_w), _p(logits), _stream(h)))

@@ -29,7 +29,7 @@ class VerifyStack:
         self.layers = []
         for w in layers:
             gu, dn = ops.expert_weights(w["w_gate_up"], w["w_down"])
-            self.layers.append({"w_router": w["w_router"], "bias": w.get("bias"), "w_gate_up": gu, "w_down": dn})
+            self.layers.append({"w_router": ops.router_weights(w["w_router"]), "bias": w.get("bias"), "w_gate_up": gu, "w_down": dn})
         self.w_lm = None if w_lm is None else ops.lm_weights(w_lm)
         # when a list: (start, end) torch.cuda.Event pairs around every grouped
         # SwiGLU launch, recorded on the stream the kernels run on

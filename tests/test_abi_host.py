@@ -49,7 +49,14 @@ def test_pack_checks(lib):
     assert lib.moe_packed_weights_bytes(66, 896, 1280, 0) == 66 * 2 * 896 * 1280 * 2
     assert lib.moe_packed_weights_bytes(1, 77, 64, 1) == 3 * 2 * 2 * 1024   # rows padded to pairs of 32
     assert f(A, A, 66, 896, 1280, 0, m.F32, None) == L.ERR_UNSUPPORTED       # fp32 weights stay row-major
-    assert f(A, A, 66, 896, 1280, 2, m.BF16, None) == L.ERR_UNSUPPORTED
+    assert f(A, A, 66, 896, 1280, 2, m.BF16, None) == L.ERR_UNSUPPORTED      # router layout is fp32
+    assert f(A, A, 66, 896, 1280, 3, m.BF16, None) == L.ERR_UNSUPPORTED
+    assert lib.moe_packed_weights_bytes(12, 64, 1280, L.PACK_ROUTER) == 12 * 1280 * 64 * 4
+    assert lib.moe_packed_weights_bytes(1, 8, 128, L.PACK_ROUTER) == 128 * 64 * 4   # padded to 64 experts
+    assert f(A, A, 1, 65, 1280, L.PACK_ROUTER, m.F32, None) == L.ERR_UNSUPPORTED
+    assert f(A, A, 1, 64, 1282, L.PACK_ROUTER, m.F32, None) == L.ERR_SHAPE
+    assert f(MIS, A, 1, 64, 1280, L.PACK_ROUTER, m.F32, None) == L.ERR_ALIGN
+    assert f(A, A, 1, 64, 1280, L.PACK_ROUTER, m.BF16, None) == L.ERR_UNSUPPORTED
     assert f(A, A, 66, 896, 1290, 0, m.BF16, None) == L.ERR_SHAPE
     assert f(A, A, 66, 900, 1280, 0, m.BF16, None) == L.ERR_SHAPE
     assert f(None, A, 66, 896, 1280, 0, m.BF16, None) == L.ERR_NULL

@@ -71,12 +71,14 @@ def test_pack_weights_layout(m, kind, shape):
 
 @pytest.mark.parametrize("shape,T", [("tiny", 16), ("layer128", 128), ("layer128", 1), ("layer128", 37),
                                      ("layer128", 300)])
-def test_route(m, shape, T):
+@pytest.mark.parametrize("packed", [False, True])
+def test_route(m, shape, T, packed):
     sh = synth.SHAPES[shape]
     w = _layer(sh, 1)
     h = synth.hidden(2, T, sh.H, sh.torch_dtype, DEV)
     bias = synth.normal(5, (sh.E,), 0.01, torch.float32, "cpu").to(DEV)   # non-zero bias exercises the add
-    xn, ids, tw, lg = m.route_alloc(h, w["w_router"], bias, sh.k)
+    wr = m.router_weights(w["w_router"]) if packed else w["w_router"]
+    xn, ids, tw, lg = m.route_alloc(h, wr, bias, sh.k)
     torch.cuda.synchronize()
     mode = sh.dtype
     ref = O.route(host(h), host(w["w_router"]), host(bias), sh.k, sh.eps, mode)
@@ -103,6 +105,17 @@ def test_route_full_softmax_and_no_norm(m):
     assert torch.equal(xn2, h)
     ref2 = O.route(host(h), host(w["w_router"]), None, 6, sh.eps, "bf16", norm=False)
     compare_ids(ids2.cpu().numpy(), ref2["ids"], ref2["gap"], "ids without norm")
+
+
+@pytest.mark.parametrize("E,H", [(64, 1280), (8, 128), (17, 1288)])
+def test_pack_router_layout(m, E, H):
+    wr = synth.normal(9, (E, H), 0.02, torch.float32, "cpu")
+    p = m.router_weights(wr.to(DEV))
+    torch.cuda.synchronize()
+    got = p.data.cpu().numpy().reshape(H // 4, 64, 4)
+    ref = np.zeros((H // 4, 64, 4), np.float32)
+    ref[:, :E, :] = wr.numpy().reshape(E, H // 4, 4).transpose(1, 0, 2)
+    np.testing.assert_array_equal(got, ref)
 
 
 def test_route_zero_router_tie_rule(m):
