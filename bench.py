@@ -35,7 +35,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="step128", choices=["step128", "batch1", "layer128"])
+    ap.add_argument("--workload", default="step128", choices=["step128", "batch1", "layer128", "copy"],
+                    help="copy: a plain 1 GiB device copy, the reference for scaling the HBM traffic counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=6, help="layers of the oracle sample")
     ap.add_argument("--cpu-vocab", type=int, default=65536, help="LM-head rows of the oracle sample")
@@ -46,12 +47,67 @@ def expert_bytes(sh) -> int:
     return 3 * sh.H * sh.I * 2
 
 
+# HBM traffic of the gate/up kernel per launch, from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE runs scaled by the same counters on a plain copy of known size;
+# valid only while the kernel's sources are the ones that were measured
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "expert_gate_up_step128_traffic.txt")
+KERNEL_SOURCES = ["moe_decoder_step_amd/csrc/swiglu.hip", "moe_decoder_step_amd/csrc/common.hpp"]
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    d = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            d.update(fh.read())
+    return d.hexdigest()[:16]
+
+
+def measured_traffic():
+    """(fetch + write bytes per launch, note) or (None, reason)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None, "no counter run recorded"
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != kernel_source_hash():
+        return None, "kernel changed since the counters were taken"
+    return float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"]), TRAFFIC_FILE
+
+
+def copy_calibration(args) -> int:
+    """A plain device copy of 1 GiB: the known-size reference for the counters."""
+    import torch
+    n = 1 << 29                      # bf16 elements = 1 GiB
+    a = torch.ones(n, dtype=torch.bfloat16, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(args.warmup):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    print(json.dumps({"workload": "copy", "bytes_read": 2 * n, "bytes_written": 2 * n, "ms": ms,
+                      "GBs": 4 * n / (ms * 1e-3) / 1e9}), flush=True)
+    return 0
+
+
 def main() -> int:
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(the step is sharded by design only; see the sharding notes).", file=sys.stderr)
         return 2
+
+    if args.workload == "copy":
+        return copy_calibration(args)
 
     import numpy as np
     import torch
@@ -87,7 +143,10 @@ def main() -> int:
     touched = [int(np.unique(r["ids"].cpu().numpy()).size) for r in rec]
     layer_bytes = [(t + sh.S) * expert_bytes(sh) + sh.E * sh.H * 4 + 2 * T * sh.H * 2 for t in touched]
     step_bytes = sum(layer_bytes) + (sh.V * sh.H * 2 if sh.V else 0)
-    ffn_bytes = [(t + sh.S) * expert_bytes(sh) + T * sh.H * 2 + (T * sh.k + sh.S * T) * sh.H * 2 for t in touched]
+    # gate/up kernel per launch: gate and up rows of every touched expert, the
+    # normed tokens in, the SwiGLU activation rows out
+    n_rows = T * sh.k + sh.S * T
+    gu_bytes = [(t + sh.S) * 2 * sh.I * sh.H * 2 + T * sh.H * 2 + n_rows * sh.I * 2 for t in touched]
 
     for _ in range(args.warmup):
         step()
@@ -102,17 +161,18 @@ def main() -> int:
     ms = e0.elapsed_time(e1) / args.steps
     log(f"{ms:.3f} ms/step")
 
-    # dominant op (grouped SwiGLU, routed + shared experts): HIP events around
-    # each launch on the stream it runs on, over a second timed pass
+    # dominant kernel (expert gate/up, routed + shared experts): HIP events
+    # around each launch on the stream it runs on, over a second timed pass
     st.ffn_events = ev = []
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     st.ffn_events = None
-    ffn_ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
-    ffn_b = float(np.mean(ffn_bytes))
-    achieved = ffn_b / (ffn_ms * 1e-3) / 1e9
-    log(f"grouped SwiGLU: {ffn_ms * 1e3:.1f} us/launch, {achieved:.0f} GB/s")
+    gu_ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
+    gu_b = float(np.mean(gu_bytes))
+    achieved = gu_b / (gu_ms * 1e-3) / 1e9
+    log(f"expert gate/up: {gu_ms * 1e3:.1f} us/launch, {achieved:.0f} GB/s")
+    traffic, traffic_src = measured_traffic() if sh.name == "step128" else (None, "counters taken on step128")
 
     out = {
         "metric": "MoE verify-step tokens/s (32 seq x 4 tok, 12 layers)" if sh.name == "step128"
@@ -135,10 +195,10 @@ def main() -> int:
         "step_hbm": {"algorithmic_bytes": step_bytes, "achieved_GBs": step_bytes / (ms * 1e-3) / 1e9,
                      "frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "touched_experts_per_layer": touched},
-        "roofline": {"kernel": "moe_grouped_swiglu (gate/up + down launches)", "bound": "hbm",
+        "roofline": {"kernel": "moe_expert_gate_up (skinny_kernel<true>)", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "us_per_launch": ffn_ms * 1e3, "algorithmic_bytes_per_launch": ffn_b},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "traffic_source": traffic_src,
+                     "us_per_launch": gu_ms * 1e3, "algorithmic_bytes_per_launch": gu_b},
     }
 
     if not args.no_cpu_baseline:

@@ -186,6 +186,27 @@ int moe_grouped_swiglu(const void* x, const int32_t* gather, const int32_t* offs
                        void* y, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * moe_expert_gate_up, moe_expert_down -- the two halves of moe_grouped_swiglu
+ * as separate calls (same kernels, same results):
+ *
+ *   moe_expert_gate_up: act[r] = silu(W_g[g] x[t]) * (W_u[g] x[t])
+ *   moe_expert_down:    y[r]   = W_d[g] act[r]
+ *
+ * for every row r of every group g, with t and the arguments as in
+ * moe_grouped_swiglu.  act is [n_rows, I] in dtype (caller-owned, 16-byte
+ * aligned); rows outside every group are untouched.  A caller that times or
+ * overlaps the halves, or keeps act, uses these; moe_grouped_swiglu is
+ * exactly moe_expert_gate_up into its workspace followed by moe_expert_down.
+ * Limits and errors as for moe_grouped_swiglu.
+ * ------------------------------------------------------------------------- */
+int moe_expert_gate_up(const void* x, const int32_t* gather, const int32_t* offsets,
+                       int G, int n_rows, const void* w_gate_up, int T, int H, int I,
+                       int max_rows, int dtype, void* act, void* stream);
+int moe_expert_down(const void* act, const int32_t* offsets, int G, int n_rows,
+                    const void* w_down, int H, int I, int max_rows, int dtype,
+                    void* y, void* stream);
+
+/* ---------------------------------------------------------------------------
  * moe_combine -- weighted sum of the expert outputs plus the residual.
  *
  *   c[t]   = sum_{j<k} topk_w[t,j] * y[inv[t*k+j]] + sum_{s<S} y_shared[s*T+t]

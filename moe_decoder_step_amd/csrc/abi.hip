@@ -69,8 +69,26 @@ int moe_grouped_swiglu(const void* x, const int32_t* gather, const int32_t* offs
   int st = moe::check_swiglu(x, offsets, G, n_rows, w_gate_up, w_down, T, H, I, max_rows, dtype, y, ws,
                              ws_bytes);
   if (st != MOE_OK || n_rows == 0 || T == 0) return st;
-  return hip_status(moe::launch_swiglu(x, gather, offsets, G, n_rows, w_gate_up, w_down, T, H, I, max_rows,
-                                       dtype, y, ws, as_stream(stream)));
+  const hipError_t e = moe::launch_gate_up(x, gather, offsets, G, n_rows, w_gate_up, T, H, I, max_rows, dtype, ws,
+                                           as_stream(stream));
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(moe::launch_down(ws, offsets, G, n_rows, w_down, H, I, max_rows, dtype, y, as_stream(stream)));
+}
+
+int moe_expert_gate_up(const void* x, const int32_t* gather, const int32_t* offsets, int G, int n_rows,
+                       const void* w_gate_up, int T, int H, int I, int max_rows, int dtype, void* act,
+                       void* stream) {
+  int st = moe::check_gate_up(x, offsets, G, n_rows, w_gate_up, T, H, I, max_rows, dtype, act);
+  if (st != MOE_OK || n_rows == 0 || T == 0) return st;
+  return hip_status(moe::launch_gate_up(x, gather, offsets, G, n_rows, w_gate_up, T, H, I, max_rows, dtype, act,
+                                        as_stream(stream)));
+}
+
+int moe_expert_down(const void* act, const int32_t* offsets, int G, int n_rows, const void* w_down, int H, int I,
+                    int max_rows, int dtype, void* y, void* stream) {
+  int st = moe::check_down(act, offsets, G, n_rows, w_down, H, I, max_rows, dtype, y);
+  if (st != MOE_OK || n_rows == 0) return st;
+  return hip_status(moe::launch_down(act, offsets, G, n_rows, w_down, H, I, max_rows, dtype, y, as_stream(stream)));
 }
 
 int moe_combine(const void* y, const int32_t* inv, const float* topk_w, const void* y_shared, int S,

@@ -17,9 +17,11 @@ hipError_t launch_route(const void* h, const float* gain, float eps, const float
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int S, int32_t* offsets,
                           int32_t* gather, int32_t* inv, void* ws, hipStream_t s);
 
-hipError_t launch_swiglu(const void* x, const int32_t* gather, const int32_t* offsets, int G,
-                         int n_rows, const void* w_gate_up, const void* w_down, int T, int H, int I,
-                         int max_rows, int dtype, void* y, void* ws, hipStream_t s);
+hipError_t launch_gate_up(const void* x, const int32_t* gather, const int32_t* offsets, int G, int n_rows,
+                          const void* w_gate_up, int T, int H, int I, int max_rows, int dtype, void* act,
+                          hipStream_t s);
+hipError_t launch_down(const void* act, const int32_t* offsets, int G, int n_rows, const void* w_down, int H,
+                       int I, int max_rows, int dtype, void* y, hipStream_t s);
 
 hipError_t launch_combine(const void* y, const int32_t* inv, const float* topk_w,
                           const void* y_shared, int S, const void* residual, int T, int H, int k,

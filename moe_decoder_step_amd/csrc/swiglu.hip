@@ -250,15 +250,6 @@ hipError_t launch_skinny(const bf16_t* x, const int32_t* gather, const int32_t* 
   return hipGetLastError();
 }
 
-hipError_t launch_bf16(const bf16_t* x, const int32_t* gather, const int32_t* offsets, int G, int n_rows,
-                       const bf16_t* wgu, const bf16_t* wd, int T, int H, int I, int max_rows, bf16_t* act,
-                       bf16_t* y, hipStream_t s) {
-  (void)max_rows;
-  hipError_t e = launch_skinny<true>(x, gather, offsets, G, n_rows, T, wgu, H, I, act, s);
-  if (e != hipSuccess) return e;
-  return launch_skinny<false>(act, nullptr, offsets, G, n_rows, T, wd, I, H, y, s);
-}
-
 // ---------------------------------------------------------------- fp32 path
 
 __device__ __forceinline__ int find_group(const int32_t* offsets, int G, int n_rows, int r, int* r_begin) {
@@ -314,23 +305,30 @@ __global__ __launch_bounds__(256) void f32_down_kernel(const float* __restrict__
 
 }  // namespace
 
-hipError_t launch_swiglu(const void* x, const int32_t* gather, const int32_t* offsets, int G,
-                         int n_rows, const void* w_gate_up, const void* w_down, int T, int H, int I,
-                         int max_rows, int dtype, void* y, void* ws, hipStream_t s) {
+hipError_t launch_gate_up(const void* x, const int32_t* gather, const int32_t* offsets, int G, int n_rows,
+                          const void* w_gate_up, int T, int H, int I, int max_rows, int dtype, void* act,
+                          hipStream_t s) {
+  (void)max_rows;
   if (dtype == kF32) {
-    float* act = static_cast<float*>(ws);
     hipLaunchKernelGGL(f32_gate_up_kernel, dim3(n_rows), dim3(256), 0, s, static_cast<const float*>(x), gather,
-                       offsets, G, n_rows, T, static_cast<const float*>(w_gate_up), H, I, act);
-    hipLaunchKernelGGL(f32_down_kernel, dim3(n_rows), dim3(256), 0, s, act, offsets, G, n_rows,
-                       static_cast<const float*>(w_down), H, I, static_cast<float*>(y));
+                       offsets, G, n_rows, T, static_cast<const float*>(w_gate_up), H, I,
+                       static_cast<float*>(act));
     return hipGetLastError();
   }
-  const bf16_t* xb = static_cast<const bf16_t*>(x);
-  const bf16_t* wgu = static_cast<const bf16_t*>(w_gate_up);
-  const bf16_t* wd = static_cast<const bf16_t*>(w_down);
-  bf16_t* act = static_cast<bf16_t*>(ws);
-  bf16_t* yb = static_cast<bf16_t*>(y);
-  return launch_bf16(xb, gather, offsets, G, n_rows, wgu, wd, T, H, I, max_rows, act, yb, s);
+  return launch_skinny<true>(static_cast<const bf16_t*>(x), gather, offsets, G, n_rows, T,
+                             static_cast<const bf16_t*>(w_gate_up), H, I, static_cast<bf16_t*>(act), s);
+}
+
+hipError_t launch_down(const void* act, const int32_t* offsets, int G, int n_rows, const void* w_down, int H,
+                       int I, int max_rows, int dtype, void* y, hipStream_t s) {
+  (void)max_rows;
+  if (dtype == kF32) {
+    hipLaunchKernelGGL(f32_down_kernel, dim3(n_rows), dim3(256), 0, s, static_cast<const float*>(act), offsets,
+                       G, n_rows, static_cast<const float*>(w_down), H, I, static_cast<float*>(y));
+    return hipGetLastError();
+  }
+  return launch_skinny<false>(static_cast<const bf16_t*>(act), nullptr, offsets, G, n_rows, n_rows,
+                              static_cast<const bf16_t*>(w_down), I, H, static_cast<bf16_t*>(y), s);
 }
 
 }  // namespace moe

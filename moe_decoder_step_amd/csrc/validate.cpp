@@ -89,14 +89,37 @@ int check_permute(const int32_t* ids, int T, int k, int E, int S, const int32_t*
   return kOk;
 }
 
-int check_swiglu(const void* x, const int32_t* offsets, int G, int n_rows, const void* w_gate_up,
-                 const void* w_down, int T, int H, int I, int max_rows, int dtype, const void* y,
-                 const void* ws, size_t ws_bytes) {
+int check_expert_shape(int G, int n_rows, int T, int H, int I, int max_rows, int dtype) {
   if (!valid_dtype(dtype)) return kErrUnsupported;
   if (G <= 0 || n_rows < 0 || T < 0 || H <= 0 || I <= 0 || max_rows < 0) return kErrShape;
   if (dtype == kBf16 && (H % 32 != 0 || I % 32 != 0 || H > 4096 || I > 4096 || G > 128)) return kErrUnsupported;
   if (dtype == kF32 && (H % 4 != 0 || I % 4 != 0)) return kErrUnsupported;
-  if (n_rows == 0 || T == 0) return kOk;
+  return kOk;
+}
+
+int check_gate_up(const void* x, const int32_t* offsets, int G, int n_rows, const void* w_gate_up, int T,
+                  int H, int I, int max_rows, int dtype, const void* act) {
+  int st = check_expert_shape(G, n_rows, T, H, I, max_rows, dtype);
+  if (st != kOk || n_rows == 0 || T == 0) return st;
+  if (!x || !offsets || !w_gate_up || !act) return kErrNull;
+  if (!aligned16(x) || !aligned16(w_gate_up) || !aligned16(act)) return kErrAlign;
+  return kOk;
+}
+
+int check_down(const void* act, const int32_t* offsets, int G, int n_rows, const void* w_down, int H, int I,
+               int max_rows, int dtype, const void* y) {
+  int st = check_expert_shape(G, n_rows, 1, H, I, max_rows, dtype);
+  if (st != kOk || n_rows == 0) return st;
+  if (!act || !offsets || !w_down || !y) return kErrNull;
+  if (!aligned16(act) || !aligned16(w_down) || !aligned16(y)) return kErrAlign;
+  return kOk;
+}
+
+int check_swiglu(const void* x, const int32_t* offsets, int G, int n_rows, const void* w_gate_up,
+                 const void* w_down, int T, int H, int I, int max_rows, int dtype, const void* y,
+                 const void* ws, size_t ws_bytes) {
+  int st = check_expert_shape(G, n_rows, T, H, I, max_rows, dtype);
+  if (st != kOk || n_rows == 0 || T == 0) return st;
   if (!x || !offsets || !w_gate_up || !w_down || !y) return kErrNull;
   if (!aligned16(x) || !aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(y)) return kErrAlign;
   size_t need = swiglu_ws_bytes(n_rows, I, dtype);

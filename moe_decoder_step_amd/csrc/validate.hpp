@@ -32,6 +32,11 @@ int check_route(const void* h, const float* w_router, int T, int H, int E, int k
                 const void* xn, const int32_t* ids, const float* w);
 int check_permute(const int32_t* ids, int T, int k, int E, int S, const int32_t* offsets,
                   const int32_t* gather, const int32_t* inv, const void* ws, size_t ws_bytes);
+int check_expert_shape(int G, int n_rows, int T, int H, int I, int max_rows, int dtype);
+int check_gate_up(const void* x, const int32_t* offsets, int G, int n_rows, const void* w_gate_up, int T,
+                  int H, int I, int max_rows, int dtype, const void* act);
+int check_down(const void* act, const int32_t* offsets, int G, int n_rows, const void* w_down, int H, int I,
+               int max_rows, int dtype, const void* y);
 int check_swiglu(const void* x, const int32_t* offsets, int G, int n_rows, const void* w_gate_up,
                  const void* w_down, int T, int H, int I, int max_rows, int dtype, const void* y,
                  const void* ws, size_t ws_bytes);

@@ -16,7 +16,7 @@ from . import _lib as L
 
 __all__ = [
     "Packed", "pack_weights", "packed_weights_bytes", "moe_route", "moe_permute", "moe_grouped_swiglu", "moe_combine", "lmhead_argmax",
-    "spec_verify", "spec_plant_drafts", "permute_workspace_bytes", "swiglu_workspace_bytes",
+    "moe_expert_gate_up", "moe_expert_down", "spec_verify", "spec_plant_drafts", "permute_workspace_bytes", "swiglu_workspace_bytes",
     "lmhead_workspace_bytes", "dtype_code", "expert_weights", "lm_weights", "router_weights", "route_alloc", "permute_alloc", "swiglu_alloc",
     "combine_alloc", "lmhead_alloc", "verify_alloc",
 ]
@@ -168,6 +168,35 @@ def moe_grouped_swiglu(x, gather, offsets, w_gate_up, w_down, y, ws, max_rows=No
         _p(x), _p(gather), _p(offsets), G, n_rows, _p(w_gate_up), _p(w_down), T, H, I2 // 2,
         T if max_rows is None else int(max_rows), dtype_code(x), _p(y), _p(ws),
         ws.numel() * ws.element_size(), _stream(x)))
+
+
+def moe_expert_gate_up(x, gather, offsets, w_gate_up, act, max_rows=None):
+    """First half of the grouped SwiGLU: act[r] = silu(x W_g^T) * (x W_u^T) per group."""
+    T, H = x.shape
+    G, I2, _ = w_gate_up.shape
+    n_rows = act.shape[0]
+    if x.dtype == torch.bfloat16 and not (isinstance(w_gate_up, Packed) and w_gate_up.kind == L.PACK_GATE_UP):
+        raise TypeError("bf16 expert weights must be packed (expert_weights / pack_weights)")
+    for t, d, n in ((x, None, "x"), (gather, torch.int32, "gather"), (offsets, torch.int32, "offsets"),
+                    (w_gate_up, x.dtype, "w_gate_up"), (act, x.dtype, "act")):
+        _need(t, d, n)
+    L.check("moe_expert_gate_up", L.load().moe_expert_gate_up(
+        _p(x), _p(gather), _p(offsets), G, n_rows, _p(w_gate_up), T, H, I2 // 2,
+        T if max_rows is None else int(max_rows), dtype_code(x), _p(act), _stream(x)))
+
+
+def moe_expert_down(act, offsets, w_down, y, max_rows=None):
+    """Second half of the grouped SwiGLU: y[r] = act[r] W_d^T per group."""
+    n_rows, I = act.shape
+    G, H, _ = w_down.shape
+    if act.dtype == torch.bfloat16 and not (isinstance(w_down, Packed) and w_down.kind == L.PACK_ROWS):
+        raise TypeError("bf16 expert weights must be packed (expert_weights / pack_weights)")
+    for t, d, n in ((act, None, "act"), (offsets, torch.int32, "offsets"), (w_down, act.dtype, "w_down"),
+                    (y, act.dtype, "y")):
+        _need(t, d, n)
+    L.check("moe_expert_down", L.load().moe_expert_down(
+        _p(act), _p(offsets), G, n_rows, _p(w_down), H, I, n_rows if max_rows is None else int(max_rows),
+        dtype_code(act), _p(y), _stream(act)))
 
 
 def moe_combine(y, inv, topk_w, y_shared, S, residual, out, combined=None):

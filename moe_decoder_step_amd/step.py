@@ -31,8 +31,8 @@ class VerifyStack:
             gu, dn = ops.expert_weights(w["w_gate_up"], w["w_down"])
             self.layers.append({"w_router": ops.router_weights(w["w_router"]), "bias": w.get("bias"), "w_gate_up": gu, "w_down": dn})
         self.w_lm = None if w_lm is None else ops.lm_weights(w_lm)
-        # when a list: (start, end) torch.cuda.Event pairs around every grouped
-        # SwiGLU launch, recorded on the stream the kernels run on
+        # when a list: (start, end) torch.cuda.Event pairs around every expert
+        # gate/up launch, recorded on the stream the kernels run on
         self.ffn_events = None
         self.E, self.k, self.S, self.eps = E, k, S, eps
         wgu = layers[0]["w_gate_up"]
@@ -55,8 +55,7 @@ class VerifyStack:
         self.pws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
         self.n_rows = T * k + S * T
         self.y = torch.empty((self.n_rows, H), dtype=self.dtype, device=dev)
-        self.sws = torch.empty(max(ops.swiglu_workspace_bytes(self.n_rows, self.I, self.dtype), 16),
-                               dtype=torch.uint8, device=dev)
+        self.act = torch.empty((self.n_rows, self.I), dtype=self.dtype, device=dev)
         if w_lm is not None:
             V = w_lm.shape[0]
             self.argmax = torch.empty(T, **i32)
@@ -78,14 +77,15 @@ class VerifyStack:
         ops.moe_permute(self.ids[:T], E, S, self.offsets, self.gather[:T * k + S * T], self.inv[:T * k], self.pws)
         n_rows = T * k + S * T
         y = self.y[:n_rows]
+        act = self.act[:n_rows]
         if self.ffn_events is not None:
             ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             ev[0].record()
-        ops.moe_grouped_swiglu(self.xn[:T], self.gather[:n_rows], self.offsets, w["w_gate_up"], w["w_down"], y,
-                               self.sws, max_rows=T)
+        ops.moe_expert_gate_up(self.xn[:T], self.gather[:n_rows], self.offsets, w["w_gate_up"], act, max_rows=T)
         if self.ffn_events is not None:
             ev[1].record()
             self.ffn_events.append(ev)
+        ops.moe_expert_down(act, self.offsets, w["w_down"], y, max_rows=T)
         ops.moe_combine(y[:T * k], self.inv[:T * k], self.tw[:T], y[T * k:] if S else None, S, h, h)
 
     def forward(self, h_in: torch.Tensor, record: list | None = None) -> torch.Tensor:

@@ -21,7 +21,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = L.header_functions()
-    assert len(names) == 14
+    assert len(names) == 16
     assert set(names) == set(L.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
@@ -117,6 +117,18 @@ def test_swiglu_checks(lib):
     assert call(ws=None) == L.ERR_WORKSPACE
     assert call(wsb=need - 1) == L.ERR_WORKSPACE
     assert call(n=0, x=None) == L.OK
+
+
+def test_expert_halves_checks(lib):
+    gu, dn = lib.moe_expert_gate_up, lib.moe_expert_down
+    assert gu(A, None, A, 66, 40, A, 4, 1280, 896, 4, m.BF16, None, None) == L.ERR_NULL
+    assert gu(A, None, A, 66, 40, MIS, 4, 1280, 896, 4, m.BF16, A, None) == L.ERR_ALIGN
+    assert gu(A, None, A, 66, 40, A, 4, 1288, 896, 4, m.BF16, A, None) == L.ERR_UNSUPPORTED
+    assert gu(None, None, None, 66, 0, None, 4, 1280, 896, 4, m.BF16, None, None) == L.OK
+    assert dn(A, A, 66, 40, A, 1280, 896, 4, m.BF16, None, None) == L.ERR_NULL
+    assert dn(A, A, 0, 40, A, 1280, 896, 4, m.BF16, A, None) == L.ERR_SHAPE
+    assert dn(MIS, A, 66, 40, A, 1280, 896, 4, m.BF16, A, None) == L.ERR_ALIGN
+    assert dn(None, None, 66, 0, None, 1280, 896, 4, m.BF16, None, None) == L.OK
 
 
 def test_combine_lmhead_verify_plant_checks(lib):

@@ -171,6 +171,35 @@ def test_grouped_swiglu(m, shape, T):
         assert_close(yg[a:b], ref, BF16_TOL if sh.dtype == "bf16" else F32_TOL, f"group {g}")
 
 
+@pytest.mark.parametrize("shape,T", [("layer128", 37), ("tiny", 16)])
+def test_expert_halves(m, shape, T):
+    """moe_expert_gate_up + moe_expert_down: the activation rows against the
+    oracle (its SwiGLU with an identity down projection returns them), and y
+    bit-identical to moe_grouped_swiglu."""
+    sh = synth.SHAPES[shape]
+    w = _layer(sh, 3)
+    h = synth.hidden(4, T, sh.H, sh.torch_dtype, DEV)
+    xn, ids, tw, _ = m.route_alloc(h, w["w_router"], None, sh.k)
+    off, gat, inv = m.permute_alloc(ids, sh.E, sh.S)
+    n_rows = T * sh.k + sh.S * T
+    wgu_p, wd_p = m.expert_weights(w["w_gate_up"], w["w_down"])
+    act = torch.full((n_rows, sh.I), float("nan"), dtype=sh.torch_dtype, device=DEV)
+    y = torch.empty((n_rows, sh.H), dtype=sh.torch_dtype, device=DEV)
+    m.moe_expert_gate_up(xn, gat, off, wgu_p, act, max_rows=T)
+    m.moe_expert_down(act, off, wd_p, y, max_rows=T)
+    y_fused = m.swiglu_alloc(xn, gat, off, wgu_p, wd_p, n_rows, max_rows=T)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_fused)
+    xh, offh, gath = O.f64(host(xn)), off.cpu().numpy(), gat.cpu().numpy()
+    wgu, eye = host(w["w_gate_up"]), np.eye(sh.I)
+    ag = as_f64(act)
+    tol = BF16_TOL if sh.dtype == "bf16" else F32_TOL
+    for g in range(sh.E + sh.S):
+        a, b = offh[g], offh[g + 1]
+        if a < b:
+            assert_close(ag[a:b], O.swiglu(xh[gath[a:b]], wgu[g], eye, sh.dtype), tol, f"act group {g}")
+
+
 def test_grouped_swiglu_identity_gather_and_skewed_groups(m):
     """gather = NULL (row r of a group reads token r - offsets[g]); groups of
     0, 1, 15, 16, 17, 33, 100 rows (ragged M-blocks, several row blocks)."""
