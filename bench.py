@@ -22,6 +22,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+ZIPF_BIAS = os.path.join(ROOT, "tests", "golden", "zipf_bias_prefill.json")
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, TFLOP/s
 
@@ -35,11 +36,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="step128", choices=["step128", "batch1", "layer128", "copy"],
+    ap.add_argument("--workload", default="step128", choices=["step128", "batch1", "layer128", "prefill", "copy"],
                     help="copy: a plain 1 GiB device copy, the reference for scaling the HBM traffic counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=6, help="layers of the oracle sample")
     ap.add_argument("--cpu-vocab", type=int, default=65536, help="LM-head rows of the oracle sample")
+    ap.add_argument("--cpu-tokens", type=int, default=512, help="tokens of the oracle sample (at most T)")
     return ap.parse_args()
 
 
@@ -122,9 +124,19 @@ def main() -> int:
     T = sh.T
     log(f"workload {sh.name}: T={T} L={sh.L} V={sh.V}; generating weights on {dev}")
     t0 = time.time()
-    layers = [synth.layer_weights(0, l, sh, dev) for l in range(sh.L)]
+    prefill = sh.name == "prefill"
+    if prefill:
+        # the real-shape layer's weights with the Zipf(1.1) router bias
+        # (calibrated by tests/golden/make_zipf_bias.py); hidden states seed 3
+        with open(ZIPF_BIAS) as f:
+            fx = json.load(f)
+        layers = [synth.layer_weights(fx["router_weight"]["seed"], fx["router_weight"]["layer"], sh, dev)]
+        layers[0]["bias"] = torch.tensor(fx["bias"], dtype=torch.float32, device=dev)
+        h_in = synth.hidden(3, T, sh.H, torch.bfloat16, dev)
+    else:
+        layers = [synth.layer_weights(0, l, sh, dev) for l in range(sh.L)]
+        h_in = synth.hidden(0, T, sh.H, torch.bfloat16, dev, name="step_hidden")
     w_lm = synth.lm_weight(0, sh, dev) if sh.V else None
-    h_in = synth.hidden(0, T, sh.H, torch.bfloat16, dev, name="step_hidden")
     drafts = synth.uniform_ids(0, (sh.B, sh.K), sh.V or 2).to(dev)
     torch.cuda.synchronize()
     log(f"weights ready in {time.time() - t0:.1f}s")
@@ -141,12 +153,16 @@ def main() -> int:
     rec = []
     st.forward(h_in, rec)
     touched = [int(np.unique(r["ids"].cpu().numpy()).size) for r in rec]
+    load = np.bincount(rec[0]["ids"].cpu().numpy().ravel(), minlength=sh.E)
+    del rec
     layer_bytes = [(t + sh.S) * expert_bytes(sh) + sh.E * sh.H * 4 + 2 * T * sh.H * 2 for t in touched]
     step_bytes = sum(layer_bytes) + (sh.V * sh.H * 2 if sh.V else 0)
     # gate/up kernel per launch: gate and up rows of every touched expert, the
     # normed tokens in, the SwiGLU activation rows out
     n_rows = T * sh.k + sh.S * T
     gu_bytes = [(t + sh.S) * 2 * sh.I * sh.H * 2 + T * sh.H * 2 + n_rows * sh.I * 2 for t in touched]
+    gu_flops = n_rows * 2 * (2 * sh.I) * sh.H
+    layer_flops = 2 * T * sh.H * sh.E + n_rows * 6 * sh.H * sh.I      # router + experts
 
     for _ in range(args.warmup):
         step()
@@ -173,10 +189,27 @@ def main() -> int:
     achieved = gu_b / (gu_ms * 1e-3) / 1e9
     log(f"expert gate/up: {gu_ms * 1e3:.1f} us/launch, {achieved:.0f} GB/s")
     traffic, traffic_src = measured_traffic() if sh.name == "step128" else (None, "counters taken on step128")
+    if prefill:
+        tflops = gu_flops / (gu_ms * 1e-3) / 1e12
+        log(f"expert gate/up: {gu_ms * 1e3:.1f} us/launch, {tflops:.0f} TFLOP/s")
+        roofline = {"kernel": "moe_expert_gate_up (gemm_kernel<true>)", "bound": "mfma", "achieved": tflops,
+                    "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tflops / BF16_PEAK_TFLOPS,
+                    "traffic": None, "traffic_source": "no counter run recorded for this kernel",
+                    "us_per_launch": gu_ms * 1e3, "algorithmic_flops_per_launch": gu_flops}
+    else:
+        roofline = {"kernel": "moe_expert_gate_up (skinny_kernel<true>)", "bound": "hbm",
+                    "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "traffic_source": traffic_src,
+                    "us_per_launch": gu_ms * 1e3, "algorithmic_bytes_per_launch": gu_b}
 
+    if sh.name == "step128":
+        metric = "MoE verify-step tokens/s (32 seq x 4 tok, 12 layers)"
+    elif prefill:
+        metric = "MoE prefill-layer tokens/s (32 pages x 1,156 tokens, Zipf(1.1) experts)"
+    else:
+        metric = f"MoE verify tokens/s ({sh.name})"
     out = {
-        "metric": "MoE verify-step tokens/s (32 seq x 4 tok, 12 layers)" if sh.name == "step128"
-        else f"MoE verify tokens/s ({sh.name})",
+        "metric": metric,
         "value": T / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -188,18 +221,22 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"verify pass, {sh.B} seq x {sh.P} positions = {T} tokens, {sh.L} MoE layers"
-                   + (f" + LM head {sh.H}x{sh.V} argmax + greedy acceptance" if sh.V else ""),
+        "config": {"workload": (f"prefill MoE layer, {sh.B} pages x {sh.P} tokens = {T} tokens, "
+                                "router bias for Zipf(1.1) expert popularity") if prefill else
+                   (f"verify pass, {sh.B} seq x {sh.P} positions = {T} tokens, {sh.L} MoE layers"
+                    + (f" + LM head {sh.H}x{sh.V} argmax + greedy acceptance" if sh.V else "")),
                    "hidden": sh.H, "experts": f"{sh.E} routed + {sh.S} shared, top-{sh.k}",
                    "expert_intermediate": sh.I, "global_batch": T},
         "step_hbm": {"algorithmic_bytes": step_bytes, "achieved_GBs": step_bytes / (ms * 1e-3) / 1e9,
                      "frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "touched_experts_per_layer": touched},
-        "roofline": {"kernel": "moe_expert_gate_up (skinny_kernel<true>)", "bound": "hbm",
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "traffic_source": traffic_src,
-                     "us_per_launch": gu_ms * 1e3, "algorithmic_bytes_per_launch": gu_b},
+        "roofline": roofline,
     }
+    if prefill:
+        out["layer_mfma"] = {"algorithmic_flops": layer_flops,
+                             "achieved_TFLOPs": layer_flops / (ms * 1e-3) / 1e12,
+                             "frac": layer_flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                             "expert_rows_desc": np.sort(load)[::-1].tolist()}
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, sh, layers, w_lm, h_in, T)
@@ -220,9 +257,10 @@ def cpu_baseline(args, sh, layers, w_lm, h_in, T) -> dict:
         t = t.detach().cpu().contiguous()
         return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
     nl = min(args.cpu_layers, sh.L)
-    log(f"cpu baseline: oracle on {nl} layer(s) + {args.cpu_vocab} LM rows")
+    nt = min(args.cpu_tokens, T)
+    log(f"cpu baseline: oracle on {nl} layer(s) x {nt} tokens + {args.cpu_vocab} LM rows")
     hw = [{k: host(v) for k, v in layers[l].items()} for l in range(nl)]
-    x = host(h_in)
+    x = host(h_in[:nt])
     t0 = time.perf_counter()
     cur = x
     for l in range(nl):
@@ -236,14 +274,14 @@ def cpu_baseline(args, sh, layers, w_lm, h_in, T) -> dict:
         t1 = time.perf_counter()
         O.lm_argmax(cur, wl)
         t_lm = time.perf_counter() - t1
-    t_step = t_layers * sh.L / nl + (t_lm * sh.V / vs if vs else 0.0)
+    t_step = (t_layers * sh.L / nl + (t_lm * sh.V / vs if vs else 0.0)) * T / nt
     try:
         from threadpoolctl import threadpool_info
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         cores = os.cpu_count() or 1
     return {"value": T / t_step, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{nl} of {sh.L} MoE layers on all {T} tokens ({t_layers:.1f}s) + LM head over "
+            "sample": f"{nl} of {sh.L} MoE layers on {nt} of {T} tokens ({t_layers:.1f}s) + LM head over "
                       f"{vs} of {sh.V} vocabulary rows ({t_lm:.1f}s), scaled to the full step "
                       f"({t_step:.1f}s per step)"}
 

@@ -21,7 +21,7 @@ LIB = os.path.join(HERE, "libmoestep.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["abi.hip", "pack.hip", "route.hip", "permute.hip", "swiglu.hip", "combine.hip", "lmhead.hip",
+SOURCES = ["abi.hip", "pack.hip", "route.hip", "permute.hip", "swiglu.hip", "gemm.hip", "combine.hip", "lmhead.hip",
            "verify.hip", "validate.cpp"]
 
 # Packed-fp32 VALU ops are switched off for all device code.

@@ -20,6 +20,10 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int S, int32_
 hipError_t launch_gate_up(const void* x, const int32_t* gather, const int32_t* offsets, int G, int n_rows,
                           const void* w_gate_up, int T, int H, int I, int max_rows, int dtype, void* act,
                           hipStream_t s);
+// grouped expert GEMM (bf16, prefill-sized groups): gated = gate/up stage
+bool gemm_path_ok(int K, int N, int max_rows);
+hipError_t launch_gemm(bool gated, const void* x, const int32_t* gather, const int32_t* offsets, int G, int n_rows,
+                       int T, const void* W, int K, int N, void* out, hipStream_t s);
 hipError_t launch_down(const void* act, const int32_t* offsets, int G, int n_rows, const void* w_down, int H,
                        int I, int max_rows, int dtype, void* y, hipStream_t s);
 

@@ -308,25 +308,27 @@ __global__ __launch_bounds__(256) void f32_down_kernel(const float* __restrict__
 hipError_t launch_gate_up(const void* x, const int32_t* gather, const int32_t* offsets, int G, int n_rows,
                           const void* w_gate_up, int T, int H, int I, int max_rows, int dtype, void* act,
                           hipStream_t s) {
-  (void)max_rows;
   if (dtype == kF32) {
     hipLaunchKernelGGL(f32_gate_up_kernel, dim3(n_rows), dim3(256), 0, s, static_cast<const float*>(x), gather,
                        offsets, G, n_rows, T, static_cast<const float*>(w_gate_up), H, I,
                        static_cast<float*>(act));
     return hipGetLastError();
   }
+  if (gemm_path_ok(H, I, max_rows))
+    return launch_gemm(true, x, gather, offsets, G, n_rows, T, w_gate_up, H, I, act, s);
   return launch_skinny<true>(static_cast<const bf16_t*>(x), gather, offsets, G, n_rows, T,
                              static_cast<const bf16_t*>(w_gate_up), H, I, static_cast<bf16_t*>(act), s);
 }
 
 hipError_t launch_down(const void* act, const int32_t* offsets, int G, int n_rows, const void* w_down, int H,
                        int I, int max_rows, int dtype, void* y, hipStream_t s) {
-  (void)max_rows;
   if (dtype == kF32) {
     hipLaunchKernelGGL(f32_down_kernel, dim3(n_rows), dim3(256), 0, s, static_cast<const float*>(act), offsets,
                        G, n_rows, static_cast<const float*>(w_down), H, I, static_cast<float*>(y));
     return hipGetLastError();
   }
+  if (gemm_path_ok(I, H, max_rows))
+    return launch_gemm(false, act, nullptr, offsets, G, n_rows, n_rows, w_down, I, H, y, s);
   return launch_skinny<false>(static_cast<const bf16_t*>(act), nullptr, offsets, G, n_rows, n_rows,
                               static_cast<const bf16_t*>(w_down), I, H, static_cast<bf16_t*>(y), s);
 }

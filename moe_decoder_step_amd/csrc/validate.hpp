@@ -16,6 +16,7 @@ constexpr int kMaxHidden = 2048;     // route kernel keeps a block's normed rows
 constexpr int kMaxShared = 8;
 constexpr int kMaxDrafts = 15;
 constexpr int kPermuteChunk = 4096;  // slots per block of the permutation kernels
+constexpr int kGemmMinRows = 1024;   // max_rows from which the grouped SwiGLU runs as a tiled GEMM
 constexpr int kLmRowsPerBlock = 128; // vocabulary rows per LM-head block (bf16 path)
 constexpr int kLmF32RowsPerBlock = 256;
 

@@ -31,7 +31,7 @@ from dataclasses import dataclass
 import torch
 
 __all__ = [
-    "Shape", "SHAPES", "subseed", "normal", "layer_weights", "lm_weight",
+    "Shape", "SHAPES", "subseed", "normal", "router_weight", "layer_weights", "lm_weight",
     "hidden", "uniform_ids", "plant_schedule", "bf16_bits",
 ]
 
@@ -100,6 +100,11 @@ def normal(seed: int, shape, std: float, dtype, device="cpu") -> torch.Tensor:
     return x.to(dtype)
 
 
+def router_weight(seed: int, layer: int, sh: Shape) -> torch.Tensor:
+    """Router weight [E, H] fp32 ~N(0, 0.02), always drawn on the CPU."""
+    return normal(subseed(seed, "w_router", layer), (sh.E, sh.H), 0.02, torch.float32, "cpu")
+
+
 def layer_weights(seed: int, layer: int, sh: Shape, device="cpu") -> dict:
     """Weights of one MoE layer.
 
@@ -112,7 +117,7 @@ def layer_weights(seed: int, layer: int, sh: Shape, device="cpu") -> dict:
     """
     G = sh.E + sh.S
     dt = sh.torch_dtype
-    w_router = normal(subseed(seed, "w_router", layer), (sh.E, sh.H), 0.02, torch.float32, "cpu")
+    w_router = router_weight(seed, layer, sh)
     return {
         "w_router": w_router.to(device),
         "bias": torch.zeros(sh.E, dtype=torch.float32, device=device),

@@ -1,0 +1,137 @@
+"""Prefill-sized MoE layers: the grouped SwiGLU's tiled-GEMM path and the
+36,992-token layer (32 pages x 1,156 visual tokens) with Zipf(1.1) expert
+popularity, against the fp64 oracle.
+
+Sizes the oracle finishes in seconds are compared row by row; the full-size
+layer is compared on its permutation (bit-exact, every row) and on sampled
+tokens (routing and output rows), since every token's result depends only on
+its own input row and the weights.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from tests._util import BF16_TOL, F32_TOL, as_f64, assert_close, compare_ids, host
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+GEMM_MIN_ROWS = 1024      # max_rows from which the library runs the grouped SwiGLU as a tiled GEMM
+ZIPF = os.path.join(os.path.dirname(__file__), "golden", "zipf_bias_prefill.json")
+
+
+@pytest.fixture(scope="module")
+def m():
+    import moe_decoder_step_amd as mod
+    mod.load()
+    return mod
+
+
+def _zipf_bias():
+    with open(ZIPF) as f:
+        fx = json.load(f)
+    return torch.tensor(fx["bias"], dtype=torch.float32), fx
+
+
+def test_gemm_path_ragged_groups(m):
+    """Identity gather, groups of 0, 1, 255, 256, 257, 600, 1500, 0 and 40 rows
+    (ragged and multiple 256-row tiles), max_rows selecting the GEMM path."""
+    H, I, T = 1280, 896, 1500
+    counts = [0, 1, 255, 256, 257, 600, 1500, 0, 40]
+    G = len(counts)
+    gen = torch.Generator(device=DEV).manual_seed(21)
+    x = torch.randn(T, H, generator=gen, device=DEV).to(torch.bfloat16)
+    wgu = (torch.randn(G, 2 * I, H, generator=gen, device=DEV) * 0.02).to(torch.bfloat16)
+    wd = (torch.randn(G, H, I, generator=gen, device=DEV) * 0.02).to(torch.bfloat16)
+    off = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32, device=DEV)
+    n_rows = int(sum(counts))
+    wgu_p, wd_p = m.expert_weights(wgu, wd)
+    y = m.swiglu_alloc(x, None, off, wgu_p, wd_p, n_rows, max_rows=max(counts))
+    torch.cuda.synchronize()
+    xh, yg = O.f64(host(x)), as_f64(y)
+    wguh, wdh = host(wgu), host(wd)
+    for g, c in enumerate(counts):
+        a = int(off[g])
+        if c:
+            ref = O.swiglu(xh[:c], wguh[g], wdh[g], "bf16")
+            assert_close(yg[a:a + c], ref, BF16_TOL, f"group {g} ({c} rows)")
+
+
+def test_gemm_path_routed_zipf_1024_tokens(m):
+    """Route -> permute -> gate/up -> down at 1,024 tokens with the Zipf
+    router bias (max_rows = T selects the GEMM path): activation rows and
+    expert outputs of every group against the oracle."""
+    sh = synth.SHAPES["prefill"]
+    T = 1024
+    assert T >= GEMM_MIN_ROWS
+    w = synth.layer_weights(1, 0, sh, DEV)
+    bias, _ = _zipf_bias()
+    h = synth.hidden(5, T, sh.H, torch.bfloat16, DEV)
+    xn, ids, tw, _ = m.route_alloc(h, w["w_router"], bias.to(DEV), sh.k)
+    off, gat, inv = m.permute_alloc(ids, sh.E, sh.S)
+    n_rows = T * sh.k + sh.S * T
+    wgu_p, wd_p = m.expert_weights(w["w_gate_up"], w["w_down"])
+    act = torch.empty((n_rows, sh.I), dtype=torch.bfloat16, device=DEV)
+    y = torch.empty((n_rows, sh.H), dtype=torch.bfloat16, device=DEV)
+    m.moe_expert_gate_up(xn, gat, off, wgu_p, act, max_rows=T)
+    m.moe_expert_down(act, off, wd_p, y, max_rows=T)
+    torch.cuda.synchronize()
+    xh, offh, gath = O.f64(host(xn)), off.cpu().numpy(), gat.cpu().numpy()
+    wgu, wd = host(w["w_gate_up"]), host(w["w_down"])
+    ag, yg = as_f64(act), as_f64(y)
+    sizes = np.diff(offh)
+    assert sizes[:sh.E].max() > 3 * sizes[:sh.E].mean()     # the bias makes the groups unequal
+    for g in range(sh.E + sh.S):
+        a, b = offh[g], offh[g + 1]
+        if a == b:
+            continue
+        xa = xh[gath[a:b]]
+        assert_close(ag[a:b], O.swiglu(xa, wgu[g], np.eye(sh.I), "bf16"), BF16_TOL, f"act group {g}")
+        assert_close(yg[a:b], O.swiglu(xa, wgu[g], wd[g], "bf16"), BF16_TOL, f"y group {g}")
+
+
+def test_prefill_layer_36992_tokens(m):
+    """The full prefill layer (32 x 1,156 tokens, Zipf-biased router): the
+    permutation of every (token, slot) bit-exact; routing and the layer output
+    of sampled tokens (random ones plus tokens of the coldest and hottest
+    experts, and the last tokens) against the oracle."""
+    sh = synth.SHAPES["prefill"]
+    T = sh.T
+    assert T == 36992
+    w = synth.layer_weights(1, 0, sh, DEV)
+    bias, fx = _zipf_bias()
+    w["bias"] = bias.to(DEV)
+    st = m.VerifyStack([w], None, sh.E, sh.k, sh.S, max_tokens=T)
+    h = synth.hidden(3, T, sh.H, torch.bfloat16, DEV)
+    rec = []
+    st.forward(h, rec)
+    torch.cuda.synchronize()
+    ids = rec[0]["ids"].cpu().numpy()
+    # permutation: every row, against the oracle's stable counting sort of the GPU's ids
+    roff, rgat, rinv = O.permute(ids, sh.E, sh.S)
+    np.testing.assert_array_equal(st.offsets.cpu().numpy(), roff)
+    np.testing.assert_array_equal(st.gather[:T * sh.k + sh.S * T].cpu().numpy(), rgat)
+    np.testing.assert_array_equal(st.inv[:T * sh.k].cpu().numpy(), rinv)
+    load = np.bincount(ids.ravel(), minlength=sh.E)
+    order = np.argsort(-load, kind="stable")
+    print(f"\nrealised expert load (desc): {load[order][:8].tolist()} ... {load[order][-4:].tolist()}")
+    assert load.max() > 20 * load.min() > 0                  # Zipf-like skew, no starved expert
+    # sampled tokens
+    rng = np.random.Generator(np.random.PCG64(17))
+    hot, cold = order[0], order[-1]
+    tok = np.concatenate([rng.choice(T, 160, replace=False), np.nonzero((ids == cold).any(1))[0][:24],
+                          np.nonzero((ids == hot).any(1))[0][-24:], np.arange(T - 8, T)])
+    tok = np.unique(tok)
+    hin = host(rec[0]["input"])[tok]
+    hw = {k: host(v) for k, v in w.items()}
+    ref = O.moe_layer(hin, hw, sh.k, sh.eps, "bf16")
+    n_flag, flagged = compare_ids(ids[tok], ref["route"]["ids"], ref["route"]["gap"], "sampled ids")
+    ok = ~flagged
+    assert_close(rec[0]["w"].cpu().numpy()[tok][ok], ref["route"]["w"][ok], F32_TOL, "sampled weights")
+    assert_close(as_f64(rec[0]["output"])[tok][ok], ref["h_out"][ok], BF16_TOL, "sampled layer output")

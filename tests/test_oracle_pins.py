@@ -439,3 +439,34 @@ def test_active_and_total_params_match_pages():
     assert f["visual_tokens_base"] + f["visual_tiles_max"] * f["visual_tokens_per_tile"] == f["visual_tokens_max"]
     # throughput arithmetic on the A100 run
     assert abs(f["pages_per_s_a100"] * f["tokens_per_page"] / f["tokens_per_s_a100"] - 1) < 0.005
+
+
+# ---------------------------------------------------------------- Zipf router bias (prefill layer)
+
+def test_zipf_bias_fixture_reproduces_its_counts():
+    """The stored prefill router bias: its targets are the water-filled Zipf(1.1)
+    counts (sum 6 T, capped at T, ratio ((r+1)/r)^1.1 below the cap), and the
+    oracle's own routing of the calibration batch with that bias gives the
+    stored realised counts, which follow the targets."""
+    import synth
+    from tests.golden.make_zipf_bias import counts, zipf_targets
+    with open(os.path.join(os.path.dirname(__file__), "golden", "zipf_bias_prefill.json")) as f:
+        fx = json.load(f)
+    cal = fx["calibration"]
+    T, k, E = cal["tokens"], 6, 64
+    tgt = np.array(fx["target_counts_by_rank"])
+    np.testing.assert_allclose(tgt, zipf_targets(T, k, E, cal["zipf_s"]))
+    assert abs(tgt.sum() - k * T) < 1e-6 * T and tgt.max() <= T
+    free = tgt < T
+    r = np.arange(1, E + 1)[free]
+    np.testing.assert_allclose(tgt[free][:-1] / tgt[free][1:], ((r[1:]) / r[:-1]) ** cal["zipf_s"], rtol=1e-9)
+    assert sorted(fx["rank_to_expert"]) == list(range(E))
+    sh = synth.SHAPES["prefill"]
+    wr = synth.router_weight(fx["router_weight"]["seed"], fx["router_weight"]["layer"], sh).numpy()
+    h = synth.bf16_bits(synth.hidden(cal["seed"], T, sh.H, torch.bfloat16, name=cal["hidden_name"]))
+    xn = O.store(O.rmsnorm(O.f64(h), sh.eps), "bf16")
+    n = counts(xn, wr, np.array(fx["bias"], np.float32).astype(np.float64), k, E)
+    by_rank = n[fx["rank_to_expert"]]
+    np.testing.assert_array_equal(by_rank, fx["realised_counts_by_rank"])
+    assert n.sum() == k * T
+    assert np.all(np.abs(by_rank - tgt) <= 0.1 * tgt + 10)
