@@ -6,25 +6,29 @@
 // tile of 256 rows (tokens of one group) by 8 weight-row pairs:
 //   gated stage: 8 (gate 16-row, up 16-row) pairs = 128 activation columns;
 //   down stage:  8 pairs of 16 weight rows = 256 output columns.
-// The reduction runs in stages of 64 (two 32-wide MFMA k-steps).  Each stage
-// stages 32 KB of activation rows and 32 KB of weights in LDS, double
-// buffered (128 KB), both in fragment order: a 1 KB fragment holds, in lane
-// order, the 16 rows x 32 k-elements one wavefront feeds to
-// v_mfma_f32_16x16x32_bf16, so every LDS read is 1 KB of consecutive bytes
-// (no bank conflicts) and the packed weights (moe_pack_weights) copy into LDS
-// as they lie in memory.  Global loads of the next stage are in flight while
-// the current one is multiplied; one barrier per stage.
+// The reduction runs in stages of 32 (one MFMA k-step).  A stage is 16 KB of
+// activation rows and 16 KB of weights in LDS, both in fragment order: a 1 KB
+// fragment holds, in lane order, the 16 rows x 32 k-elements one wavefront
+// feeds to v_mfma_f32_16x16x32_bf16, so every LDS read is 1 KB of
+// consecutive bytes (no bank conflicts).  Stages are loaded straight from
+// global memory into LDS (global_load_lds_dwordx4: lane l's 16 bytes land at
+// fragment offset 16 l), into a ring of 4 stage buffers, 3 stages ahead of
+// the multiply; the packed weights (moe_pack_weights) copy as they lie in
+// memory, activation rows are gathered per lane.  Per stage: wait for this
+// wavefront's loads of the stage, one barrier (after it every wavefront's
+// loads of the stage have landed and every wavefront has finished the stage
+// whose buffer is refilled next), issue the loads 3 stages ahead, multiply.
 //
 // Wavefront (wm, wn) = (w / 4, w % 4) computes rows 128 wm .. +127 (8 MFMA
 // row blocks) by pairs 2 wn, 2 wn + 1 (4 weight fragments): 32 MFMAs per
-// k-step, 128 fp32 accumulators per lane.  The weights are the MFMA A operand
+// stage, 128 fp32 accumulators per lane.  The weights are the MFMA A operand
 // and the activations the B operand, so a lane ends with 4 consecutive output
 // columns of one row (8-byte stores).
 //
 // M-tiles are numbered group by group; M-tile m runs on XCD m % 8 (block b
-// runs on XCD b % 8) and its 8 (or 5, 7 ...) column tiles are consecutive
-// blocks of that XCD, so they share the XCD's L2 copy of the activation
-// rows, and neighbouring M-tiles of one group share the weight tiles.
+// runs on XCD b % 8) and its column tiles are consecutive blocks of that XCD,
+// so they share the XCD's L2 copy of the activation rows, and neighbouring
+// M-tiles of one group share the weight tiles.
 // The fp32 accumulation order along K is fixed: 32 elements per MFMA, in
 // increasing k.
 #include "common.hpp"
@@ -36,15 +40,59 @@ namespace {
 
 constexpr int kGM = 256;                  // rows per tile
 constexpr int kGPairs = 8;                // weight-row pairs per tile
-constexpr int kGK = 64;                   // reduction elements per stage
+constexpr int kGK = 32;                   // reduction elements per stage
+constexpr int kGRing = 4;                 // stage buffers (3 stages in flight)
 constexpr int kGWaves = 8;
 constexpr int kGThreads = kGWaves * 64;
-constexpr int kGStage = 2 * 32768;        // bytes per stage: A 32 KB + B 32 KB
-constexpr size_t kGLds = 2 * (size_t)kGStage;
+constexpr int kGStage = 2 * 16384;        // bytes per stage: A 16 KB + B 16 KB
+constexpr size_t kGLds = (size_t)kGRing * kGStage;
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// 16 bytes per lane from global memory straight into LDS at base + 16 lane
+__device__ __forceinline__ void load_lds16(const bf16_t* g, char* base) {
+  __builtin_amdgcn_global_load_lds(static_cast<const void*>(g), (lds_void_t*)(base), 16, 0, 0);
+}
+
+// wait until at most N of this wavefront's global loads are outstanding (and
+// all its LDS accesses are done), then a workgroup barrier; no fence, so the
+// loads of later stages stay in flight
+template <int N>
+__device__ __forceinline__ void wait_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0070 | N);  // vmcnt(N) expcnt(7) lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+}
 
 __device__ __forceinline__ float silu_g(float z) { return z / (1.0f + expf(-z)); }
 
 __device__ __forceinline__ uint4 lds16(const char* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// One stage: issue this wavefront's loads of a later stage into `nxt` (when
+// `issue`), then multiply the stage in `cur`.  The two buffers are distinct;
+// saying so (restrict) lets the compiler see that the reads of `cur` do not
+// depend on the loads into `nxt` still in flight, so it adds no wait for them.
+__device__ __forceinline__ void gemm_stage(const char* __restrict__ cur, char* __restrict__ nxt, bool issue,
+                                           const bf16_t* const (&src)[4], size_t step, f32x4_t (&acc)[8][2][2],
+                                           int wm, int wn, int lane) {
+  if (issue) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) load_lds16(src[u] + step, nxt + u * 1024);
+  }
+  bf16x8_t bw[2][2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      bw[q][h] = as_bf16x8(lds16(cur + 16384 + ((wn * 2 + q) * 2 + h) * 1024 + lane * 16));
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const bf16x8_t xa = as_bf16x8(lds16(cur + (wm * 8 + i) * 1024 + lane * 16));
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) acc[i][q][h] = mfma16x16x32(bw[q][h], xa, acc[i][q][h]);
+  }
+}
 
 template <bool GATED>
 __global__ __launch_bounds__(kGThreads) void gemm_kernel(
@@ -94,47 +142,30 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(
   const int m0 = s_m0, m1 = s_m1, r_begin = s_rb;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int nK = K / 32;
-  const int nS = K / kGK;
+  const int nS = K / kGK;                 // stages = MFMA k-steps
 
-  // activation loads: round u fills fragment f = 8u + wave (row block f/2,
-  // k-step f%2) of the stage; this lane's row and 16-byte segment
-  const bf16_t* asrc[4];
+  // loads: wavefronts 0-3 fetch the stage's 16 activation fragments (row
+  // block 4w + u), wavefronts 4-7 its 16 weight fragments (pair 2(w-4) + u/2,
+  // set u%2); 4 fragments per wavefront and stage
+  const bf16_t* src[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const int f = u * kGWaves + wave;
-    const int r = min(m0 + 16 * (f >> 1) + (lane & 15), m1 - 1);  // rows past the group repeat a valid row
-    int src;
-    if (GATED) src = gather ? clampi(gather[r], 0, T - 1) : clampi(r - r_begin, 0, T - 1);
-    else src = r;
-    asrc[u] = x + (size_t)src * K + 8 * (4 * (f & 1) + (lane >> 4));
-  }
-  // weight loads: 16-byte unit c = 512u + tid of the stage's 8 pairs x 4 KB
-  // (pairs past the last are clamped: loaded, never stored)
-  const bf16_t* bsrc[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int c = u * kGThreads + threadIdx.x;
-    const int pair = min(nt * kGPairs + (c >> 8), n_pairs - 1);
-    bsrc[u] = W + ((size_t)g * n_pairs + pair) * nK * 1024 + (c & 255) * 8;
-  }
-
-  uint4 ra[4], rb[4];
-  auto load = [&](int s) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      ra[u] = ldg16(asrc[u] + s * kGK);
-      rb[u] = ldg16(bsrc[u] + (size_t)s * 2048);
+    const int f = wave * 4 + u;
+    if (f < 16) {
+      const int r = min(m0 + 16 * f + (lane & 15), m1 - 1);  // rows past the group repeat a valid row
+      int t;
+      if (GATED) t = gather ? clampi(gather[r], 0, T - 1) : clampi(r - r_begin, 0, T - 1);
+      else t = r;
+      src[u] = x + (size_t)t * K + 8 * (lane >> 4);
+    } else {
+      const int b = f - 16;
+      const int pair = min(nt * kGPairs + (b >> 1), n_pairs - 1);  // clamped pairs: loaded, never stored
+      src[u] = W + ((size_t)g * n_pairs + pair) * nS * 1024 + (b & 1) * 512 + lane * 8;
     }
-  };
-  auto store = [&](int buf) __attribute__((always_inline)) {
-    char* base = lds + buf * kGStage;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      *reinterpret_cast<uint4*>(base + (u * kGWaves + wave) * 1024 + lane * 16) = ra[u];
-      *reinterpret_cast<uint4*>(base + 32768 + (u * kGThreads + threadIdx.x) * 16) = rb[u];
-    }
-  };
+  }
+  // per stage, an activation fragment advances 32 elements along its row, a
+  // weight fragment one packed k-step (1024 elements)
+  const size_t step = wave < 4 ? kGK : 1024;
 
   const int wm = wave >> 2, wn = wave & 3;
   f32x4_t acc[8][2][2];
@@ -145,31 +176,22 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(
 #pragma unroll
       for (int h = 0; h < 2; ++h) acc[i][q][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int s = 0; s < nS; ++s) {
-    if (s + 1 < nS) load(s + 1);
-    const char* base = lds + (s & 1) * kGStage;
+  char* const mine = lds + wave * 4 * 1024;  // this wavefront's 4 fragments of a stage buffer
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8_t bw[2][2];
+  for (int s = 0; s < kGRing - 1; ++s)
+    if (s < nS) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          bw[q][h] = as_bf16x8(lds16(base + 32768 + (wn * 2 + q) * 4096 + ks * 2048 + h * 1024 + lane * 16));
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const bf16x8_t xa = as_bf16x8(lds16(base + ((wm * 8 + i) * 2 + ks) * 1024 + lane * 16));
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-#pragma unroll
-          for (int h = 0; h < 2; ++h) acc[i][q][h] = mfma16x16x32(bw[q][h], xa, acc[i][q][h]);
-      }
+      for (int u = 0; u < 4; ++u) load_lds16(src[u] + s * step, mine + s * kGStage + u * 1024);
     }
-    if (s + 1 < nS) store((s + 1) & 1);
-    __syncthreads();
+  for (int s = 0; s < nS; ++s) {
+    // this wavefront's loads of stage s are done once at most those of the
+    // (up to two) later stages are outstanding
+    if (s + 2 < nS) wait_barrier<8>();
+    else if (s + 1 < nS) wait_barrier<4>();
+    else wait_barrier<0>();
+    const int sn = s + kGRing - 1;  // refills the buffer of stage s-1, which every wavefront has finished
+    gemm_stage(lds + (s % kGRing) * kGStage, mine + (sn % kGRing) * kGStage, sn < nS, src, sn * step, acc, wm,
+               wn, lane);
   }
 
   // lane holds D[4 (lane/16) + v][lane % 16]: weight rows (output columns)
