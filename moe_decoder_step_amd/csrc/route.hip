@@ -14,7 +14,13 @@
 //      maximum wins, which is the lower-id rule for equal logits; then the
 //      softmax weights.
 // Decode batches use 2 tokens per block so that a 128-token batch spreads
-// over 64 blocks; large batches use up to 16 to amortise the router reads.
+// over 64 blocks; larger batches use 8, and prefill-sized ones 32 to
+// amortise the router reads (then the normed rows and the slice partials
+// share one LDS region, the rows being dead once the partials exist, and the
+// router slice is read in the loop rather than held in registers).  The
+// summation order of a logit is the same for every block size.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "validate.hpp"
@@ -23,8 +29,14 @@ namespace moe {
 namespace {
 
 constexpr int kWaves = 16;     // wavefronts per block (hidden split in 16 slices)
-constexpr int kPre = 20;       // router-weight float4 per lane loaded at kernel entry
 constexpr int kThreads = kWaves * 64;
+
+// router-weight float4 per lane loaded at kernel entry
+template <int TPB> constexpr int pre_count() { return TPB <= 16 ? 20 : 0; }
+// the slice partials reuse the normed rows' LDS, which then hold fp32 (exact
+// copies of the stored values, converted once instead of at every use)
+template <int TPB> constexpr bool lds_union() { return TPB > 16; }
+template <typename St, int TPB> using lds_row_t = typename std::conditional<lds_union<TPB>(), float, St>::type;
 
 __device__ __forceinline__ void load8(const bf16_t* p, float* f) { unpack8(ldg16(p), f); }
 __device__ __forceinline__ void load8(const float* p, float* f) {
@@ -39,6 +51,12 @@ __device__ __forceinline__ void store8(bf16_t* p, const bf16_t* v) {
 __device__ __forceinline__ void store8(float* p, const float* v) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
   *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+__device__ __forceinline__ void store8(float* p, const bf16_t* v) {
+  float f[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f[j] = __uint_as_float((uint32_t)v[j] << 16);
+  store8(p, f);
 }
 __device__ __forceinline__ bf16_t round_store(double v, bf16_t*) { return f64_to_bf16(v); }
 __device__ __forceinline__ float round_store(double v, float*) { return (float)v; }
@@ -57,9 +75,12 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     const float* __restrict__ wr, const float* __restrict__ bias, int T, int H, int E, int k,
     int flags, St* __restrict__ xn, int32_t* __restrict__ ids, float* __restrict__ wts,
     float* __restrict__ logits) {
+  constexpr int kPre = pre_count<TPB>();
+  using Xs = lds_row_t<St, TPB>;
   extern __shared__ __align__(16) char smem[];
-  St* xs = reinterpret_cast<St*>(smem);
-  float* part = reinterpret_cast<float*>(smem + ((TPB * H * (int)sizeof(St) + 15) & ~15));  // [kWaves][TPB][64]
+  Xs* xs = reinterpret_cast<Xs*>(smem);
+  float* part = reinterpret_cast<float*>(                        // [kWaves][TPB][64]
+      smem + (lds_union<TPB>() ? 0 : ((TPB * H * (int)sizeof(Xs) + 15) & ~15)));
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t0 = blockIdx.x * TPB;
@@ -75,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     if (PACKED) return *reinterpret_cast<const float4*>(wr + ((size_t)(hh >> 2) * kWave + e) * 4);
     return *reinterpret_cast<const float4*>(wr + (size_t)min(e, E - 1) * H + hh);
   };
-  float4 wpre[kPre];
+  float4 wpre[kPre > 0 ? kPre : 1];
 #pragma unroll
   for (int u = 0; u < kPre; ++u) wpre[u] = wload(min(h_lo + 4 * u, H - 4));
 
@@ -85,7 +106,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     const int t = t0 + i;
     if (t >= T) break;
     const St* hrow = h + (size_t)t * H;
-    St* xrow = xs + i * H;
+    Xs* xrow = xs + i * H;
     double scale = 1.0;
     if (norm) {
       double ss = 0.0;
@@ -135,6 +156,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   for (int u = 0; u < kPre; ++u)
     if (h_lo + 4 * u < h_hi) fma4(wpre[u], h_lo + 4 * u);
   for (int hh = h_lo + 4 * kPre; hh < h_hi; hh += 4) fma4(wload(hh), hh);
+  if (lds_union<TPB>()) __syncthreads();  // every wavefront is done with the normed rows
 #pragma unroll
   for (int i = 0; i < TPB; ++i) part[(wave * TPB + i) * kWave + e] = acc[i];
   __syncthreads();
@@ -174,7 +196,9 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
 
 template <typename St, int TPB>
 size_t lds_bytes(int H) {
-  return ((TPB * H * sizeof(St) + 15) & ~size_t(15)) + (size_t)kWaves * TPB * kWave * sizeof(float);
+  const size_t rows = (TPB * H * sizeof(lds_row_t<St, TPB>) + 15) & ~size_t(15);
+  const size_t parts = (size_t)kWaves * TPB * kWave * sizeof(float);
+  return lds_union<TPB>() ? (rows > parts ? rows : parts) : rows + parts;
 }
 
 template <typename St, int TPB>
@@ -183,6 +207,12 @@ hipError_t launch_tpb(const void* h, const float* gain, float eps, const float* 
                       float* logits, hipStream_t s) {
   const int grid = (T + TPB - 1) / TPB;
   const size_t lds = lds_bytes<St, TPB>(H);
+  if (lds > 64 * 1024) {
+    const void* k = (flags & 4) ? reinterpret_cast<const void*>(&route_kernel<St, TPB, true>)
+                                : reinterpret_cast<const void*>(&route_kernel<St, TPB, false>);
+    hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
   if (flags & 4)
     hipLaunchKernelGGL((route_kernel<St, TPB, true>), dim3(grid), dim3(kThreads), lds, s,
                        static_cast<const St*>(h), gain, eps, wr, bias, T, H, E, k, flags,
@@ -199,6 +229,8 @@ hipError_t launch_st(const void* h, const float* gain, float eps, const float* w
                      int T, int H, int E, int k, int flags, void* xn, int32_t* ids, float* w,
                      float* logits, hipStream_t s) {
   constexpr size_t kLds = 64 * 1024;
+  if (T >= 4096 && lds_bytes<St, 32>(H) <= 160 * 1024)
+    return launch_tpb<St, 32>(h, gain, eps, wr, bias, T, H, E, k, flags, xn, ids, w, logits, s);
   if (T > 256 && lds_bytes<St, 16>(H) <= kLds)
     return launch_tpb<St, 16>(h, gain, eps, wr, bias, T, H, E, k, flags, xn, ids, w, logits, s);
   if (T > 256 && lds_bytes<St, 8>(H) <= kLds)

@@ -70,7 +70,7 @@ def test_pack_weights_layout(m, kind, shape):
 # --------------------------------------------------------------------------- route
 
 @pytest.mark.parametrize("shape,T", [("tiny", 16), ("layer128", 128), ("layer128", 1), ("layer128", 37),
-                                     ("layer128", 300)])
+                                     ("layer128", 300), ("layer128", 4100), ("tiny", 4100)])
 @pytest.mark.parametrize("packed", [False, True])
 def test_route(m, shape, T, packed):
     sh = synth.SHAPES[shape]
