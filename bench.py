@@ -24,6 +24,7 @@ if ROOT not in sys.path:
 
 ZIPF_BIAS = os.path.join(ROOT, "tests", "golden", "zipf_bias_prefill.json")
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E, GB/s
+P_KEEP = 0.576                # per-position draft keep probability (the pages' acceptance rate)
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, TFLOP/s
 
 
@@ -42,6 +43,8 @@ def parse():
     ap.add_argument("--cpu-layers", type=int, default=6, help="layers of the oracle sample")
     ap.add_argument("--cpu-vocab", type=int, default=65536, help="LM-head rows of the oracle sample")
     ap.add_argument("--cpu-tokens", type=int, default=512, help="tokens of the oracle sample (at most T)")
+    ap.add_argument("--drafts", type=int, default=None, help="drafts K per sequence (positions = K + 1)")
+    ap.add_argument("--no-graph", action="store_true", help="batch1: time eager launches only")
     return ap.parse_args()
 
 
@@ -121,6 +124,9 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     sh = synth.SHAPES[args.workload]
+    if args.drafts is not None:
+        import dataclasses
+        sh = dataclasses.replace(sh, P=args.drafts + 1)
     T = sh.T
     log(f"workload {sh.name}: T={T} L={sh.L} V={sh.V}; generating weights on {dev}")
     t0 = time.time()
@@ -143,11 +149,22 @@ def main() -> int:
 
     st = m.VerifyStack(layers, w_lm, sh.E, sh.k, sh.S, max_tokens=T, max_seqs=sh.B, K=sh.K)
 
-    def step():
-        st.forward(h_in)
-        if w_lm is not None:
-            st.head(T)
-            st.verify(drafts)
+    batch1 = sh.name == "batch1"
+    if batch1:
+        # drafts planted from each pass's own greedy tokens, keep probability
+        # 0.576 per position (200 steps of masks; the timed steps reuse step 0's)
+        keep_all, repl_all = synth.plant_schedule(0, 200, sh.B, sh.K, sh.V, P_KEEP)
+        keep_d, repl_d = keep_all.to(dev), repl_all.to(dev)
+        keep_s, repl_s = keep_d[0].clone(), repl_d[0].clone()
+
+        def step():
+            st.step_planted(h_in, keep_s, repl_s, drafts)
+    else:
+        def step():
+            st.forward(h_in)
+            if w_lm is not None:
+                st.head(T)
+                st.verify(drafts)
 
     # routed experts touched per layer (weights the step must read)
     rec = []
@@ -177,6 +194,47 @@ def main() -> int:
     ms = e0.elapsed_time(e1) / args.steps
     log(f"{ms:.3f} ms/step")
 
+    graph_info = None
+    if batch1:
+        # committed tokens per pass over the 200 planted steps (eager)
+        commits = []
+        for i in range(keep_d.shape[0]):
+            keep_s.copy_(keep_d[i])
+            repl_s.copy_(repl_d[i])
+            step()
+            commits.append(st.n_commit[:sh.B].clone())
+        commit_mean = float(torch.stack(commits).float().mean())
+        keep_s.copy_(keep_d[0])
+        repl_s.copy_(repl_d[0])
+        eager_ms = ms
+        graph_ms = None
+        if not args.no_graph:
+            # the whole pass (65 launches) captured once and replayed
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                step()
+            torch.cuda.current_stream().wait_stream(side)
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                step()
+            for _ in range(args.warmup):
+                graph.replay()
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(args.steps):
+                graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            graph_ms = e0.elapsed_time(e1) / args.steps
+            ms = graph_ms
+            log(f"graph replay: {graph_ms:.3f} ms/step (eager {eager_ms:.3f})")
+        expected = sum(P_KEEP ** i for i in range(sh.K + 1))
+        graph_info = {"K": sh.K, "eager_ms_per_step": eager_ms, "graph_ms_per_step": graph_ms,
+                      "committed_per_step_mean": commit_mean, "committed_per_step_expected": expected,
+                      "committed_tokens_per_s": commit_mean * sh.B / (ms * 1e-3),
+                      "keep_probability": P_KEEP, "planted_steps": int(keep_d.shape[0])}
+
     # dominant kernel (expert gate/up, routed + shared experts): HIP events
     # around each launch on the stream it runs on, over a second timed pass
     st.ffn_events = ev = []
@@ -204,6 +262,9 @@ def main() -> int:
 
     if sh.name == "step128":
         metric = "MoE verify-step tokens/s (32 seq x 4 tok, 12 layers)"
+    elif batch1:
+        metric = f"MoE verify-step tokens/s (batch 1 x {sh.P} tok, 12 layers"
+        metric += ", eager)" if args.no_graph else ", graph replay)"
     elif prefill:
         metric = "MoE prefill-layer tokens/s (32 pages x 1,156 tokens, Zipf(1.1) experts)"
     else:
@@ -232,6 +293,8 @@ def main() -> int:
                      "touched_experts_per_layer": touched},
         "roofline": roofline,
     }
+    if graph_info is not None:
+        out["batch1"] = graph_info
     if prefill:
         out["layer_mfma"] = {"algorithmic_flops": layer_flops,
                              "achieved_TFLOPs": layer_flops / (ms * 1e-3) / 1e12,

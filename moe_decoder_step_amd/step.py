@@ -111,6 +111,22 @@ class VerifyStack:
         ops.spec_verify(drafts, self.argmax[:B * (K + 1)].view(B, K + 1), self.accepted[:B],
                         self.committed[:B], self.n_commit[:B])
 
+    def step_planted(self, h_in: torch.Tensor, keep: torch.Tensor, repl: torch.Tensor,
+                     drafts: torch.Tensor) -> None:
+        """One verify pass whose drafts are planted from the pass's own greedy
+        tokens (keep[b, i] -> the verifier's token, else a different id drawn
+        from repl): the synthetic stand-in for a draft model of a given
+        acceptance rate.  The forward pass never reads the drafts (each
+        position's hidden state is an input), so planting after the LM head
+        is the same as planting before the pass.  Allocates nothing, so the
+        whole pass can be captured in a graph."""
+        T = h_in.shape[0]
+        B, K = keep.shape
+        self.forward(h_in)
+        self.head(T)
+        ops.spec_plant_drafts(self.argmax[:B * (K + 1)].view(B, K + 1), keep, repl, self.w_lm.shape[0], drafts)
+        self.verify(drafts)
+
     def step(self, h_in: torch.Tensor, drafts: torch.Tensor, record: list | None = None) -> None:
         """One verify pass: blocks, LM-head argmax, acceptance (results in self.*)."""
         T = h_in.shape[0]
