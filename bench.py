@@ -37,7 +37,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="step128", choices=["step128", "batch1", "layer128", "prefill", "copy"],
+    ap.add_argument("--workload", default="step128",
+                    choices=["step128", "batch1", "layer128", "prefill", "decode32", "copy"],
                     help="copy: a plain 1 GiB device copy, the reference for scaling the HBM traffic counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=6, help="layers of the oracle sample")
@@ -45,6 +46,7 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=512, help="tokens of the oracle sample (at most T)")
     ap.add_argument("--drafts", type=int, default=None, help="drafts K per sequence (positions = K + 1)")
     ap.add_argument("--no-graph", action="store_true", help="batch1: time eager launches only")
+    ap.add_argument("--target", type=int, default=1085, help="decode32: committed tokens per sequence")
     return ap.parse_args()
 
 
@@ -113,6 +115,8 @@ def main() -> int:
 
     if args.workload == "copy":
         return copy_calibration(args)
+    if args.workload == "decode32":
+        return decode_loop_bench(args)
 
     import numpy as np
     import torch
@@ -303,6 +307,62 @@ def main() -> int:
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, sh, layers, w_lm, h_in, T)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def decode_loop_bench(args) -> int:
+    """Concurrency-32 decode loop: 32 sequences of `target` committed tokens,
+    K = 3 drafts planted with keep probability 0.576, the 12-layer stack and
+    LM head; finished sequences leave the batch.  Timed: whole loops, wall
+    clock, including the per-pass copy of the active count to the host."""
+    import numpy as np
+    import torch
+
+    import moe_decoder_step_amd as m
+    import synth
+
+    m.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sh = synth.SHAPES["step128"]
+    S, K, P, target = sh.B, sh.K, sh.P, args.target
+    log(f"decode loop: {S} sequences x {target} tokens, K={K}; generating weights and input pools")
+    layers = [synth.layer_weights(0, l, sh, dev) for l in range(sh.L)]
+    w_lm = synth.lm_weight(0, sh, dev)
+    st = m.VerifyStack(layers, w_lm, sh.E, sh.k, sh.S, max_tokens=S * P, max_seqs=S, K=K)
+    del layers, w_lm
+    h_pool = synth.normal(synth.subseed(4, "decode_hidden"), (S, target, P, sh.H), 1.0, torch.bfloat16, dev)
+    keep, repl = synth.plant_schedule(4, target, S, K, sh.V, P_KEEP)
+    loop = m.DecodeLoop(st, h_pool, keep.permute(1, 0, 2).contiguous().to(dev),
+                        repl.permute(1, 0, 2).contiguous().to(dev), target)
+    torch.cuda.synchronize()
+    for _ in range(max(args.warmup, 0) and 1):
+        loop.run()
+    n_loops = max(1, min(args.steps, 3))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n_loops):
+        res = loop.run()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / n_loops
+    committed = S * target
+    sizes = res["batch_sizes"]
+    log(f"{res['passes']} passes, {wall * 1e3:.1f} ms per loop, {committed / wall:.0f} committed tokens/s")
+    out = {
+        "metric": f"MoE decode-loop committed tokens/s ({S} seq x {target} tok, K={K}, 12 layers)",
+        "value": committed / wall, "unit": "tokens/s", "n_gpus": 1, "steps": n_loops, "warmup": 1,
+        "ms_per_step": wall * 1e3 / res["passes"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"decode loop, {S} sequences to {target} committed tokens, {P} positions per pass, "
+                               f"drafts planted with keep probability {P_KEEP}, finished sequences compacted out",
+                   "hidden": sh.H, "experts": f"{sh.E} routed + {sh.S} shared, top-{sh.k}",
+                   "expert_intermediate": sh.I, "vocab": sh.V, "layers": sh.L},
+        "loop": {"passes": res["passes"], "wall_ms": wall * 1e3, "mean_batch": float(np.mean(sizes)),
+                 "full_batch_passes": int(sum(1 for b in sizes if b == S)),
+                 "committed_per_pass_per_seq": committed / float(np.sum(sizes)),
+                 "expected_committed_per_pass": sum(P_KEEP ** i for i in range(K + 1))},
+    }
     print(json.dumps(out), flush=True)
     return 0
 

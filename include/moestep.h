@@ -282,6 +282,41 @@ int spec_verify(const int32_t* drafts, const int32_t* argmax_ids, int B, int K,
 int spec_plant_drafts(const int32_t* argmax_ids, const uint8_t* keep, const int32_t* repl,
                       int B, int K, int V, int32_t* drafts, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Decode loop over a shrinking batch (the concurrency-32 document workload:
+ * 32 pages decoded together, about 1,085 output tokens each -- alphasignal
+ * page "Jina AI's 3.4B OCR model targets faster page parsing", section
+ * "Quality and speed").  A pass verifies the B active sequences; afterwards
+ * spec_advance appends each one's committed tokens to its stream, stops a
+ * sequence at `target` tokens (the excess of its last pass is dropped) and
+ * compacts the still-active sequence ids in their order.  The caller reads
+ * n_active (one 4-byte copy per pass) to size the next pass.
+ *
+ * spec_advance:
+ *   n_commit  [B] int32, committed [B,K+1] int32   in  (spec_verify's outputs)
+ *   seq_ids   [B] int32                            in  sequence of each slot, in [0,S)
+ *   total     [S] int32                            in/out tokens committed so far
+ *   steps     [S] int32                            in/out passes taken so far
+ *   tokens    [S,target] int32                     out committed streams
+ *   seq_ids_out [<= B] int32                       out active sequences, in slot order
+ *   n_active  [1] int32                            out number of them
+ *   Limits: 0 <= B <= min(S, 1024), 0 <= K <= 15, target >= 1.  The ids in
+ *   seq_ids are distinct; seq_ids_out must not alias seq_ids.  B = 0 writes
+ *   n_active = 0.
+ *
+ * spec_gather_rows: the per-pass inputs of the active sequences from pools
+ * laid out [S, J, R] rows of row_bytes bytes (J passes per sequence, R rows
+ * per pass):  out row i*R + r = pool row (seq_ids[i] * J + min(steps[s], J-1))
+ * * R + r, with s = seq_ids[i].  Used for the hidden states of the verify
+ * positions (R = K+1 rows of H bf16) and the planting draws (R = 1 row of K
+ * bytes or K int32).  row_bytes = 0 (K = 0 drafts) is a no-op.
+ * ------------------------------------------------------------------------- */
+int spec_advance(const int32_t* n_commit, const int32_t* committed, const int32_t* seq_ids,
+                 int B, int K, int S, int target, int32_t* total, int32_t* steps,
+                 int32_t* tokens, int32_t* seq_ids_out, int32_t* n_active, void* stream);
+int spec_gather_rows(const void* pool, const int32_t* seq_ids, const int32_t* steps, int B,
+                     int R, int J, int S, int row_bytes, void* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

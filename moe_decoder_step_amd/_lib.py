@@ -41,6 +41,8 @@ SIGNATURES = {
     "lmhead_argmax": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _Z, _P]),
     "spec_verify": (_I, [_P, _P, _I, _I, _P, _P, _P, _P]),
     "spec_plant_drafts": (_I, [_P, _P, _P, _I, _I, _I, _P, _P]),
+    "spec_advance": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
+    "spec_gather_rows": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
 }
 
 _lib = None

@@ -122,4 +122,22 @@ int spec_plant_drafts(const int32_t* argmax_ids, const uint8_t* keep, const int3
   return hip_status(moe::launch_plant(argmax_ids, keep, repl, B, K, V, drafts, as_stream(stream)));
 }
 
+int spec_advance(const int32_t* n_commit, const int32_t* committed, const int32_t* seq_ids, int B, int K, int S,
+                 int target, int32_t* total, int32_t* steps, int32_t* tokens, int32_t* seq_ids_out,
+                 int32_t* n_active, void* stream) {
+  int st = moe::check_advance(n_commit, committed, seq_ids, B, K, S, target, total, steps, tokens, seq_ids_out,
+                              n_active);
+  if (st != MOE_OK) return st;
+  // B == 0 still writes n_active = 0, with the same one-block kernel
+  return hip_status(moe::launch_advance(n_commit, committed, seq_ids, B, K, S, target, total, steps, tokens,
+                                        seq_ids_out, n_active, as_stream(stream)));
+}
+
+int spec_gather_rows(const void* pool, const int32_t* seq_ids, const int32_t* steps, int B, int R, int J, int S,
+                     int row_bytes, void* out, void* stream) {
+  int st = moe::check_gather_rows(pool, seq_ids, steps, B, R, J, S, row_bytes, out);
+  if (st != MOE_OK || B == 0 || row_bytes == 0) return st;
+  return hip_status(moe::launch_gather_rows(pool, seq_ids, steps, B, R, J, S, row_bytes, out, as_stream(stream)));
+}
+
 }  // extern "C"

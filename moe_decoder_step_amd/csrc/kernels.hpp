@@ -40,4 +40,11 @@ hipError_t launch_verify(const int32_t* drafts, const int32_t* argmax_ids, int B
 hipError_t launch_plant(const int32_t* argmax_ids, const uint8_t* keep, const int32_t* repl, int B,
                         int K, int V, int32_t* drafts, hipStream_t s);
 
+hipError_t launch_advance(const int32_t* n_commit, const int32_t* committed, const int32_t* seq_ids, int B, int K,
+                          int S, int target, int32_t* total, int32_t* steps, int32_t* tokens, int32_t* seq_out,
+                          int32_t* n_active, hipStream_t s);
+
+hipError_t launch_gather_rows(const void* pool, const int32_t* seq_ids, const int32_t* steps, int B, int R, int J,
+                              int S, int row_bytes, void* out, hipStream_t s);
+
 }  // namespace moe

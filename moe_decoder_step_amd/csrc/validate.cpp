@@ -65,6 +65,26 @@ size_t lmhead_ws_bytes(int T, int V, int dtype) {
   return align256((size_t)T * (size_t)lmhead_blocks(V, dtype) * 8);
 }
 
+int check_advance(const int32_t* n_commit, const int32_t* committed, const int32_t* seq_ids, int B, int K, int S,
+                  int target, const int32_t* total, const int32_t* steps, const int32_t* tokens, const int32_t* seq_out,
+                  const int32_t* n_active) {
+  if (B < 0 || K < 0 || S <= 0 || target <= 0 || B > S) return kErrShape;
+  if (B > kAdvanceMaxB || K > kMaxDrafts) return kErrUnsupported;
+  if (!n_active) return kErrNull;
+  if (B == 0) return kOk;
+  if (!n_commit || !committed || !seq_ids || !total || !steps || !tokens || !seq_out) return kErrNull;
+  return kOk;
+}
+
+int check_gather_rows(const void* pool, const int32_t* seq_ids, const int32_t* steps, int B, int R, int J, int S,
+                      int row_bytes, const void* out) {
+  if (B < 0 || R <= 0 || J <= 0 || S <= 0 || row_bytes < 0) return kErrShape;
+  if ((long long)B * R > 0x7fffffffLL) return kErrUnsupported;
+  if (B == 0 || row_bytes == 0) return kOk;
+  if (!pool || !seq_ids || !steps || !out) return kErrNull;
+  return kOk;
+}
+
 int check_route(const void* h, const float* w_router, int T, int H, int E, int k, int dtype,
                 const void* xn, const int32_t* ids, const float* w) {
   if (!valid_dtype(dtype)) return kErrUnsupported;

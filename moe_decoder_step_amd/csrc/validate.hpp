@@ -16,6 +16,7 @@ constexpr int kMaxHidden = 2048;     // route kernel keeps a block's normed rows
 constexpr int kMaxShared = 8;
 constexpr int kMaxDrafts = 15;
 constexpr int kPermuteChunk = 4096;  // slots per block of the permutation kernels
+constexpr int kAdvanceMaxB = 1024;   // sequences of one spec_advance call (one block)
 constexpr int kGemmMinRows = 1024;   // max_rows from which the grouped SwiGLU runs as a tiled GEMM
 constexpr int kLmRowsPerBlock = 128; // vocabulary rows per LM-head block (bf16 path)
 constexpr int kLmF32RowsPerBlock = 256;
@@ -29,6 +30,11 @@ size_t swiglu_ws_bytes(int n_rows, int I, int dtype);
 size_t lmhead_ws_bytes(int T, int V, int dtype);
 int lmhead_blocks(int V, int dtype);
 
+int check_advance(const int32_t* n_commit, const int32_t* committed, const int32_t* seq_ids, int B, int K, int S,
+                  int target, const int32_t* total, const int32_t* steps, const int32_t* tokens, const int32_t* seq_out,
+                  const int32_t* n_active);
+int check_gather_rows(const void* pool, const int32_t* seq_ids, const int32_t* steps, int B, int R, int J, int S,
+                      int row_bytes, const void* out);
 int check_route(const void* h, const float* w_router, int T, int H, int E, int k, int dtype,
                 const void* xn, const int32_t* ids, const float* w);
 int check_permute(const int32_t* ids, int T, int k, int E, int S, const int32_t* offsets,

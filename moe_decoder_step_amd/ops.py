@@ -16,7 +16,8 @@ from . import _lib as L
 
 __all__ = [
     "Packed", "pack_weights", "packed_weights_bytes", "moe_route", "moe_permute", "moe_grouped_swiglu", "moe_combine", "lmhead_argmax",
-    "moe_expert_gate_up", "moe_expert_down", "spec_verify", "spec_plant_drafts", "permute_workspace_bytes", "swiglu_workspace_bytes",
+    "moe_expert_gate_up", "moe_expert_down", "spec_verify", "spec_plant_drafts", "spec_advance",
+    "spec_gather_rows", "permute_workspace_bytes", "swiglu_workspace_bytes",
     "lmhead_workspace_bytes", "dtype_code", "expert_weights", "lm_weights", "router_weights", "route_alloc", "permute_alloc", "swiglu_alloc",
     "combine_alloc", "lmhead_alloc", "verify_alloc",
 ]
@@ -245,6 +246,37 @@ def spec_plant_drafts(argmax_ids, keep, repl, V, drafts):
     _need(drafts, torch.int32, "drafts")
     L.check("spec_plant_drafts", L.load().spec_plant_drafts(
         _p(argmax_ids), _p(keep), _p(repl), B, K, V, _p(drafts), _stream(argmax_ids)))
+
+
+def spec_advance(n_commit, committed, seq_ids, target, total, steps, tokens, seq_ids_out, n_active):
+    """Decode-loop bookkeeping after a pass: append committed tokens to each
+    active sequence's stream (capped at `target`), compact the active ids."""
+    B = seq_ids.shape[0]
+    K = committed.shape[1] - 1
+    S = total.shape[0]
+    for t, n in ((n_commit, "n_commit"), (committed, "committed"), (seq_ids, "seq_ids"), (total, "total"),
+                 (steps, "steps"), (tokens, "tokens"), (seq_ids_out, "seq_ids_out"), (n_active, "n_active")):
+        _need(t, torch.int32, n)
+    L.check("spec_advance", L.load().spec_advance(
+        _p(n_commit), _p(committed), _p(seq_ids), B, K, S, int(target), _p(total), _p(steps), _p(tokens),
+        _p(seq_ids_out), _p(n_active), _stream(total)))
+
+
+def spec_gather_rows(pool, seq_ids, steps, out):
+    """out[i] = pool[seq_ids[i], min(steps[seq_ids[i]], J-1)] for pools [S, J, ...]."""
+    S, J = pool.shape[0], pool.shape[1]
+    B = seq_ids.shape[0]
+    R = pool.shape[2] if pool.dim() > 3 else 1
+    row_bytes = pool[0, 0].numel() * pool.element_size() // R
+    for t, d, n in ((pool, None, "pool"), (seq_ids, torch.int32, "seq_ids"), (steps, torch.int32, "steps"),
+                    (out, pool.dtype, "out")):
+        _need(t, d, n)
+    if row_bytes == 0:
+        return
+    if out.numel() < B * R * row_bytes // pool.element_size():
+        raise ValueError("out is too small")
+    L.check("spec_gather_rows", L.load().spec_gather_rows(
+        _p(pool), _p(seq_ids), _p(steps), B, R, J, S, row_bytes, _p(out), _stream(out)))
 
 
 # ------------------------------------------------------------------ allocating helpers

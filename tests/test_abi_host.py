@@ -21,7 +21,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = L.header_functions()
-    assert len(names) == 16
+    assert len(names) == 18
     assert set(names) == set(L.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
@@ -129,6 +129,23 @@ def test_expert_halves_checks(lib):
     assert dn(A, A, 0, 40, A, 1280, 896, 4, m.BF16, A, None) == L.ERR_SHAPE
     assert dn(MIS, A, 66, 40, A, 1280, 896, 4, m.BF16, A, None) == L.ERR_ALIGN
     assert dn(None, None, 66, 0, None, 1280, 896, 4, m.BF16, None, None) == L.OK
+
+
+def test_advance_and_gather_checks(lib):
+    adv, gat = lib.spec_advance, lib.spec_gather_rows
+    # n_commit, committed, seq_ids, B, K, S, target, total, steps, tokens, seq_out, n_active, stream
+    assert adv(A, A, A, 4, 3, 32, 1085, A, A, A, A, None, None) == L.ERR_NULL
+    assert adv(A, A, A, 33, 3, 32, 1085, A, A, A, A, A, None) == L.ERR_SHAPE      # more slots than sequences
+    assert adv(A, A, A, 4, 3, 32, 0, A, A, A, A, A, None) == L.ERR_SHAPE
+    assert adv(A, A, A, 4, 16, 32, 10, A, A, A, A, A, None) == L.ERR_UNSUPPORTED   # K <= 15
+    assert adv(A, A, A, 1025, 3, 2000, 10, A, A, A, A, A, None) == L.ERR_UNSUPPORTED
+    assert adv(A, None, A, 4, 3, 32, 10, A, A, A, A, A, None) == L.ERR_NULL
+    # pool, seq_ids, steps, B, R, J, S, row_bytes, out, stream
+    assert gat(A, A, A, 4, 4, 10, 32, 2560, None, None) == L.ERR_NULL
+    assert gat(A, A, A, 4, 0, 10, 32, 2560, A, None) == L.ERR_SHAPE
+    assert gat(None, None, None, 0, 4, 10, 32, 2560, None, None) == L.OK
+    assert gat(A, A, A, 4, 1, 10, 32, 0, A, None) == L.OK           # K = 0 drafts: nothing to gather
+    assert gat(A, A, A, 4, 1, 10, 32, -1, A, None) == L.ERR_SHAPE
 
 
 def test_combine_lmhead_verify_plant_checks(lib):
