@@ -229,6 +229,25 @@ int moe_combine(const void* y, const int32_t* inv, const float* topk_w,
                 void* out, void* combined, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * moe_combine_route -- the end of one MoE block fused with the start of the
+ * next: moe_combine of the previous layer in place on the hidden state,
+ *   h[t] = h[t] + sum_j topk_w_prev[t,j] y[inv[t,j]] + sum_s y_shared[s*T+t]
+ * (the same fixed-order fp32 sums and rounding as moe_combine), then
+ * moe_route on the new h (RMSNorm, logits, top-k, weights), as the two calls
+ * would compute them, bit for bit.  Each token's previous routing weights
+ * are read before its new ones are written, so topk_w may alias
+ * topk_w_prev; inv must not alias topk_ids.  Arguments as in moe_combine
+ * (k_prev, n_rows, y, inv, y_shared, S) and moe_route (the rest); h is the
+ * residual in and the combined hidden state out.  Batches of 4,096 tokens
+ * or more run the combine as a launch of its own.
+ * ------------------------------------------------------------------------- */
+int moe_combine_route(const void* y, const int32_t* inv, const float* topk_w_prev,
+                      const void* y_shared, int S, int n_rows, int k_prev, void* h, int T, int H,
+                      const float* gain, float eps, const float* w_router, const float* bias,
+                      int E, int k, int flags, int dtype, void* xn, int32_t* topk_ids,
+                      float* topk_w, float* logits, void* stream);
+
+/* ---------------------------------------------------------------------------
  * lmhead_argmax -- greedy next token of every row: argmax_v (h W_lm^T)[v].
  *
  * The logits (vocabulary 129,280: jina.ai/ko model card, architecture

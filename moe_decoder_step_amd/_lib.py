@@ -38,6 +38,8 @@ SIGNATURES = {
     "moe_expert_gate_up": (_I, [_P, _P, _P, _I, _I, _P, _I, _I, _I, _I, _I, _P, _P]),
     "moe_expert_down": (_I, [_P, _P, _I, _I, _P, _I, _I, _I, _I, _P, _P]),
     "moe_combine": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _P, _P, _P]),
+    "moe_combine_route": (_I, [_P, _P, _P, _P, _I, _I, _I, _P, _I, _I, _P, _F, _P, _P, _I, _I, _I, _I,
+                               _P, _P, _P, _P, _P]),
     "lmhead_argmax": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _Z, _P]),
     "spec_verify": (_I, [_P, _P, _I, _I, _P, _P, _P, _P]),
     "spec_plant_drafts": (_I, [_P, _P, _P, _I, _I, _I, _P, _P]),

@@ -122,6 +122,19 @@ int spec_plant_drafts(const int32_t* argmax_ids, const uint8_t* keep, const int3
   return hip_status(moe::launch_plant(argmax_ids, keep, repl, B, K, V, drafts, as_stream(stream)));
 }
 
+int moe_combine_route(const void* y, const int32_t* inv, const float* topk_w_prev, const void* y_shared, int S,
+                      int n_rows, int k_prev, void* h, int T, int H, const float* gain, float eps,
+                      const float* w_router, const float* bias, int E, int k, int flags, int dtype, void* xn,
+                      int32_t* topk_ids, float* topk_w, float* logits, void* stream) {
+  int st = moe::check_combine(y, inv, topk_w_prev, y_shared, S, h, T, H, k_prev, n_rows, dtype, h, nullptr);
+  if (st != MOE_OK) return st;
+  st = moe::check_route(h, w_router, T, H, E, k, dtype, xn, topk_ids, topk_w);
+  if (st != MOE_OK || T == 0) return st;
+  const moe::CombineArgs ca{y, inv, topk_w_prev, y_shared, S, n_rows, k_prev};
+  return hip_status(moe::launch_combine_route(ca, h, gain, eps, w_router, bias, T, H, E, k, flags, dtype, xn,
+                                              topk_ids, topk_w, logits, as_stream(stream)));
+}
+
 int spec_advance(const int32_t* n_commit, const int32_t* committed, const int32_t* seq_ids, int B, int K, int S,
                  int target, int32_t* total, int32_t* steps, int32_t* tokens, int32_t* seq_ids_out,
                  int32_t* n_active, void* stream) {

@@ -10,6 +10,19 @@ namespace moe {
 hipError_t launch_pack(const void* src, void* dst, int G, int N, int K, int kind, hipStream_t s);
 hipError_t launch_pack_router(const void* src, void* dst, int G, int E, int K, hipStream_t s);
 
+// the previous layer's combine, fused in front of a route (moe_combine_route)
+struct CombineArgs {
+  const void* y;         // [n_rows, H] expert outputs, permuted order
+  const int32_t* inv;    // [T, k] row of each (token, slot)
+  const float* w;        // [T, k] routing weights
+  const void* ys;        // [S*T, H] shared-expert outputs or NULL
+  int S, n_rows, k;
+};
+
+hipError_t launch_combine_route(const CombineArgs& ca, void* h, const float* gain, float eps, const float* w_router,
+                                const float* bias, int T, int H, int E, int k, int flags, int dtype, void* xn,
+                                int32_t* ids, float* w, float* logits, hipStream_t s);
+
 hipError_t launch_route(const void* h, const float* gain, float eps, const float* w_router,
                         const float* bias, int T, int H, int E, int k, int flags, int dtype,
                         void* xn, int32_t* ids, float* w, float* logits, hipStream_t s);

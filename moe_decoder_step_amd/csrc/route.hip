@@ -58,6 +58,8 @@ __device__ __forceinline__ void store8(float* p, const bf16_t* v) {
   for (int j = 0; j < 8; ++j) f[j] = __uint_as_float((uint32_t)v[j] << 16);
   store8(p, f);
 }
+__device__ __forceinline__ bf16_t to_store(float v, bf16_t*) { return f32_to_bf16(v); }
+__device__ __forceinline__ float to_store(float v, float*) { return v; }
 __device__ __forceinline__ bf16_t round_store(double v, bf16_t*) { return f64_to_bf16(v); }
 __device__ __forceinline__ float round_store(double v, float*) { return (float)v; }
 
@@ -69,14 +71,15 @@ __device__ __forceinline__ float4 lds4(const bf16_t* p) {
 }
 __device__ __forceinline__ float4 lds4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 
-template <typename St, int TPB, bool PACKED>
+template <typename St, int TPB, bool PACKED, bool COMBINE>
 __global__ __launch_bounds__(kThreads) void route_kernel(
-    const St* __restrict__ h, const float* __restrict__ gain, float eps,
+    const St* h, St* hout, CombineArgs ca, const float* __restrict__ gain, float eps,
     const float* __restrict__ wr, const float* __restrict__ bias, int T, int H, int E, int k,
     int flags, St* __restrict__ xn, int32_t* __restrict__ ids, float* __restrict__ wts,
     float* __restrict__ logits) {
   constexpr int kPre = pre_count<TPB>();
   using Xs = lds_row_t<St, TPB>;
+  static_assert(!COMBINE || std::is_same<Xs, St>::value, "the fused combine keeps rows in the storage type");
   extern __shared__ __align__(16) char smem[];
   Xs* xs = reinterpret_cast<Xs*>(smem);
   float* part = reinterpret_cast<float*>(                        // [kWaves][TPB][64]
@@ -85,6 +88,47 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t0 = blockIdx.x * TPB;
   const int e = lane;
+
+  // ---- 0. (fused) the previous layer's combine: h' = h + sum_j w_j y[inv] + sum_s ys,
+  //         the same fixed-order fp32 sums as moe_combine, into h and the LDS rows ----
+  if constexpr (COMBINE) {
+    __shared__ int crow[TPB][kMaxExperts];
+    __shared__ float cwt[TPB][kMaxExperts];
+    const St* y = static_cast<const St*>(ca.y);
+    const St* ys = static_cast<const St*>(ca.ys);
+    for (int idx = threadIdx.x; idx < TPB * ca.k; idx += kThreads) {
+      const int i = idx / ca.k, j = idx % ca.k, t = min(t0 + i, T - 1);
+      crow[i][j] = clampi(ca.inv[(size_t)t * ca.k + j], 0, ca.n_rows - 1);
+      cwt[i][j] = ca.w[(size_t)t * ca.k + j];
+    }
+    __syncthreads();
+    const int nseg = H / 8;
+    for (int idx = threadIdx.x; idx < TPB * nseg; idx += kThreads) {
+      const int i = idx / nseg, c = (idx % nseg) * 8, t = t0 + i;
+      if (t >= T) continue;
+      float acc[8], f[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+      for (int j = 0; j < ca.k; ++j) {
+        const float wj = cwt[i][j];
+        load8(y + (size_t)crow[i][j] * H + c, f);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = fmaf(wj, f[q], acc[q]);
+      }
+      for (int s = 0; s < ca.S; ++s) {
+        load8(ys + ((size_t)s * T + t) * H + c, f);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] += f[q];
+      }
+      load8(h + (size_t)t * H + c, f);
+      St o[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) o[q] = to_store(f[q] + acc[q], (St*)nullptr);
+      store8(hout + (size_t)t * H + c, o);
+      store8(xs + i * H + c, o);
+    }
+    __syncthreads();
+  }
 
   // this wavefront's slice of the hidden dim; its router weights go out first
   // (they do not depend on the norm) and land while the norm runs
@@ -105,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   for (int i = wave; i < TPB; i += kWaves) {
     const int t = t0 + i;
     if (t >= T) break;
-    const St* hrow = h + (size_t)t * H;
+    const St* hrow = COMBINE ? reinterpret_cast<const St*>(xs + i * H) : h + (size_t)t * H;
     Xs* xrow = xs + i * H;
     double scale = 1.0;
     if (norm) {
@@ -201,41 +245,63 @@ size_t lds_bytes(int H) {
   return lds_union<TPB>() ? (rows > parts ? rows : parts) : rows + parts;
 }
 
-template <typename St, int TPB>
-hipError_t launch_tpb(const void* h, const float* gain, float eps, const float* wr, const float* bias,
-                      int T, int H, int E, int k, int flags, void* xn, int32_t* ids, float* w,
-                      float* logits, hipStream_t s) {
+template <typename St, int TPB, bool PACKED, bool COMBINE>
+hipError_t launch_one(const void* h, void* hout, const CombineArgs& ca, const float* gain, float eps,
+                      const float* wr, const float* bias, int T, int H, int E, int k, int flags, void* xn,
+                      int32_t* ids, float* w, float* logits, hipStream_t s) {
   const int grid = (T + TPB - 1) / TPB;
   const size_t lds = lds_bytes<St, TPB>(H);
   if (lds > 64 * 1024) {
-    const void* k = (flags & 4) ? reinterpret_cast<const void*>(&route_kernel<St, TPB, true>)
-                                : reinterpret_cast<const void*>(&route_kernel<St, TPB, false>);
-    hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&route_kernel<St, TPB, PACKED, COMBINE>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  if (flags & 4)
-    hipLaunchKernelGGL((route_kernel<St, TPB, true>), dim3(grid), dim3(kThreads), lds, s,
-                       static_cast<const St*>(h), gain, eps, wr, bias, T, H, E, k, flags,
-                       static_cast<St*>(xn), ids, w, logits);
-  else
-    hipLaunchKernelGGL((route_kernel<St, TPB, false>), dim3(grid), dim3(kThreads), lds, s,
-                       static_cast<const St*>(h), gain, eps, wr, bias, T, H, E, k, flags,
-                       static_cast<St*>(xn), ids, w, logits);
+  hipLaunchKernelGGL((route_kernel<St, TPB, PACKED, COMBINE>), dim3(grid), dim3(kThreads), lds, s,
+                     static_cast<const St*>(h), static_cast<St*>(hout), ca, gain, eps, wr, bias, T, H, E, k, flags,
+                     static_cast<St*>(xn), ids, w, logits);
   return hipGetLastError();
 }
 
+template <typename St, int TPB>
+hipError_t launch_tpb(const void* h, void* hout, const CombineArgs* ca, const float* gain, float eps,
+                      const float* wr, const float* bias, int T, int H, int E, int k, int flags, void* xn,
+                      int32_t* ids, float* w, float* logits, hipStream_t s) {
+  const CombineArgs none{};
+  if constexpr (!lds_union<TPB>()) {
+    if (ca) {
+      if (flags & 4)
+        return launch_one<St, TPB, true, true>(h, hout, *ca, gain, eps, wr, bias, T, H, E, k, flags, xn, ids, w,
+                                               logits, s);
+      return launch_one<St, TPB, false, true>(h, hout, *ca, gain, eps, wr, bias, T, H, E, k, flags, xn, ids, w,
+                                              logits, s);
+    }
+  }
+  if (flags & 4)
+    return launch_one<St, TPB, true, false>(h, nullptr, none, gain, eps, wr, bias, T, H, E, k, flags, xn, ids, w,
+                                            logits, s);
+  return launch_one<St, TPB, false, false>(h, nullptr, none, gain, eps, wr, bias, T, H, E, k, flags, xn, ids, w,
+                                           logits, s);
+}
+
 template <typename St>
-hipError_t launch_st(const void* h, const float* gain, float eps, const float* wr, const float* bias,
-                     int T, int H, int E, int k, int flags, void* xn, int32_t* ids, float* w,
-                     float* logits, hipStream_t s) {
+hipError_t launch_st(const void* h, void* hout, const CombineArgs* ca, const float* gain, float eps,
+                     const float* wr, const float* bias, int T, int H, int E, int k, int flags, void* xn,
+                     int32_t* ids, float* w, float* logits, hipStream_t s) {
   constexpr size_t kLds = 64 * 1024;
-  if (T >= 4096 && lds_bytes<St, 32>(H) <= 160 * 1024)
-    return launch_tpb<St, 32>(h, gain, eps, wr, bias, T, H, E, k, flags, xn, ids, w, logits, s);
+  if (T >= 4096 && lds_bytes<St, 32>(H) <= 160 * 1024) {
+    if (ca) {  // prefill-sized batches: the combine as its own launch, then the 32-token route
+      hipError_t e = launch_combine(ca->y, ca->inv, ca->w, ca->ys, ca->S, h, T, H, ca->k, ca->n_rows,
+                                    sizeof(St) == 2 ? kBf16 : kF32, hout, nullptr, s);
+      if (e != hipSuccess) return e;
+      h = hout;
+    }
+    return launch_tpb<St, 32>(h, nullptr, nullptr, gain, eps, wr, bias, T, H, E, k, flags, xn, ids, w, logits, s);
+  }
   if (T > 256 && lds_bytes<St, 16>(H) <= kLds)
-    return launch_tpb<St, 16>(h, gain, eps, wr, bias, T, H, E, k, flags, xn, ids, w, logits, s);
+    return launch_tpb<St, 16>(h, hout, ca, gain, eps, wr, bias, T, H, E, k, flags, xn, ids, w, logits, s);
   if (T > 256 && lds_bytes<St, 8>(H) <= kLds)
-    return launch_tpb<St, 8>(h, gain, eps, wr, bias, T, H, E, k, flags, xn, ids, w, logits, s);
-  return launch_tpb<St, 2>(h, gain, eps, wr, bias, T, H, E, k, flags, xn, ids, w, logits, s);
+    return launch_tpb<St, 8>(h, hout, ca, gain, eps, wr, bias, T, H, E, k, flags, xn, ids, w, logits, s);
+  return launch_tpb<St, 2>(h, hout, ca, gain, eps, wr, bias, T, H, E, k, flags, xn, ids, w, logits, s);
 }
 
 }  // namespace
@@ -244,8 +310,17 @@ hipError_t launch_route(const void* h, const float* gain, float eps, const float
                         const float* bias, int T, int H, int E, int k, int flags, int dtype,
                         void* xn, int32_t* ids, float* w, float* logits, hipStream_t s) {
   if (dtype == kBf16)
-    return launch_st<bf16_t>(h, gain, eps, w_router, bias, T, H, E, k, flags, xn, ids, w, logits, s);
-  return launch_st<float>(h, gain, eps, w_router, bias, T, H, E, k, flags, xn, ids, w, logits, s);
+    return launch_st<bf16_t>(h, nullptr, nullptr, gain, eps, w_router, bias, T, H, E, k, flags, xn, ids, w, logits,
+                             s);
+  return launch_st<float>(h, nullptr, nullptr, gain, eps, w_router, bias, T, H, E, k, flags, xn, ids, w, logits, s);
+}
+
+hipError_t launch_combine_route(const CombineArgs& ca, void* h, const float* gain, float eps, const float* w_router,
+                                const float* bias, int T, int H, int E, int k, int flags, int dtype, void* xn,
+                                int32_t* ids, float* w, float* logits, hipStream_t s) {
+  if (dtype == kBf16)
+    return launch_st<bf16_t>(h, h, &ca, gain, eps, w_router, bias, T, H, E, k, flags, xn, ids, w, logits, s);
+  return launch_st<float>(h, h, &ca, gain, eps, w_router, bias, T, H, E, k, flags, xn, ids, w, logits, s);
 }
 
 }  // namespace moe

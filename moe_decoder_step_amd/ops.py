@@ -15,7 +15,7 @@ import torch
 from . import _lib as L
 
 __all__ = [
-    "Packed", "pack_weights", "packed_weights_bytes", "moe_route", "moe_permute", "moe_grouped_swiglu", "moe_combine", "lmhead_argmax",
+    "Packed", "pack_weights", "packed_weights_bytes", "moe_route", "moe_combine_route", "moe_permute", "moe_grouped_swiglu", "moe_combine", "lmhead_argmax",
     "moe_expert_gate_up", "moe_expert_down", "spec_verify", "spec_plant_drafts", "spec_advance",
     "spec_gather_rows", "permute_workspace_bytes", "swiglu_workspace_bytes",
     "lmhead_workspace_bytes", "dtype_code", "expert_weights", "lm_weights", "router_weights", "route_alloc", "permute_alloc", "swiglu_alloc",
@@ -142,6 +142,29 @@ def moe_route(h, w_router, bias, k, xn, topk_ids, topk_w, logits=None, gain=None
     L.check("moe_route", L.load().moe_route(
         _p(h), _p(gain), float(eps), _p(w_router), _p(bias), T, H, E, k, flags, dtype_code(h),
         _p(xn), _p(topk_ids), _p(topk_w), _p(logits), _stream(h)))
+
+
+def moe_combine_route(y, inv, topk_w_prev, y_shared, S, h, w_router, bias, k, xn, topk_ids, topk_w,
+                      logits=None, gain=None, eps=1e-6, norm=True, renormalize=True):
+    """The previous layer's moe_combine in place on h, then moe_route on it (one launch)."""
+    T, H = h.shape
+    E = w_router.shape[0]
+    k_prev = topk_w_prev.shape[1]
+    packed = isinstance(w_router, Packed)
+    if packed and w_router.kind != L.PACK_ROUTER:
+        raise TypeError("w_router must be packed with router_weights")
+    for t, d, n in ((y, h.dtype, "y"), (inv, torch.int32, "inv"), (topk_w_prev, torch.float32, "topk_w_prev"),
+                    (y_shared, h.dtype, "y_shared"), (h, None, "h"), (xn, h.dtype, "xn"),
+                    (w_router, torch.float32, "w_router"), (bias, torch.float32, "bias"),
+                    (gain, torch.float32, "gain"), (topk_ids, torch.int32, "topk_ids"),
+                    (topk_w, torch.float32, "topk_w"), (logits, torch.float32, "logits")):
+        _need(t, d, n)
+    flags = ((L.ROUTE_NORM if norm else 0) | (L.ROUTE_RENORM if renormalize else 0)
+             | (L.ROUTE_WPACKED if packed else 0))
+    L.check("moe_combine_route", L.load().moe_combine_route(
+        _p(y), _p(inv), _p(topk_w_prev), _p(y_shared), S, y.shape[0], k_prev, _p(h), T, H, _p(gain), float(eps),
+        _p(w_router), _p(bias), E, k, flags, dtype_code(h), _p(xn), _p(topk_ids), _p(topk_w), _p(logits),
+        _stream(h)))
 
 
 def moe_permute(topk_ids, E, S, offsets, gather, inv, ws=None):

@@ -34,6 +34,8 @@ class VerifyStack:
         # when a list: (start, end) torch.cuda.Event pairs around every expert
         # gate/up launch, recorded on the stream the kernels run on
         self.ffn_events = None
+        # fuse each block's combine with the next block's routing
+        self.fuse = True
         self.E, self.k, self.S, self.eps = E, k, S, eps
         wgu = layers[0]["w_gate_up"]
         self.dtype = wgu.dtype
@@ -67,16 +69,27 @@ class VerifyStack:
             self.committed = torch.empty((max_seqs, K + 1), **i32)
             self.n_commit = torch.empty(max_seqs, **i32)
 
-    def layer(self, li: int, T: int) -> None:
-        """One MoE block in place on self.h[:T]."""
+    def _route(self, li: int, T: int, combine_prev: bool) -> None:
+        """Layer li's routing of self.h[:T]; with combine_prev, layer li-1's
+        combine runs in the same launch first (moe_combine_route)."""
+        w = self.layers[li]
+        lg = None if self.logits is None else self.logits[:T]
+        if combine_prev:
+            k, S = self.k, self.S
+            y = self.y[:T * k + S * T]
+            ops.moe_combine_route(y[:T * k], self.inv[:T * k], self.tw[:T], y[T * k:] if S else None, S,
+                                  self.h[:T], w["w_router"], w.get("bias"), k, self.xn[:T], self.ids[:T],
+                                  self.tw[:T], lg, eps=self.eps)
+        else:
+            ops.moe_route(self.h[:T], w["w_router"], w.get("bias"), self.k, self.xn[:T], self.ids[:T],
+                          self.tw[:T], lg, eps=self.eps)
+
+    def _experts(self, li: int, T: int) -> None:
+        """Layer li's permutation and routed + shared expert FFN (y rows)."""
         E, k, S = self.E, self.k, self.S
         w = self.layers[li]
-        h = self.h[:T]
-        ops.moe_route(h, w["w_router"], w.get("bias"), k, self.xn[:T], self.ids[:T], self.tw[:T],
-                      None if self.logits is None else self.logits[:T], eps=self.eps)
         ops.moe_permute(self.ids[:T], E, S, self.offsets, self.gather[:T * k + S * T], self.inv[:T * k], self.pws)
         n_rows = T * k + S * T
-        y = self.y[:n_rows]
         act = self.act[:n_rows]
         if self.ffn_events is not None:
             ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -85,22 +98,48 @@ class VerifyStack:
         if self.ffn_events is not None:
             ev[1].record()
             self.ffn_events.append(ev)
-        ops.moe_expert_down(act, self.offsets, w["w_down"], y, max_rows=T)
+        ops.moe_expert_down(act, self.offsets, w["w_down"], self.y[:n_rows], max_rows=T)
+
+    def _combine(self, T: int) -> None:
+        """The last routed layer's weighted combine + residual, in place on self.h[:T]."""
+        k, S = self.k, self.S
+        y = self.y[:T * k + S * T]
+        h = self.h[:T]
         ops.moe_combine(y[:T * k], self.inv[:T * k], self.tw[:T], y[T * k:] if S else None, S, h, h)
+
+    def layer(self, li: int, T: int) -> None:
+        """One MoE block in place on self.h[:T], unfused (route, permute,
+        experts, combine)."""
+        self._route(li, T, False)
+        self._experts(li, T)
+        self._combine(T)
 
     def forward(self, h_in: torch.Tensor, record: list | None = None) -> torch.Tensor:
         """All MoE blocks on a copy of h_in; returns the final hidden state (a view).
 
-        With `record` (a list), a copy of every block's input, expert ids and
-        routing weights is appended to it (for teacher-forced comparison)."""
+        Block l's combine runs fused with block l+1's routing (moe_combine_route)
+        unless self.fuse is False.  With `record` (a list), a copy of every
+        block's input, expert ids, routing weights and output is appended to
+        it (for teacher-forced comparison)."""
         T = h_in.shape[0]
         self.h[:T].copy_(h_in)
-        for li in range(len(self.layers)):
-            inp = self.h[:T].clone() if record is not None else None
-            self.layer(li, T)
+        L = len(self.layers)
+        for li in range(L):
+            if self.fuse:
+                self._route(li, T, li > 0)
+            else:
+                if li > 0:
+                    self._combine(T)
+                self._route(li, T, False)
             if record is not None:
-                record.append({"input": inp, "ids": self.ids[:T].clone(), "w": self.tw[:T].clone(),
-                               "output": self.h[:T].clone()})
+                inp = self.h[:T].clone()
+                if li > 0:
+                    record[-1]["output"] = inp
+                record.append({"input": inp, "ids": self.ids[:T].clone(), "w": self.tw[:T].clone()})
+            self._experts(li, T)
+        self._combine(T)
+        if record is not None:
+            record[-1]["output"] = self.h[:T].clone()
         return self.h[:T]
 
     def head(self, T: int) -> None:

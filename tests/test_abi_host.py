@@ -21,7 +21,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = L.header_functions()
-    assert len(names) == 18
+    assert len(names) == 19
     assert set(names) == set(L.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
@@ -129,6 +129,27 @@ def test_expert_halves_checks(lib):
     assert dn(A, A, 0, 40, A, 1280, 896, 4, m.BF16, A, None) == L.ERR_SHAPE
     assert dn(MIS, A, 66, 40, A, 1280, 896, 4, m.BF16, A, None) == L.ERR_ALIGN
     assert dn(None, None, 66, 0, None, 1280, 896, 4, m.BF16, None, None) == L.OK
+
+
+def test_combine_route_checks(lib):
+    f = lib.moe_combine_route
+    # y, inv, w_prev, ys, S, n_rows, k_prev, h, T, H, gain, eps, wr, bias, E, k, flags, dtype, xn, ids, w, lg, s
+    base = [A, A, A, A, 2, 1024, 6, A, 128, 1280, None, 1e-6, A, None, 64, 6, 3, m.BF16, A, A, A, None, None]
+
+    def call(**kw):
+        a = list(base)
+        names = ["y", "inv", "wp", "ys", "S", "n_rows", "kp", "h", "T", "H", "gain", "eps", "wr", "b", "E", "k",
+                 "flags", "dt", "xn", "ids", "w", "lg", "s"]
+        for key, v in kw.items():
+            a[names.index(key)] = v
+        return f(*a)
+    assert call(inv=None) == L.ERR_NULL
+    assert call(ids=None) == L.ERR_NULL
+    assert call(H=1284) == L.ERR_UNSUPPORTED
+    assert call(E=65) == L.ERR_UNSUPPORTED
+    assert call(k=7, E=6) == L.ERR_SHAPE
+    assert call(h=MIS) == L.ERR_ALIGN
+    assert call(T=0) == L.OK
 
 
 def test_advance_and_gather_checks(lib):

@@ -153,3 +153,24 @@ def test_determinism_and_batch_invariance(m):
         torch.cuda.synchronize()
         assert torch.equal(st.h[:n], out1[sub]), f"hidden of rows {sub} depends on the batch"
         assert torch.equal(st.argmax[:n], ids1[sub])
+
+
+@pytest.mark.parametrize("shape,T,L", [("step128", 128, 3), ("step128", 4, 2), ("tiny", 16, 1), ("step128", 300, 2)])
+def test_fused_combine_route_matches_separate_calls(m, shape, T, L):
+    """moe_combine_route (each block's combine fused with the next block's
+    routing) gives the same hidden states, ids and weights as moe_combine
+    followed by moe_route, bit for bit."""
+    sh = synth.SHAPES[shape]
+    st, layers, w_lm = _stack(m, sh, 2, T, L=L)
+    h = synth.hidden(13, T, sh.H, sh.torch_dtype, DEV)
+    outs = []
+    for fuse in (True, False):
+        st.fuse = fuse
+        rec = []
+        st.forward(h, rec)
+        torch.cuda.synchronize()
+        outs.append(rec)
+    for a, b in zip(*outs):
+        for key in ("input", "ids", "w", "output"):
+            assert torch.equal(a[key], b[key]), key
+
