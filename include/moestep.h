@@ -202,6 +202,29 @@ int moe_grouped_swiglu(const void* x, const int32_t* gather, const int32_t* offs
 int moe_expert_gate_up(const void* x, const int32_t* gather, const int32_t* offsets,
                        int G, int n_rows, const void* w_gate_up, int T, int H, int I,
                        int max_rows, int dtype, void* act, void* stream);
+/* ---------------------------------------------------------------------------
+ * moe_expert_gate_up_routed -- moe_permute and moe_expert_gate_up in one
+ * launch for decode-sized batches: each block derives the rows it needs from
+ * the expert ids (a histogram of the ids and a stable scan of its group's
+ * (token, slot) pairs), so the permutation is never a launch of its own.
+ * The rows, act and the outputs offsets and inv are exactly those of
+ * moe_permute (E routed groups in expert order, then S shared groups of T
+ * token-ordered rows) followed by moe_expert_gate_up; the gather list is not
+ * produced.  offsets feeds moe_expert_down, inv feeds the combine.
+ *
+ * x         [T,H] bf16           in   normed tokens
+ * topk_ids  [T,k] int32          in   (clamped into [0,E))
+ * w_gate_up [E+S, 2I, H] bf16    in   packed (MOE_PACK_GATE_UP, N = I)
+ * act       [T*k + S*T, I] bf16  out
+ * offsets   [E+S+1] int32        out  (written also for T = 0)
+ * inv       [T,k] int32          out
+ * Limits: MOE_BF16 only; T*k <= 4096; E <= 64, S <= 8, E+S <= 128; H, I as
+ * for moe_grouped_swiglu.  Larger batches use moe_permute and
+ * moe_expert_gate_up (MOE_ERR_UNSUPPORTED here).
+ * ------------------------------------------------------------------------- */
+int moe_expert_gate_up_routed(const void* x, const int32_t* topk_ids, int T, int k, int E, int S,
+                              const void* w_gate_up, int H, int I, int dtype, void* act,
+                              int32_t* offsets, int32_t* inv, void* stream);
 int moe_expert_down(const void* act, const int32_t* offsets, int G, int n_rows,
                     const void* w_down, int H, int I, int max_rows, int dtype,
                     void* y, void* stream);

@@ -84,6 +84,17 @@ int moe_expert_gate_up(const void* x, const int32_t* gather, const int32_t* offs
                                         as_stream(stream)));
 }
 
+int moe_expert_gate_up_routed(const void* x, const int32_t* topk_ids, int T, int k, int E, int S,
+                              const void* w_gate_up, int H, int I, int dtype, void* act, int32_t* offsets,
+                              int32_t* inv, void* stream) {
+  int st = moe::check_gate_up_routed(x, topk_ids, T, k, E, S, w_gate_up, H, I, dtype, act, offsets, inv);
+  if (st != MOE_OK) return st;
+  if (T == 0)  // every group empty: offsets all zero, written by moe_permute's kernel
+    return hip_status(moe::launch_permute(topk_ids, 0, k, E, S, offsets, nullptr, nullptr, nullptr, as_stream(stream)));
+  return hip_status(moe::launch_gate_up_routed(x, topk_ids, T, k, E, S, w_gate_up, H, I, act, offsets, inv,
+                                               as_stream(stream)));
+}
+
 int moe_expert_down(const void* act, const int32_t* offsets, int G, int n_rows, const void* w_down, int H, int I,
                     int max_rows, int dtype, void* y, void* stream) {
   int st = moe::check_down(act, offsets, G, n_rows, w_down, H, I, max_rows, dtype, y);

@@ -33,6 +33,16 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int S, int32_
 hipError_t launch_gate_up(const void* x, const int32_t* gather, const int32_t* offsets, int G, int n_rows,
                           const void* w_gate_up, int T, int H, int I, int max_rows, int dtype, void* act,
                           hipStream_t s);
+// the gate/up stage deriving its rows from the expert ids (moe_permute's layout)
+struct RoutedArgs {
+  const int32_t* ids;  // [T, k] expert of each (token, slot)
+  int k, E, S;
+  int32_t* offsets;    // [E+S+1] out
+  int32_t* inv;        // [T, k] out
+};
+hipError_t launch_gate_up_routed(const void* x, const int32_t* ids, int T, int k, int E, int S, const void* w_gate_up,
+                                 int H, int I, void* act, int32_t* offsets, int32_t* inv, hipStream_t s);
+
 // grouped expert GEMM (bf16, prefill-sized groups): gated = gate/up stage
 bool gemm_path_ok(int K, int N, int max_rows);
 hipError_t launch_gemm(bool gated, const void* x, const int32_t* gather, const int32_t* offsets, int G, int n_rows,

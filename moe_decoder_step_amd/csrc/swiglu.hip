@@ -93,11 +93,12 @@ __device__ __forceinline__ void stream_rows(const bf16_t* wa, const bf16_t* wb, 
 //        streams as many bytes per k-step as in the gated stage.
 // A block of 8 wavefronts owns one column tile of one group and one range of
 // up to 16 rows, staged once into LDS (one barrier) and shared by its waves.
-template <bool GATED>
+template <bool GATED, bool ROUTED>
 __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
     const bf16_t* __restrict__ x, const int32_t* __restrict__ gather,
     const int32_t* __restrict__ offsets, int G, int n_rows, int T,
-    const bf16_t* __restrict__ W, int K, int N, int n_ctiles, bf16_t* __restrict__ out) {
+    const bf16_t* __restrict__ W, int K, int N, int n_ctiles, bf16_t* __restrict__ out, RoutedArgs rt) {
+  static_assert(!ROUTED || GATED, "only the gate/up stage derives its rows from the expert ids");
   constexpr int D = 3;                    // k-steps of weights in flight per wavefront
   constexpr int WCOLS = GATED ? 16 : 32;  // output columns per wavefront
   extern __shared__ __align__(16) bf16_t xl[];   // [kRows][lds_row(K)]
@@ -111,16 +112,55 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
   // items per XCD and the surplus blocks, last in every XCD's list, exit.
   // Wavefront 0 finds the item: lane l handles groups l and l+64 (G <= 128),
   // counts its items on this XCD, and a wavefront prefix sum places them.
-  __shared__ int item_g, item_ct, item_r0, item_r1;
+  __shared__ int item_g, item_ct, item_r0, item_r1, item_gs;
+  __shared__ int s_cnt[2 * kWave];   // ROUTED: rows per group
+  __shared__ int s_tok[kRows];       // ROUTED: tokens of the block's rows (routed groups)
   const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  if (ROUTED) {
+    // rows per group: a histogram of the (token, slot) expert ids; each
+    // shared group holds every token
+    for (int g = threadIdx.x; g < G; g += kBlockThreads) s_cnt[g] = g < rt.E ? 0 : T;
+    __syncthreads();
+    for (int p = threadIdx.x; p < T * rt.k; p += kBlockThreads) atomicAdd(&s_cnt[clampi(rt.ids[p], 0, rt.E - 1)], 1);
+    __syncthreads();
+  }
   if (threadIdx.x < kWave) {
     const int l = threadIdx.x;
     int r0[2], r1[2], nr[2], nc[2];
+    if (ROUTED) {
+      // group row ranges: an exclusive scan of the counts (routed groups in
+      // expert order, then the shared groups), as moe_permute lays them out
+      int c[2], inc[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int g = l + h * kWave;
+        c[h] = g < G ? s_cnt[g] : 0;
+        inc[h] = c[h];
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+          const int v = __shfl_up(inc[h], o, kWave);
+          if (l >= o) inc[h] += v;
+        }
+      }
+      inc[1] += __shfl(inc[0], kWave - 1, kWave);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        r1[h] = inc[h];
+        r0[h] = inc[h] - c[h];
+      }
+      if (blockIdx.x == 0) {  // the offsets for the down projection and the combine
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          if (l + h * kWave <= G) rt.offsets[l + h * kWave] = l + h * kWave < G ? r0[h] : n_rows;
+      }
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int g = l + h * kWave;
-      r0[h] = g < G ? clampi(offsets[g], 0, n_rows) : 0;
-      r1[h] = g < G ? clampi(offsets[g + 1], r0[h], n_rows) : 0;
+      if (!ROUTED) {
+        r0[h] = g < G ? clampi(offsets[g], 0, n_rows) : 0;
+        r1[h] = g < G ? clampi(offsets[g + 1], r0[h], n_rows) : 0;
+      }
       nr[h] = (r1[h] - r0[h] + kRows - 1) / kRows;
       // tiles of group g on this XCD: ct = c0, c0+8, ... < n_ctiles
       const int c0 = ((xcd - g * n_ctiles) % 8 + 8) % 8;
@@ -150,6 +190,7 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
         item_ct = c0 + 8 * (li / nr[h]);
         item_r0 = r0[h] + (li % nr[h]) * kRows;
         item_r1 = r1[h];
+        item_gs = r0[h];
       }
     }
   }
@@ -159,7 +200,30 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
   const int ct = item_ct;
   const int mstart = item_r0;
   const int mr = min(kRows, item_r1 - mstart);
-  const int r_begin = clampi(offsets[g], 0, n_rows);
+  const int r_begin = ROUTED ? item_gs : clampi(offsets[g], 0, n_rows);
+  if (ROUTED && g < rt.E) {
+    // the tokens of this block's rows: the group's (token, slot) pairs in
+    // ascending order, ranks mstart - r_begin .. +mr; the blocks of the first
+    // column tile also record each pair's row (inv) for the combine
+    if (threadIdx.x < kWave) {
+      const int lane = threadIdx.x;
+      const int want0 = mstart - r_begin, want1 = want0 + mr;
+      const bool owner = ct == 0;
+      int base = 0;
+      for (int c0 = 0; c0 < T * rt.k && base < want1; c0 += kWave) {
+        const int p = c0 + lane;
+        const bool f = p < T * rt.k && clampi(rt.ids[p], 0, rt.E - 1) == g;
+        const unsigned long long m = __ballot(f);
+        const int rank = base + __popcll(m & ((1ull << lane) - 1ull));
+        if (f && rank >= want0 && rank < want1) {
+          s_tok[rank - want0] = p / rt.k;
+          if (owner) rt.inv[p] = r_begin + rank;
+        }
+        base += __popcll(m);
+      }
+    }
+    __syncthreads();
+  }
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col0 = ct * (kWaves * WCOLS) + wave * WCOLS;
@@ -193,7 +257,8 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
         const int row = idx / nseg, seg = idx % nseg;
         const int r = mstart + min(row, mr - 1);
         int s;
-        if (GATED) s = gather ? clampi(gather[r], 0, T - 1) : clampi(r - r_begin, 0, T - 1);
+        if (ROUTED) s = g < rt.E ? s_tok[min(row, mr - 1)] : clampi(r - r_begin, 0, T - 1);
+        else if (GATED) s = gather ? clampi(gather[r], 0, T - 1) : clampi(r - r_begin, 0, T - 1);
         else s = r;
         v[u] = ldg16(x + (size_t)s * K + seg * 8);
         dst[u] = row * ldr + seg * 8;
@@ -230,9 +295,9 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
   }
 }
 
-template <bool GATED>
+template <bool GATED, bool ROUTED = false>
 hipError_t launch_skinny(const bf16_t* x, const int32_t* gather, const int32_t* offsets, int G, int n_rows, int T,
-                         const bf16_t* W, int K, int N, bf16_t* out, hipStream_t s) {
+                         const bf16_t* W, int K, int N, bf16_t* out, hipStream_t s, RoutedArgs ra = {}) {
   constexpr int tile = kWaves * (GATED ? 16 : 32);
   const int n_ctiles = (N + tile - 1) / tile;
   // items on one XCD <= ceil(n_ctiles / 8) * sum over groups of ceil(rows / 16)
@@ -241,12 +306,12 @@ hipError_t launch_skinny(const bf16_t* x, const int32_t* gather, const int32_t* 
   const int blocks = 8 * per_xcd;
   const size_t lds = (size_t)kRows * lds_row(K) * sizeof(bf16_t);
   if (lds > 64 * 1024) {  // K > 2040: allow up to the CU's 160 KB of LDS
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&skinny_kernel<GATED>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&skinny_kernel<GATED, ROUTED>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((skinny_kernel<GATED>), dim3(blocks), dim3(kBlockThreads), lds, s, x, gather, offsets, G,
-                     n_rows, T, W, K, N, n_ctiles, out);
+  hipLaunchKernelGGL((skinny_kernel<GATED, ROUTED>), dim3(blocks), dim3(kBlockThreads), lds, s, x, gather, offsets,
+                     G, n_rows, T, W, K, N, n_ctiles, out, ra);
   return hipGetLastError();
 }
 
@@ -318,6 +383,13 @@ hipError_t launch_gate_up(const void* x, const int32_t* gather, const int32_t* o
     return launch_gemm(true, x, gather, offsets, G, n_rows, T, w_gate_up, H, I, act, s);
   return launch_skinny<true>(static_cast<const bf16_t*>(x), gather, offsets, G, n_rows, T,
                              static_cast<const bf16_t*>(w_gate_up), H, I, static_cast<bf16_t*>(act), s);
+}
+
+hipError_t launch_gate_up_routed(const void* x, const int32_t* ids, int T, int k, int E, int S, const void* w_gate_up,
+                                 int H, int I, void* act, int32_t* offsets, int32_t* inv, hipStream_t s) {
+  const RoutedArgs ra{ids, k, E, S, offsets, inv};
+  return launch_skinny<true, true>(static_cast<const bf16_t*>(x), nullptr, nullptr, E + S, T * k + S * T, T,
+                                   static_cast<const bf16_t*>(w_gate_up), H, I, static_cast<bf16_t*>(act), s, ra);
 }
 
 hipError_t launch_down(const void* act, const int32_t* offsets, int G, int n_rows, const void* w_down, int H,

@@ -85,6 +85,19 @@ int check_gather_rows(const void* pool, const int32_t* seq_ids, const int32_t* s
   return kOk;
 }
 
+int check_gate_up_routed(const void* x, const int32_t* ids, int T, int k, int E, int S, const void* w_gate_up, int H,
+                         int I, int dtype, const void* act, const int32_t* offsets, const int32_t* inv) {
+  if (!valid_dtype(dtype)) return kErrUnsupported;
+  if (T < 0 || k <= 0 || E <= 0 || k > E || S < 0 || H <= 0 || I <= 0) return kErrShape;
+  if (dtype != kBf16 || E > kMaxExperts || S > kMaxShared || (long long)T * k > kPermuteChunk) return kErrUnsupported;
+  if (H % 32 != 0 || I % 32 != 0 || H > 4096 || I > 4096 || E + S > 128) return kErrUnsupported;
+  if (!offsets) return kErrNull;
+  if (T == 0) return kOk;
+  if (!x || !ids || !w_gate_up || !act || !inv) return kErrNull;
+  if (!aligned16(x) || !aligned16(w_gate_up) || !aligned16(act)) return kErrAlign;
+  return kOk;
+}
+
 int check_route(const void* h, const float* w_router, int T, int H, int E, int k, int dtype,
                 const void* xn, const int32_t* ids, const float* w) {
   if (!valid_dtype(dtype)) return kErrUnsupported;

@@ -35,6 +35,8 @@ int check_advance(const int32_t* n_commit, const int32_t* committed, const int32
                   const int32_t* n_active);
 int check_gather_rows(const void* pool, const int32_t* seq_ids, const int32_t* steps, int B, int R, int J, int S,
                       int row_bytes, const void* out);
+int check_gate_up_routed(const void* x, const int32_t* ids, int T, int k, int E, int S, const void* w_gate_up, int H,
+                         int I, int dtype, const void* act, const int32_t* offsets, const int32_t* inv);
 int check_route(const void* h, const float* w_router, int T, int H, int E, int k, int dtype,
                 const void* xn, const int32_t* ids, const float* w);
 int check_permute(const int32_t* ids, int T, int k, int E, int S, const int32_t* offsets,

@@ -16,7 +16,7 @@ from . import _lib as L
 
 __all__ = [
     "Packed", "pack_weights", "packed_weights_bytes", "moe_route", "moe_combine_route", "moe_permute", "moe_grouped_swiglu", "moe_combine", "lmhead_argmax",
-    "moe_expert_gate_up", "moe_expert_down", "spec_verify", "spec_plant_drafts", "spec_advance",
+    "moe_expert_gate_up", "moe_expert_gate_up_routed", "moe_expert_down", "ROUTED_MAX_PAIRS", "spec_verify", "spec_plant_drafts", "spec_advance",
     "spec_gather_rows", "permute_workspace_bytes", "swiglu_workspace_bytes",
     "lmhead_workspace_bytes", "dtype_code", "expert_weights", "lm_weights", "router_weights", "route_alloc", "permute_alloc", "swiglu_alloc",
     "combine_alloc", "lmhead_alloc", "verify_alloc",
@@ -207,6 +207,25 @@ def moe_expert_gate_up(x, gather, offsets, w_gate_up, act, max_rows=None):
     L.check("moe_expert_gate_up", L.load().moe_expert_gate_up(
         _p(x), _p(gather), _p(offsets), G, n_rows, _p(w_gate_up), T, H, I2 // 2,
         T if max_rows is None else int(max_rows), dtype_code(x), _p(act), _stream(x)))
+
+
+ROUTED_MAX_PAIRS = 4096   # T*k up to which moe_expert_gate_up_routed runs
+
+
+def moe_expert_gate_up_routed(x, topk_ids, E, S, w_gate_up, act, offsets, inv):
+    """moe_permute + moe_expert_gate_up in one launch (decode-sized batches):
+    writes act, offsets and inv as the two calls would (no gather list)."""
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    I = w_gate_up.shape[1] // 2
+    if not (isinstance(w_gate_up, Packed) and w_gate_up.kind == L.PACK_GATE_UP):
+        raise TypeError("bf16 expert weights must be packed (expert_weights / pack_weights)")
+    for t, d, n in ((x, torch.bfloat16, "x"), (topk_ids, torch.int32, "topk_ids"), (act, torch.bfloat16, "act"),
+                    (offsets, torch.int32, "offsets"), (inv, torch.int32, "inv")):
+        _need(t, d, n)
+    L.check("moe_expert_gate_up_routed", L.load().moe_expert_gate_up_routed(
+        _p(x), _p(topk_ids), T, k, E, S, _p(w_gate_up), H, I, dtype_code(x), _p(act), _p(offsets), _p(inv),
+        _stream(x)))
 
 
 def moe_expert_down(act, offsets, w_down, y, max_rows=None):

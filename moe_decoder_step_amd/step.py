@@ -34,7 +34,8 @@ class VerifyStack:
         # when a list: (start, end) torch.cuda.Event pairs around every expert
         # gate/up launch, recorded on the stream the kernels run on
         self.ffn_events = None
-        # fuse each block's combine with the next block's routing
+        # fuse each block's combine with the next block's routing, and (bf16,
+        # decode-sized batches) the permutation into the gate/up launch
         self.fuse = True
         self.E, self.k, self.S, self.eps = E, k, S, eps
         wgu = layers[0]["w_gate_up"]
@@ -88,13 +89,20 @@ class VerifyStack:
         """Layer li's permutation and routed + shared expert FFN (y rows)."""
         E, k, S = self.E, self.k, self.S
         w = self.layers[li]
-        ops.moe_permute(self.ids[:T], E, S, self.offsets, self.gather[:T * k + S * T], self.inv[:T * k], self.pws)
         n_rows = T * k + S * T
         act = self.act[:n_rows]
+        routed = self.fuse and self.dtype == torch.bfloat16 and T * k <= ops.ROUTED_MAX_PAIRS
+        if not routed:
+            ops.moe_permute(self.ids[:T], E, S, self.offsets, self.gather[:n_rows], self.inv[:T * k], self.pws)
         if self.ffn_events is not None:
             ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             ev[0].record()
-        ops.moe_expert_gate_up(self.xn[:T], self.gather[:n_rows], self.offsets, w["w_gate_up"], act, max_rows=T)
+        if routed:  # the permutation is derived inside the gate/up launch
+            ops.moe_expert_gate_up_routed(self.xn[:T], self.ids[:T], E, S, w["w_gate_up"], act, self.offsets,
+                                          self.inv[:T * k].view(T, k))
+        else:
+            ops.moe_expert_gate_up(self.xn[:T], self.gather[:n_rows], self.offsets, w["w_gate_up"], act,
+                                   max_rows=T)
         if self.ffn_events is not None:
             ev[1].record()
             self.ffn_events.append(ev)

@@ -21,7 +21,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = L.header_functions()
-    assert len(names) == 19
+    assert len(names) == 20
     assert set(names) == set(L.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
@@ -129,6 +129,17 @@ def test_expert_halves_checks(lib):
     assert dn(A, A, 0, 40, A, 1280, 896, 4, m.BF16, A, None) == L.ERR_SHAPE
     assert dn(MIS, A, 66, 40, A, 1280, 896, 4, m.BF16, A, None) == L.ERR_ALIGN
     assert dn(None, None, 66, 0, None, 1280, 896, 4, m.BF16, None, None) == L.OK
+
+
+def test_gate_up_routed_checks(lib):
+    f = lib.moe_expert_gate_up_routed
+    # x, ids, T, k, E, S, wgu, H, I, dtype, act, offsets, inv, stream
+    assert f(A, A, 128, 6, 64, 2, A, 1280, 896, m.BF16, A, None, A, None) == L.ERR_NULL
+    assert f(A, A, 128, 6, 64, 2, A, 1280, 896, m.F32, A, A, A, None) == L.ERR_UNSUPPORTED   # bf16 only
+    assert f(A, A, 683, 6, 64, 2, A, 1280, 896, m.BF16, A, A, A, None) == L.ERR_UNSUPPORTED  # > 4096 pairs
+    assert f(A, A, 128, 7, 6, 2, A, 1280, 896, m.BF16, A, A, A, None) == L.ERR_SHAPE
+    assert f(A, A, 128, 6, 64, 2, MIS, 1280, 896, m.BF16, A, A, A, None) == L.ERR_ALIGN
+    assert f(A, A, 128, 6, 64, 2, A, 1280, 896, m.BF16, A, A, None, None) == L.ERR_NULL
 
 
 def test_combine_route_checks(lib):

@@ -200,6 +200,30 @@ def test_expert_halves(m, shape, T):
             assert_close(ag[a:b], O.swiglu(xh[gath[a:b]], wgu[g], eye, sh.dtype), tol, f"act group {g}")
 
 
+@pytest.mark.parametrize("T", [1, 4, 37, 128, 300, 682])
+def test_gate_up_routed_matches_permute_path(m, T):
+    """moe_expert_gate_up_routed: activation rows, offsets and inv identical to
+    moe_permute + moe_expert_gate_up (bit for bit); 682 tokens x 6 slots is
+    the largest batch it takes (4,092 pairs)."""
+    sh = synth.SHAPES["layer128"]
+    w = _layer(sh, 4)
+    h = synth.hidden(6, T, sh.H, torch.bfloat16, DEV)
+    xn, ids, tw, _ = m.route_alloc(h, w["w_router"], None, sh.k)
+    off, gat, inv = m.permute_alloc(ids, sh.E, sh.S)
+    n_rows = T * sh.k + sh.S * T
+    wgu_p, _ = m.expert_weights(w["w_gate_up"], w["w_down"])
+    act = torch.empty((n_rows, sh.I), dtype=torch.bfloat16, device=DEV)
+    m.moe_expert_gate_up(xn, gat, off, wgu_p, act, max_rows=T)
+    act2 = torch.full_like(act, float("nan"))
+    off2 = torch.full_like(off, -7)
+    inv2 = torch.full((T, sh.k), -7, dtype=torch.int32, device=DEV)
+    m.moe_expert_gate_up_routed(xn, ids, sh.E, sh.S, wgu_p, act2, off2, inv2)
+    torch.cuda.synchronize()
+    assert torch.equal(off2, off)
+    assert torch.equal(inv2.view(-1), inv)
+    assert torch.equal(act2, act)
+
+
 def test_grouped_swiglu_identity_gather_and_skewed_groups(m):
     """gather = NULL (row r of a group reads token r - offsets[g]); groups of
     0, 1, 15, 16, 17, 33, 100 rows (ragged M-blocks, several row blocks)."""
