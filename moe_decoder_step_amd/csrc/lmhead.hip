@@ -14,6 +14,8 @@
 //     per (row, block) goes to the workspace;
 //   * a second kernel takes the max over blocks for each row.
 // Max is exact, so the result does not depend on reduction order.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "validate.hpp"
@@ -167,6 +169,129 @@ __global__ __launch_bounds__(kThreads) void lm_bf16_kernel(const bf16_t* __restr
   }
 }
 
+// Streaming form (H % 128 == 0): a block of 8 wavefronts owns 256 vocabulary
+// rows; wavefront w streams its pair of 16-row sets with a rotating register
+// pipeline 4 k-steps deep that runs across the chunk barriers, so the
+// weights never wait on the h staging.  h goes through LDS in 64-element
+// chunks (2 k-steps, double buffered) in fragment order: the 1 KB B operand
+// of token block i and k-step s is lane-ordered, so each read is one
+// conflict-free ds_read_b128.  A chunk is loaded into registers two chunks
+// ahead and written to LDS one chunk ahead; one barrier per chunk.
+constexpr int kSWaves = 8;
+constexpr int kSThreads = kSWaves * 64;
+constexpr int kSRows = kSWaves * 32;      // vocabulary rows per block
+
+template <int MB>
+__global__ __launch_bounds__(kSThreads) void lm_stream_kernel(const bf16_t* __restrict__ h,
+                                                              const bf16_t* __restrict__ W, int T, int H, int V,
+                                                              unsigned long long* __restrict__ part, int nblk) {
+  constexpr int MROWS = MB * 16;
+  constexpr int NF = MB * 2;              // h fragments per chunk
+  constexpr int FPT = (NF + kSWaves - 1) / kSWaves;  // fragments staged per thread
+  __shared__ __align__(16) char xl[2][NF * 1024];
+  __shared__ unsigned long long red[kSWaves][MROWS];
+
+  const int blk = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nK = H / 32, nC = H / 64;
+  const int n_pairs = (V + 31) / 32;
+  const int pair = min(blk * kSWaves + wave, n_pairs - 1);  // past the vocabulary: a valid pair, masked below
+  const int vbase = (blk * kSWaves + wave) * 32;
+  const bf16_t* wa = W + (size_t)pair * nK * 1024 + lane * 8;
+  const bf16_t* wb = wa + 512;
+
+  for (int mstart = 0; mstart < T; mstart += MROWS) {
+    const int mr = min(MROWS, T - mstart);
+    // h staging: thread stages fragments f = wave + 8u (token block f/2,
+    // k-step f%2 of the chunk), lane's token and 8-element segment
+    const bf16_t* hsrc[FPT];
+#pragma unroll
+    for (int u = 0; u < FPT; ++u) {
+      const int f = min(wave + kSWaves * u, NF - 1);
+      const int tok = mstart + min(16 * (f >> 1) + (lane & 15), mr - 1);   // past T: a valid row, never stored
+      hsrc[u] = h + (size_t)tok * H + 32 * (f & 1) + 8 * (lane >> 4);
+    }
+    uint4 hs[FPT];
+    auto hload = [&](int c) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < FPT; ++u) hs[u] = ldg16(hsrc[u] + c * 64);
+    };
+    auto hstore = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < FPT; ++u)
+        if (wave + kSWaves * u < NF) *reinterpret_cast<uint4*>(&xl[buf][(wave + kSWaves * u) * 1024 + lane * 16]) = hs[u];
+    };
+
+    f32x4_t acc[2][MB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) acc[0][i] = acc[1][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    uint4 ra[4], rb[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      ra[d] = ldg16(wa + min(d, nK - 1) * 1024);
+      rb[d] = ldg16(wb + min(d, nK - 1) * 1024);
+    }
+    hload(0);
+    hstore(0);
+    if (nC > 1) hload(1);
+    lds_barrier();
+
+    // one chunk: k-steps 2c, 2c+1 use ring slots S0, S0+1 and refill them 4 ahead
+    auto chunk = [&](int c, auto S0) __attribute__((always_inline)) {
+      constexpr int s0 = decltype(S0)::value;
+      if (c + 1 < nC) hstore((c + 1) & 1);
+      if (c + 2 < nC) hload(c + 2);
+      const char* buf = xl[c & 1];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+          const bf16x8_t bx = as_bf16x8(*reinterpret_cast<const uint4*>(buf + (i * 2 + ks) * 1024 + lane * 16));
+          acc[0][i] = mfma16x16x32(as_bf16x8(ra[s0 + ks]), bx, acc[0][i]);
+          acc[1][i] = mfma16x16x32(as_bf16x8(rb[s0 + ks]), bx, acc[1][i]);
+        }
+        const int kk = min(2 * c + ks + 4, nK - 1);
+        ra[s0 + ks] = ldg16(wa + kk * 1024);
+        rb[s0 + ks] = ldg16(wb + kk * 1024);
+      }
+      lds_barrier();
+    };
+    int c = 0;
+    for (; c + 1 < nC; c += 2) {
+      chunk(c, std::integral_constant<int, 0>());
+      chunk(c + 1, std::integral_constant<int, 2>());
+    }
+    if (c < nC) chunk(c, std::integral_constant<int, 0>());
+
+    // lane holds D[vocab 4*(lane/16)+v][token lane%16] of each (set, token block)
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      unsigned long long best = 0ull;
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int vocab = vbase + st * 16 + 4 * (lane >> 4) + v;
+          const unsigned long long key = vocab < V ? make_key(acc[st][i][v], vocab) : 0ull;
+          best = key > best ? key : best;
+        }
+      unsigned long long o = __shfl_xor(best, 16, kWave);
+      best = o > best ? o : best;
+      o = __shfl_xor(best, 32, kWave);
+      best = o > best ? o : best;
+      if (lane < 16) red[wave][i * 16 + lane] = best;
+    }
+    lds_barrier();
+    if (threadIdx.x < mr) {
+      unsigned long long best = red[0][threadIdx.x];
+#pragma unroll
+      for (int w = 1; w < kSWaves; ++w) best = red[w][threadIdx.x] > best ? red[w][threadIdx.x] : best;
+      part[(size_t)(mstart + threadIdx.x) * nblk + blk] = best;
+    }
+    lds_barrier();
+  }
+}
+
 // fp32 path: one thread per vocabulary row, plain sequential dot products.
 __global__ __launch_bounds__(256) void lm_f32_kernel(const float* __restrict__ h, const float* __restrict__ W,
                                                      int T, int H, int V, unsigned long long* __restrict__ part,
@@ -210,7 +335,10 @@ __global__ __launch_bounds__(64) void lm_reduce_kernel(const unsigned long long*
 template <int MB>
 void launch_mb(const bf16_t* h, const bf16_t* W, int T, int H, int V, unsigned long long* part, int nblk,
                hipStream_t s) {
-  hipLaunchKernelGGL((lm_bf16_kernel<MB>), dim3(nblk), dim3(kThreads), 0, s, h, W, T, H, V, part, nblk);
+  if (H % 128 == 0)  // nblk = ceil(V / 256): one block per 256 vocabulary rows
+    hipLaunchKernelGGL((lm_stream_kernel<MB>), dim3(nblk), dim3(kSThreads), 0, s, h, W, T, H, V, part, nblk);
+  else
+    hipLaunchKernelGGL((lm_bf16_kernel<MB>), dim3(nblk), dim3(kThreads), 0, s, h, W, T, H, V, part, nblk);
 }
 
 }  // namespace
@@ -218,7 +346,8 @@ void launch_mb(const bf16_t* h, const bf16_t* W, int T, int H, int V, unsigned l
 hipError_t launch_lmhead(const void* h, const void* w_lm, int T, int H, int V, int dtype,
                          int32_t* ids, float* max_logit, void* ws, hipStream_t s) {
   unsigned long long* part = static_cast<unsigned long long*>(ws);
-  const int nblk = lmhead_blocks(V, dtype);
+  // the streaming bf16 form has half as many (256-row) blocks as the workspace is sized for
+  const int nblk = dtype == kBf16 && H % 128 == 0 ? (V + kSRows - 1) / kSRows : lmhead_blocks(V, dtype);
   if (dtype == kF32) {
     hipLaunchKernelGGL(lm_f32_kernel, dim3(nblk), dim3(256), 0, s, static_cast<const float*>(h),
                        static_cast<const float*>(w_lm), T, H, V, part, nblk);
