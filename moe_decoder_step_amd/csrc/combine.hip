@@ -46,22 +46,12 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
   __syncthreads();
   for (int c = threadIdx.x * 8; c < H; c += kThreads * 8) {
     float acc[8], f[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const float wj = wk[j];
-      load8(y + (size_t)rows[j] * H + c, f);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, f[i], acc[i]);
-    }
-    for (int s = 0; s < S; ++s) {
-      load8(ys + ((size_t)s * T + t) * H + c, f);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += f[i];
-    }
+    typename Row8<St>::raw rres{};
+    if (res) rres = Row8<St>::load(res + (size_t)t * H + c);   // in flight with the expert rows
+    combine8(y, rows, wk, k, ys, S, T, t, H, c, acc);
     if (combined) store8(combined + (size_t)t * H + c, acc);
     if (res) {
-      load8(res + (size_t)t * H + c, f);
+      Row8<St>::unpack(rres, f);
 #pragma unroll
       for (int i = 0; i < 8; ++i) f[i] += acc[i];
       store8(out + (size_t)t * H + c, f);

@@ -142,4 +142,60 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// ---- the weighted combine of one token's expert rows, 8 hidden elements ----
+// acc[q] = sum_j w[j] * y[rows[j]][c+q] (j ascending, fmaf) + sum_s ys[s*T+t][c+q]
+// (s ascending), in fp32.  Every row load of a batch of 8 is issued before
+// any of the sums, so the k rows cost one memory round trip, not k.
+template <typename St> struct Row8;
+template <> struct Row8<bf16_t> {
+  typedef uint4 raw;
+  static __device__ __forceinline__ raw load(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+  static __device__ __forceinline__ void unpack(const raw& r, float* f) { unpack8(r, f); }
+};
+template <> struct Row8<float> {
+  struct raw { float4 a, b; };
+  static __device__ __forceinline__ raw load(const float* p) {
+    return raw{*reinterpret_cast<const float4*>(p), *reinterpret_cast<const float4*>(p + 4)};
+  }
+  static __device__ __forceinline__ void unpack(const raw& r, float* f) {
+    f[0] = r.a.x; f[1] = r.a.y; f[2] = r.a.z; f[3] = r.a.w; f[4] = r.b.x; f[5] = r.b.y; f[6] = r.b.z; f[7] = r.b.w;
+  }
+};
+
+template <typename St>
+__device__ __forceinline__ void combine8(const St* y, const int* rows, const float* wk, int k, const St* ys, int S,
+                                         int T, int t, int H, int c, float* acc) {
+#pragma unroll
+  for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    typename Row8<St>::raw r[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) r[u] = Row8<St>::load(y + (size_t)rows[min(j0 + u, k - 1)] * H + c);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (j0 + u < k) {
+        float f[8];
+        Row8<St>::unpack(r[u], f);
+        const float wj = wk[j0 + u];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = fmaf(wj, f[q], acc[q]);
+      }
+    }
+  }
+  for (int s0 = 0; s0 < S; s0 += 4) {
+    typename Row8<St>::raw r[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) r[u] = Row8<St>::load(ys + ((size_t)min(s0 + u, S - 1) * T + t) * H + c);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (s0 + u < S) {
+        float f[8];
+        Row8<St>::unpack(r[u], f);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] += f[q];
+      }
+    }
+  }
+}
+
 }  // namespace moe

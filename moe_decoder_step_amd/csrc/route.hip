@@ -58,6 +58,25 @@ __device__ __forceinline__ void store8(float* p, const bf16_t* v) {
   for (int j = 0; j < 8; ++j) f[j] = __uint_as_float((uint32_t)v[j] << 16);
   store8(p, f);
 }
+// sum of squares of 8 values in fp64, in order
+__device__ __forceinline__ double seg_sumsq(const float* f) {
+  double s = 0.0;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) s += (double)f[q] * (double)f[q];
+  return s;
+}
+__device__ __forceinline__ bf16_t round_store(double v, bf16_t*);
+__device__ __forceinline__ float round_store(double v, float*);
+// xn = f * scale (* gain[c+q]) in fp64, one rounding to the storage type
+template <typename St>
+__device__ __forceinline__ void norm8(const float* f, double scale, const float* gain, int c, St* o) {
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    double v = (double)f[q] * scale;
+    if (gain) v *= (double)gain[c + q];
+    o[q] = round_store(v, (St*)nullptr);
+  }
+}
 __device__ __forceinline__ bf16_t to_store(float v, bf16_t*) { return f32_to_bf16(v); }
 __device__ __forceinline__ float to_store(float v, float*) { return v; }
 __device__ __forceinline__ bf16_t round_store(double v, bf16_t*) { return f64_to_bf16(v); }
@@ -89,49 +108,8 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   const int t0 = blockIdx.x * TPB;
   const int e = lane;
 
-  // ---- 0. (fused) the previous layer's combine: h' = h + sum_j w_j y[inv] + sum_s ys,
-  //         the same fixed-order fp32 sums as moe_combine, into h and the LDS rows ----
-  if constexpr (COMBINE) {
-    __shared__ int crow[TPB][kMaxExperts];
-    __shared__ float cwt[TPB][kMaxExperts];
-    const St* y = static_cast<const St*>(ca.y);
-    const St* ys = static_cast<const St*>(ca.ys);
-    for (int idx = threadIdx.x; idx < TPB * ca.k; idx += kThreads) {
-      const int i = idx / ca.k, j = idx % ca.k, t = min(t0 + i, T - 1);
-      crow[i][j] = clampi(ca.inv[(size_t)t * ca.k + j], 0, ca.n_rows - 1);
-      cwt[i][j] = ca.w[(size_t)t * ca.k + j];
-    }
-    __syncthreads();
-    const int nseg = H / 8;
-    for (int idx = threadIdx.x; idx < TPB * nseg; idx += kThreads) {
-      const int i = idx / nseg, c = (idx % nseg) * 8, t = t0 + i;
-      if (t >= T) continue;
-      float acc[8], f[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = 0.f;
-      for (int j = 0; j < ca.k; ++j) {
-        const float wj = cwt[i][j];
-        load8(y + (size_t)crow[i][j] * H + c, f);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) acc[q] = fmaf(wj, f[q], acc[q]);
-      }
-      for (int s = 0; s < ca.S; ++s) {
-        load8(ys + ((size_t)s * T + t) * H + c, f);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) acc[q] += f[q];
-      }
-      load8(h + (size_t)t * H + c, f);
-      St o[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) o[q] = to_store(f[q] + acc[q], (St*)nullptr);
-      store8(hout + (size_t)t * H + c, o);
-      store8(xs + i * H + c, o);
-    }
-    __syncthreads();
-  }
-
   // this wavefront's slice of the hidden dim; its router weights go out first
-  // (they do not depend on the norm) and land while the norm runs
+  // (they depend on nothing) and land while the combine and the norm run
   const int hq = ((H / kWaves + 3) / 4) * 4;
   const int h_lo = min(H, wave * hq), h_hi = min(H, h_lo + hq);
   // router weights of hidden elements hh..hh+3 for this lane's expert: packed,
@@ -140,47 +118,105 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     if (PACKED) return *reinterpret_cast<const float4*>(wr + ((size_t)(hh >> 2) * kWave + e) * 4);
     return *reinterpret_cast<const float4*>(wr + (size_t)min(e, E - 1) * H + hh);
   };
+  // the fused form holds only the first kPreA of them in registers during
+  // the combine (the combine's row loads need registers too), the rest go out
+  // right after it
+  constexpr int kPreA = COMBINE ? (kPre < 8 ? kPre : 8) : kPre;
   float4 wpre[kPre > 0 ? kPre : 1];
 #pragma unroll
-  for (int u = 0; u < kPre; ++u) wpre[u] = wload(min(h_lo + 4 * u, H - 4));
+  for (int u = 0; u < kPreA; ++u) wpre[u] = wload(min(h_lo + 4 * u, H - 4));
 
-  // ---- 1. RMSNorm: xn = h / sqrt(mean(h^2) + eps) * gain, scale in fp64, one rounding ----
-  const bool norm = (flags & 1) != 0;
-  for (int i = wave; i < TPB; i += kWaves) {
-    const int t = t0 + i;
-    if (t >= T) break;
-    const St* hrow = COMBINE ? reinterpret_cast<const St*>(xs + i * H) : h + (size_t)t * H;
-    Xs* xrow = xs + i * H;
-    double scale = 1.0;
-    if (norm) {
-      double ss = 0.0;
-      for (int c = lane * 8; c < H; c += 8 * kWave) {
-        float f[8];
-        load8(hrow + c, f);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) ss += (double)f[j] * (double)f[j];
-      }
-      ss = __shfl(wave_sum_f64(ss), 0, kWave);
-      scale = 1.0 / sqrt(ss / (double)H + (double)eps);
+  // ---- 0. (fused) the previous layer's combine: h' = h + sum_j w_j y[inv] + sum_s ys,
+  //         the same fixed-order fp32 sums as moe_combine, into h and the LDS rows ----
+  if constexpr (COMBINE) {
+    __shared__ int crow[TPB][kMaxExperts];
+    __shared__ float cwt[TPB][kMaxExperts];
+    __shared__ double s_scale[TPB];
+    double* ssp = reinterpret_cast<double*>(part);  // [TPB][H/8] segment sums (part is free until the logits)
+    const St* y = static_cast<const St*>(ca.y);
+    const St* ys = static_cast<const St*>(ca.ys);
+    for (int idx = threadIdx.x; idx < TPB * ca.k; idx += kThreads) {
+      const int i = idx / ca.k, j = idx % ca.k, t = min(t0 + i, T - 1);
+      crow[i][j] = clampi(ca.inv[(size_t)t * ca.k + j], 0, ca.n_rows - 1);
+      cwt[i][j] = ca.w[(size_t)t * ca.k + j];
     }
-    for (int c = lane * 8; c < H; c += 8 * kWave) {
+    lds_barrier();
+    const int nseg = H / 8;
+    for (int idx = threadIdx.x; idx < TPB * nseg; idx += kThreads) {
+      const int i = idx / nseg, c = (idx % nseg) * 8, t = t0 + i;
+      if (t >= T) continue;
+      float acc[8], f[8];
+      const typename Row8<St>::raw rres = Row8<St>::load(h + (size_t)t * H + c);
+      combine8(y, crow[i], cwt[i], ca.k, ys, ca.S, T, t, H, c, acc);
+      Row8<St>::unpack(rres, f);
+      St o[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) o[q] = to_store(f[q] + acc[q], (St*)nullptr);
+      store8(hout + (size_t)t * H + c, o);
+      store8(xs + i * H + c, o);
+      float g[8];
+      load8(o, g);
+      ssp[idx] = seg_sumsq(g);   // this 8-element segment's sum of squares
+    }
+    lds_barrier();
+    // scale per token from its segment sums, in the order the unfused norm uses
+    for (int i = wave; i < TPB; i += kWaves) {
+      if (t0 + i >= T) break;
+      double ss = 0.0;
+      for (int sg = lane; sg < nseg; sg += kWave) ss += ssp[i * nseg + sg];
+      ss = __shfl(wave_sum_f64(ss), 0, kWave);
+      if (lane == 0) s_scale[i] = (flags & 1) ? 1.0 / sqrt(ss / (double)H + (double)eps) : 1.0;
+    }
+    lds_barrier();
+    for (int idx = threadIdx.x; idx < TPB * nseg; idx += kThreads) {
+      const int i = idx / nseg, c = (idx % nseg) * 8, t = t0 + i;
+      if (t >= T) continue;
       float f[8];
       St o[8];
-      load8(hrow + c, f);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        double v = (double)f[j];
-        if (norm) {
-          v *= scale;
-          if (gain) v *= (double)gain[c + j];
-        }
-        o[j] = round_store(v, (St*)nullptr);
-      }
+      load8(xs + i * H + c, f);
+      norm8(f, s_scale[i], (flags & 1) ? gain : nullptr, c, o);
       store8(xn + (size_t)t * H + c, o);
-      store8(xrow + c, o);
+      store8(xs + i * H + c, o);
     }
   }
-  __syncthreads();
+
+
+#pragma unroll
+  for (int u = kPreA; u < kPre; ++u) wpre[u] = wload(min(h_lo + 4 * u, H - 4));
+
+  // ---- 1. RMSNorm: xn = h / sqrt(mean(h^2) + eps) * gain, scale in fp64, one rounding ----
+  // (the fused form did this above with the whole block).  The sum of squares
+  // is taken per 8-element segment, lane l adding segments l, l+64, ... in
+  // order, then a wavefront tree: the same order in both forms.
+  if constexpr (!COMBINE) {
+    const bool norm = (flags & 1) != 0;
+    for (int i = wave; i < TPB; i += kWaves) {
+      const int t = t0 + i;
+      if (t >= T) break;
+      const St* hrow = h + (size_t)t * H;
+      Xs* xrow = xs + i * H;
+      double scale = 1.0;
+      if (norm) {
+        double ss = 0.0;
+        for (int c = lane * 8; c < H; c += 8 * kWave) {
+          float f[8];
+          load8(hrow + c, f);
+          ss += seg_sumsq(f);
+        }
+        ss = __shfl(wave_sum_f64(ss), 0, kWave);
+        scale = 1.0 / sqrt(ss / (double)H + (double)eps);
+      }
+      for (int c = lane * 8; c < H; c += 8 * kWave) {
+        float f[8];
+        St o[8];
+        load8(hrow + c, f);
+        norm8(f, scale, norm ? gain : nullptr, c, o);
+        store8(xn + (size_t)t * H + c, o);
+        store8(xrow + c, o);
+      }
+    }
+  }
+  lds_barrier();
 
   // ---- 2. partial logits over this wavefront's slice, fp32, ascending h ----
   float acc[TPB];
@@ -200,10 +236,10 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   for (int u = 0; u < kPre; ++u)
     if (h_lo + 4 * u < h_hi) fma4(wpre[u], h_lo + 4 * u);
   for (int hh = h_lo + 4 * kPre; hh < h_hi; hh += 4) fma4(wload(hh), hh);
-  if (lds_union<TPB>()) __syncthreads();  // every wavefront is done with the normed rows
+  if (lds_union<TPB>()) lds_barrier();  // every wavefront is done with the normed rows
 #pragma unroll
   for (int i = 0; i < TPB; ++i) part[(wave * TPB + i) * kWave + e] = acc[i];
-  __syncthreads();
+  lds_barrier();
 
   // ---- 3. top-k by (logit desc, expert id asc), then softmax weights ----
   for (int i = wave; i < TPB; i += kWaves) {

@@ -120,9 +120,9 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
     // rows per group: a histogram of the (token, slot) expert ids; each
     // shared group holds every token
     for (int g = threadIdx.x; g < G; g += kBlockThreads) s_cnt[g] = g < rt.E ? 0 : T;
-    __syncthreads();
+    lds_barrier();
     for (int p = threadIdx.x; p < T * rt.k; p += kBlockThreads) atomicAdd(&s_cnt[clampi(rt.ids[p], 0, rt.E - 1)], 1);
-    __syncthreads();
+    lds_barrier();
   }
   if (threadIdx.x < kWave) {
     const int l = threadIdx.x;
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
   const int g = item_g;
   if (g < 0) return;
   const int ct = item_ct;
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
         base += __popcll(m);
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
