@@ -41,8 +41,9 @@ def parse():
                     choices=["step128", "batch1", "layer128", "prefill", "decode32", "copy"],
                     help="copy: a plain 1 GiB device copy, the reference for scaling the HBM traffic counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-layers", type=int, default=6, help="layers of the oracle sample")
-    ap.add_argument("--cpu-vocab", type=int, default=65536, help="LM-head rows of the oracle sample")
+    ap.add_argument("--cpu-layers", type=int, default=12, help="layers of the oracle sample")
+    ap.add_argument("--cpu-vocab", type=int, default=129280, help="LM-head rows of the oracle sample")
+    ap.add_argument("--cpu-reps", type=int, default=3, help="repetitions of the oracle sample")
     ap.add_argument("--cpu-tokens", type=int, default=512, help="tokens of the oracle sample (at most T)")
     ap.add_argument("--drafts", type=int, default=None, help="drafts K per sequence (positions = K + 1)")
     ap.add_argument("--no-graph", action="store_true", help="batch1: time eager launches only")
@@ -82,7 +83,8 @@ def measured_traffic():
                 kv[k.strip()] = v.strip()
     if kv.get("source_sha256") != kernel_source_hash():
         return None, "kernel changed since the counters were taken"
-    return float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"]), TRAFFIC_FILE
+    return (float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"]),
+            os.path.relpath(TRAFFIC_FILE, ROOT))
 
 
 def copy_calibration(args) -> int:
@@ -259,7 +261,8 @@ def main() -> int:
                     "traffic": None, "traffic_source": "no counter run recorded for this kernel",
                     "us_per_launch": gu_ms * 1e3, "algorithmic_flops_per_launch": gu_flops}
     else:
-        roofline = {"kernel": "moe_expert_gate_up (skinny_kernel<true>)", "bound": "hbm",
+        roofline = {"kernel": "moe_expert_gate_up_routed (skinny_kernel<true, true>)" if T * sh.k <= 4096
+                    else "moe_expert_gate_up (skinny_kernel<true, false>)", "bound": "hbm",
                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "traffic_source": traffic_src,
                     "us_per_launch": gu_ms * 1e3, "algorithmic_bytes_per_launch": gu_b}
@@ -368,9 +371,10 @@ def decode_loop_bench(args) -> int:
 
 
 def cpu_baseline(args, sh, layers, w_lm, h_in, T) -> dict:
-    """The fp64 oracle on the host cores over a bounded sample of the same step:
-    `cpu_layers` MoE layers on all T tokens plus the LM head over `cpu_vocab`
-    vocabulary rows, scaled to the full 12 layers and vocabulary."""
+    """The fp64 oracle on the host cores over a bounded sample of the same
+    step: `cpu_layers` MoE layers on `cpu_tokens` tokens plus the LM head over
+    `cpu_vocab` vocabulary rows (by default the whole 128-token step), timed
+    `cpu_reps` times and scaled to the full step when the sample is smaller."""
     import numpy as np
     import torch
 
@@ -384,19 +388,22 @@ def cpu_baseline(args, sh, layers, w_lm, h_in, T) -> dict:
     log(f"cpu baseline: oracle on {nl} layer(s) x {nt} tokens + {args.cpu_vocab} LM rows")
     hw = [{k: host(v) for k, v in layers[l].items()} for l in range(nl)]
     x = host(h_in[:nt])
-    t0 = time.perf_counter()
-    cur = x
-    for l in range(nl):
-        cur = O.moe_layer(cur, hw[l], sh.k, sh.eps, "bf16")["h_out"]
-    t_layers = time.perf_counter() - t0
-    t_lm = 0.0
-    vs = 0
-    if w_lm is not None:
-        vs = min(args.cpu_vocab, sh.V)
-        wl = host(w_lm[:vs])
+    vs = min(args.cpu_vocab, sh.V) if w_lm is not None else 0
+    wl = host(w_lm[:vs]) if vs else None
+    reps = max(1, args.cpu_reps)
+    t_layers = t_lm = 0.0
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        cur = x
+        for l in range(nl):
+            cur = O.moe_layer(cur, hw[l], sh.k, sh.eps, "bf16")["h_out"]
         t1 = time.perf_counter()
-        O.lm_argmax(cur, wl)
-        t_lm = time.perf_counter() - t1
+        if vs:
+            O.lm_argmax(cur, wl)
+        t_layers += t1 - t0
+        t_lm += time.perf_counter() - t1
+    t_layers /= reps
+    t_lm /= reps
     t_step = (t_layers * sh.L / nl + (t_lm * sh.V / vs if vs else 0.0)) * T / nt
     try:
         from threadpoolctl import threadpool_info
@@ -405,8 +412,8 @@ def cpu_baseline(args, sh, layers, w_lm, h_in, T) -> dict:
         cores = os.cpu_count() or 1
     return {"value": T / t_step, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{nl} of {sh.L} MoE layers on {nt} of {T} tokens ({t_layers:.1f}s) + LM head over "
-                      f"{vs} of {sh.V} vocabulary rows ({t_lm:.1f}s), scaled to the full step "
-                      f"({t_step:.1f}s per step)"}
+                      f"{vs} of {sh.V} vocabulary rows ({t_lm:.1f}s), mean of {reps} runs, scaled to the full "
+                      f"step ({t_step:.1f}s per step)"}
 
 
 if __name__ == "__main__":
