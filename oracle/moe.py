@@ -13,7 +13,7 @@ __all__ = [
     "rmsnorm", "router_logits", "topk_ids", "topk_weights", "topk_gap", "route",
     "permute", "silu", "swiglu", "moe_layer", "lm_logits", "lm_argmax",
     "spec_verify", "plant_drafts", "greedy_decode", "speculative_decode",
-    "verify_step", "active_params", "total_params",
+    "verify_step", "draft_step", "draft_propose", "active_params", "total_params",
 ]
 
 
@@ -348,6 +348,57 @@ def verify_step(h, layers, w_lm, drafts, k: int, eps: float, mode: str,
     acc, com, nc = spec_verify(d, ids.reshape(B, K + 1))
     return {"layers": outs, "argmax": ids, "max_logit": mx, "gap": gap,
             "accepted": acc, "committed": com, "n_commit": nc}
+
+
+# ----------------------------------------------------------------------------
+# the draft block (FastMTP)
+# ----------------------------------------------------------------------------
+
+def draft_step(h, tok, wts: dict, w_lm, eps: float, mode: str) -> dict:
+    """One recursive step of the dense draft block.
+
+    The pages describe FastMTP as one dense block applied recursively for K
+    prediction steps, fed back its own hidden state ("Jina AI's 3.4B OCR model
+    targets faster page parsing", section "FastMTP cuts decoding work";
+    jina.ai/de page, sections "Modell und Training" and "Erste Schritte",
+    where the head runs as vLLM's eagle method).  The block's inside is not
+    given; the reading is a DeepSeek-style multi-token-prediction block with
+    attention omitted (as in the verifier):
+
+        x  = [rmsnorm(h) ; rmsnorm(E[tok])]          (2H)
+        h0 = W_p x                                   (H)
+        h1 = h0 + W_d (silu(W_g z) * (W_u z)),  z = rmsnorm(h0)
+        draft = argmax_v (W_lm h1)[v]                (the verifier's LM head)
+
+    wts: emb [V,H], w_proj [H,2H], w_gate_up [2I,H] (gate rows, then up),
+    w_down [H,I].  Storage rounding (`mode`) at x, h0, z, the SwiGLU
+    activation, the FFN output and h1.  Returns h1, the draft ids and the
+    LM-head gaps (top-1 minus top-2).
+    """
+    h = f64(h)
+    e = f64(np.asarray(wts["emb"])[np.asarray(tok, dtype=np.int64)])
+    x = np.concatenate([store(rmsnorm(h, eps), mode), store(rmsnorm(e, eps), mode)], axis=1)
+    h0 = store(x @ f64(wts["w_proj"]).T, mode)
+    z = store(rmsnorm(h0, eps), mode)
+    f = swiglu(z, wts["w_gate_up"], wts["w_down"], mode)
+    h1 = store(h0 + f, mode)
+    ids, mx, gap = lm_argmax(h1, w_lm)
+    return {"x": x, "h0": h0, "z": z, "h1": h1, "ids": ids, "gap": gap}
+
+
+def draft_propose(h, tok, wts: dict, w_lm, K: int, eps: float, mode: str) -> dict:
+    """K recursive draft steps from the verifier's hidden state h [B,H] at the
+    last committed token tok [B]: step i reads the previous step's output
+    hidden state and draft token.  Returns drafts [B,K] and the steps."""
+    steps = []
+    cur_h, cur_t = f64(h), np.asarray(tok, dtype=np.int64)
+    for _ in range(K):
+        st = draft_step(cur_h, cur_t, wts, w_lm, eps, mode)
+        steps.append(st)
+        cur_h, cur_t = st["h1"], st["ids"]
+    B = np.asarray(tok).shape[0]
+    drafts = np.stack([st["ids"] for st in steps], axis=1) if K else np.zeros((B, 0), np.int64)
+    return {"drafts": drafts, "steps": steps}
 
 
 # ----------------------------------------------------------------------------

@@ -32,6 +32,7 @@ import torch
 
 __all__ = [
     "Shape", "SHAPES", "subseed", "normal", "router_weight", "layer_weights", "lm_weight",
+    "DRAFT_INTERMEDIATE", "draft_weights",
     "hidden", "uniform_ids", "plant_schedule", "bf16_bits",
 ]
 
@@ -123,6 +124,25 @@ def layer_weights(seed: int, layer: int, sh: Shape, device="cpu") -> dict:
         "bias": torch.zeros(sh.E, dtype=torch.float32, device=device),
         "w_gate_up": normal(subseed(seed, "w_gate_up", layer), (G, 2 * sh.I, sh.H), 0.02, dt, device),
         "w_down": normal(subseed(seed, "w_down", layer), (G, sh.H, sh.I), 0.02, dt, device),
+    }
+
+
+DRAFT_INTERMEDIATE = 3584   # dense draft-block FFN width (a synthetic choice: 4 x 896)
+
+
+def draft_weights(seed: int, sh: Shape, device="cpu", I: int = DRAFT_INTERMEDIATE) -> dict:
+    """Weights of the dense draft block (storage dtype):
+      emb        [V, H]     token embedding ~N(0, 1)
+      w_proj     [H, 2H]    projection of [norm(h); norm(emb)] ~N(0, 0.02)
+      w_gate_up  [1, 2I, H] dense SwiGLU gate rows then up rows ~N(0, 0.02)
+      w_down     [1, H, I]  ~N(0, 0.02)
+    """
+    dt = sh.torch_dtype
+    return {
+        "emb": normal(subseed(seed, "draft_emb"), (sh.V, sh.H), 1.0, dt, device),
+        "w_proj": normal(subseed(seed, "draft_proj"), (sh.H, 2 * sh.H), 0.02, dt, device),
+        "w_gate_up": normal(subseed(seed, "draft_gate_up"), (1, 2 * I, sh.H), 0.02, dt, device),
+        "w_down": normal(subseed(seed, "draft_down"), (1, sh.H, I), 0.02, dt, device),
     }
 
 

@@ -420,6 +420,87 @@ def test_speculative_equals_greedy(K):
 
 
 # --------------------------------------------------------------------------
+# the dense draft block
+# --------------------------------------------------------------------------
+
+def _draft_tiny(rng, V=97, H=64, I=48):
+    return {"emb": rng.standard_normal((V, H)), "w_proj": rng.standard_normal((H, 2 * H)) * 0.02,
+            "w_gate_up": rng.standard_normal((2 * I, H)) * 0.02, "w_down": rng.standard_normal((H, I)) * 0.02}
+
+
+def test_draft_identity_projection_reduces_to_greedy_head():
+    """W_p = [I | 0] and a zero FFN: each step's hidden state is the normed
+    input, so every draft is the LM head's argmax of rmsnorm(h), and feeding
+    the hidden state back (rmsnorm of a normed row is the row) repeats it."""
+    rng = np.random.default_rng(21)
+    V, H = 97, 64
+    w = _draft_tiny(rng, V, H)
+    w["w_proj"] = np.concatenate([np.eye(H), np.zeros((H, H))], axis=1)
+    w["w_down"] = np.zeros_like(w["w_down"])
+    w_lm = rng.standard_normal((V, H))
+    h = rng.standard_normal((5, H)) * 3.0
+    tok = rng.integers(0, V, 5)
+    out = O.draft_propose(h, tok, w, w_lm, 3, 1e-6, "exact")
+    ref, _, gap = O.lm_argmax(O.rmsnorm(h, 1e-6), w_lm)
+    ok = gap > 1e-9
+    np.testing.assert_allclose(out["steps"][0]["h1"], O.rmsnorm(h, 1e-6), rtol=1e-14, atol=0)
+    for i in range(3):
+        np.testing.assert_array_equal(out["drafts"][ok, i], ref[ok])
+        # a normed row has mean square 1 - O(eps), so renorming moves it by O(eps)
+        np.testing.assert_allclose(out["steps"][i]["h1"], O.rmsnorm(h, 1e-6), rtol=1e-5, atol=0)
+
+
+def test_draft_token_projection_copies_the_token():
+    """W_p = [0 | I], zero FFN and the LM head tied to the embedding: the
+    draft is the token whose embedding best matches rmsnorm(E[tok]), i.e. tok
+    itself for random high-dimensional embeddings; the recursion feeds each
+    draft back as the next input token, so all K drafts repeat it."""
+    rng = np.random.default_rng(22)
+    V, H = 97, 64
+    w = _draft_tiny(rng, V, H)
+    w["w_proj"] = np.concatenate([np.zeros((H, H)), np.eye(H)], axis=1)
+    w["w_down"] = np.zeros_like(w["w_down"])
+    h = rng.standard_normal((6, H))
+    tok = rng.integers(0, V, 6)
+    # embeddings with equal norms so the best match is the token itself
+    w["emb"] = w["emb"] / np.linalg.norm(w["emb"], axis=1, keepdims=True)
+    out = O.draft_propose(h, tok, w, w["emb"], 4, 1e-6, "exact")
+    np.testing.assert_array_equal(out["drafts"], np.repeat(tok[:, None], 4, axis=1))
+
+
+def test_draft_block_ffn_is_the_residual_swiglu():
+    """A zero projection makes h0 = 0, whose RMSNorm is 0, so the FFN adds
+    silu(0) * 0 = 0: h1 = 0 and the draft is the lowest vocabulary id (all
+    logits equal) -- the tie rule through the whole block."""
+    rng = np.random.default_rng(23)
+    w = _draft_tiny(rng)
+    w["w_proj"] = np.zeros_like(w["w_proj"])
+    out = O.draft_step(rng.standard_normal((3, 64)), np.array([1, 2, 3]), w, rng.standard_normal((97, 64)),
+                       1e-6, "bf16")
+    assert not out["h1"].any()
+    np.testing.assert_array_equal(out["ids"], [0, 0, 0])
+
+
+@pytest.mark.parametrize("K", [1, 3])
+def test_speculation_with_draft_block_proposals_equals_greedy(K):
+    """Drafts from the (untrained, random) draft block: the committed
+    sequence is still exactly the greedy one."""
+    next_tokens, V = _tiny_token_model()
+    rng = np.random.default_rng(300 + K)
+    H = 128
+    w = _draft_tiny(rng, V, H, 64)
+    w_lm = rng.standard_normal((V, H)) * 0.02
+    emb = rng.standard_normal((V, H))
+
+    def propose(s, K):
+        out = O.draft_propose(emb[[s[-1]]], np.array([s[-1]]), w, w_lm, K, 1e-6, "exact")
+        return [int(d) for d in out["drafts"][0]]
+    ref = O.greedy_decode(7, 40, next_tokens)
+    seq, passes, commits = O.speculative_decode(7, 40, next_tokens, propose, K)
+    assert seq == ref and all(1 <= c <= K + 1 for c in commits)
+
+
+# --------------------------------------------------------------------------
 # parameter accounting against the pages
 # --------------------------------------------------------------------------
 
