@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="step128",
-                    choices=["step128", "batch1", "layer128", "prefill", "decode32", "copy"],
+                    choices=["step128", "batch1", "layer128", "prefill", "decode32", "spec128", "copy"],
                     help="copy: a plain 1 GiB device copy, the reference for scaling the HBM traffic counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=12, help="layers of the oracle sample")
@@ -48,6 +48,7 @@ def parse():
     ap.add_argument("--drafts", type=int, default=None, help="drafts K per sequence (positions = K + 1)")
     ap.add_argument("--no-graph", action="store_true", help="batch1: time eager launches only")
     ap.add_argument("--target", type=int, default=1085, help="decode32: committed tokens per sequence")
+    ap.add_argument("--seqs", type=int, default=32, help="spec128: sequences per step")
     return ap.parse_args()
 
 
@@ -119,6 +120,8 @@ def main() -> int:
         return copy_calibration(args)
     if args.workload == "decode32":
         return decode_loop_bench(args)
+    if args.workload == "spec128":
+        return spec_step_bench(args)
 
     import numpy as np
     import torch
@@ -365,6 +368,87 @@ def decode_loop_bench(args) -> int:
                  "full_batch_passes": int(sum(1 for b in sizes if b == S)),
                  "committed_per_pass_per_seq": committed / float(np.sum(sizes)),
                  "expected_committed_per_pass": sum(P_KEEP ** i for i in range(K + 1))},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def spec_step_bench(args) -> int:
+    """One speculative step at concurrency 32: the dense draft block proposes
+    K = 3 tokens per sequence (3 recursive steps, each through the 129,280-row
+    LM head), then the verify pass checks them (32 x 4 tokens, 12 layers, LM
+    head, acceptance).  Also times a plain greedy pass (32 x 1 tokens) to give
+    the step cost c in greedy passes, and the speedup tau / c at the planted
+    acceptance and at the pages' tau."""
+    import torch
+
+    import moe_decoder_step_amd as m
+    import synth
+
+    m.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    import dataclasses
+    sh = dataclasses.replace(synth.SHAPES["step128"], B=args.seqs)
+    B, K, P = sh.B, sh.K, sh.P
+    log(f"spec step: {B} sequences, K={K}; generating weights")
+    layers = [synth.layer_weights(0, l, sh, dev) for l in range(sh.L)]
+    w_lm = synth.lm_weight(0, sh, dev)
+    st = m.VerifyStack(layers, w_lm, sh.E, sh.k, sh.S, max_tokens=B * P, max_seqs=B, K=K)
+    head = m.DraftHead(synth.draft_weights(0, sh, dev), st.w_lm, max_seqs=B, K=K)
+    del layers, w_lm
+    h_in = synth.hidden(0, B * P, sh.H, torch.bfloat16, dev, name="step_hidden")
+    h_last = synth.hidden(1, B, sh.H, torch.bfloat16, dev, name="draft_hidden")
+    tok = synth.uniform_ids(0, (B,), sh.V, name="last_tokens").to(dev)
+    drafts = torch.empty((B, K), dtype=torch.int32, device=dev)
+    no_drafts = torch.empty((B, 0), dtype=torch.int32, device=dev)
+
+    def draft():
+        drafts.copy_(head.propose(h_last, tok))
+
+    def verify():
+        st.forward(h_in)
+        st.head(B * P)
+        st.verify(drafts)
+
+    def greedy():
+        st.forward(h_in[:B])
+        st.head(B)
+        st.verify(no_drafts)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    t_draft = timed(draft)
+    t_verify = timed(verify)
+    t_spec = timed(lambda: (draft(), verify()))
+    t_ar = timed(greedy)
+    c = t_spec / t_ar
+    tau_planted = sum(P_KEEP ** i for i in range(K + 1))
+    log(f"draft {t_draft:.3f} ms, verify {t_verify:.3f} ms, step {t_spec:.3f} ms, greedy pass {t_ar:.3f} ms, "
+        f"c = {c:.2f}")
+    out = {
+        "metric": f"MoE speculative-step tokens/s ({B} seq, K={K} drafts + verify, 12 layers, planted tau)",
+        "value": tau_planted * B / (t_spec * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": t_spec, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"dense draft block x {K} recursive steps (each through the {sh.V}-row LM head) "
+                               f"+ verify pass of {B} x {P} tokens; value uses tau = {tau_planted:.3f} committed "
+                               f"tokens per pass (keep probability {P_KEEP}): random draft weights cannot "
+                               f"predict the verifier",
+                   "hidden": sh.H, "draft_intermediate": synth.DRAFT_INTERMEDIATE, "vocab": sh.V, "layers": sh.L},
+        "spec": {"draft_ms": t_draft, "verify_ms": t_verify, "step_ms": t_spec, "greedy_pass_ms": t_ar,
+                 "step_cost_in_greedy_passes": c, "speedup_at_planted_tau": tau_planted / c,
+                 "speedup_at_pages_tau_2.73": 2.73 / c, "planted_tau": tau_planted},
     }
     print(json.dumps(out), flush=True)
     return 0

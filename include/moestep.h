@@ -252,6 +252,24 @@ int moe_combine(const void* y, const int32_t* inv, const float* topk_w,
                 void* out, void* combined, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * moe_rmsnorm -- RMSNorm of rows: out[t] = x[r] / sqrt(mean(x[r]^2) + eps)
+ * (* gain), r = rows[t] (a gather, e.g. of token embeddings; clamped into
+ * [0, x_rows)) or t when rows is NULL.  The scale is fp64 with one rounding
+ * to the storage type, in the same order as moe_route's norm, so a row
+ * normalises to the same bits in both.  Used for the inputs of the draft
+ * block ("Jina AI's 3.4B OCR model targets faster page parsing", section
+ * "FastMTP cuts decoding work": one dense block applied recursively).
+ *
+ * x     [x_rows, H] dtype          in
+ * rows  [T] int32 or NULL          in
+ * gain  [H] fp32 or NULL           in
+ * out   rows of H at stride out_stride elements (>= H; a multiple of 16 bytes)  out
+ * Limits: H % 8 == 0, H <= 8192.
+ * ------------------------------------------------------------------------- */
+int moe_rmsnorm(const void* x, const int32_t* rows, int x_rows, int T, int H, const float* gain,
+                float eps, int dtype, void* out, int out_stride, void* stream);
+
+/* ---------------------------------------------------------------------------
  * moe_combine_route -- the end of one MoE block fused with the start of the
  * next: moe_combine of the previous layer in place on the hidden state,
  *   h[t] = h[t] + sum_j topk_w_prev[t,j] y[inv[t,j]] + sum_s y_shared[s*T+t]

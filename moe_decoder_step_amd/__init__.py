@@ -12,3 +12,4 @@ from ._lib import (BF16, F32, MoeError, ROUTE_NORM, ROUTE_RENORM, LIB_PATH, head
 from .ops import *  # noqa: F401,F403
 from .step import VerifyStack  # noqa: F401
 from .loop import DecodeLoop  # noqa: F401
+from .draft import DraftHead  # noqa: F401

@@ -133,6 +133,13 @@ int spec_plant_drafts(const int32_t* argmax_ids, const uint8_t* keep, const int3
   return hip_status(moe::launch_plant(argmax_ids, keep, repl, B, K, V, drafts, as_stream(stream)));
 }
 
+int moe_rmsnorm(const void* x, const int32_t* rows, int x_rows, int T, int H, const float* gain, float eps, int dtype,
+                void* out, int out_stride, void* stream) {
+  int st = moe::check_rmsnorm(x, rows, x_rows, T, H, dtype, out, out_stride);
+  if (st != MOE_OK || T == 0) return st;
+  return hip_status(moe::launch_rmsnorm(x, rows, x_rows, T, H, gain, eps, dtype, out, out_stride, as_stream(stream)));
+}
+
 int moe_combine_route(const void* y, const int32_t* inv, const float* topk_w_prev, const void* y_shared, int S,
                       int n_rows, int k_prev, void* h, int T, int H, const float* gain, float eps,
                       const float* w_router, const float* bias, int E, int k, int flags, int dtype, void* xn,

@@ -23,6 +23,9 @@ hipError_t launch_combine_route(const CombineArgs& ca, void* h, const float* gai
                                 const float* bias, int T, int H, int E, int k, int flags, int dtype, void* xn,
                                 int32_t* ids, float* w, float* logits, hipStream_t s);
 
+hipError_t launch_rmsnorm(const void* x, const int32_t* rows, int x_rows, int T, int H, const float* gain, float eps,
+                          int dtype, void* out, int out_stride, hipStream_t s);
+
 hipError_t launch_route(const void* h, const float* gain, float eps, const float* w_router,
                         const float* bias, int T, int H, int E, int k, int flags, int dtype,
                         void* xn, int32_t* ids, float* w, float* logits, hipStream_t s);

@@ -340,7 +340,47 @@ hipError_t launch_st(const void* h, void* hout, const CombineArgs* ca, const flo
   return launch_tpb<St, 2>(h, hout, ca, gain, eps, wr, bias, T, H, E, k, flags, xn, ids, w, logits, s);
 }
 
+// RMSNorm of rows (the draft block's inputs): one wavefront per output row,
+// the same segment-order fp64 sum of squares and single rounding as the
+// route kernel's norm, so a row normalises to the same bits in both.
+template <typename St>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const St* __restrict__ x, const int32_t* __restrict__ rows,
+                                                      int x_rows, int T, int H, const float* __restrict__ gain,
+                                                      float eps, St* __restrict__ out, int out_stride) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (t >= T) return;
+  const int r = rows ? clampi(rows[t], 0, x_rows - 1) : t;
+  const St* xr = x + (size_t)r * H;
+  double ss = 0.0;
+  for (int c = lane * 8; c < H; c += 8 * kWave) {
+    float f[8];
+    load8(xr + c, f);
+    ss += seg_sumsq(f);
+  }
+  ss = __shfl(wave_sum_f64(ss), 0, kWave);
+  const double scale = 1.0 / sqrt(ss / (double)H + (double)eps);
+  for (int c = lane * 8; c < H; c += 8 * kWave) {
+    float f[8];
+    St o[8];
+    load8(xr + c, f);
+    norm8(f, scale, gain, c, o);
+    store8(out + (size_t)t * out_stride + c, o);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_rmsnorm(const void* x, const int32_t* rows, int x_rows, int T, int H, const float* gain, float eps,
+                          int dtype, void* out, int out_stride, hipStream_t s) {
+  const dim3 grid((T + 3) / 4), block(256);
+  if (dtype == kBf16)
+    hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, grid, block, 0, s, static_cast<const bf16_t*>(x), rows, x_rows, T, H,
+                       gain, eps, static_cast<bf16_t*>(out), out_stride);
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel<float>, grid, block, 0, s, static_cast<const float*>(x), rows, x_rows, T, H,
+                       gain, eps, static_cast<float*>(out), out_stride);
+  return hipGetLastError();
+}
 
 hipError_t launch_route(const void* h, const float* gain, float eps, const float* w_router,
                         const float* bias, int T, int H, int E, int k, int flags, int dtype,

@@ -307,7 +307,7 @@ hipError_t launch_skinny(const bf16_t* x, const int32_t* gather, const int32_t* 
   const size_t lds = (size_t)kRows * lds_row(K) * sizeof(bf16_t);
   if (lds > 64 * 1024) {  // K > 2040: allow up to the CU's 160 KB of LDS
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&skinny_kernel<GATED, ROUTED>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((skinny_kernel<GATED, ROUTED>), dim3(blocks), dim3(kBlockThreads), lds, s, x, gather, offsets,

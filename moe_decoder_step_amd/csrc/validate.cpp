@@ -98,6 +98,19 @@ int check_gate_up_routed(const void* x, const int32_t* ids, int T, int k, int E,
   return kOk;
 }
 
+int check_rmsnorm(const void* x, const int32_t* rows, int x_rows, int T, int H, int dtype, const void* out,
+                  int out_stride) {
+  if (!valid_dtype(dtype)) return kErrUnsupported;
+  if (T < 0 || H <= 0 || x_rows <= 0 || out_stride < H) return kErrShape;
+  if (!rows && x_rows < T) return kErrShape;
+  if (H % 8 != 0 || H > 8192) return kErrUnsupported;
+  if (T == 0) return kOk;
+  if (!x || !out) return kErrNull;
+  const size_t es = dtype == kBf16 ? 2 : 4;
+  if (!aligned16(x) || !aligned16(out) || ((size_t)out_stride * es) % 16 != 0) return kErrAlign;
+  return kOk;
+}
+
 int check_route(const void* h, const float* w_router, int T, int H, int E, int k, int dtype,
                 const void* xn, const int32_t* ids, const float* w) {
   if (!valid_dtype(dtype)) return kErrUnsupported;

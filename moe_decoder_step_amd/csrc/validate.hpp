@@ -37,6 +37,8 @@ int check_gather_rows(const void* pool, const int32_t* seq_ids, const int32_t* s
                       int row_bytes, const void* out);
 int check_gate_up_routed(const void* x, const int32_t* ids, int T, int k, int E, int S, const void* w_gate_up, int H,
                          int I, int dtype, const void* act, const int32_t* offsets, const int32_t* inv);
+int check_rmsnorm(const void* x, const int32_t* rows, int x_rows, int T, int H, int dtype, const void* out,
+                  int out_stride);
 int check_route(const void* h, const float* w_router, int T, int H, int E, int k, int dtype,
                 const void* xn, const int32_t* ids, const float* w);
 int check_permute(const int32_t* ids, int T, int k, int E, int S, const int32_t* offsets,

@@ -15,7 +15,7 @@ import torch
 from . import _lib as L
 
 __all__ = [
-    "Packed", "pack_weights", "packed_weights_bytes", "moe_route", "moe_combine_route", "moe_permute", "moe_grouped_swiglu", "moe_combine", "lmhead_argmax",
+    "Packed", "pack_weights", "packed_weights_bytes", "moe_route", "moe_rmsnorm", "moe_combine_route", "moe_permute", "moe_grouped_swiglu", "moe_combine", "lmhead_argmax",
     "moe_expert_gate_up", "moe_expert_gate_up_routed", "moe_expert_down", "ROUTED_MAX_PAIRS", "spec_verify", "spec_plant_drafts", "spec_advance",
     "spec_gather_rows", "permute_workspace_bytes", "swiglu_workspace_bytes",
     "lmhead_workspace_bytes", "dtype_code", "expert_weights", "lm_weights", "router_weights", "route_alloc", "permute_alloc", "swiglu_alloc",
@@ -144,6 +144,21 @@ def moe_route(h, w_router, bias, k, xn, topk_ids, topk_w, logits=None, gain=None
         _p(xn), _p(topk_ids), _p(topk_w), _p(logits), _stream(h)))
 
 
+def moe_rmsnorm(x, out, rows=None, gain=None, eps=1e-6):
+    """out[t] = RMSNorm(x[rows[t]] or x[t]); `out` may be a strided view of
+    rows (e.g. one half of a [T, 2H] buffer)."""
+    x_rows, H = x.shape
+    T = out.shape[0]
+    if out.stride(1) != 1:
+        raise ValueError("out rows must be contiguous")
+    for t, d, n in ((x, None, "x"), (rows, torch.int32, "rows"), (gain, torch.float32, "gain")):
+        _need(t, d, n)
+    if out.dtype != x.dtype or not out.is_cuda:
+        raise TypeError("out must be a device tensor of x's dtype")
+    L.check("moe_rmsnorm", L.load().moe_rmsnorm(
+        _p(x), _p(rows), x_rows, T, H, _p(gain), float(eps), dtype_code(x), _p(out), out.stride(0), _stream(x)))
+
+
 def moe_combine_route(y, inv, topk_w_prev, y_shared, S, h, w_router, bias, k, xn, topk_ids, topk_w,
                       logits=None, gain=None, eps=1e-6, norm=True, renormalize=True):
     """The previous layer's moe_combine in place on h, then moe_route on it (one launch)."""
@@ -251,8 +266,8 @@ def moe_combine(y, inv, topk_w, y_shared, S, residual, out, combined=None):
                     (combined, out.dtype, "combined")):
         _need(t, d, n)
     L.check("moe_combine", L.load().moe_combine(
-        _p(y), _p(inv), _p(topk_w), _p(y_shared), S, _p(residual), T, H, k, y.shape[0], dtype_code(out),
-        _p(out), _p(combined), _stream(out)))
+        _p(y), _p(inv), _p(topk_w), _p(y_shared), S, _p(residual), T, H, k, 0 if y is None else y.shape[0],
+        dtype_code(out), _p(out), _p(combined), _stream(out)))
 
 
 def lmhead_argmax(h, w_lm, argmax_ids, max_logit, ws):

@@ -224,6 +224,25 @@ def test_gate_up_routed_matches_permute_path(m, T):
     assert torch.equal(act2, act)
 
 
+def test_grouped_swiglu_long_reduction(m):
+    """A reduction length of 2,560 (its 16 staged rows need 82 KB of LDS, more
+    than the default 64 KB a launch gets) in both stages."""
+    H, I, T = 2560, 2560, 20
+    counts = [7, 13]
+    gen = torch.Generator(device=DEV).manual_seed(17)
+    x = torch.randn(T, H, generator=gen, device=DEV).to(torch.bfloat16)
+    wgu = (torch.randn(2, 2 * I, H, generator=gen, device=DEV) * 0.02).to(torch.bfloat16)
+    wd = (torch.randn(2, H, I, generator=gen, device=DEV) * 0.02).to(torch.bfloat16)
+    off = torch.tensor([0, 7, 20], dtype=torch.int32, device=DEV)
+    wgu_p, wd_p = m.expert_weights(wgu, wd)
+    y = m.swiglu_alloc(x, None, off, wgu_p, wd_p, T, max_rows=13)
+    torch.cuda.synchronize()
+    xh, yg = O.f64(host(x)), as_f64(y)
+    for g, (a, c) in enumerate(zip([0, 7], counts)):
+        ref = O.swiglu(xh[:c], host(wgu[g]), host(wd[g]), "bf16")
+        assert_close(yg[a:a + c], ref, BF16_TOL, f"group {g}")
+
+
 def test_grouped_swiglu_identity_gather_and_skewed_groups(m):
     """gather = NULL (row r of a group reads token r - offsets[g]); groups of
     0, 1, 15, 16, 17, 33, 100 rows (ragged M-blocks, several row blocks)."""
