@@ -21,7 +21,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = L.header_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     assert set(names) == set(L.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
@@ -129,6 +129,17 @@ def test_expert_halves_checks(lib):
     assert dn(A, A, 0, 40, A, 1280, 896, 4, m.BF16, A, None) == L.ERR_SHAPE
     assert dn(MIS, A, 66, 40, A, 1280, 896, 4, m.BF16, A, None) == L.ERR_ALIGN
     assert dn(None, None, 66, 0, None, 1280, 896, 4, m.BF16, None, None) == L.OK
+
+
+def test_rmsnorm_checks(lib):
+    f = lib.moe_rmsnorm
+    # x, rows, x_rows, T, H, gain, eps, dtype, out, out_stride, stream
+    assert f(A, None, 10, 10, 1280, None, 1e-6, m.BF16, None, 1280, None) == L.ERR_NULL
+    assert f(A, None, 10, 11, 1280, None, 1e-6, m.BF16, A, 1280, None) == L.ERR_SHAPE     # more rows than x has
+    assert f(A, None, 10, 10, 1280, None, 1e-6, m.BF16, A, 1000, None) == L.ERR_SHAPE     # stride < H
+    assert f(A, None, 10, 10, 1284, None, 1e-6, m.BF16, A, 1284, None) == L.ERR_UNSUPPORTED
+    assert f(A, None, 10, 10, 1280, None, 1e-6, m.BF16, A, 1284, None) == L.ERR_ALIGN     # 2568-byte stride
+    assert f(None, None, 10, 0, 1280, None, 1e-6, m.BF16, None, 1280, None) == L.OK
 
 
 def test_gate_up_routed_checks(lib):
