@@ -13,7 +13,7 @@ __all__ = [
     "rmsnorm", "router_logits", "topk_ids", "topk_weights", "topk_gap", "route",
     "permute", "silu", "swiglu", "moe_layer", "lm_logits", "lm_argmax",
     "spec_verify", "plant_drafts", "greedy_decode", "speculative_decode",
-    "verify_step", "draft_step", "draft_propose", "active_params", "total_params",
+    "verify_step", "rope", "attention_block", "draft_step", "draft_propose", "active_params", "total_params",
 ]
 
 
@@ -348,6 +348,71 @@ def verify_step(h, layers, w_lm, drafts, k: int, eps: float, mode: str,
     acc, com, nc = spec_verify(d, ids.reshape(B, K + 1))
     return {"layers": outs, "argmax": ids, "max_logit": mx, "gap": gap,
             "accepted": acc, "committed": com, "n_commit": nc}
+
+
+# ----------------------------------------------------------------------------
+# attention over a KV cache (the verify positions)
+# ----------------------------------------------------------------------------
+
+def rope(x, pos, base: float = 10000.0) -> np.ndarray:
+    """Rotary position embedding, rotate-half form, per head of d = 2m dims:
+    (x_j, x_{j+m}) -> (x_j cos a - x_{j+m} sin a, x_j sin a + x_{j+m} cos a)
+    with a = pos * base^(-j/m), j < m.  x [T, n_heads, d], pos [T]."""
+    x = np.asarray(x, np.float64)
+    d = x.shape[-1]
+    m = d // 2
+    inv = base ** (-np.arange(m, dtype=np.float64) / m)
+    a = np.asarray(pos, np.float64)[:, None, None] * inv[None, None, :]
+    c, s = np.cos(a), np.sin(a)
+    x1, x2 = x[..., :m], x[..., m:]
+    return np.concatenate([x1 * c - x2 * s, x1 * s + x2 * c], axis=-1)
+
+
+def attention_block(h, w_qkv, w_o, cache_k, cache_v, lengths, P: int, n_heads: int, eps: float, mode: str) -> dict:
+    """Pre-norm causal self-attention of the verify positions over a KV cache.
+
+    The pages give the decoder's position limit (32,768; jina.ai/ko model
+    card, architecture paragraph) but not its attention; the reading is plain
+    multi-head attention with rotary positions:
+        xa = rmsnorm(h);  q, k, v = split(xa W_qkv^T)  (n_heads heads of d)
+        q, k <- rope(., position);  cache[b, :, L_b + i] <- k, v
+        o_i = sum_{j <= L_b + i} softmax_j(q_i . k_j / sqrt(d)) v_j
+        h' = h + o W_o^T
+    h is [B*P, H] in sequence-major order: sequence b's position i sits at
+    L_b + i (position 0 is its last committed token, then the drafts).
+    cache_k / cache_v [B, n_heads, max_len, d] hold the committed prefix and
+    are written in place.  Storage rounding at xa, q/k/v (after rope), o and
+    h'.  Returns o and h'.
+    """
+    h = f64(h)
+    T, H = h.shape
+    d = H // n_heads
+    B = T // P
+    xa = store(rmsnorm(h, eps), mode)
+    qkv = xa @ f64(w_qkv).T
+    pos = np.concatenate([np.arange(P) + int(lengths[b]) for b in range(B)])
+    q = store(rope(store(qkv[:, :H], mode).reshape(T, n_heads, d), pos), mode)
+    k = store(rope(store(qkv[:, H:2 * H], mode).reshape(T, n_heads, d), pos), mode)
+    v = store(qkv[:, 2 * H:], mode).reshape(T, n_heads, d)
+    o = np.zeros((T, n_heads, d))
+    for b in range(B):
+        L = int(lengths[b])
+        for i in range(P):
+            t = b * P + i
+            cache_k[b, :, L + i] = k[t]
+            cache_v[b, :, L + i] = v[t]
+        for i in range(P):
+            t = b * P + i
+            kk = f64(cache_k[b, :, :L + i + 1])            # [n_heads, keys, d]
+            vv = f64(cache_v[b, :, :L + i + 1])
+            sc = np.einsum("hd,hjd->hj", q[t], kk) / np.sqrt(d)
+            sc -= sc.max(axis=1, keepdims=True)
+            p = np.exp(sc)
+            p /= p.sum(axis=1, keepdims=True)
+            o[t] = np.einsum("hj,hjd->hd", p, vv)
+    o = store(o.reshape(T, H), mode)
+    h_out = store(h + store(o @ f64(w_o).T, mode), mode)
+    return {"xa": xa, "q": q, "k": k, "v": v, "o": o, "h_out": h_out}
 
 
 # ----------------------------------------------------------------------------

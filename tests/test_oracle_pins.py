@@ -420,6 +420,104 @@ def test_speculative_equals_greedy(K):
 
 
 # --------------------------------------------------------------------------
+# attention over a KV cache
+# --------------------------------------------------------------------------
+
+def test_rope_position_zero_is_identity_and_rotations_keep_norms():
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((5, 3, 16))
+    np.testing.assert_allclose(O.rope(x, np.zeros(5)), x, rtol=0, atol=0)
+    y = O.rope(x, rng.integers(0, 30000, 5))
+    n_x = x[..., :8] ** 2 + x[..., 8:] ** 2
+    n_y = y[..., :8] ** 2 + y[..., 8:] ** 2
+    np.testing.assert_allclose(n_y, n_x, rtol=1e-12)
+
+
+def test_rope_scores_depend_only_on_the_position_difference():
+    rng = np.random.default_rng(32)
+    q, k = rng.standard_normal((1, 2, 32)), rng.standard_normal((1, 2, 32))
+    for shift in (1, 17, 4000):
+        for dp in (0, 3, 250):
+            a = (O.rope(q, [dp + 5]) * O.rope(k, [5])).sum(-1)
+            b = (O.rope(q, [dp + 5 + shift]) * O.rope(k, [5 + shift])).sum(-1)
+            np.testing.assert_allclose(a, b, rtol=1e-9, atol=1e-9)
+
+
+def _attn_weights(rng, H, n_heads):
+    return rng.standard_normal((3 * H, H)) * 0.05, rng.standard_normal((H, H)) * 0.05
+
+
+def test_attention_first_position_returns_its_own_value():
+    """An empty cache and one position: softmax over one key is 1, so the
+    output is the value of the position itself."""
+    rng = np.random.default_rng(33)
+    H, nh = 64, 4
+    wqkv, wo = _attn_weights(rng, H, nh)
+    ck, cv = np.zeros((2, nh, 8, 16)), np.zeros((2, nh, 8, 16))
+    out = O.attention_block(rng.standard_normal((2, H)), wqkv, wo, ck, cv, [0, 0], 1, nh, 1e-6, "exact")
+    np.testing.assert_allclose(out["o"], out["v"].reshape(2, H), rtol=1e-12)
+
+
+def test_attention_zero_queries_average_the_values():
+    """q = 0 makes every score equal: the output is the plain mean of the
+    visible values, over the cached prefix and the causal part of the pass."""
+    rng = np.random.default_rng(34)
+    H, nh, P = 64, 4, 3
+    wqkv, wo = _attn_weights(rng, H, nh)
+    wqkv[:H] = 0.0
+    ck = rng.standard_normal((1, nh, 20, 16))
+    cv = rng.standard_normal((1, nh, 20, 16))
+    cv0 = cv.copy()
+    out = O.attention_block(rng.standard_normal((P, H)), wqkv, wo, ck, cv, [5], P, nh, 1e-6, "exact")
+    v = out["v"]
+    for i in range(P):
+        vis = np.concatenate([cv0[0, :, :5], np.moveaxis(v[:i + 1], 0, 1)], axis=1)   # [nh, 5+i+1, d]
+        np.testing.assert_allclose(out["o"][i].reshape(nh, 16), vis.mean(axis=1), rtol=1e-10, atol=1e-12)
+
+
+def test_attention_ignores_cache_entries_past_each_position():
+    """Causality, and rollback for free: entries past L+i (rejected drafts of
+    an earlier pass) never change the result."""
+    rng = np.random.default_rng(35)
+    H, nh, P = 64, 4, 4
+    wqkv, wo = _attn_weights(rng, H, nh)
+    h = rng.standard_normal((2 * P, H))
+    base_k = rng.standard_normal((2, nh, 40, 16))
+    base_v = rng.standard_normal((2, nh, 40, 16))
+    outs = []
+    for junk in (0.0, 1e3):
+        ck, cv = base_k.copy(), base_v.copy()
+        ck[:, :, 12:] += junk
+        cv[:, :, 12:] -= junk
+        outs.append(O.attention_block(h, wqkv, wo, ck, cv, [12, 7], P, nh, 1e-6, "exact"))
+    np.testing.assert_allclose(outs[0]["h_out"], outs[1]["h_out"], rtol=1e-12, atol=1e-12)
+
+
+def test_attention_commit_then_next_pass_equals_prefix_only_cache():
+    """Pass 1 writes P positions; only n+1 are committed; pass 2 starts at the
+    committed length and overwrites the rest.  Its result equals running pass
+    2 on a cache holding the committed prefix alone."""
+    rng = np.random.default_rng(36)
+    H, nh, P = 64, 4, 4
+    wqkv, wo = _attn_weights(rng, H, nh)
+    ck, cv = np.zeros((1, nh, 32, 16)), np.zeros((1, nh, 32, 16))
+    ck[:, :, :6] = rng.standard_normal((1, nh, 6, 16))
+    cv[:, :, :6] = rng.standard_normal((1, nh, 6, 16))
+    pre_k, pre_v = ck.copy(), cv.copy()
+    h1 = rng.standard_normal((P, H))
+    O.attention_block(h1, wqkv, wo, ck, cv, [6], P, nh, 1e-6, "exact")   # writes 6..9
+    n_commit = 2                                                            # 6, 7 kept; 8, 9 rejected
+    h2 = rng.standard_normal((P, H))
+    a = O.attention_block(h2, wqkv, wo, ck, cv, [6 + n_commit], P, nh, 1e-6, "exact")
+    # reference: a fresh cache with the prefix and the two committed positions only
+    fk, fv = pre_k.copy(), pre_v.copy()
+    O.attention_block(h1[:n_commit], wqkv, wo, fk, fv, [6], n_commit, nh, 1e-6, "exact")
+    fk[:, :, 8:], fv[:, :, 8:] = 0.0, 0.0
+    b = O.attention_block(h2, wqkv, wo, fk, fv, [6 + n_commit], P, nh, 1e-6, "exact")
+    np.testing.assert_allclose(a["h_out"], b["h_out"], rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
 # the dense draft block
 # --------------------------------------------------------------------------
 
