@@ -38,7 +38,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="step128",
-                    choices=["step128", "batch1", "layer128", "prefill", "decode32", "spec128", "copy"],
+                    choices=["step128", "batch1", "layer128", "prefill", "decode32", "spec128", "attn128", "step128attn",
+                             "copy"],
                     help="copy: a plain 1 GiB device copy, the reference for scaling the HBM traffic counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=12, help="layers of the oracle sample")
@@ -49,6 +50,9 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="batch1: time eager launches only")
     ap.add_argument("--target", type=int, default=1085, help="decode32: committed tokens per sequence")
     ap.add_argument("--seqs", type=int, default=32, help="spec128: sequences per step")
+    ap.add_argument("--context", default=None,
+                    help="attn128: committed lengths to time (comma list, first = reported value; default "
+                         "2241,1156,8192,32768); step128attn: the committed length (default 1700)")
     return ap.parse_args()
 
 
@@ -122,6 +126,10 @@ def main() -> int:
         return decode_loop_bench(args)
     if args.workload == "spec128":
         return spec_step_bench(args)
+    if args.workload == "attn128":
+        return attention_bench(args)
+    if args.workload == "step128attn":
+        return attention_step_bench(args)
 
     import numpy as np
     import torch
@@ -449,6 +457,146 @@ def spec_step_bench(args) -> int:
         "spec": {"draft_ms": t_draft, "verify_ms": t_verify, "step_ms": t_spec, "greedy_pass_ms": t_ar,
                  "step_cost_in_greedy_passes": c, "speedup_at_planted_tau": tau_planted / c,
                  "speedup_at_pages_tau_2.73": 2.73 / c, "planted_tau": tau_planted},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def _event_timer(steps, warmup, fn):
+    """Average ms of fn over `steps` calls after `warmup`, HIP events on the
+    current stream (the stream the library's kernels are launched on)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def attention_bench(args) -> int:
+    """Causal attention of one layer's verify pass over its KV cache (32 seq x
+    4 positions x 10 heads of 128), at several committed lengths: the rope +
+    cache write and the split attention + merge (one moe_attention call), with
+    the algorithmic bytes of the call (every visible key and value row once,
+    the queries in, the output out)."""
+    import torch
+
+    import moe_decoder_step_amd as m
+    import synth
+
+    m.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sh = synth.SHAPES["step128"]
+    B, P, nh, D = sh.B, sh.P, sh.H // synth.ATTN_HEAD_DIM, synth.ATTN_HEAD_DIM
+    T, H = B * P, sh.H
+    ctx = [int(c) for c in (args.context or "2241,1156,8192,32768").split(",")]
+    qkv = synth.normal(1, (T, 3 * H), 1.0, torch.bfloat16, dev)
+    q = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    o = torch.empty_like(q)
+    rows = []
+    for L in ctx:
+        max_len = L + P
+        ck = synth.kv_prefix(2, 0, (B, nh, max_len, D), torch.bfloat16, dev, "k")
+        cv = synth.kv_prefix(2, 0, (B, nh, max_len, D), torch.bfloat16, dev, "v")
+        lengths = torch.full((B,), L, dtype=torch.int32, device=dev)
+        ws = torch.empty(m.attention_workspace_bytes(B, P, nh, max_len), dtype=torch.uint8, device=dev)
+        t_rope = _event_timer(args.steps, args.warmup, lambda: m.moe_attn_rope_cache(qkv, lengths, P, q, ck, cv))
+        t_att = _event_timer(args.steps, args.warmup, lambda: m.moe_attention(q, ck, cv, lengths, P, o, ws))
+        kv_bytes = B * nh * (L + P) * D * 2 * 2
+        nbytes = kv_bytes + 2 * T * H * 2
+        gbs = nbytes / (t_att * 1e-3) / 1e9
+        log(f"context {L}: rope+cache {t_rope * 1e3:.1f} us, attention {t_att * 1e3:.1f} us, {gbs:.0f} GB/s")
+        rows.append({"context": L, "rope_cache_us": t_rope * 1e3, "attention_us": t_att * 1e3,
+                     "algorithmic_bytes": nbytes, "GBs": gbs, "frac": gbs / HBM_PEAK_GBS})
+        del ck, cv, ws
+        torch.cuda.empty_cache()
+    r0 = rows[0]
+    ms = (r0["rope_cache_us"] + r0["attention_us"]) * 1e-3
+    out = {
+        "metric": f"verify-pass attention tokens/s (32 seq x 4 tok, one layer, context {r0['context']})",
+        "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"causal attention of {B} seq x {P} positions over a {nh}-head KV cache "
+                               f"(head 128) of {r0['context']} committed positions, one layer",
+                   "hidden": H, "heads": nh, "contexts": ctx},
+        "roofline": {"kernel": "moe_attention (attn_split_kernel + attn_merge_kernel)", "bound": "hbm",
+                     "achieved": r0["GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": r0["frac"],
+                     "traffic": None, "traffic_source": "no counter run recorded for this kernel",
+                     "us_per_launch": r0["attention_us"], "algorithmic_bytes_per_launch": r0["algorithmic_bytes"]},
+        "contexts": rows,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def attention_step_bench(args) -> int:
+    """The verify step with attention: 12 layers of (attention over a KV
+    cache of `context` committed positions + MoE block), LM head, acceptance,
+    32 seq x 4 tokens.  Lengths are not advanced between timed passes (each
+    pass re-verifies at the same positions), so every pass costs the same."""
+    import numpy as np
+    import torch
+
+    import moe_decoder_step_amd as m
+    import synth
+
+    m.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sh = synth.SHAPES["step128"]
+    L = int(args.context or 1700)
+    T, nh = sh.T, sh.H // synth.ATTN_HEAD_DIM
+    log(f"verify step with attention at context {L}: generating weights")
+    layers = [synth.layer_weights(0, l, sh, dev) for l in range(sh.L)]
+    attn = [synth.attn_weights(0, l, sh, dev) for l in range(sh.L)]
+    w_lm = synth.lm_weight(0, sh, dev)
+    st = m.VerifyStack(layers, w_lm, sh.E, sh.k, sh.S, max_tokens=T, max_seqs=sh.B, K=sh.K, attn=attn,
+                       n_heads=nh, max_len=L + sh.P)
+    for li, blk in enumerate(st.attn):
+        blk.cache_k.copy_(synth.kv_prefix(3, li, blk.cache_k.shape, torch.bfloat16, dev, "k"))
+        blk.cache_v.copy_(synth.kv_prefix(3, li, blk.cache_v.shape, torch.bfloat16, dev, "v"))
+    st.lengths.fill_(L)
+    del layers, attn, w_lm
+    h_in = synth.hidden(0, T, sh.H, torch.bfloat16, dev, name="step_hidden")
+    drafts = synth.uniform_ids(0, (sh.B, sh.K), sh.V).to(dev)
+
+    def step():
+        st.forward(h_in)
+        st.head(T)
+        st.verify(drafts)
+
+    ms = _event_timer(args.steps, args.warmup, step)
+    # attention share: one layer's moe_attention call timed alone
+    blk = st.attn[0]
+    lengths = st.lengths[:sh.B]
+    t_att = _event_timer(args.steps, args.warmup, lambda: m.moe_attention(
+        blk.q[:T], blk.cache_k, blk.cache_v, lengths, sh.P, blk.o[:T], blk.ws))
+    kv_bytes = sh.B * nh * (L + sh.P) * synth.ATTN_HEAD_DIM * 2 * 2
+    nbytes = kv_bytes + 2 * T * sh.H * 2
+    gbs = nbytes / (t_att * 1e-3) / 1e9
+    log(f"{ms:.3f} ms/step; attention {t_att * 1e3:.1f} us/layer, {gbs:.0f} GB/s")
+    out = {
+        "metric": f"verify-step tokens/s with attention (32 seq x 4 tok, 12 layers, context {L})",
+        "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"verify pass, {sh.B} seq x {sh.P} positions, {sh.L} layers of causal attention "
+                               f"({nh} heads of 128, KV cache of {L} committed positions) + MoE block, LM head "
+                               f"{sh.H}x{sh.V} argmax + greedy acceptance",
+                   "hidden": sh.H, "context": L, "global_batch": T},
+        "roofline": {"kernel": "moe_attention (attn_split_kernel + attn_merge_kernel)", "bound": "hbm",
+                     "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": None, "traffic_source": "no counter run recorded for this kernel",
+                     "us_per_launch": t_att * 1e3, "algorithmic_bytes_per_launch": nbytes},
+        "attention_share": {"attention_us_per_layer": t_att * 1e3,
+                            "fraction_of_step": sh.L * t_att / ms},
     }
     print(json.dumps(out), flush=True)
     return 0

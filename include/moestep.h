@@ -377,6 +377,54 @@ int spec_advance(const int32_t* n_commit, const int32_t* committed, const int32_
 int spec_gather_rows(const void* pool, const int32_t* seq_ids, const int32_t* steps, int B,
                      int R, int J, int S, int row_bytes, void* out, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Causal self-attention of the verify positions over a per-sequence KV cache.
+ *
+ * The pages give the decoder's context limit (32,768 positions; jina.ai/ko
+ * model card "jina-ocr-v1", architecture paragraph) but not its attention;
+ * these calls read it as plain multi-head attention with head size 128 and
+ * rotary positions (rotate-half form, angle pos * base^(-j/64), j < 64).
+ * A verify pass of sequence b holds P = K+1 positions at L_b .. L_b+P-1,
+ * L_b = lengths[b] (its last committed token, then the drafts); tokens are
+ * laid out [B*P] sequence-major, H = n_heads * 128.
+ *
+ * moe_attn_rope_cache: q, k, v = split(qkv) (columns [0,H), [H,2H), [2H,3H));
+ *   q <- rope(q), written to q [B*P, H]; rope(k) and v are written into the
+ *   caches at [b][head][L_b + i][0..128).  Rotation in fp64 from the stored
+ *   bf16 inputs, one rounding to bf16.
+ *   qkv [B*P, 3H] bf16                          in
+ *   lengths [B] int32                           in   clamped to [0, max_len-P]
+ *   q [B*P, H] bf16                             out
+ *   cache_k, cache_v [B, n_heads, max_len, 128] bf16   in/out (P rows each)
+ *
+ * moe_attention: o_i = sum_{j <= L_b+i} softmax_j(q_i . k_j / sqrt(128)) v_j
+ *   per head, over the cached keys (split over the key axis; fp32 scores,
+ *   online softmax, fp32 merge of the splits, one rounding to bf16).
+ *   Cache rows past L_b + i (drafts of an earlier pass that the verifier
+ *   rejected) are never read, so rejecting drafts needs no cache write.
+ *   max_keys bounds lengths[b] + P for every b (it sizes the grid and the
+ *   workspace; a longer length is clamped to max_keys - P).
+ *   q [B*P, H] bf16, caches as above            in
+ *   o [B*P, H] bf16                             out
+ *   ws                                          scratch of
+ *                                               moe_attention_workspace_bytes(B, P, n_heads, 128, max_keys)
+ *
+ * spec_commit: lengths[b] += n_commit[b] (spec_verify's output): the accepted
+ *   drafts and the bonus token's predecessor become the committed prefix; the
+ *   rest of the pass's cache rows are overwritten by the next pass.
+ *
+ * Limits: dtype MOE_BF16, head_dim 128, 1 <= P <= 16, P <= max_keys <=
+ * max_len; the cache pointers 16-byte aligned.
+ * ------------------------------------------------------------------------- */
+int moe_attn_rope_cache(const void* qkv, const int32_t* lengths, int B, int P, int n_heads,
+                        int head_dim, float rope_base, int max_len, int dtype, void* q,
+                        void* cache_k, void* cache_v, void* stream);
+size_t moe_attention_workspace_bytes(int B, int P, int n_heads, int head_dim, int max_keys);
+int moe_attention(const void* q, const void* cache_k, const void* cache_v, const int32_t* lengths,
+                  int B, int P, int n_heads, int head_dim, int max_len, int max_keys, int dtype,
+                  void* o, void* ws, size_t ws_bytes, void* stream);
+int spec_commit(const int32_t* n_commit, int B, int32_t* lengths, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -13,3 +13,4 @@ from .ops import *  # noqa: F401,F403
 from .step import VerifyStack  # noqa: F401
 from .loop import DecodeLoop  # noqa: F401
 from .draft import DraftHead  # noqa: F401
+from .attention import AttentionBlock  # noqa: F401

@@ -22,7 +22,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["abi.hip", "pack.hip", "route.hip", "permute.hip", "swiglu.hip", "gemm.hip", "combine.hip", "lmhead.hip",
-           "verify.hip", "validate.cpp"]
+           "verify.hip", "attention.hip", "validate.cpp"]
 
 # Packed-fp32 VALU ops are switched off for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -171,4 +171,34 @@ int spec_gather_rows(const void* pool, const int32_t* seq_ids, const int32_t* st
   return hip_status(moe::launch_gather_rows(pool, seq_ids, steps, B, R, J, S, row_bytes, out, as_stream(stream)));
 }
 
+int moe_attn_rope_cache(const void* qkv, const int32_t* lengths, int B, int P, int n_heads, int head_dim,
+                        float rope_base, int max_len, int dtype, void* q, void* cache_k, void* cache_v,
+                        void* stream) {
+  int st = moe::check_rope_cache(qkv, lengths, B, P, n_heads, head_dim, rope_base, max_len, dtype, q, cache_k,
+                                 cache_v);
+  if (st != MOE_OK || B == 0) return st;
+  return hip_status(moe::launch_rope_cache(qkv, lengths, B, P, n_heads, rope_base, max_len, q, cache_k, cache_v,
+                                           as_stream(stream)));
+}
+
+size_t moe_attention_workspace_bytes(int B, int P, int n_heads, int head_dim, int max_keys) {
+  return moe::attention_ws_bytes(B, P, n_heads, head_dim, max_keys);
+}
+
+int moe_attention(const void* q, const void* cache_k, const void* cache_v, const int32_t* lengths, int B, int P,
+                  int n_heads, int head_dim, int max_len, int max_keys, int dtype, void* o, void* ws,
+                  size_t ws_bytes, void* stream) {
+  int st = moe::check_attention(q, cache_k, cache_v, lengths, B, P, n_heads, head_dim, max_len, max_keys, dtype, o);
+  if (st != MOE_OK || B == 0) return st;
+  if (!ws || ws_bytes < moe::attention_ws_bytes(B, P, n_heads, head_dim, max_keys)) return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_attention(q, cache_k, cache_v, lengths, B, P, n_heads, max_len, max_keys, o, ws,
+                                          as_stream(stream)));
+}
+
+int spec_commit(const int32_t* n_commit, int B, int32_t* lengths, void* stream) {
+  int st = moe::check_commit(n_commit, B, lengths);
+  if (st != MOE_OK || B == 0) return st;
+  return hip_status(moe::launch_commit(n_commit, B, lengths, as_stream(stream)));
+}
+
 }  // extern "C"

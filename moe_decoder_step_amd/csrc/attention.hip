@@ -1,0 +1,217 @@
+// Causal attention of the verify positions over a per-sequence KV cache.
+//
+// The verify pass of sequence b holds P positions at L_b .. L_b+P-1 (its last
+// committed token, then the drafts).  Each layer:
+//   rope_cache_kernel  q, k <- rotary(q, k) at their positions (angle and
+//                      rotation in fp64, one rounding to bf16); k and v go
+//                      into the cache at [b][head][L_b + i][d];
+//   attn_split_kernel  flash-decoding: block (b, head, split) scores its span
+//                      of cached keys for the P queries, with an online fp32
+//                      softmax, and writes (max, sum, unnormalised output);
+//                      keys and values pass through LDS in 64-key tiles;
+//   attn_merge_kernel  merges the splits of each (b, head, query), one
+//                      rounding to bf16.
+// Query i of sequence b sees keys 0 .. L_b + i: entries past that (drafts a
+// previous pass wrote and the verifier rejected) are never read, so rolling
+// back is only a matter of not advancing the length (spec_commit).
+#include "common.hpp"
+#include "kernels.hpp"
+#include "validate.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kD = kAttnHeadDim;      // 128
+constexpr int kTile = 64;             // keys per LDS tile
+constexpr int kRowPad = kD + 8;       // bf16 per LDS row (conflict-free column reads)
+
+__global__ __launch_bounds__(256) void rope_cache_kernel(const bf16_t* __restrict__ qkv,
+                                                         const int32_t* __restrict__ lengths, int B, int P,
+                                                         int n_heads, int max_len, double log_base,
+                                                         bf16_t* __restrict__ q, bf16_t* __restrict__ ck,
+                                                         bf16_t* __restrict__ cv) {
+  // one thread per (token, head, rotation pair j < 64)
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const int half = kD / 2;
+  if (idx >= (long long)B * P * n_heads * half) return;
+  const int j = (int)(idx % half);
+  const int hd = (int)((idx / half) % n_heads);
+  const int t = (int)(idx / ((long long)half * n_heads));
+  const int b = t / P, i = t % P;
+  const int pos = clampi(lengths[b], 0, max_len - P) + i;
+  const int H = n_heads * kD;
+  const double ang = (double)pos * exp(-(double)j / (double)half * log_base);
+  const double c = cos(ang), s = sin(ang);
+  const bf16_t* row = qkv + (size_t)t * 3 * H + hd * kD;
+  auto bf = [](bf16_t v) { return (double)__uint_as_float((uint32_t)v << 16); };
+  // q
+  const double q1 = bf(row[j]), q2 = bf(row[j + half]);
+  bf16_t* qo = q + (size_t)t * H + hd * kD;
+  qo[j] = f64_to_bf16(q1 * c - q2 * s);
+  qo[j + half] = f64_to_bf16(q1 * s + q2 * c);
+  // k (rotated) and v (as it is) into the cache
+  const double k1 = bf(row[H + j]), k2 = bf(row[H + j + half]);
+  const size_t crow = (((size_t)b * n_heads + hd) * max_len + pos) * kD;
+  ck[crow + j] = f64_to_bf16(k1 * c - k2 * s);
+  ck[crow + j + half] = f64_to_bf16(k1 * s + k2 * c);
+  cv[crow + j] = row[2 * H + j];
+  cv[crow + j + half] = row[2 * H + j + half];
+}
+
+// block (b, head, split): keys [k0, k1) of sequence b, all P queries (P <= 16);
+// wavefront w handles queries w, w+4, ...  Partials: ws[((b*nh + head)*nsplit
+// + split)*P + i] = {max, sum, out[128]} (fp32).
+__global__ __launch_bounds__(256) void attn_split_kernel(const bf16_t* __restrict__ q,
+                                                         const bf16_t* __restrict__ ck,
+                                                         const bf16_t* __restrict__ cv,
+                                                         const int32_t* __restrict__ lengths, int P, int n_heads,
+                                                         int max_len, int max_keys, int split_keys, int nsplit,
+                                                         float scale, float* __restrict__ ws) {
+  __shared__ __align__(16) bf16_t ks[kTile][kRowPad];
+  __shared__ __align__(16) bf16_t vs[kTile][kD];
+  __shared__ float qs[kMaxAttnP][kD];
+  __shared__ float ps[4][kTile];
+  const int split = blockIdx.x % nsplit;
+  const int hd = (blockIdx.x / nsplit) % n_heads;
+  const int b = blockIdx.x / (nsplit * n_heads);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int H = n_heads * kD;
+  // the grid covers keys < max_keys (<= max_len); a longer length is clamped
+  const int L = clampi(lengths[b], 0, max_keys - P);
+  const int k0 = split * split_keys, k1 = min(k0 + split_keys, L + P);
+  const size_t base = ((size_t)b * n_heads + hd) * max_len;
+
+  for (int e = threadIdx.x; e < P * kD; e += 256) {
+    const int i = e / kD, dd = e % kD;
+    qs[i][dd] = __uint_as_float((uint32_t)q[(size_t)(b * P + i) * H + hd * kD + dd] << 16);
+  }
+  // per query this wavefront owns: running max, sum and 2 output dims per lane
+  float m[4], l[4], o0[4], o1[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) { m[u] = -INFINITY; l[u] = 0.f; o0[u] = 0.f; o1[u] = 0.f; }
+  lds_barrier();
+
+  for (int t0 = k0; t0 < k1; t0 += kTile) {
+    const int nk = min(kTile, k1 - t0);
+    // stage the tile: 64 keys x 128 dims of k and v, 16 bytes per thread per step
+    for (int e = threadIdx.x; e < kTile * (kD / 8); e += 256) {
+      const int r = e / (kD / 8), sg = (e % (kD / 8)) * 8;
+      const int key = t0 + min(r, nk - 1);
+      *reinterpret_cast<uint4*>(&ks[r][sg]) = ldg16(ck + (base + key) * kD + sg);
+      *reinterpret_cast<uint4*>(&vs[r][sg]) = ldg16(cv + (base + key) * kD + sg);
+    }
+    lds_barrier();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = wave + 4 * u;
+      if (i >= P) break;
+      // lane = key of the tile
+      const int key = t0 + lane;
+      // 16-byte reads of the key row: lanes 272 bytes apart cover all banks
+      float s = 0.f;
+#pragma unroll 4
+      for (int dd = 0; dd < kD; dd += 8) {
+        float kf[8];
+        unpack8(*reinterpret_cast<const uint4*>(&ks[lane][dd]), kf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s = fmaf(qs[i][dd + e], kf[e], s);
+      }
+      const bool vis = lane < nk && key <= L + i;
+      s = vis ? s * scale : -INFINITY;
+      const float mt = wave_max_dpp(s);
+      const float mn = fmaxf(m[u], mt);
+      const float p = vis ? expf(s - mn) : 0.f;
+      const float corr = m[u] == -INFINITY ? 0.f : expf(m[u] - mn);
+      l[u] = l[u] * corr + wave_sum_dpp(p);
+      m[u] = mn;
+      ps[wave][lane] = p;
+      // the wavefront's own LDS row: only its lanes wrote it
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+      float a0 = o0[u] * corr, a1 = o1[u] * corr;
+      for (int jj = 0; jj < nk; ++jj) {
+        const float pj = ps[wave][jj];
+        const uint32_t vv = *reinterpret_cast<const uint32_t*>(&vs[jj][2 * lane]);
+        a0 = fmaf(pj, __uint_as_float(vv << 16), a0);
+        a1 = fmaf(pj, __uint_as_float(vv & 0xffff0000u), a1);
+      }
+      o0[u] = a0;
+      o1[u] = a1;
+      __builtin_amdgcn_wave_barrier();
+    }
+    lds_barrier();
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = wave + 4 * u;
+    if (i >= P) break;
+    float* w = ws + ((((size_t)b * n_heads + hd) * nsplit + split) * P + i) * (kD + 2);
+    if (lane == 0) {
+      w[0] = m[u];
+      w[1] = l[u];
+    }
+    w[2 + 2 * lane] = o0[u];
+    w[3 + 2 * lane] = o1[u];
+  }
+}
+
+// one wavefront per (b, head, query): merge the splits, lane owns 2 dims
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ ws, int B, int P, int n_heads,
+                                                         int nsplit, bf16_t* __restrict__ o) {
+  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (gw >= B * n_heads * P) return;
+  const int i = gw % P, hd = (gw / P) % n_heads, b = gw / (P * n_heads);
+  float M = -INFINITY;
+  for (int sp = 0; sp < nsplit; ++sp)
+    M = fmaxf(M, ws[((((size_t)b * n_heads + hd) * nsplit + sp) * P + i) * (kD + 2)]);
+  float Ls = 0.f, a0 = 0.f, a1 = 0.f;
+  for (int sp = 0; sp < nsplit; ++sp) {
+    const float* w = ws + ((((size_t)b * n_heads + hd) * nsplit + sp) * P + i) * (kD + 2);
+    if (w[0] == -INFINITY) continue;   // a split with no visible key
+    const float f = expf(w[0] - M);
+    Ls = fmaf(f, w[1], Ls);
+    a0 = fmaf(f, w[2 + 2 * lane], a0);
+    a1 = fmaf(f, w[3 + 2 * lane], a1);
+  }
+  const int H = n_heads * kD;
+  bf16_t* out = o + (size_t)(b * P + i) * H + hd * kD + 2 * lane;
+  *reinterpret_cast<uint32_t*>(out) = pack2(f32_to_bf16(a0 / Ls), f32_to_bf16(a1 / Ls));
+}
+
+__global__ void commit_kernel(const int32_t* __restrict__ n_commit, int B, int32_t* __restrict__ lengths) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < B) lengths[b] += n_commit[b];
+}
+
+}  // namespace
+
+hipError_t launch_rope_cache(const void* qkv, const int32_t* lengths, int B, int P, int n_heads, float rope_base,
+                             int max_len, void* q, void* cache_k, void* cache_v, hipStream_t s) {
+  const long long n = (long long)B * P * n_heads * (kD / 2);
+  hipLaunchKernelGGL(rope_cache_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     static_cast<const bf16_t*>(qkv), lengths, B, P, n_heads, max_len, log((double)rope_base),
+                     static_cast<bf16_t*>(q), static_cast<bf16_t*>(cache_k), static_cast<bf16_t*>(cache_v));
+  return hipGetLastError();
+}
+
+hipError_t launch_attention(const void* q, const void* cache_k, const void* cache_v, const int32_t* lengths, int B,
+                            int P, int n_heads, int max_len, int max_keys, void* o, void* ws, hipStream_t s) {
+  const int sk = attn_split_keys(max_keys);
+  const int nsplit = (max_keys + sk - 1) / sk;
+  float* w = static_cast<float*>(ws);
+  hipLaunchKernelGGL(attn_split_kernel, dim3(B * n_heads * nsplit), dim3(256), 0, s, static_cast<const bf16_t*>(q),
+                     static_cast<const bf16_t*>(cache_k), static_cast<const bf16_t*>(cache_v), lengths, P, n_heads,
+                     max_len, max_keys, sk, nsplit, 1.0f / sqrtf((float)kD), w);
+  const int waves = B * n_heads * P;
+  hipLaunchKernelGGL(attn_merge_kernel, dim3((waves + 3) / 4), dim3(256), 0, s, w, B, P, n_heads, nsplit,
+                     static_cast<bf16_t*>(o));
+  return hipGetLastError();
+}
+
+hipError_t launch_commit(const int32_t* n_commit, int B, int32_t* lengths, hipStream_t s) {
+  hipLaunchKernelGGL(commit_kernel, dim3((B + 255) / 256), dim3(256), 0, s, n_commit, B, lengths);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -111,6 +111,50 @@ int check_rmsnorm(const void* x, const int32_t* rows, int x_rows, int T, int H, 
   return kOk;
 }
 
+int attn_split_keys(int max_keys) {
+  // at most 64 splits per (sequence, head), at least 256 keys each, a multiple of the 64-key tile
+  int sk = (max_keys + 63) / 64;
+  sk = ((sk + 63) / 64) * 64;
+  return sk < 256 ? 256 : sk;
+}
+
+int check_rope_cache(const void* qkv, const int32_t* lengths, int B, int P, int n_heads, int head_dim, float rope_base,
+                     int max_len, int dtype, const void* q, const void* cache_k, const void* cache_v) {
+  if (!valid_dtype(dtype)) return kErrUnsupported;
+  if (B < 0 || P <= 0 || n_heads <= 0 || max_len < P || !(rope_base > 1.f)) return kErrShape;
+  if (dtype != kBf16 || head_dim != kAttnHeadDim || P > kMaxAttnP) return kErrUnsupported;
+  if ((long long)B * n_heads * max_len * head_dim > (1LL << 40)) return kErrUnsupported;
+  if (B == 0) return kOk;
+  if (!qkv || !lengths || !q || !cache_k || !cache_v) return kErrNull;
+  return kOk;
+}
+
+int check_commit(const int32_t* n_commit, int B, const int32_t* lengths) {
+  if (B < 0) return kErrShape;
+  if (B == 0) return kOk;
+  if (!n_commit || !lengths) return kErrNull;
+  return kOk;
+}
+
+int check_attention(const void* q, const void* cache_k, const void* cache_v, const int32_t* lengths, int B, int P,
+                    int n_heads, int head_dim, int max_len, int max_keys, int dtype, const void* o) {
+  if (!valid_dtype(dtype)) return kErrUnsupported;
+  if (B < 0 || P <= 0 || n_heads <= 0 || max_len < P || max_keys < P || max_keys > max_len) return kErrShape;
+  if (dtype != kBf16 || head_dim != kAttnHeadDim || P > kMaxAttnP) return kErrUnsupported;
+  if ((long long)B * n_heads * max_len * head_dim > (1LL << 40)) return kErrUnsupported;
+  if (B == 0) return kOk;
+  if (!q || !cache_k || !cache_v || !lengths || !o) return kErrNull;
+  if (!aligned16(cache_k) || !aligned16(cache_v)) return kErrAlign;
+  return kOk;
+}
+
+size_t attention_ws_bytes(int B, int P, int n_heads, int head_dim, int max_keys) {
+  if (B <= 0 || P <= 0 || n_heads <= 0 || max_keys <= 0) return 0;
+  const int sk = attn_split_keys(max_keys);
+  const size_t nsplit = (size_t)((max_keys + sk - 1) / sk);
+  return align256((size_t)B * n_heads * nsplit * P * (head_dim + 2) * sizeof(float));
+}
+
 int check_route(const void* h, const float* w_router, int T, int H, int E, int k, int dtype,
                 const void* xn, const int32_t* ids, const float* w) {
   if (!valid_dtype(dtype)) return kErrUnsupported;

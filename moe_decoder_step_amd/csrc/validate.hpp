@@ -16,7 +16,9 @@ constexpr int kMaxHidden = 2048;     // route kernel keeps a block's normed rows
 constexpr int kMaxShared = 8;
 constexpr int kMaxDrafts = 15;
 constexpr int kPermuteChunk = 4096;  // slots per block of the permutation kernels
-constexpr int kAdvanceMaxB = 1024;   // sequences of one spec_advance call (one block)
+constexpr int kAdvanceMaxB = 1024;
+constexpr int kAttnHeadDim = 128;    // attention head size
+constexpr int kMaxAttnP = 16;        // verify positions per sequence in one attention call   // sequences of one spec_advance call (one block)
 constexpr int kGemmMinRows = 1024;   // max_rows from which the grouped SwiGLU runs as a tiled GEMM
 constexpr int kLmRowsPerBlock = 128; // vocabulary rows per LM-head block (bf16 path)
 constexpr int kLmF32RowsPerBlock = 256;
@@ -39,6 +41,13 @@ int check_gate_up_routed(const void* x, const int32_t* ids, int T, int k, int E,
                          int I, int dtype, const void* act, const int32_t* offsets, const int32_t* inv);
 int check_rmsnorm(const void* x, const int32_t* rows, int x_rows, int T, int H, int dtype, const void* out,
                   int out_stride);
+int attn_split_keys(int max_keys);
+int check_rope_cache(const void* qkv, const int32_t* lengths, int B, int P, int n_heads, int head_dim, float rope_base,
+                     int max_len, int dtype, const void* q, const void* cache_k, const void* cache_v);
+int check_commit(const int32_t* n_commit, int B, const int32_t* lengths);
+int check_attention(const void* q, const void* cache_k, const void* cache_v, const int32_t* lengths, int B, int P,
+                    int n_heads, int head_dim, int max_len, int max_keys, int dtype, const void* o);
+size_t attention_ws_bytes(int B, int P, int n_heads, int head_dim, int max_keys);
 int check_route(const void* h, const float* w_router, int T, int H, int E, int k, int dtype,
                 const void* xn, const int32_t* ids, const float* w);
 int check_permute(const int32_t* ids, int T, int k, int E, int S, const int32_t* offsets,

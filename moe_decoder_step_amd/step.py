@@ -7,7 +7,10 @@ pass of T = B*(K+1) positions runs, per MoE layer,
     moe_route -> moe_permute -> moe_grouped_swiglu -> moe_combine
 
 (the residual add is fused into the combine, in place on the hidden state),
-then lmhead_argmax over all positions and spec_verify per sequence.  Every
+then lmhead_argmax over all positions and spec_verify per sequence.  With
+attention weights, each MoE block is preceded by causal attention over a
+per-layer KV cache (attention.AttentionBlock) and spec_commit advances the
+committed lengths after acceptance.  Every
 step runs in libmoestep's HIP kernels; torch only owns memory and streams.
 """
 
@@ -21,11 +24,18 @@ from . import ops
 class VerifyStack:
     def __init__(self, layers: list[dict], w_lm: torch.Tensor | None, E: int, k: int, S: int,
                  max_tokens: int, max_seqs: int = 0, K: int = 0, eps: float = 1e-6,
-                 keep_logits: bool = False):
+                 keep_logits: bool = False, attn: list[dict] | None = None, n_heads: int = 0,
+                 max_len: int = 0):
         """layers: per layer w_router [E,H] fp32, bias [E] fp32 (or absent),
         w_gate_up [E+S, 2I, H], w_down [E+S, H, I] row-major; w_lm [V, H].
         bf16 expert and LM-head weights are packed here (moe_pack_weights)
-        into the stack's own copies; the caller may drop its tensors."""
+        into the stack's own copies; the caller may drop its tensors.
+
+        attn (optional): per layer w_qkv [3H, H], w_o [H, H]; each MoE block
+        is then preceded by causal attention over a per-layer KV cache of
+        max_len positions for max_seqs sequences of K+1 verify positions
+        (AttentionBlock), and `lengths` holds each sequence's committed
+        length (advanced by step() after acceptance)."""
         self.layers = []
         for w in layers:
             gu, dn = ops.expert_weights(w["w_gate_up"], w["w_down"])
@@ -65,6 +75,14 @@ class VerifyStack:
             self.max_logit = torch.empty(T, dtype=torch.float32, device=dev)
             self.lws = torch.empty(max(ops.lmhead_workspace_bytes(T, V, self.dtype), 16), dtype=torch.uint8,
                                    device=dev)
+        self.attn = None
+        if attn:
+            from .attention import AttentionBlock
+            if len(attn) != len(layers) or not max_seqs or not max_len:
+                raise ValueError("attention needs one block per layer, max_seqs and max_len")
+            self.attn = [AttentionBlock(a, n_heads, max_seqs, K + 1, max_len, eps) for a in attn]
+            self.lengths = torch.zeros(max_seqs, **i32)
+            self.max_keys = None        # a known bound on lengths + K + 1 (default: max_len)
         if max_seqs:
             self.accepted = torch.empty(max_seqs, **i32)
             self.committed = torch.empty((max_seqs, K + 1), **i32)
@@ -131,6 +149,8 @@ class VerifyStack:
         it (for teacher-forced comparison)."""
         T = h_in.shape[0]
         self.h[:T].copy_(h_in)
+        if self.attn is not None:
+            return self._forward_attn(T, record)
         L = len(self.layers)
         for li in range(L):
             if self.fuse:
@@ -149,6 +169,33 @@ class VerifyStack:
         if record is not None:
             record[-1]["output"] = self.h[:T].clone()
         return self.h[:T]
+
+    def _forward_attn(self, T: int, record: list | None) -> torch.Tensor:
+        """Attention block then MoE block per layer, in place on self.h[:T]
+        (the combine cannot fuse with the next routing: attention sits
+        between them)."""
+        B = T // self.attn[0].P
+        lengths = self.lengths[:B]
+        for li, blk in enumerate(self.attn):
+            if li > 0:
+                self._combine(T)
+            rec = None if record is None else {}
+            if record is not None and li > 0:
+                record[-1]["output"] = self.h[:T].clone()
+            blk.forward(self.h[:T], lengths, self.max_keys, rec)
+            self._route(li, T, False)
+            if record is not None:
+                rec.update({"input": self.h[:T].clone(), "ids": self.ids[:T].clone(), "w": self.tw[:T].clone()})
+                record.append(rec)
+            self._experts(li, T)
+        self._combine(T)
+        if record is not None:
+            record[-1]["output"] = self.h[:T].clone()
+        return self.h[:T]
+
+    def commit(self, B: int) -> None:
+        """Advance the committed lengths by the last verify's n_commit."""
+        ops.spec_commit(self.n_commit[:B], self.lengths[:B])
 
     def head(self, T: int) -> None:
         ops.lmhead_argmax(self.h[:T], self.w_lm, self.argmax[:T], self.max_logit[:T], self.lws)
@@ -173,6 +220,8 @@ class VerifyStack:
         self.head(T)
         ops.spec_plant_drafts(self.argmax[:B * (K + 1)].view(B, K + 1), keep, repl, self.w_lm.shape[0], drafts)
         self.verify(drafts)
+        if self.attn is not None:
+            self.commit(B)
 
     def step(self, h_in: torch.Tensor, drafts: torch.Tensor, record: list | None = None) -> None:
         """One verify pass: blocks, LM-head argmax, acceptance (results in self.*)."""
@@ -180,3 +229,5 @@ class VerifyStack:
         self.forward(h_in, record)
         self.head(T)
         self.verify(drafts)
+        if self.attn is not None:
+            self.commit(drafts.shape[0])

@@ -13,7 +13,7 @@ __all__ = [
     "rmsnorm", "router_logits", "topk_ids", "topk_weights", "topk_gap", "route",
     "permute", "silu", "swiglu", "moe_layer", "lm_logits", "lm_argmax",
     "spec_verify", "plant_drafts", "greedy_decode", "speculative_decode",
-    "verify_step", "rope", "attention_block", "draft_step", "draft_propose", "active_params", "total_params",
+    "verify_step", "rope", "rope_cache", "causal_attention", "attention_block", "draft_step", "draft_propose", "active_params", "total_params",
 ]
 
 
@@ -368,6 +368,48 @@ def rope(x, pos, base: float = 10000.0) -> np.ndarray:
     return np.concatenate([x1 * c - x2 * s, x1 * s + x2 * c], axis=-1)
 
 
+def causal_attention(q, cache_k, cache_v, lengths, P: int) -> np.ndarray:
+    """o[b*P+i] = sum_{j <= L_b+i} softmax_j(q . k_j / sqrt(d)) v_j per head,
+    in fp64 over the cache as it stands (rows past L_b + i are not read).
+    q [B*P, n_heads, d]; caches [B, n_heads, max_len, d]; returns [B*P, n_heads, d]."""
+    q = f64(q)
+    T, n_heads, d = q.shape
+    o = np.zeros((T, n_heads, d))
+    for b in range(T // P):
+        L = int(lengths[b])
+        for i in range(P):
+            t = b * P + i
+            kk = f64(cache_k[b, :, :L + i + 1])            # [n_heads, keys, d]
+            vv = f64(cache_v[b, :, :L + i + 1])
+            sc = np.einsum("hd,hjd->hj", q[t], kk) / np.sqrt(d)
+            sc -= sc.max(axis=1, keepdims=True)
+            p = np.exp(sc)
+            p /= p.sum(axis=1, keepdims=True)
+            o[t] = np.einsum("hj,hjd->hd", p, vv)
+    return o
+
+
+def rope_cache(qkv, lengths, P: int, n_heads: int, cache_k, cache_v, mode: str, base: float = 10000.0):
+    """Split stored qkv [B*P, 3H] into heads, rotate q and k at their
+    positions L_b + i, store (round) them, and write k, v into the caches at
+    [b, :, L_b + i] (in place).  Returns q, k, v [B*P, n_heads, d]."""
+    qkv = f64(qkv)
+    T, H3 = qkv.shape
+    H = H3 // 3
+    d = H // n_heads
+    B = T // P
+    pos = np.concatenate([np.arange(P) + int(lengths[b]) for b in range(B)])
+    q = store(rope(qkv[:, :H].reshape(T, n_heads, d), pos, base), mode)
+    k = store(rope(qkv[:, H:2 * H].reshape(T, n_heads, d), pos, base), mode)
+    v = qkv[:, 2 * H:].reshape(T, n_heads, d)
+    for b in range(B):
+        L = int(lengths[b])
+        for i in range(P):
+            cache_k[b, :, L + i] = k[b * P + i]
+            cache_v[b, :, L + i] = v[b * P + i]
+    return q, k, v
+
+
 def attention_block(h, w_qkv, w_o, cache_k, cache_v, lengths, P: int, n_heads: int, eps: float, mode: str) -> dict:
     """Pre-norm causal self-attention of the verify positions over a KV cache.
 
@@ -386,33 +428,12 @@ def attention_block(h, w_qkv, w_o, cache_k, cache_v, lengths, P: int, n_heads: i
     """
     h = f64(h)
     T, H = h.shape
-    d = H // n_heads
-    B = T // P
     xa = store(rmsnorm(h, eps), mode)
-    qkv = xa @ f64(w_qkv).T
-    pos = np.concatenate([np.arange(P) + int(lengths[b]) for b in range(B)])
-    q = store(rope(store(qkv[:, :H], mode).reshape(T, n_heads, d), pos), mode)
-    k = store(rope(store(qkv[:, H:2 * H], mode).reshape(T, n_heads, d), pos), mode)
-    v = store(qkv[:, 2 * H:], mode).reshape(T, n_heads, d)
-    o = np.zeros((T, n_heads, d))
-    for b in range(B):
-        L = int(lengths[b])
-        for i in range(P):
-            t = b * P + i
-            cache_k[b, :, L + i] = k[t]
-            cache_v[b, :, L + i] = v[t]
-        for i in range(P):
-            t = b * P + i
-            kk = f64(cache_k[b, :, :L + i + 1])            # [n_heads, keys, d]
-            vv = f64(cache_v[b, :, :L + i + 1])
-            sc = np.einsum("hd,hjd->hj", q[t], kk) / np.sqrt(d)
-            sc -= sc.max(axis=1, keepdims=True)
-            p = np.exp(sc)
-            p /= p.sum(axis=1, keepdims=True)
-            o[t] = np.einsum("hj,hjd->hd", p, vv)
-    o = store(o.reshape(T, H), mode)
+    qkv = store(xa @ f64(w_qkv).T, mode)
+    q, k, v = rope_cache(qkv, lengths, P, n_heads, cache_k, cache_v, mode)
+    o = store(causal_attention(q, cache_k, cache_v, lengths, P).reshape(T, H), mode)
     h_out = store(h + store(o @ f64(w_o).T, mode), mode)
-    return {"xa": xa, "q": q, "k": k, "v": v, "o": o, "h_out": h_out}
+    return {"xa": xa, "qkv": qkv, "q": q, "k": k, "v": v, "o": o, "h_out": h_out}
 
 
 # ----------------------------------------------------------------------------

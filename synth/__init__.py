@@ -32,7 +32,7 @@ import torch
 
 __all__ = [
     "Shape", "SHAPES", "subseed", "normal", "router_weight", "layer_weights", "lm_weight",
-    "DRAFT_INTERMEDIATE", "draft_weights",
+    "DRAFT_INTERMEDIATE", "draft_weights", "ATTN_HEAD_DIM", "attn_weights", "kv_prefix",
     "hidden", "uniform_ids", "plant_schedule", "bf16_bits",
 ]
 
@@ -144,6 +144,28 @@ def draft_weights(seed: int, sh: Shape, device="cpu", I: int = DRAFT_INTERMEDIAT
         "w_gate_up": normal(subseed(seed, "draft_gate_up"), (1, 2 * I, sh.H), 0.02, dt, device),
         "w_down": normal(subseed(seed, "draft_down"), (1, sh.H, I), 0.02, dt, device),
     }
+
+
+ATTN_HEAD_DIM = 128   # attention head size (a synthetic choice: hidden 1280 = 10 heads x 128)
+
+
+def attn_weights(seed: int, layer: int, sh: Shape, device="cpu") -> dict:
+    """Weights of one attention block (storage dtype, row-major):
+      w_qkv  [3H, H]  q rows, then k rows, then v rows ~N(0, 0.04)
+      w_o    [H, H]   ~N(0, 0.02)
+    The q/k scale gives attention scores of standard deviation about 2 on
+    normed inputs at H = 1280 (a softmax that is neither flat nor one-hot)."""
+    dt = sh.torch_dtype
+    return {
+        "w_qkv": normal(subseed(seed, "w_qkv", layer), (3 * sh.H, sh.H), 0.04, dt, device),
+        "w_o": normal(subseed(seed, "w_o", layer), (sh.H, sh.H), 0.02, dt, device),
+    }
+
+
+def kv_prefix(seed: int, layer: int, shape, dtype, device="cpu", name: str = "k") -> torch.Tensor:
+    """A committed KV-cache prefix [B, n_heads, max_len, d] ~N(0, 1.4^2): the
+    spread of the rotated keys and values the block writes itself."""
+    return normal(subseed(seed, "kv_" + name, layer), shape, 1.4, dtype, device)
 
 
 def lm_weight(seed: int, sh: Shape, device="cpu") -> torch.Tensor:

@@ -21,7 +21,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = L.header_functions()
-    assert len(names) == 21
+    assert len(names) == 25
     assert set(names) == set(L.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
@@ -189,6 +189,35 @@ def test_advance_and_gather_checks(lib):
     assert gat(None, None, None, 0, 4, 10, 32, 2560, None, None) == L.OK
     assert gat(A, A, A, 4, 1, 10, 32, 0, A, None) == L.OK           # K = 0 drafts: nothing to gather
     assert gat(A, A, A, 4, 1, 10, 32, -1, A, None) == L.ERR_SHAPE
+
+
+def test_attention_checks(lib):
+    rope, att, com = lib.moe_attn_rope_cache, lib.moe_attention, lib.spec_commit
+    ws = lib.moe_attention_workspace_bytes
+    # one split per 256 keys up to 64 splits: 32 x 4 queries x 10 heads at 2,048 keys -> 8 splits
+    assert ws(32, 4, 10, 128, 2048) == 32 * 10 * 8 * 4 * 130 * 4
+    assert ws(1, 4, 10, 128, 32768) == 10 * 64 * 4 * 130 * 4          # 512 keys per split
+    assert ws(0, 4, 10, 128, 2048) == 0
+    # qkv, lengths, B, P, n_heads, head_dim, base, max_len, dtype, q, ck, cv, stream
+    assert rope(A, A, 2, 4, 10, 128, 1e4, 64, m.BF16, A, A, None, None) == L.ERR_NULL
+    assert rope(A, A, 2, 4, 10, 64, 1e4, 64, m.BF16, A, A, A, None) == L.ERR_UNSUPPORTED    # head size 128
+    assert rope(A, A, 2, 17, 10, 128, 1e4, 64, m.BF16, A, A, A, None) == L.ERR_UNSUPPORTED  # P <= 16
+    assert rope(A, A, 2, 4, 10, 128, 1e4, 64, m.F32, A, A, A, None) == L.ERR_UNSUPPORTED
+    assert rope(A, A, 2, 4, 10, 128, 1e4, 3, m.BF16, A, A, A, None) == L.ERR_SHAPE           # max_len < P
+    assert rope(A, A, 2, 4, 10, 128, 1.0, 64, m.BF16, A, A, A, None) == L.ERR_SHAPE
+    assert rope(None, None, 0, 4, 10, 128, 1e4, 64, m.BF16, None, None, None, None) == L.OK
+    # q, ck, cv, lengths, B, P, n_heads, head_dim, max_len, max_keys, dtype, o, ws, ws_bytes, stream
+    need = ws(2, 4, 10, 128, 64)
+    assert att(A, A, A, A, 2, 4, 10, 128, 64, 64, m.BF16, A, A, need - 1, None) == L.ERR_WORKSPACE
+    assert att(A, A, A, A, 2, 4, 10, 128, 64, 64, m.BF16, A, None, need, None) == L.ERR_WORKSPACE
+    assert att(A, MIS, A, A, 2, 4, 10, 128, 64, 64, m.BF16, A, A, need, None) == L.ERR_ALIGN
+    assert att(A, A, A, A, 2, 4, 10, 128, 64, 65, m.BF16, A, A, need, None) == L.ERR_SHAPE  # max_keys > max_len
+    assert att(A, A, A, A, 2, 4, 10, 128, 64, 3, m.BF16, A, A, need, None) == L.ERR_SHAPE   # max_keys < P
+    assert att(A, A, A, None, 2, 4, 10, 128, 64, 64, m.BF16, A, A, need, None) == L.ERR_NULL
+    assert att(None, None, None, None, 0, 4, 10, 128, 64, 64, m.BF16, None, None, 0, None) == L.OK
+    assert com(A, -1, A, None) == L.ERR_SHAPE
+    assert com(None, 4, A, None) == L.ERR_NULL
+    assert com(None, 0, None, None) == L.OK
 
 
 def test_combine_lmhead_verify_plant_checks(lib):
