@@ -81,26 +81,44 @@ __global__ __launch_bounds__(256) void attn_split_kernel(const bf16_t* __restric
   const int k0 = split * split_keys, k1 = min(k0 + split_keys, L + P);
   const size_t base = ((size_t)b * n_heads + hd) * max_len;
 
-  for (int e = threadIdx.x; e < P * kD; e += 256) {
-    const int i = e / kD, dd = e % kD;
-    qs[i][dd] = __uint_as_float((uint32_t)q[(size_t)(b * P + i) * H + hd * kD + dd] << 16);
+  if (threadIdx.x < P * (kD / 8)) {   // P <= 16 queries: one 16-byte segment per thread
+    const int i = threadIdx.x >> 4, sg = (threadIdx.x & 15) * 8;
+    float f[8];
+    unpack8(ldg16(q + (size_t)(b * P + i) * H + hd * kD + sg), f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qs[i][sg + e] = f[e];
   }
   // per query this wavefront owns: running max, sum and 2 output dims per lane
   float m[4], l[4], o0[4], o1[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) { m[u] = -INFINITY; l[u] = 0.f; o0[u] = 0.f; o1[u] = 0.f; }
-  lds_barrier();
+
+  // staging: thread owns the 16-byte segment sg of rows tid/16 + 16 s (s < 4)
+  // of each 64-key tile; the next tile's loads are in flight while the
+  // current one is scored
+  const int sg = (threadIdx.x & 15) * 8;
+  uint4 kr[4], vr[4];
+  auto fetch = [&](int t0) {
+    const int nk = min(kTile, k1 - t0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int key = t0 + min((threadIdx.x >> 4) + 16 * s, nk - 1);
+      kr[s] = ldg16(ck + (base + key) * kD + sg);
+      vr[s] = ldg16(cv + (base + key) * kD + sg);
+    }
+  };
+  if (k0 < k1) fetch(k0);
 
   for (int t0 = k0; t0 < k1; t0 += kTile) {
     const int nk = min(kTile, k1 - t0);
-    // stage the tile: 64 keys x 128 dims of k and v, 16 bytes per thread per step
-    for (int e = threadIdx.x; e < kTile * (kD / 8); e += 256) {
-      const int r = e / (kD / 8), sg = (e % (kD / 8)) * 8;
-      const int key = t0 + min(r, nk - 1);
-      *reinterpret_cast<uint4*>(&ks[r][sg]) = ldg16(ck + (base + key) * kD + sg);
-      *reinterpret_cast<uint4*>(&vs[r][sg]) = ldg16(cv + (base + key) * kD + sg);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int r = (threadIdx.x >> 4) + 16 * s;
+      *reinterpret_cast<uint4*>(&ks[r][sg]) = kr[s];
+      *reinterpret_cast<uint4*>(&vs[r][sg]) = vr[s];
     }
     lds_barrier();
+    if (t0 + kTile < k1) fetch(t0 + kTile);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int i = wave + 4 * u;
@@ -130,6 +148,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(const bf16_t* __restric
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
       float a0 = o0[u] * corr, a1 = o1[u] * corr;
+#pragma unroll 8
       for (int jj = 0; jj < nk; ++jj) {
         const float pj = ps[wave][jj];
         const uint32_t vv = *reinterpret_cast<const uint32_t*>(&vs[jj][2 * lane]);
@@ -156,23 +175,32 @@ __global__ __launch_bounds__(256) void attn_split_kernel(const bf16_t* __restric
   }
 }
 
-// one wavefront per (b, head, query): merge the splits, lane owns 2 dims
+// one wavefront per (b, head, query): merge the splits (nsplit <= 64), lane
+// owns 2 dims.  Lane s first reads split s's (max, sum) so the global max and
+// the scale of every split come from two wave reductions; the output sums
+// then run over the splits in order with their loads batched.
 __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ ws, int B, int P, int n_heads,
                                                          int nsplit, bf16_t* __restrict__ o) {
   const int gw = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (gw >= B * n_heads * P) return;
   const int i = gw % P, hd = (gw / P) % n_heads, b = gw / (P * n_heads);
-  float M = -INFINITY;
-  for (int sp = 0; sp < nsplit; ++sp)
-    M = fmaxf(M, ws[((((size_t)b * n_heads + hd) * nsplit + sp) * P + i) * (kD + 2)]);
-  float Ls = 0.f, a0 = 0.f, a1 = 0.f;
+  const size_t stride = (size_t)P * (kD + 2);   // between splits
+  const float* w0 = ws + ((((size_t)b * n_heads + hd) * nsplit) * P + i) * (kD + 2);
+  float ms = -INFINITY, ls = 0.f;
+  if (lane < nsplit) {
+    ms = w0[lane * stride];
+    ls = w0[lane * stride + 1];
+  }
+  const float M = wave_max_dpp(ms);
+  const float fs = ms == -INFINITY ? 0.f : expf(ms - M);   // a split with no visible key weighs 0
+  const float Ls = wave_sum_dpp(fs * ls);
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll 8
   for (int sp = 0; sp < nsplit; ++sp) {
-    const float* w = ws + ((((size_t)b * n_heads + hd) * nsplit + sp) * P + i) * (kD + 2);
-    if (w[0] == -INFINITY) continue;   // a split with no visible key
-    const float f = expf(w[0] - M);
-    Ls = fmaf(f, w[1], Ls);
-    a0 = fmaf(f, w[2 + 2 * lane], a0);
-    a1 = fmaf(f, w[3 + 2 * lane], a1);
+    const float f = __shfl(fs, sp);
+    const float2 v = *reinterpret_cast<const float2*>(w0 + sp * stride + 2 + 2 * lane);
+    a0 = fmaf(f, v.x, a0);
+    a1 = fmaf(f, v.y, a1);
   }
   const int H = n_heads * kD;
   bf16_t* out = o + (size_t)(b * P + i) * H + hd * kD + 2 * lane;
