@@ -14,3 +14,4 @@ from .step import VerifyStack  # noqa: F401
 from .loop import DecodeLoop  # noqa: F401
 from .draft import DraftHead  # noqa: F401
 from .attention import AttentionBlock  # noqa: F401
+from .pipeline import PagePipeline  # noqa: F401

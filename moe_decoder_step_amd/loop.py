@@ -51,15 +51,23 @@ class DecodeLoop:
         self.tokens = torch.empty((S, self.target), **i32)
         self.n_active = torch.empty(1, **i32)
 
-    def run(self, record: list | None = None) -> dict:
+    def run(self, record: list | None = None, first: torch.Tensor | None = None) -> dict:
         """Decode every sequence to `target` tokens; returns the number of passes
         and the batch size of each.  With `record`, every pass's active ids,
-        inputs and greedy tokens are appended to it."""
+        inputs and greedy tokens are appended to it.  With `first` [S] int32
+        (the greedy token after each prompt, from the prefill), each stream
+        starts with it and the loop commits the other target - 1 tokens."""
         S, P, K = self.S, self.P, self.K
         self.seq[0].copy_(torch.arange(S, dtype=torch.int32))
-        self.total.zero_()
         self.steps.zero_()
         self.tokens.fill_(-1)
+        if first is None:
+            self.total.zero_()
+        else:
+            if self.target < 2 or first.shape != (S,) or first.dtype != torch.int32:
+                raise ValueError("first must be [S] int32 and target at least 2")
+            self.tokens[:, 0].copy_(first)
+            self.total.fill_(1)
         cur, B, sizes = 0, S, []
         while B > 0:
             ids = self.seq[cur][:B]

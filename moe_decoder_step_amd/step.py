@@ -41,18 +41,42 @@ class VerifyStack:
             gu, dn = ops.expert_weights(w["w_gate_up"], w["w_down"])
             self.layers.append({"w_router": ops.router_weights(w["w_router"]), "bias": w.get("bias"), "w_gate_up": gu, "w_down": dn})
         self.w_lm = None if w_lm is None else ops.lm_weights(w_lm)
-        # when a list: (start, end) torch.cuda.Event pairs around every expert
-        # gate/up launch, recorded on the stream the kernels run on
-        self.ffn_events = None
-        # fuse each block's combine with the next block's routing, and (bf16,
-        # decode-sized batches) the permutation into the gate/up launch
-        self.fuse = True
+        self.V = None if w_lm is None else w_lm.shape[0]
         self.E, self.k, self.S, self.eps = E, k, S, eps
         wgu = layers[0]["w_gate_up"]
         self.dtype = wgu.dtype
         self.device = wgu.device
         self.H = wgu.shape[2]
         self.I = wgu.shape[1] // 2
+        self.attn = None
+        if attn:
+            from .attention import AttentionBlock
+            if len(attn) != len(layers) or not max_seqs or not max_len:
+                raise ValueError("attention needs one block per layer, max_seqs and max_len")
+            self.attn = [AttentionBlock(a, n_heads, max_seqs, K + 1, max_len, eps) for a in attn]
+        self._alloc(max_tokens, max_seqs, K, keep_logits)
+
+    def sibling(self, max_tokens: int, max_seqs: int = 0, K: int = 0, keep_logits: bool = False) -> "VerifyStack":
+        """A stack over the same packed weights with buffers of its own, sized
+        for another batch (e.g. a prefill batch next to the decode batch).
+        Attention-free."""
+        if self.attn is not None:
+            raise ValueError("a sibling of a stack with attention is not supported")
+        other = object.__new__(VerifyStack)
+        for name in ("layers", "w_lm", "V", "E", "k", "S", "eps", "dtype", "device", "H", "I", "attn"):
+            setattr(other, name, getattr(self, name))
+        other._alloc(max_tokens, max_seqs, K, keep_logits)
+        return other
+
+    def _alloc(self, max_tokens: int, max_seqs: int, K: int, keep_logits: bool) -> None:
+        """The buffers of one batch of up to max_tokens positions."""
+        E, k, S = self.E, self.k, self.S
+        # when a list: (start, end) torch.cuda.Event pairs around every expert
+        # gate/up launch, recorded on the stream the kernels run on
+        self.ffn_events = None
+        # fuse each block's combine with the next block's routing, and (bf16,
+        # decode-sized batches) the permutation into the gate/up launch
+        self.fuse = True
         self.max_tokens = T = max_tokens
         dev, H = self.device, self.H
         i32 = dict(dtype=torch.int32, device=dev)
@@ -69,18 +93,12 @@ class VerifyStack:
         self.n_rows = T * k + S * T
         self.y = torch.empty((self.n_rows, H), dtype=self.dtype, device=dev)
         self.act = torch.empty((self.n_rows, self.I), dtype=self.dtype, device=dev)
-        if w_lm is not None:
-            V = w_lm.shape[0]
+        if self.w_lm is not None:
             self.argmax = torch.empty(T, **i32)
             self.max_logit = torch.empty(T, dtype=torch.float32, device=dev)
-            self.lws = torch.empty(max(ops.lmhead_workspace_bytes(T, V, self.dtype), 16), dtype=torch.uint8,
+            self.lws = torch.empty(max(ops.lmhead_workspace_bytes(T, self.V, self.dtype), 16), dtype=torch.uint8,
                                    device=dev)
-        self.attn = None
-        if attn:
-            from .attention import AttentionBlock
-            if len(attn) != len(layers) or not max_seqs or not max_len:
-                raise ValueError("attention needs one block per layer, max_seqs and max_len")
-            self.attn = [AttentionBlock(a, n_heads, max_seqs, K + 1, max_len, eps) for a in attn]
+        if self.attn is not None:
             self.lengths = torch.zeros(max_seqs, **i32)
             self.max_keys = None        # a known bound on lengths + K + 1 (default: max_len)
         if max_seqs:

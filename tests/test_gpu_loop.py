@@ -29,13 +29,14 @@ def m():
     return mod
 
 
-def _reference_loop(passes, keep_pool, repl_pool, target, S):
-    """Bookkeeping of the loop from each pass's greedy tokens g (oracle side)."""
+def _reference_loop(passes, keep_pool, repl_pool, target, S, first=None):
+    """Bookkeeping of the loop from each pass's greedy tokens g (oracle side);
+    with `first`, every stream starts with that sequence's token."""
     K = keep_pool.shape[2]
     active = list(range(S))
-    total = [0] * S
+    total = [0 if first is None else 1] * S
     steps = [0] * S
-    streams = [[] for _ in range(S)]
+    streams = [[] if first is None else [int(first[s])] for s in range(S)]
     for p in passes:
         assert p["seq"].cpu().numpy().tolist() == active
         g = p["argmax"].cpu().numpy().reshape(len(active), K + 1).astype(np.int64)
