@@ -80,7 +80,7 @@ __global__ __launch_bounds__(kThreads) void lm_bf16_kernel(const bf16_t* __restr
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
-        for (int s = 0; s < kSteps; ++s) d[nb][s] = ldg16(wp[nb] + min(c * kSteps + s, nK - 1) * 1024);
+        for (int s = 0; s < kSteps; ++s) d[nb][s] = ldg16_stream(wp[nb] + min(c * kSteps + s, nK - 1) * 1024);
     };
     auto load_x = [&](int c) __attribute__((always_inline)) {
       const int kofs = c * kKC + sseg;
@@ -228,8 +228,8 @@ __global__ __launch_bounds__(kSThreads) void lm_stream_kernel(const bf16_t* __re
     uint4 ra[4], rb[4];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      ra[d] = ldg16(wa + min(d, nK - 1) * 1024);
-      rb[d] = ldg16(wb + min(d, nK - 1) * 1024);
+      ra[d] = ldg16_stream(wa + min(d, nK - 1) * 1024);
+      rb[d] = ldg16_stream(wb + min(d, nK - 1) * 1024);
     }
     hload(0);
     hstore(0);
@@ -251,8 +251,8 @@ __global__ __launch_bounds__(kSThreads) void lm_stream_kernel(const bf16_t* __re
           acc[1][i] = mfma16x16x32(as_bf16x8(rb[s0 + ks]), bx, acc[1][i]);
         }
         const int kk = min(2 * c + ks + 4, nK - 1);
-        ra[s0 + ks] = ldg16(wa + kk * 1024);
-        rb[s0 + ks] = ldg16(wb + kk * 1024);
+        ra[s0 + ks] = ldg16_stream(wa + kk * 1024);
+        rb[s0 + ks] = ldg16_stream(wb + kk * 1024);
       }
       lds_barrier();
     };
