@@ -103,11 +103,23 @@ __device__ __forceinline__ void stream_rows(const bf16_t* wa, const bf16_t* wb, 
 //        streams as many bytes per k-step as in the gated stage.
 // A block of 8 wavefronts owns one column tile of one group and one range of
 // up to 16 rows, staged once into LDS (one barrier) and shared by its waves.
+//
+// K split (one-group launches, the dense projections): the block's 8
+// wavefronts are CG column groups x KS slices of the reduction (KS = 2^
+// ks_log2, CG = 8 / KS); slice ks streams k-steps [ks nK/KS, (ks+1) nK/KS)
+// and the KS partial sums of a column group are added in slice order
+// through LDS.  A dense layer has one group, so with one column group per
+// wavefront it would get as few as N / 256 blocks (5 for N = 1280, each
+// streaming 1.8 MB at K = 3584) where an expert launch gets one per touched
+// expert and tile; the split multiplies the blocks by KS.  KS depends on
+// the weight shape only, never on the number of rows, so a row's result
+// does not depend on the batch.
 template <bool GATED, bool ROUTED>
 __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
     const bf16_t* __restrict__ x, const int32_t* __restrict__ gather,
     const int32_t* __restrict__ offsets, int G, int n_rows, int T,
-    const bf16_t* __restrict__ W, int K, int N, int n_ctiles, bf16_t* __restrict__ out, RoutedArgs rt) {
+    const bf16_t* __restrict__ W, int K, int N, int n_ctiles, int ks_log2, bf16_t* __restrict__ out,
+    RoutedArgs rt) {
   static_assert(!ROUTED || GATED, "only the gate/up stage derives its rows from the expert ids");
   constexpr int D = 3;                    // k-steps of weights in flight per wavefront
   constexpr int WCOLS = GATED ? 16 : 32;  // output columns per wavefront
@@ -236,14 +248,17 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
   }
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int col0 = ct * (kWaves * WCOLS) + wave * WCOLS;
+  const int KS = 1 << ks_log2, CG = kWaves >> ks_log2;
+  const int cg = wave & (CG - 1), ks = wave >> (3 - ks_log2);
+  const int col0 = ct * (CG * WCOLS) + cg * WCOLS;
   const bool active = col0 < N;
   // packed weights: [group][pair][k-step][set][lane][8]; a pair is this
   // wavefront's two 16-row sets, a (pair, k-step) is 2 KB of consecutive bytes
   const int nK = K / 32;
+  const int nKs = nK >> ks_log2, k0 = ks * nKs;   // this wavefront's k-steps
   const int n_pairs = GATED ? N / 16 : (N + 31) / 32;
   const int pair = min(col0 / WCOLS, n_pairs - 1);  // inactive wavefronts load a valid pair, store nothing
-  const bf16_t* wa = W + ((size_t)g * n_pairs + pair) * nK * 1024 + lane * 8;
+  const bf16_t* wa = W + (((size_t)g * n_pairs + pair) * nK + k0) * 1024 + lane * 8;
   const bf16_t* wb = wa + 512;
   const int ldr = lds_row(K);
   const int nseg = K / 8;                 // 16-byte segments per activation row
@@ -254,7 +269,7 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
     uint4 ra[D], rb[D];
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      const int kk = min(d, nK - 1);
+      const int kk = min(d, nKs - 1);
       ra[d] = wload<NT>(wa + kk * 1024);
       rb[d] = wload<NT>(wb + kk * 1024);
     }
@@ -280,9 +295,26 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
     }
     lds_barrier();
 
-    if (active) {
-      f32x4_t acc_a = f32x4_t{0.f, 0.f, 0.f, 0.f}, acc_b = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      stream_rows<D, NT>(wa, wb, xl + (lane & 15) * ldr + (lane >> 4) * 8, nK, ra, rb, acc_a, acc_b);
+    f32x4_t acc_a = f32x4_t{0.f, 0.f, 0.f, 0.f}, acc_b = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (active || KS > 1)   // with a K split every wavefront streams (inactive ones a valid pair) to reach the barriers
+      stream_rows<D, NT>(wa, wb, xl + (lane & 15) * ldr + (lane >> 4) * 8 + k0 * 32, nKs, ra, rb, acc_a, acc_b);
+    if (KS > 1) {
+      // partial sums of the slices, added in slice order; the staged rows are
+      // dead, their LDS holds the partials [wavefront][lane][8]
+      float* red = reinterpret_cast<float*>(xl);
+      lds_barrier();
+      if (ks > 0) {
+        *reinterpret_cast<f32x4_t*>(red + (wave * kWave + lane) * 8) = acc_a;
+        *reinterpret_cast<f32x4_t*>(red + (wave * kWave + lane) * 8 + 4) = acc_b;
+      }
+      lds_barrier();
+      if (ks == 0)
+        for (int q = 1; q < KS; ++q) {
+          acc_a += *reinterpret_cast<const f32x4_t*>(red + ((cg + q * CG) * kWave + lane) * 8);
+          acc_b += *reinterpret_cast<const f32x4_t*>(red + ((cg + q * CG) * kWave + lane) * 8 + 4);
+        }
+    }
+    if (active && ks == 0) {
       // lane holds D[col 4*(lane/16)+v][row lane%16]: 4 consecutive output columns of one row
       const int row = lane & 15;
       if (row < mr) {
@@ -311,7 +343,16 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
 template <bool GATED, bool ROUTED = false>
 hipError_t launch_skinny(const bf16_t* x, const int32_t* gather, const int32_t* offsets, int G, int n_rows, int T,
                          const bf16_t* W, int K, int N, bf16_t* out, hipStream_t s, RoutedArgs ra = {}) {
-  constexpr int tile = kWaves * (GATED ? 16 : 32);
+  // K split for one-group launches (by the weight shape only): enough
+  // slices for ~64 column tiles, each slice at least 2 k-steps, the staged
+  // rows' LDS large enough for the partials (K >= 512)
+  const int nK = K / 32;
+  const int n_cg = GATED ? N / 16 : (N + 31) / 32;
+  int ks_log2 = 0;
+  if (G == 1 && !ROUTED && K >= 512)
+    while (ks_log2 < 3 && (n_cg << ks_log2) < 64 * kWaves && nK % (2 << ks_log2) == 0 && nK / (2 << ks_log2) >= 2)
+      ++ks_log2;
+  const int tile = (kWaves >> ks_log2) * (GATED ? 16 : 32);
   const int n_ctiles = (N + tile - 1) / tile;
   // items on one XCD <= ceil(n_ctiles / 8) * sum over groups of ceil(rows / 16)
   //                  <= ceil(n_ctiles / 8) * (n_rows / 16 + G)
@@ -324,7 +365,7 @@ hipError_t launch_skinny(const bf16_t* x, const int32_t* gather, const int32_t* 
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((skinny_kernel<GATED, ROUTED>), dim3(blocks), dim3(kBlockThreads), lds, s, x, gather, offsets,
-                     G, n_rows, T, W, K, N, n_ctiles, out, ra);
+                     G, n_rows, T, W, K, N, n_ctiles, ks_log2, out, ra);
   return hipGetLastError();
 }
 
