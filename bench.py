@@ -61,6 +61,32 @@ def expert_bytes(sh) -> int:
     return 3 * sh.H * sh.I * 2
 
 
+def ffn_roofline(st, h_in, sh, steps: int) -> dict:
+    """The routed gate/up kernel of a verify pass over h_in: algorithmic
+    bytes from the pass's own routing (gate and up rows of every touched
+    expert and the shared ones, the normed tokens in, the SwiGLU rows out)
+    over its mean launch duration, HIP events on its stream."""
+    import numpy as np
+    import torch
+    T = h_in.shape[0]
+    rec = []
+    st.forward(h_in, rec)
+    touched = [int(np.unique(r["ids"].cpu().numpy()).size) for r in rec]
+    n_rows = T * sh.k + sh.S * T
+    gu_b = float(np.mean([(t + sh.S) * 2 * sh.I * sh.H * 2 + T * sh.H * 2 + n_rows * sh.I * 2 for t in touched]))
+    st.ffn_events = ev = []
+    for _ in range(steps):
+        st.forward(h_in)
+    torch.cuda.synchronize()
+    st.ffn_events = None
+    us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    gbs = gu_b / (us * 1e-6) / 1e9
+    return {"kernel": "moe_expert_gate_up_routed (skinny_kernel<true, true>)", "bound": "hbm", "achieved": gbs,
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+            "traffic_source": f"counters recorded for the {sh.B} x {sh.P}-token verify pass (step128 workload)",
+            "us_per_launch": us, "algorithmic_bytes_per_launch": gu_b, "tokens_per_pass": T}
+
+
 # HBM traffic of the gate/up kernel per launch, from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE runs scaled by the same counters on a plain copy of known size;
 # valid only while the kernel's sources are the ones that were measured
@@ -375,6 +401,7 @@ def decode_loop_bench(args) -> int:
                                f"drafts planted with keep probability {P_KEEP}, finished sequences compacted out",
                    "hidden": sh.H, "experts": f"{sh.E} routed + {sh.S} shared, top-{sh.k}",
                    "expert_intermediate": sh.I, "vocab": sh.V, "layers": sh.L},
+        "roofline": ffn_roofline(st, h_pool[:, 0].reshape(S * P, sh.H), sh, 5),
         "loop": {"passes": res["passes"], "wall_ms": wall * 1e3, "mean_batch": float(np.mean(sizes)),
                  "full_batch_passes": int(sum(1 for b in sizes if b == S)),
                  "committed_per_pass_per_seq": committed / float(np.sum(sizes)),
@@ -525,6 +552,7 @@ def spec_step_bench(args) -> int:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps
 
+    roofline = ffn_roofline(st, h_in, sh, args.steps)
     t_draft = timed(draft)
     t_verify = timed(verify)
     t_spec = timed(lambda: (draft(), verify()))
@@ -543,6 +571,7 @@ def spec_step_bench(args) -> int:
                                f"tokens per pass (keep probability {P_KEEP}): random draft weights cannot "
                                f"predict the verifier",
                    "hidden": sh.H, "draft_intermediate": synth.DRAFT_INTERMEDIATE, "vocab": sh.V, "layers": sh.L},
+        "roofline": roofline,
         "spec": {"draft_ms": t_draft, "verify_ms": t_verify, "step_ms": t_spec, "greedy_pass_ms": t_ar,
                  "step_cost_in_greedy_passes": c, "speedup_at_planted_tau": tau_planted / c,
                  "speedup_at_pages_tau_2.73": 2.73 / c, "planted_tau": tau_planted},
