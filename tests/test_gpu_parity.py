@@ -353,3 +353,42 @@ def test_out_of_vocab_draft_is_a_mismatch(m):
     drafts = torch.tensor([[5, 2 ** 31 - 1, 7]], dtype=torch.int32, device=DEV)
     acc, com, nc = m.verify_alloc(drafts, argmax)
     assert acc.item() == 1 and nc.item() == 2 and com.cpu().tolist() == [[5, 6, -1, -1]]
+
+
+@pytest.mark.parametrize("gated,N,K", [
+    (False, 1312, 896),    # K split in 4, the last column tile half idle
+    (False, 1280, 3584),   # K split in 8 (the draft block's down projection)
+    (False, 3840, 1280),   # the attention qkv projection
+    (True, 3584, 1280),    # K split in 4 (the draft block's gate/up)
+    (False, 128, 256),     # too short to split
+])
+def test_one_group_dense_launches(m, gated, N, K):
+    """One-group (dense) launches split the reduction across a block's
+    wavefronts: outputs against the oracle's product, and a row's result is
+    the same bits whatever the number of rows (the split depends on the
+    weight shape only)."""
+    Wrows = 2 * N if gated else N
+    w = synth.normal(21, (1, Wrows, K), 0.02, torch.bfloat16, DEV)
+    wp = m.pack_weights(w, m._lib.PACK_GATE_UP if gated else m._lib.PACK_ROWS)
+    x = synth.normal(22, (130, K), 1.0, torch.bfloat16, DEV)
+    wh = O.f64(host(w[0]))
+    first = None
+    for rows in (1, 17, 130):
+        xr = x[:rows].contiguous()
+        out = torch.full((rows, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+        off = torch.tensor([0, rows], dtype=torch.int32, device=DEV)
+        if gated:
+            m.moe_expert_gate_up(xr, None, off, wp, out, max_rows=rows)
+        else:
+            m.moe_expert_down(xr, off, wp, out, max_rows=rows)
+        torch.cuda.synchronize()
+        xh = O.f64(host(xr))
+        if gated:
+            ref = O.swiglu(xh, wh, np.eye(N), "bf16")
+        else:
+            ref = O.store(xh @ wh.T, "bf16")
+        assert_close(as_f64(out), ref, BF16_TOL, f"rows {rows}")
+        if first is None:
+            first = out[0].clone()
+        else:
+            assert torch.equal(out[0], first), f"row 0 depends on the number of rows ({rows})"
