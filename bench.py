@@ -620,19 +620,18 @@ def attention_bench(args) -> int:
     rows = []
     for L in ctx:
         max_len = L + P
-        ck = synth.kv_prefix(2, 0, (B, nh, max_len, D), torch.bfloat16, dev, "k")
-        cv = synth.kv_prefix(2, 0, (B, nh, max_len, D), torch.bfloat16, dev, "v")
+        kv = synth.kv_prefix(2, 0, (B, nh, max_len, 2, D), torch.bfloat16, dev, "kv")
         lengths = torch.full((B,), L, dtype=torch.int32, device=dev)
         ws = torch.empty(m.attention_workspace_bytes(B, P, nh, max_len), dtype=torch.uint8, device=dev)
-        t_rope = _event_timer(args.steps, args.warmup, lambda: m.moe_attn_rope_cache(qkv, lengths, P, q, ck, cv))
-        t_att = _event_timer(args.steps, args.warmup, lambda: m.moe_attention(q, ck, cv, lengths, P, o, ws))
+        t_rope = _event_timer(args.steps, args.warmup, lambda: m.moe_attn_rope_cache(qkv, lengths, P, q, kv))
+        t_att = _event_timer(args.steps, args.warmup, lambda: m.moe_attention(q, kv, lengths, P, o, ws))
         kv_bytes = B * nh * (L + P) * D * 2 * 2
         nbytes = kv_bytes + 2 * T * H * 2
         gbs = nbytes / (t_att * 1e-3) / 1e9
         log(f"context {L}: rope+cache {t_rope * 1e3:.1f} us, attention {t_att * 1e3:.1f} us, {gbs:.0f} GB/s")
         rows.append({"context": L, "rope_cache_us": t_rope * 1e3, "attention_us": t_att * 1e3,
                      "algorithmic_bytes": nbytes, "GBs": gbs, "frac": gbs / HBM_PEAK_GBS})
-        del ck, cv, ws
+        del kv, ws
         torch.cuda.empty_cache()
     r0 = rows[0]
     ms = (r0["rope_cache_us"] + r0["attention_us"]) * 1e-3
@@ -695,7 +694,7 @@ def attention_step_bench(args) -> int:
     blk = st.attn[0]
     lengths = st.lengths[:sh.B]
     t_att = _event_timer(args.steps, args.warmup, lambda: m.moe_attention(
-        blk.q[:T], blk.cache_k, blk.cache_v, lengths, sh.P, blk.o[:T], blk.ws))
+        blk.q[:T], blk.kv, lengths, sh.P, blk.o[:T], blk.ws))
     kv_bytes = sh.B * nh * (L + sh.P) * synth.ATTN_HEAD_DIM * 2 * 2
     nbytes = kv_bytes + 2 * T * sh.H * 2
     gbs = nbytes / (t_att * 1e-3) / 1e9

@@ -386,16 +386,19 @@ int spec_gather_rows(const void* pool, const int32_t* seq_ids, const int32_t* st
  * rotary positions (rotate-half form, angle pos * base^(-j/64), j < 64).
  * A verify pass of sequence b holds P = K+1 positions at L_b .. L_b+P-1,
  * L_b = lengths[b] (its last committed token, then the drafts); tokens are
- * laid out [B*P] sequence-major, H = n_heads * 128.
+ * laid out [B*P] sequence-major, H = n_heads * 128.  The cache holds k and v
+ * interleaved per position: kv [B, n_heads, max_len, 2, 128] bf16, [..][0][..]
+ * the rotated key, [..][1][..] the value (one 512-byte row per position, so
+ * a span of positions is one contiguous stream).
  *
  * moe_attn_rope_cache: q, k, v = split(qkv) (columns [0,H), [H,2H), [2H,3H));
  *   q <- rope(q), written to q [B*P, H]; rope(k) and v are written into the
- *   caches at [b][head][L_b + i][0..128).  Rotation in fp64 from the stored
+ *   cache at [b][head][L_b + i][0] and [1].  Rotation in fp64 from the stored
  *   bf16 inputs, one rounding to bf16.
  *   qkv [B*P, 3H] bf16                          in
  *   lengths [B] int32                           in   clamped to [0, max_len-P]
  *   q [B*P, H] bf16                             out
- *   cache_k, cache_v [B, n_heads, max_len, 128] bf16   in/out (P rows each)
+ *   kv [B, n_heads, max_len, 2, 128] bf16       in/out (P positions each)
  *
  * moe_attention: o_i = sum_{j <= L_b+i} softmax_j(q_i . k_j / sqrt(128)) v_j
  *   per head, over the cached keys (split over the key axis; fp32 scores,
@@ -404,7 +407,7 @@ int spec_gather_rows(const void* pool, const int32_t* seq_ids, const int32_t* st
  *   rejected) are never read, so rejecting drafts needs no cache write.
  *   max_keys bounds lengths[b] + P for every b (it sizes the grid and the
  *   workspace; a longer length is clamped to max_keys - P).
- *   q [B*P, H] bf16, caches as above            in
+ *   q [B*P, H] bf16, kv as above                in
  *   o [B*P, H] bf16                             out
  *   ws                                          scratch of
  *                                               moe_attention_workspace_bytes(B, P, n_heads, 128, max_keys)
@@ -414,15 +417,15 @@ int spec_gather_rows(const void* pool, const int32_t* seq_ids, const int32_t* st
  *   rest of the pass's cache rows are overwritten by the next pass.
  *
  * Limits: dtype MOE_BF16, head_dim 128, 1 <= P <= 16, P <= max_keys <=
- * max_len; the cache pointers 16-byte aligned.
+ * max_len; the cache pointer 16-byte aligned.
  * ------------------------------------------------------------------------- */
 int moe_attn_rope_cache(const void* qkv, const int32_t* lengths, int B, int P, int n_heads,
                         int head_dim, float rope_base, int max_len, int dtype, void* q,
-                        void* cache_k, void* cache_v, void* stream);
+                        void* kv_cache, void* stream);
 size_t moe_attention_workspace_bytes(int B, int P, int n_heads, int head_dim, int max_keys);
-int moe_attention(const void* q, const void* cache_k, const void* cache_v, const int32_t* lengths,
-                  int B, int P, int n_heads, int head_dim, int max_len, int max_keys, int dtype,
-                  void* o, void* ws, size_t ws_bytes, void* stream);
+int moe_attention(const void* q, const void* kv_cache, const int32_t* lengths, int B, int P,
+                  int n_heads, int head_dim, int max_len, int max_keys, int dtype, void* o,
+                  void* ws, size_t ws_bytes, void* stream);
 int spec_commit(const int32_t* n_commit, int B, int32_t* lengths, void* stream);
 
 #ifdef __cplusplus

@@ -47,9 +47,9 @@ SIGNATURES = {
     "spec_plant_drafts": (_I, [_P, _P, _P, _I, _I, _I, _P, _P]),
     "spec_advance": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
     "spec_gather_rows": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
-    "moe_attn_rope_cache": (_I, [_P, _P, _I, _I, _I, _I, _F, _I, _I, _P, _P, _P, _P]),
+    "moe_attn_rope_cache": (_I, [_P, _P, _I, _I, _I, _I, _F, _I, _I, _P, _P, _P]),
     "moe_attention_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
-    "moe_attention": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
+    "moe_attention": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
     "spec_commit": (_I, [_P, _I, _P, _P]),
 }
 

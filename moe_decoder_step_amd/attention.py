@@ -32,8 +32,9 @@ class AttentionBlock:
     def __init__(self, w: dict, n_heads: int, max_seqs: int, P: int, max_len: int, eps: float = 1e-6,
                  rope_base: float = 10000.0):
         """w: w_qkv [3H, H], w_o [H, H] bf16 row-major (packed here).  Holds
-        this layer's cache [max_seqs, n_heads, max_len, 128] (k and v) and the
-        buffers of a pass of up to max_seqs * P tokens."""
+        this layer's cache kv [max_seqs, n_heads, max_len, 2, 128] (k then v
+        per position; cache_k and cache_v are views of it) and the buffers
+        of a pass of up to max_seqs * P tokens."""
         w_qkv, w_o = w["w_qkv"], w["w_o"]
         H = w_o.shape[0]
         if w_qkv.dtype != torch.bfloat16 or H != n_heads * HEAD_DIM or tuple(w_qkv.shape) != (3 * H, H):
@@ -44,8 +45,9 @@ class AttentionBlock:
         self.w_o = ops.pack_weights(w_o.reshape(1, H, H).contiguous(), L.PACK_ROWS)
         dev, dt = w_o.device, w_o.dtype
         T = max_seqs * P
-        self.cache_k = torch.zeros((max_seqs, n_heads, max_len, HEAD_DIM), dtype=dt, device=dev)
-        self.cache_v = torch.zeros_like(self.cache_k)
+        self.kv = ops.kv_cache_alloc(max_seqs, n_heads, max_len, dev, HEAD_DIM, dt)
+        self.cache_k = self.kv[:, :, :, 0]
+        self.cache_v = self.kv[:, :, :, 1]
         self.xa = torch.empty((T, H), dtype=dt, device=dev)
         self.qkv = torch.empty((T, 3 * H), dtype=dt, device=dev)
         self.q = torch.empty((T, H), dtype=dt, device=dev)
@@ -68,9 +70,8 @@ class AttentionBlock:
         off = self.offsets[T]
         ops.moe_rmsnorm(h, self.xa[:T], eps=self.eps)
         ops.moe_expert_down(self.xa[:T], off, self.w_qkv, self.qkv[:T], max_rows=T)
-        ops.moe_attn_rope_cache(self.qkv[:T], lengths, self.P, self.q[:T], self.cache_k[:B], self.cache_v[:B],
-                                self.rope_base)
-        ops.moe_attention(self.q[:T], self.cache_k[:B], self.cache_v[:B], lengths, self.P, self.o[:T], self.ws,
+        ops.moe_attn_rope_cache(self.qkv[:T], lengths, self.P, self.q[:T], self.kv[:B], self.rope_base)
+        ops.moe_attention(self.q[:T], self.kv[:B], lengths, self.P, self.o[:T], self.ws,
                           max_keys or self.max_len)
         ops.moe_expert_down(self.o[:T], off, self.w_o, self.f[:T], max_rows=T)
         if record is not None:

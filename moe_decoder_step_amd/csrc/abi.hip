@@ -172,12 +172,10 @@ int spec_gather_rows(const void* pool, const int32_t* seq_ids, const int32_t* st
 }
 
 int moe_attn_rope_cache(const void* qkv, const int32_t* lengths, int B, int P, int n_heads, int head_dim,
-                        float rope_base, int max_len, int dtype, void* q, void* cache_k, void* cache_v,
-                        void* stream) {
-  int st = moe::check_rope_cache(qkv, lengths, B, P, n_heads, head_dim, rope_base, max_len, dtype, q, cache_k,
-                                 cache_v);
+                        float rope_base, int max_len, int dtype, void* q, void* kv_cache, void* stream) {
+  int st = moe::check_rope_cache(qkv, lengths, B, P, n_heads, head_dim, rope_base, max_len, dtype, q, kv_cache);
   if (st != MOE_OK || B == 0) return st;
-  return hip_status(moe::launch_rope_cache(qkv, lengths, B, P, n_heads, rope_base, max_len, q, cache_k, cache_v,
+  return hip_status(moe::launch_rope_cache(qkv, lengths, B, P, n_heads, rope_base, max_len, q, kv_cache,
                                            as_stream(stream)));
 }
 
@@ -185,13 +183,13 @@ size_t moe_attention_workspace_bytes(int B, int P, int n_heads, int head_dim, in
   return moe::attention_ws_bytes(B, P, n_heads, head_dim, max_keys);
 }
 
-int moe_attention(const void* q, const void* cache_k, const void* cache_v, const int32_t* lengths, int B, int P,
-                  int n_heads, int head_dim, int max_len, int max_keys, int dtype, void* o, void* ws,
-                  size_t ws_bytes, void* stream) {
-  int st = moe::check_attention(q, cache_k, cache_v, lengths, B, P, n_heads, head_dim, max_len, max_keys, dtype, o);
+int moe_attention(const void* q, const void* kv_cache, const int32_t* lengths, int B, int P, int n_heads,
+                  int head_dim, int max_len, int max_keys, int dtype, void* o, void* ws, size_t ws_bytes,
+                  void* stream) {
+  int st = moe::check_attention(q, kv_cache, lengths, B, P, n_heads, head_dim, max_len, max_keys, dtype, o);
   if (st != MOE_OK || B == 0) return st;
   if (!ws || ws_bytes < moe::attention_ws_bytes(B, P, n_heads, head_dim, max_keys)) return MOE_ERR_WORKSPACE;
-  return hip_status(moe::launch_attention(q, cache_k, cache_v, lengths, B, P, n_heads, max_len, max_keys, o, ws,
+  return hip_status(moe::launch_attention(q, kv_cache, lengths, B, P, n_heads, max_len, max_keys, o, ws,
                                           as_stream(stream)));
 }
 

@@ -4,7 +4,7 @@
 // committed token, then the drafts).  Each layer:
 //   rope_cache_kernel  q, k <- rotary(q, k) at their positions (angle and
 //                      rotation in fp64, one rounding to bf16); k and v go
-//                      into the cache at [b][head][L_b + i][d];
+//                      into the cache at [b][head][L_b + i][0 / 1][d];
 //   attn_split_kernel  flash-decoding: block (b, head, split) scores its span
 //                      of cached keys for the P queries, with an online fp32
 //                      softmax, and writes (max, sum, unnormalised output);
@@ -14,6 +14,11 @@
 // Query i of sequence b sees keys 0 .. L_b + i: entries past that (drafts a
 // previous pass wrote and the verifier rejected) are never read, so rolling
 // back is only a matter of not advancing the length (spec_commit).
+//
+// The cache interleaves k and v per position (512 bytes: k then v), so a
+// tile of keys is one contiguous stream rather than two (measured in the
+// verify step at 2,241 positions x 32 sequences x 10 heads: 79.9 against
+// 82.9 us per layer with separate k and v caches).
 #include "common.hpp"
 #include "kernels.hpp"
 #include "validate.hpp"
@@ -28,8 +33,7 @@ constexpr int kRowPad = kD + 8;       // bf16 per LDS row (conflict-free column 
 __global__ __launch_bounds__(256) void rope_cache_kernel(const bf16_t* __restrict__ qkv,
                                                          const int32_t* __restrict__ lengths, int B, int P,
                                                          int n_heads, int max_len, double log_base,
-                                                         bf16_t* __restrict__ q, bf16_t* __restrict__ ck,
-                                                         bf16_t* __restrict__ cv) {
+                                                         bf16_t* __restrict__ q, bf16_t* __restrict__ kv) {
   // one thread per (token, head, rotation pair j < 64)
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const int half = kD / 2;
@@ -51,19 +55,19 @@ __global__ __launch_bounds__(256) void rope_cache_kernel(const bf16_t* __restric
   qo[j + half] = f64_to_bf16(q1 * s + q2 * c);
   // k (rotated) and v (as it is) into the cache
   const double k1 = bf(row[H + j]), k2 = bf(row[H + j + half]);
-  const size_t crow = (((size_t)b * n_heads + hd) * max_len + pos) * kD;
-  ck[crow + j] = f64_to_bf16(k1 * c - k2 * s);
-  ck[crow + j + half] = f64_to_bf16(k1 * s + k2 * c);
-  cv[crow + j] = row[2 * H + j];
-  cv[crow + j + half] = row[2 * H + j + half];
+  bf16_t* ck = kv + (((size_t)b * n_heads + hd) * max_len + pos) * (2 * kD);
+  bf16_t* cv = ck + kD;
+  ck[j] = f64_to_bf16(k1 * c - k2 * s);
+  ck[j + half] = f64_to_bf16(k1 * s + k2 * c);
+  cv[j] = row[2 * H + j];
+  cv[j + half] = row[2 * H + j + half];
 }
 
 // block (b, head, split): keys [k0, k1) of sequence b, all P queries (P <= 16);
 // wavefront w handles queries w, w+4, ...  Partials: ws[((b*nh + head)*nsplit
 // + split)*P + i] = {max, sum, out[128]} (fp32).
 __global__ __launch_bounds__(256) void attn_split_kernel(const bf16_t* __restrict__ q,
-                                                         const bf16_t* __restrict__ ck,
-                                                         const bf16_t* __restrict__ cv,
+                                                         const bf16_t* __restrict__ kv,
                                                          const int32_t* __restrict__ lengths, int P, int n_heads,
                                                          int max_len, int max_keys, int split_keys, int nsplit,
                                                          float scale, float* __restrict__ ws) {
@@ -103,8 +107,8 @@ __global__ __launch_bounds__(256) void attn_split_kernel(const bf16_t* __restric
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int key = t0 + min((threadIdx.x >> 4) + 16 * s, nk - 1);
-      kr[s] = ldg16(ck + (base + key) * kD + sg);
-      vr[s] = ldg16(cv + (base + key) * kD + sg);
+      kr[s] = ldg16(kv + (base + key) * (2 * kD) + sg);
+      vr[s] = ldg16(kv + (base + key) * (2 * kD) + kD + sg);
     }
   };
   if (k0 < k1) fetch(k0);
@@ -215,21 +219,21 @@ __global__ void commit_kernel(const int32_t* __restrict__ n_commit, int B, int32
 }  // namespace
 
 hipError_t launch_rope_cache(const void* qkv, const int32_t* lengths, int B, int P, int n_heads, float rope_base,
-                             int max_len, void* q, void* cache_k, void* cache_v, hipStream_t s) {
+                             int max_len, void* q, void* kv_cache, hipStream_t s) {
   const long long n = (long long)B * P * n_heads * (kD / 2);
   hipLaunchKernelGGL(rope_cache_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                      static_cast<const bf16_t*>(qkv), lengths, B, P, n_heads, max_len, log((double)rope_base),
-                     static_cast<bf16_t*>(q), static_cast<bf16_t*>(cache_k), static_cast<bf16_t*>(cache_v));
+                     static_cast<bf16_t*>(q), static_cast<bf16_t*>(kv_cache));
   return hipGetLastError();
 }
 
-hipError_t launch_attention(const void* q, const void* cache_k, const void* cache_v, const int32_t* lengths, int B,
-                            int P, int n_heads, int max_len, int max_keys, void* o, void* ws, hipStream_t s) {
+hipError_t launch_attention(const void* q, const void* kv_cache, const int32_t* lengths, int B, int P, int n_heads,
+                            int max_len, int max_keys, void* o, void* ws, hipStream_t s) {
   const int sk = attn_split_keys(max_keys);
   const int nsplit = (max_keys + sk - 1) / sk;
   float* w = static_cast<float*>(ws);
   hipLaunchKernelGGL(attn_split_kernel, dim3(B * n_heads * nsplit), dim3(256), 0, s, static_cast<const bf16_t*>(q),
-                     static_cast<const bf16_t*>(cache_k), static_cast<const bf16_t*>(cache_v), lengths, P, n_heads,
+                     static_cast<const bf16_t*>(kv_cache), lengths, P, n_heads,
                      max_len, max_keys, sk, nsplit, 1.0f / sqrtf((float)kD), w);
   const int waves = B * n_heads * P;
   hipLaunchKernelGGL(attn_merge_kernel, dim3((waves + 3) / 4), dim3(256), 0, s, w, B, P, n_heads, nsplit,

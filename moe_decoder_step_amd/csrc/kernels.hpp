@@ -74,9 +74,9 @@ hipError_t launch_gather_rows(const void* pool, const int32_t* seq_ids, const in
                               int S, int row_bytes, void* out, hipStream_t s);
 
 hipError_t launch_rope_cache(const void* qkv, const int32_t* lengths, int B, int P, int n_heads, float rope_base,
-                             int max_len, void* q, void* cache_k, void* cache_v, hipStream_t s);
-hipError_t launch_attention(const void* q, const void* cache_k, const void* cache_v, const int32_t* lengths, int B,
-                            int P, int n_heads, int max_len, int max_keys, void* o, void* ws, hipStream_t s);
+                             int max_len, void* q, void* kv_cache, hipStream_t s);
+hipError_t launch_attention(const void* q, const void* kv_cache, const int32_t* lengths, int B, int P, int n_heads,
+                            int max_len, int max_keys, void* o, void* ws, hipStream_t s);
 hipError_t launch_commit(const int32_t* n_commit, int B, int32_t* lengths, hipStream_t s);
 
 }  // namespace moe

@@ -119,13 +119,13 @@ int attn_split_keys(int max_keys) {
 }
 
 int check_rope_cache(const void* qkv, const int32_t* lengths, int B, int P, int n_heads, int head_dim, float rope_base,
-                     int max_len, int dtype, const void* q, const void* cache_k, const void* cache_v) {
+                     int max_len, int dtype, const void* q, const void* kv_cache) {
   if (!valid_dtype(dtype)) return kErrUnsupported;
   if (B < 0 || P <= 0 || n_heads <= 0 || max_len < P || !(rope_base > 1.f)) return kErrShape;
   if (dtype != kBf16 || head_dim != kAttnHeadDim || P > kMaxAttnP) return kErrUnsupported;
   if ((long long)B * n_heads * max_len * head_dim > (1LL << 40)) return kErrUnsupported;
   if (B == 0) return kOk;
-  if (!qkv || !lengths || !q || !cache_k || !cache_v) return kErrNull;
+  if (!qkv || !lengths || !q || !kv_cache) return kErrNull;
   return kOk;
 }
 
@@ -136,15 +136,15 @@ int check_commit(const int32_t* n_commit, int B, const int32_t* lengths) {
   return kOk;
 }
 
-int check_attention(const void* q, const void* cache_k, const void* cache_v, const int32_t* lengths, int B, int P,
-                    int n_heads, int head_dim, int max_len, int max_keys, int dtype, const void* o) {
+int check_attention(const void* q, const void* kv_cache, const int32_t* lengths, int B, int P, int n_heads,
+                    int head_dim, int max_len, int max_keys, int dtype, const void* o) {
   if (!valid_dtype(dtype)) return kErrUnsupported;
   if (B < 0 || P <= 0 || n_heads <= 0 || max_len < P || max_keys < P || max_keys > max_len) return kErrShape;
   if (dtype != kBf16 || head_dim != kAttnHeadDim || P > kMaxAttnP) return kErrUnsupported;
   if ((long long)B * n_heads * max_len * head_dim > (1LL << 40)) return kErrUnsupported;
   if (B == 0) return kOk;
-  if (!q || !cache_k || !cache_v || !lengths || !o) return kErrNull;
-  if (!aligned16(cache_k) || !aligned16(cache_v)) return kErrAlign;
+  if (!q || !kv_cache || !lengths || !o) return kErrNull;
+  if (!aligned16(kv_cache)) return kErrAlign;
   return kOk;
 }
 

@@ -43,10 +43,10 @@ int check_rmsnorm(const void* x, const int32_t* rows, int x_rows, int T, int H, 
                   int out_stride);
 int attn_split_keys(int max_keys);
 int check_rope_cache(const void* qkv, const int32_t* lengths, int B, int P, int n_heads, int head_dim, float rope_base,
-                     int max_len, int dtype, const void* q, const void* cache_k, const void* cache_v);
+                     int max_len, int dtype, const void* q, const void* kv_cache);
 int check_commit(const int32_t* n_commit, int B, const int32_t* lengths);
-int check_attention(const void* q, const void* cache_k, const void* cache_v, const int32_t* lengths, int B, int P,
-                    int n_heads, int head_dim, int max_len, int max_keys, int dtype, const void* o);
+int check_attention(const void* q, const void* kv_cache, const int32_t* lengths, int B, int P, int n_heads,
+                    int head_dim, int max_len, int max_keys, int dtype, const void* o);
 size_t attention_ws_bytes(int B, int P, int n_heads, int head_dim, int max_keys);
 int check_route(const void* h, const float* w_router, int T, int H, int E, int k, int dtype,
                 const void* xn, const int32_t* ids, const float* w);

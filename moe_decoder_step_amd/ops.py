@@ -17,7 +17,7 @@ from . import _lib as L
 __all__ = [
     "Packed", "pack_weights", "packed_weights_bytes", "moe_route", "moe_rmsnorm", "moe_combine_route", "moe_permute", "moe_grouped_swiglu", "moe_combine", "lmhead_argmax",
     "moe_expert_gate_up", "moe_expert_gate_up_routed", "moe_expert_down", "ROUTED_MAX_PAIRS", "spec_verify", "spec_plant_drafts", "spec_advance",
-    "spec_gather_rows", "moe_attn_rope_cache", "moe_attention", "attention_workspace_bytes", "spec_commit",
+    "spec_gather_rows", "moe_attn_rope_cache", "moe_attention", "attention_workspace_bytes", "kv_cache_alloc", "spec_commit",
     "permute_workspace_bytes", "swiglu_workspace_bytes",
     "lmhead_workspace_bytes", "dtype_code", "expert_weights", "lm_weights", "router_weights", "route_alloc", "permute_alloc", "swiglu_alloc",
     "combine_alloc", "lmhead_alloc", "verify_alloc",
@@ -337,46 +337,51 @@ def spec_gather_rows(pool, seq_ids, steps, out):
         _p(pool), _p(seq_ids), _p(steps), B, R, J, S, row_bytes, _p(out), _stream(out)))
 
 
-def _cache_shape(cache_k, cache_v, B):
-    if cache_k.dim() != 4 or cache_k.shape != cache_v.shape or cache_k.shape[0] < B:
-        raise ValueError("caches must be [B, n_heads, max_len, head_dim], k and v alike")
-    return cache_k.shape[1], cache_k.shape[2], cache_k.shape[3]
+def _cache_shape(kv, B):
+    if kv.dim() != 5 or kv.shape[0] < B or kv.shape[3] != 2:
+        raise ValueError("the KV cache must be [B, n_heads, max_len, 2, head_dim] (k then v per position)")
+    return kv.shape[1], kv.shape[2], kv.shape[4]
 
 
-def moe_attn_rope_cache(qkv, lengths, P, q, cache_k, cache_v, rope_base=10000.0):
-    """q <- rope(q); rope(k) and v into the caches at positions lengths[b] + i
+def kv_cache_alloc(B: int, n_heads: int, max_len: int, device, head_dim: int = 128, dtype=torch.bfloat16):
+    """A zeroed KV cache [B, n_heads, max_len, 2, head_dim]."""
+    return torch.zeros((B, n_heads, max_len, 2, head_dim), dtype=dtype, device=device)
+
+
+def moe_attn_rope_cache(qkv, lengths, P, q, kv, rope_base=10000.0):
+    """q <- rope(q); rope(k) and v into the cache at positions lengths[b] + i
     for the B*P verify tokens of qkv [B*P, 3H]."""
     B = lengths.shape[0]
-    n_heads, max_len, d = _cache_shape(cache_k, cache_v, B)
+    n_heads, max_len, d = _cache_shape(kv, B)
     for t, dt, n in ((qkv, None, "qkv"), (lengths, torch.int32, "lengths"), (q, qkv.dtype, "q"),
-                     (cache_k, qkv.dtype, "cache_k"), (cache_v, qkv.dtype, "cache_v")):
+                     (kv, qkv.dtype, "kv")):
         _need(t, dt, n)
     if qkv.shape != (B * P, 3 * n_heads * d) or q.shape != (B * P, n_heads * d):
         raise ValueError("qkv must be [B*P, 3H] and q [B*P, H]")
     L.check("moe_attn_rope_cache", L.load().moe_attn_rope_cache(
-        _p(qkv), _p(lengths), B, int(P), n_heads, d, float(rope_base), max_len, dtype_code(qkv), _p(q),
-        _p(cache_k), _p(cache_v), _stream(q)))
+        _p(qkv), _p(lengths), B, int(P), n_heads, d, float(rope_base), max_len, dtype_code(qkv), _p(q), _p(kv),
+        _stream(q)))
 
 
 def attention_workspace_bytes(B: int, P: int, n_heads: int, max_keys: int, head_dim: int = 128) -> int:
     return int(L.load().moe_attention_workspace_bytes(B, P, n_heads, head_dim, max_keys))
 
 
-def moe_attention(q, cache_k, cache_v, lengths, P, o, ws, max_keys=None):
+def moe_attention(q, kv, lengths, P, o, ws, max_keys=None):
     """o = causal softmax attention of the B*P queries over the cached keys
     0 .. lengths[b] + i (max_keys bounds lengths[b] + P; default max_len)."""
     B = lengths.shape[0]
-    n_heads, max_len, d = _cache_shape(cache_k, cache_v, B)
+    n_heads, max_len, d = _cache_shape(kv, B)
     max_keys = max_len if max_keys is None else int(max_keys)
-    for t, dt, n in ((q, None, "q"), (cache_k, q.dtype, "cache_k"), (cache_v, q.dtype, "cache_v"),
-                     (lengths, torch.int32, "lengths"), (o, q.dtype, "o"), (ws, None, "ws")):
+    for t, dt, n in ((q, None, "q"), (kv, q.dtype, "kv"), (lengths, torch.int32, "lengths"), (o, q.dtype, "o"),
+                     (ws, None, "ws")):
         _need(t, dt, n)
     if q.shape != (B * P, n_heads * d) or o.shape != q.shape:
         raise ValueError("q and o must be [B*P, H]")
     nbytes = ws.numel() * ws.element_size()
     L.check("moe_attention", L.load().moe_attention(
-        _p(q), _p(cache_k), _p(cache_v), _p(lengths), B, int(P), n_heads, d, max_len, max_keys, dtype_code(q),
-        _p(o), _p(ws), nbytes, _stream(q)))
+        _p(q), _p(kv), _p(lengths), B, int(P), n_heads, d, max_len, max_keys, dtype_code(q), _p(o), _p(ws),
+        nbytes, _stream(q)))
 
 
 def spec_commit(n_commit, lengths):

@@ -198,23 +198,23 @@ def test_attention_checks(lib):
     assert ws(32, 4, 10, 128, 2048) == 32 * 10 * 8 * 4 * 130 * 4
     assert ws(1, 4, 10, 128, 32768) == 10 * 64 * 4 * 130 * 4          # 512 keys per split
     assert ws(0, 4, 10, 128, 2048) == 0
-    # qkv, lengths, B, P, n_heads, head_dim, base, max_len, dtype, q, ck, cv, stream
-    assert rope(A, A, 2, 4, 10, 128, 1e4, 64, m.BF16, A, A, None, None) == L.ERR_NULL
-    assert rope(A, A, 2, 4, 10, 64, 1e4, 64, m.BF16, A, A, A, None) == L.ERR_UNSUPPORTED    # head size 128
-    assert rope(A, A, 2, 17, 10, 128, 1e4, 64, m.BF16, A, A, A, None) == L.ERR_UNSUPPORTED  # P <= 16
-    assert rope(A, A, 2, 4, 10, 128, 1e4, 64, m.F32, A, A, A, None) == L.ERR_UNSUPPORTED
-    assert rope(A, A, 2, 4, 10, 128, 1e4, 3, m.BF16, A, A, A, None) == L.ERR_SHAPE           # max_len < P
-    assert rope(A, A, 2, 4, 10, 128, 1.0, 64, m.BF16, A, A, A, None) == L.ERR_SHAPE
-    assert rope(None, None, 0, 4, 10, 128, 1e4, 64, m.BF16, None, None, None, None) == L.OK
-    # q, ck, cv, lengths, B, P, n_heads, head_dim, max_len, max_keys, dtype, o, ws, ws_bytes, stream
+    # qkv, lengths, B, P, n_heads, head_dim, base, max_len, dtype, q, kv, stream
+    assert rope(A, A, 2, 4, 10, 128, 1e4, 64, m.BF16, A, None, None) == L.ERR_NULL
+    assert rope(A, A, 2, 4, 10, 64, 1e4, 64, m.BF16, A, A, None) == L.ERR_UNSUPPORTED    # head size 128
+    assert rope(A, A, 2, 17, 10, 128, 1e4, 64, m.BF16, A, A, None) == L.ERR_UNSUPPORTED  # P <= 16
+    assert rope(A, A, 2, 4, 10, 128, 1e4, 64, m.F32, A, A, None) == L.ERR_UNSUPPORTED
+    assert rope(A, A, 2, 4, 10, 128, 1e4, 3, m.BF16, A, A, None) == L.ERR_SHAPE           # max_len < P
+    assert rope(A, A, 2, 4, 10, 128, 1.0, 64, m.BF16, A, A, None) == L.ERR_SHAPE
+    assert rope(None, None, 0, 4, 10, 128, 1e4, 64, m.BF16, None, None, None) == L.OK
+    # q, kv, lengths, B, P, n_heads, head_dim, max_len, max_keys, dtype, o, ws, ws_bytes, stream
     need = ws(2, 4, 10, 128, 64)
-    assert att(A, A, A, A, 2, 4, 10, 128, 64, 64, m.BF16, A, A, need - 1, None) == L.ERR_WORKSPACE
-    assert att(A, A, A, A, 2, 4, 10, 128, 64, 64, m.BF16, A, None, need, None) == L.ERR_WORKSPACE
-    assert att(A, MIS, A, A, 2, 4, 10, 128, 64, 64, m.BF16, A, A, need, None) == L.ERR_ALIGN
-    assert att(A, A, A, A, 2, 4, 10, 128, 64, 65, m.BF16, A, A, need, None) == L.ERR_SHAPE  # max_keys > max_len
-    assert att(A, A, A, A, 2, 4, 10, 128, 64, 3, m.BF16, A, A, need, None) == L.ERR_SHAPE   # max_keys < P
-    assert att(A, A, A, None, 2, 4, 10, 128, 64, 64, m.BF16, A, A, need, None) == L.ERR_NULL
-    assert att(None, None, None, None, 0, 4, 10, 128, 64, 64, m.BF16, None, None, 0, None) == L.OK
+    assert att(A, A, A, 2, 4, 10, 128, 64, 64, m.BF16, A, A, need - 1, None) == L.ERR_WORKSPACE
+    assert att(A, A, A, 2, 4, 10, 128, 64, 64, m.BF16, A, None, need, None) == L.ERR_WORKSPACE
+    assert att(A, MIS, A, 2, 4, 10, 128, 64, 64, m.BF16, A, A, need, None) == L.ERR_ALIGN
+    assert att(A, A, A, 2, 4, 10, 128, 64, 65, m.BF16, A, A, need, None) == L.ERR_SHAPE  # max_keys > max_len
+    assert att(A, A, A, 2, 4, 10, 128, 64, 3, m.BF16, A, A, need, None) == L.ERR_SHAPE   # max_keys < P
+    assert att(A, A, None, 2, 4, 10, 128, 64, 64, m.BF16, A, A, need, None) == L.ERR_NULL
+    assert att(None, None, None, 0, 4, 10, 128, 64, 64, m.BF16, None, None, 0, None) == L.OK
     assert com(A, -1, A, None) == L.ERR_SHAPE
     assert com(None, 4, A, None) == L.ERR_NULL
     assert com(None, 0, None, None) == L.OK

@@ -32,25 +32,24 @@ def m():
 
 
 def _caches(seed, B, nh, max_len, lengths, P):
-    """A committed prefix below each length, NaN from length + P on."""
-    ck = synth.kv_prefix(seed, 0, (B, nh, max_len, D), torch.bfloat16, DEV, "k")
-    cv = synth.kv_prefix(seed, 0, (B, nh, max_len, D), torch.bfloat16, DEV, "v")
+    """A committed prefix below each length, NaN from length + P on; the
+    interleaved cache and its k and v views."""
+    kv = synth.kv_prefix(seed, 0, (B, nh, max_len, 2, D), torch.bfloat16, DEV, "kv")
     for b, L in enumerate(lengths):
-        ck[b, :, L + P:] = float("nan")
-        cv[b, :, L + P:] = float("nan")
-    return ck, cv
+        kv[b, :, L + P:] = float("nan")
+    return kv, kv[:, :, :, 0], kv[:, :, :, 1]
 
 
-def _run(m, qkv, lengths, P, nh, ck, cv, max_keys=None):
+def _run(m, qkv, lengths, P, nh, kv, max_keys=None):
     T = qkv.shape[0]
     B = len(lengths)
     lt = torch.tensor(lengths, dtype=torch.int32, device=DEV)
     q = torch.empty((T, nh * D), dtype=torch.bfloat16, device=DEV)
     o = torch.empty_like(q)
-    mk = max_keys or ck.shape[2]
+    mk = max_keys or kv.shape[2]
     ws = torch.empty(max(m.attention_workspace_bytes(B, P, nh, mk), 256), dtype=torch.uint8, device=DEV)
-    m.moe_attn_rope_cache(qkv, lt, P, q, ck, cv)
-    m.moe_attention(q, ck, cv, lt, P, o, ws, mk)
+    m.moe_attn_rope_cache(qkv, lt, P, q, kv)
+    m.moe_attention(q, kv, lt, P, o, ws, mk)
     torch.cuda.synchronize()
     return q, o
 
@@ -65,9 +64,9 @@ def test_rope_cache_bit_exact_and_attention(m, P, lengths, max_len):
     H = nh * D
     B = len(lengths)
     qkv = synth.normal(1, (B * P, 3 * H), 1.0, torch.bfloat16, DEV)
-    ck, cv = _caches(2, B, nh, max_len, lengths, P)
+    kv, ck, cv = _caches(2, B, nh, max_len, lengths, P)
     ck0, cv0 = host(ck), host(cv)
-    q, o = _run(m, qkv, lengths, P, nh, ck, cv)
+    q, o = _run(m, qkv, lengths, P, nh, kv)
     # rotation and cache write against the oracle, bit for bit; no other row changes
     rk, rv = O.f64(ck0), O.f64(cv0)
     rq, _, _ = O.rope_cache(host(qkv), lengths, P, nh, rk, rv, "bf16")
@@ -86,8 +85,8 @@ def test_attention_32768_positions(m):
     nh, P, max_len = 10, 4, 32768
     lengths = [max_len - P]
     qkv = synth.normal(3, (P, 3 * nh * D), 1.0, torch.bfloat16, DEV)
-    ck, cv = _caches(4, 1, nh, max_len, lengths, P)
-    q, o = _run(m, qkv, lengths, P, nh, ck, cv)
+    kv, ck, cv = _caches(4, 1, nh, max_len, lengths, P)
+    q, o = _run(m, qkv, lengths, P, nh, kv)
     ref = O.causal_attention(host(q).reshape(P, nh, D), host(ck), host(cv), lengths, P)
     assert_close(as_f64(o), ref.reshape(P, nh * D), BF16_TOL, "attention output at 32,768 positions")
 
@@ -100,8 +99,8 @@ def test_tighter_key_bound_same_result_within_tolerance(m):
     qkv = synth.normal(5, (len(lengths) * P, 3 * nh * D), 1.0, torch.bfloat16, DEV)
     outs = []
     for mk in (1024, None):
-        ck, cv = _caches(6, len(lengths), nh, max_len, lengths, P)
-        q, o = _run(m, qkv, lengths, P, nh, ck, cv, mk)
+        kv, ck, cv = _caches(6, len(lengths), nh, max_len, lengths, P)
+        q, o = _run(m, qkv, lengths, P, nh, kv, mk)
         ref = O.causal_attention(host(q).reshape(-1, nh, D), host(ck), host(cv), lengths, P)
         assert_close(as_f64(o), ref.reshape(-1, nh * D), BF16_TOL, f"max_keys {mk}")
         outs.append(o)
