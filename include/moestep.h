@@ -228,6 +228,17 @@ int moe_expert_gate_up_routed(const void* x, const int32_t* topk_ids, int T, int
 int moe_expert_down(const void* act, const int32_t* offsets, int G, int n_rows,
                     const void* w_down, int H, int I, int max_rows, int dtype,
                     void* y, void* stream);
+/* moe_expert_down_residual -- moe_expert_down with a residual added in the
+ * epilogue: y[r] = residual[r] + round(W_d[g] act[r]), the product rounded to
+ * dtype first and the sum rounded once (the same bits as moe_expert_down
+ * followed by moe_combine with y as its one shared row and k = 0).  For the
+ * dense layers around the MoE blocks (the attention output projection, the
+ * draft block's FFN).  residual [n_rows, H] dtype, 16-byte aligned; it may
+ * be y itself (in place).  Errors as moe_expert_down, plus MOE_ERR_NULL for
+ * a NULL residual. */
+int moe_expert_down_residual(const void* act, const int32_t* offsets, int G, int n_rows,
+                             const void* w_down, int H, int I, int max_rows, int dtype,
+                             const void* residual, void* y, void* stream);
 
 /* ---------------------------------------------------------------------------
  * moe_combine -- weighted sum of the expert outputs plus the residual.
@@ -250,6 +261,20 @@ int moe_combine(const void* y, const int32_t* inv, const float* topk_w,
                 const void* y_shared, int S, const void* residual,
                 int T, int H, int k, int n_rows, int dtype,
                 void* out, void* combined, void* stream);
+
+/* moe_combine_rmsnorm -- moe_combine (combined = NULL) followed by the
+ * RMSNorm of each output row, in one launch: xn[t] = out[t] /
+ * sqrt(mean(out[t]^2) + eps) (* gain), normalised from the stored (rounded)
+ * out row, with the same bits as moe_combine then moe_rmsnorm.  For the
+ * block that follows a combine and starts with a norm (the attention of the
+ * next layer, the final norm before the LM head).  Arguments as moe_combine,
+ * plus gain [H] fp32 or NULL and xn [T, H] dtype (16-byte aligned, distinct
+ * from out and residual; MOE_ERR_SHAPE otherwise).  out == residual is
+ * allowed.  Limits: H % 8 == 0, H <= 2048, 0 <= k <= 64. */
+int moe_combine_rmsnorm(const void* y, const int32_t* inv, const float* topk_w,
+                        const void* y_shared, int S, const void* residual,
+                        int T, int H, int k, int n_rows, const float* gain, float eps,
+                        int dtype, void* out, void* xn, void* stream);
 
 /* ---------------------------------------------------------------------------
  * moe_rmsnorm -- RMSNorm of rows: out[t] = x[r] / sqrt(mean(x[r]^2) + eps)

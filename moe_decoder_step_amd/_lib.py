@@ -38,7 +38,9 @@ SIGNATURES = {
     "moe_expert_gate_up": (_I, [_P, _P, _P, _I, _I, _P, _I, _I, _I, _I, _I, _P, _P]),
     "moe_expert_gate_up_routed": (_I, [_P, _P, _I, _I, _I, _I, _P, _I, _I, _I, _P, _P, _P, _P]),
     "moe_expert_down": (_I, [_P, _P, _I, _I, _P, _I, _I, _I, _I, _P, _P]),
+    "moe_expert_down_residual": (_I, [_P, _P, _I, _I, _P, _I, _I, _I, _I, _P, _P, _P]),
     "moe_combine": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _P, _P, _P]),
+    "moe_combine_rmsnorm": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _P, _F, _I, _P, _P, _P]),
     "moe_rmsnorm": (_I, [_P, _P, _I, _I, _I, _P, _F, _I, _P, _I, _P]),
     "moe_combine_route": (_I, [_P, _P, _P, _P, _I, _I, _I, _P, _I, _I, _P, _F, _P, _P, _I, _I, _I, _I,
                                _P, _P, _P, _P, _P]),

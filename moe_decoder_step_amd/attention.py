@@ -6,11 +6,12 @@ model card "jina-ocr-v1", architecture paragraph) but not its attention.
 The reading is pre-norm multi-head attention with rotary positions and
 heads of 128:
 
-    xa = rmsnorm(h)                         moe_rmsnorm
+    xa = rmsnorm(h)                         moe_rmsnorm (or the previous block's
+                                            moe_combine_rmsnorm)
     qkv = xa W_qkv^T                        moe_expert_down, one group (H -> 3H)
     q, cache[L_b + i] <- rope(q), rope(k), v    moe_attn_rope_cache
     o = causal softmax(q k^T / sqrt(128)) v  moe_attention (split over keys + merge)
-    h <- h + o W_o^T                        moe_expert_down + moe_combine (residual)
+    h <- h + o W_o^T                        moe_expert_down_residual
 
 A pass of sequence b holds P positions at L_b .. L_b + P - 1 (its last
 committed token, then the drafts).  Query i reads cache rows 0 .. L_b + i
@@ -52,29 +53,29 @@ class AttentionBlock:
         self.qkv = torch.empty((T, 3 * H), dtype=dt, device=dev)
         self.q = torch.empty((T, H), dtype=dt, device=dev)
         self.o = torch.empty((T, H), dtype=dt, device=dev)
-        self.f = torch.empty((T, H), dtype=dt, device=dev)
         nb = ops.attention_workspace_bytes(max_seqs, P, n_heads, max_len)
         self.ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
         self.offsets = torch.stack([torch.zeros(T + 1, dtype=torch.int32),
                                     torch.arange(T + 1, dtype=torch.int32)], 1).to(dev)
-        self.no_w = torch.empty((T, 0), dtype=torch.float32, device=dev)
 
     def forward(self, h: torch.Tensor, lengths: torch.Tensor, max_keys: int | None = None,
-                record: dict | None = None) -> None:
+                record: dict | None = None, normed: bool = False) -> None:
         """In place on h [B*P, H] (sequence-major); lengths [B] int32 device.
-        max_keys bounds lengths[b] + P (default: the cache length)."""
+        max_keys bounds lengths[b] + P (default: the cache length).  normed:
+        self.xa[:T] already holds RMSNorm(h) (written by the caller's
+        moe_combine_rmsnorm), so the norm is not run again."""
         T = h.shape[0]
         B = lengths.shape[0]
         if T != B * self.P:
             raise ValueError(f"h has {T} rows, expected {B} sequences x {self.P} positions")
         off = self.offsets[T]
-        ops.moe_rmsnorm(h, self.xa[:T], eps=self.eps)
+        if not normed:
+            ops.moe_rmsnorm(h, self.xa[:T], eps=self.eps)
         ops.moe_expert_down(self.xa[:T], off, self.w_qkv, self.qkv[:T], max_rows=T)
         ops.moe_attn_rope_cache(self.qkv[:T], lengths, self.P, self.q[:T], self.kv[:B], self.rope_base)
         ops.moe_attention(self.q[:T], self.kv[:B], lengths, self.P, self.o[:T], self.ws,
                           max_keys or self.max_len)
-        ops.moe_expert_down(self.o[:T], off, self.w_o, self.f[:T], max_rows=T)
         if record is not None:
             record.update({"attn_input": h.clone(), "qkv": self.qkv[:T].clone(), "q": self.q[:T].clone(),
                            "o": self.o[:T].clone()})
-        ops.moe_combine(None, None, self.no_w[:T], self.f[:T], 1, h, h)
+        ops.moe_expert_down_residual(self.o[:T], off, self.w_o, h, h, max_rows=T)

@@ -102,6 +102,14 @@ int moe_expert_down(const void* act, const int32_t* offsets, int G, int n_rows, 
   return hip_status(moe::launch_down(act, offsets, G, n_rows, w_down, H, I, max_rows, dtype, y, as_stream(stream)));
 }
 
+int moe_expert_down_residual(const void* act, const int32_t* offsets, int G, int n_rows, const void* w_down, int H,
+                             int I, int max_rows, int dtype, const void* residual, void* y, void* stream) {
+  int st = moe::check_down_residual(act, offsets, G, n_rows, w_down, H, I, max_rows, dtype, residual, y);
+  if (st != MOE_OK || n_rows == 0) return st;
+  return hip_status(moe::launch_down(act, offsets, G, n_rows, w_down, H, I, max_rows, dtype, y, as_stream(stream),
+                                     residual));
+}
+
 int moe_combine(const void* y, const int32_t* inv, const float* topk_w, const void* y_shared, int S,
                 const void* residual, int T, int H, int k, int n_rows, int dtype, void* out, void* combined,
                 void* stream) {
@@ -109,6 +117,15 @@ int moe_combine(const void* y, const int32_t* inv, const float* topk_w, const vo
   if (st != MOE_OK || T == 0) return st;
   return hip_status(moe::launch_combine(y, inv, topk_w, y_shared, S, residual, T, H, k, n_rows, dtype, out,
                                         combined, as_stream(stream)));
+}
+
+int moe_combine_rmsnorm(const void* y, const int32_t* inv, const float* topk_w, const void* y_shared, int S,
+                        const void* residual, int T, int H, int k, int n_rows, const float* gain, float eps,
+                        int dtype, void* out, void* xn, void* stream) {
+  int st = moe::check_combine_norm(y, inv, topk_w, y_shared, S, residual, T, H, k, n_rows, dtype, out, xn);
+  if (st != MOE_OK || T == 0) return st;
+  return hip_status(moe::launch_combine_norm(y, inv, topk_w, y_shared, S, residual, T, H, k, n_rows, gain, eps,
+                                             dtype, out, xn, as_stream(stream)));
 }
 
 int lmhead_argmax(const void* h, const void* w_lm, int T, int H, int V, int dtype, int32_t* argmax_ids,

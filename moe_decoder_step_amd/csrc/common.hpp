@@ -37,6 +37,29 @@ __device__ __forceinline__ bf16_t f64_to_bf16(double d) {
   return (bf16_t)(__float_as_uint(f) >> 16);
 }
 
+// RMSNorm pieces shared by every kernel that normalises rows (route, the
+// plain row norm, the fused combine + norm), so a row normalises to the same
+// bits in all of them: the sum of squares in fp64 per 8-element segment, in
+// order; the scale applied in fp64 with one rounding to the storage type.
+__device__ __forceinline__ double seg_sumsq(const float* f) {
+  double s = 0.0;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) s += (double)f[q] * (double)f[q];
+  return s;
+}
+__device__ __forceinline__ bf16_t round_store(double v, bf16_t*) { return f64_to_bf16(v); }
+__device__ __forceinline__ float round_store(double v, float*) { return (float)v; }
+// xn = f * scale (* gain[c+q]) in fp64, one rounding to the storage type
+template <typename St>
+__device__ __forceinline__ void norm8(const float* f, double scale, const float* gain, int c, St* o) {
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    double v = (double)f[q] * scale;
+    if (gain) v *= (double)gain[c + q];
+    o[q] = round_store(v, (St*)nullptr);
+  }
+}
+
 // Unpack 8 bf16 (one 16-byte vector) into fp32.
 __device__ __forceinline__ void unpack8(const uint4& v, float* f) {
   f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xffff0000u);

@@ -51,8 +51,11 @@ bool gemm_path_ok(int K, int N, int max_rows);
 hipError_t launch_gemm(bool gated, const void* x, const int32_t* gather, const int32_t* offsets, int G, int n_rows,
                        int T, const void* W, int K, int N, void* out, hipStream_t s);
 hipError_t launch_down(const void* act, const int32_t* offsets, int G, int n_rows, const void* w_down, int H,
-                       int I, int max_rows, int dtype, void* y, hipStream_t s);
+                       int I, int max_rows, int dtype, void* y, hipStream_t s, const void* residual = nullptr);
 
+hipError_t launch_combine_norm(const void* y, const int32_t* inv, const float* topk_w, const void* y_shared, int S,
+                               const void* residual, int T, int H, int k, int n_rows, const float* gain, float eps,
+                               int dtype, void* out, void* xn, hipStream_t s);
 hipError_t launch_combine(const void* y, const int32_t* inv, const float* topk_w,
                           const void* y_shared, int S, const void* residual, int T, int H, int k,
                           int n_rows, int dtype, void* out, void* combined, hipStream_t s);

@@ -58,29 +58,8 @@ __device__ __forceinline__ void store8(float* p, const bf16_t* v) {
   for (int j = 0; j < 8; ++j) f[j] = __uint_as_float((uint32_t)v[j] << 16);
   store8(p, f);
 }
-// sum of squares of 8 values in fp64, in order
-__device__ __forceinline__ double seg_sumsq(const float* f) {
-  double s = 0.0;
-#pragma unroll
-  for (int q = 0; q < 8; ++q) s += (double)f[q] * (double)f[q];
-  return s;
-}
-__device__ __forceinline__ bf16_t round_store(double v, bf16_t*);
-__device__ __forceinline__ float round_store(double v, float*);
-// xn = f * scale (* gain[c+q]) in fp64, one rounding to the storage type
-template <typename St>
-__device__ __forceinline__ void norm8(const float* f, double scale, const float* gain, int c, St* o) {
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    double v = (double)f[q] * scale;
-    if (gain) v *= (double)gain[c + q];
-    o[q] = round_store(v, (St*)nullptr);
-  }
-}
 __device__ __forceinline__ bf16_t to_store(float v, bf16_t*) { return f32_to_bf16(v); }
 __device__ __forceinline__ float to_store(float v, float*) { return v; }
-__device__ __forceinline__ bf16_t round_store(double v, bf16_t*) { return f64_to_bf16(v); }
-__device__ __forceinline__ float round_store(double v, float*) { return (float)v; }
 
 // four consecutive normed values of a token from LDS
 __device__ __forceinline__ float4 lds4(const bf16_t* p) {

@@ -118,7 +118,7 @@ template <bool GATED, bool ROUTED>
 __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
     const bf16_t* __restrict__ x, const int32_t* __restrict__ gather,
     const int32_t* __restrict__ offsets, int G, int n_rows, int T,
-    const bf16_t* __restrict__ W, int K, int N, int n_ctiles, int ks_log2, bf16_t* __restrict__ out,
+    const bf16_t* __restrict__ W, int K, int N, int n_ctiles, int ks_log2, bf16_t* out, const bf16_t* res,
     RoutedArgs rt) {
   static_assert(!ROUTED || GATED, "only the gate/up stage derives its rows from the expert ids");
   constexpr int D = 3;                    // k-steps of weights in flight per wavefront
@@ -325,6 +325,21 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
           pk.y = pack2(f32_to_bf16(silu(acc_a[2]) * acc_b[2]), f32_to_bf16(silu(acc_a[3]) * acc_b[3]));
           *reinterpret_cast<uint2*>(orow) = pk;
         } else {
+          if (res) {
+            // out = residual + y: y rounded to bf16 first, then the fp32 sum
+            // rounded once (the same bits as moe_combine adding y as a shared row)
+            const bf16_t* rrow = res + (size_t)(mstart + row) * N + col0 + 4 * (lane >> 4);
+            auto add = [](float a, uint32_t r16) {
+              return __uint_as_float(r16 << 16) + __uint_as_float((uint32_t)f32_to_bf16(a) << 16);
+            };
+            const uint2 ra2 = *reinterpret_cast<const uint2*>(rrow);
+            uint2 rb2 = ra2;
+            if (col0 + 16 < N) rb2 = *reinterpret_cast<const uint2*>(rrow + 16);
+            acc_a[0] = add(acc_a[0], ra2.x & 0xffffu); acc_a[1] = add(acc_a[1], ra2.x >> 16);
+            acc_a[2] = add(acc_a[2], ra2.y & 0xffffu); acc_a[3] = add(acc_a[3], ra2.y >> 16);
+            acc_b[0] = add(acc_b[0], rb2.x & 0xffffu); acc_b[1] = add(acc_b[1], rb2.x >> 16);
+            acc_b[2] = add(acc_b[2], rb2.y & 0xffffu); acc_b[3] = add(acc_b[3], rb2.y >> 16);
+          }
           uint2 pa, pb;
           pa.x = pack2(f32_to_bf16(acc_a[0]), f32_to_bf16(acc_a[1]));
           pa.y = pack2(f32_to_bf16(acc_a[2]), f32_to_bf16(acc_a[3]));
@@ -342,7 +357,8 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
 
 template <bool GATED, bool ROUTED = false>
 hipError_t launch_skinny(const bf16_t* x, const int32_t* gather, const int32_t* offsets, int G, int n_rows, int T,
-                         const bf16_t* W, int K, int N, bf16_t* out, hipStream_t s, RoutedArgs ra = {}) {
+                         const bf16_t* W, int K, int N, bf16_t* out, hipStream_t s, RoutedArgs ra = {},
+                         const bf16_t* res = nullptr) {
   // K split for one-group launches (by the weight shape only): enough
   // slices for ~64 column tiles, each slice at least 2 k-steps, the staged
   // rows' LDS large enough for the partials (K >= 512)
@@ -365,7 +381,7 @@ hipError_t launch_skinny(const bf16_t* x, const int32_t* gather, const int32_t* 
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((skinny_kernel<GATED, ROUTED>), dim3(blocks), dim3(kBlockThreads), lds, s, x, gather, offsets,
-                     G, n_rows, T, W, K, N, n_ctiles, ks_log2, out, ra);
+                     G, n_rows, T, W, K, N, n_ctiles, ks_log2, out, res, ra);
   return hipGetLastError();
 }
 
@@ -407,8 +423,8 @@ __global__ __launch_bounds__(256) void f32_gate_up_kernel(const float* __restric
 
 __global__ __launch_bounds__(256) void f32_down_kernel(const float* __restrict__ act,
                                                        const int32_t* __restrict__ offsets, int G, int n_rows,
-                                                       const float* __restrict__ wd, int H, int I,
-                                                       float* __restrict__ y) {
+                                                       const float* __restrict__ wd, int H, int I, float* y,
+                                                       const float* res) {
   const int r = blockIdx.x;
   int r_begin = 0;
   const int g = find_group(offsets, G, n_rows, r, &r_begin);
@@ -418,7 +434,7 @@ __global__ __launch_bounds__(256) void f32_down_kernel(const float* __restrict__
     const float* w = wd + ((size_t)g * H + o) * I;
     float acc = 0.f;
     for (int c = 0; c < I; ++c) acc = fmaf(w[c], ar[c], acc);
-    y[(size_t)r * H + o] = acc;
+    y[(size_t)r * H + o] = res ? res[(size_t)r * H + o] + acc : acc;
   }
 }
 
@@ -447,16 +463,19 @@ hipError_t launch_gate_up_routed(const void* x, const int32_t* ids, int T, int k
 }
 
 hipError_t launch_down(const void* act, const int32_t* offsets, int G, int n_rows, const void* w_down, int H,
-                       int I, int max_rows, int dtype, void* y, hipStream_t s) {
+                       int I, int max_rows, int dtype, void* y, hipStream_t s, const void* residual) {
   if (dtype == kF32) {
     hipLaunchKernelGGL(f32_down_kernel, dim3(n_rows), dim3(256), 0, s, static_cast<const float*>(act), offsets,
-                       G, n_rows, static_cast<const float*>(w_down), H, I, static_cast<float*>(y));
+                       G, n_rows, static_cast<const float*>(w_down), H, I, static_cast<float*>(y),
+                       static_cast<const float*>(residual));
     return hipGetLastError();
   }
-  if (gemm_path_ok(I, H, max_rows))
+  // the tiled GEMM has no residual epilogue: with a residual the weight-streaming form serves every size
+  if (!residual && gemm_path_ok(I, H, max_rows))
     return launch_gemm(false, act, nullptr, offsets, G, n_rows, n_rows, w_down, I, H, y, s);
   return launch_skinny<false>(static_cast<const bf16_t*>(act), nullptr, offsets, G, n_rows, n_rows,
-                              static_cast<const bf16_t*>(w_down), I, H, static_cast<bf16_t*>(y), s);
+                              static_cast<const bf16_t*>(w_down), I, H, static_cast<bf16_t*>(y), s, RoutedArgs{},
+                              static_cast<const bf16_t*>(residual));
 }
 
 }  // namespace moe

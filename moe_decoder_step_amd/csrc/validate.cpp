@@ -111,6 +111,19 @@ int check_rmsnorm(const void* x, const int32_t* rows, int x_rows, int T, int H, 
   return kOk;
 }
 
+int check_combine_norm(const void* y, const int32_t* inv, const float* topk_w, const void* y_shared,
+                       int S, const void* residual, int T, int H, int k, int n_rows, int dtype,
+                       const void* out, const void* xn) {
+  int st = check_combine(y, inv, topk_w, y_shared, S, residual, T, H, k, n_rows, dtype, out, nullptr);
+  if (st != kOk) return st;
+  if (H > 2048) return kErrUnsupported;
+  if (T == 0) return kOk;
+  if (!xn) return kErrNull;
+  if (!aligned16(xn)) return kErrAlign;
+  if (xn == out || (residual && xn == residual)) return kErrShape;
+  return kOk;
+}
+
 int attn_split_keys(int max_keys) {
   // at most 64 splits per (sequence, head), at least 256 keys each, a multiple of the 64-key tile
   int sk = (max_keys + 63) / 64;
@@ -193,6 +206,15 @@ int check_gate_up(const void* x, const int32_t* offsets, int G, int n_rows, cons
   if (st != kOk || n_rows == 0 || T == 0) return st;
   if (!x || !offsets || !w_gate_up || !act) return kErrNull;
   if (!aligned16(x) || !aligned16(w_gate_up) || !aligned16(act)) return kErrAlign;
+  return kOk;
+}
+
+int check_down_residual(const void* act, const int32_t* offsets, int G, int n_rows, const void* w_down, int H, int I,
+                        int max_rows, int dtype, const void* residual, const void* y) {
+  int st = check_down(act, offsets, G, n_rows, w_down, H, I, max_rows, dtype, y);
+  if (st != kOk || n_rows == 0) return st;
+  if (!residual) return kErrNull;
+  if (!aligned16(residual)) return kErrAlign;
   return kOk;
 }
 

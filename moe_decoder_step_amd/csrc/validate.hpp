@@ -55,6 +55,8 @@ int check_permute(const int32_t* ids, int T, int k, int E, int S, const int32_t*
 int check_expert_shape(int G, int n_rows, int T, int H, int I, int max_rows, int dtype);
 int check_gate_up(const void* x, const int32_t* offsets, int G, int n_rows, const void* w_gate_up, int T,
                   int H, int I, int max_rows, int dtype, const void* act);
+int check_down_residual(const void* act, const int32_t* offsets, int G, int n_rows, const void* w_down, int H, int I,
+                        int max_rows, int dtype, const void* residual, const void* y);
 int check_down(const void* act, const int32_t* offsets, int G, int n_rows, const void* w_down, int H, int I,
                int max_rows, int dtype, const void* y);
 int check_swiglu(const void* x, const int32_t* offsets, int G, int n_rows, const void* w_gate_up,
@@ -63,6 +65,11 @@ int check_swiglu(const void* x, const int32_t* offsets, int G, int n_rows, const
 int check_combine(const void* y, const int32_t* inv, const float* topk_w, const void* y_shared,
                   int S, const void* residual, int T, int H, int k, int n_rows, int dtype,
                   const void* out, const void* combined);
+// moe_combine_rmsnorm: the checks of moe_combine, plus H <= 2048 (one block
+// of 256 threads x 8 elements per row) and a distinct, aligned xn.
+int check_combine_norm(const void* y, const int32_t* inv, const float* topk_w, const void* y_shared,
+                       int S, const void* residual, int T, int H, int k, int n_rows, int dtype,
+                       const void* out, const void* xn);
 int check_lmhead(const void* h, const void* w_lm, int T, int H, int V, int dtype,
                  const int32_t* ids, const void* ws, size_t ws_bytes);
 int check_verify(const int32_t* drafts, const int32_t* argmax_ids, int B, int K,

@@ -10,7 +10,7 @@ with attention omitted as in the verifier:
     h0 = W_p x                                 moe_expert_down, one group (2H -> H)
     z  = rmsnorm(h0)                           moe_rmsnorm
     a  = silu(W_g z) * (W_u z)                 moe_expert_gate_up, one group
-    h1 = h0 + W_d a                            moe_expert_down + moe_combine (residual)
+    h1 = h0 + W_d a                            moe_expert_down_residual
     draft = argmax W_lm h1                     lmhead_argmax (the verifier's head)
 
 Step i + 1 reads h1 and the draft of step i.  Every step runs in libmoestep's
@@ -45,7 +45,6 @@ class DraftHead:
         self.h0 = torch.empty((B, H), dtype=dt, device=dev)
         self.z = torch.empty((B, H), dtype=dt, device=dev)
         self.act = torch.empty((B, self.I), dtype=dt, device=dev)
-        self.f = torch.empty((B, H), dtype=dt, device=dev)
         self.h1 = [torch.empty((B, H), dtype=dt, device=dev) for _ in range(2)]
         self.drafts = torch.empty((K, B), dtype=torch.int32, device=dev)   # step-major: step i's tokens contiguous
         self.max_logit = torch.empty(B, dtype=torch.float32, device=dev)
@@ -53,7 +52,6 @@ class DraftHead:
         # the one-group row ranges [0, b] for every batch size b <= B
         self.offsets = torch.stack([torch.zeros(B + 1, dtype=torch.int32),
                                     torch.arange(B + 1, dtype=torch.int32)], 1).to(dev)
-        self.no_w = torch.empty((B, 0), dtype=torch.float32, device=dev)
 
     def propose(self, h: torch.Tensor, tok: torch.Tensor, record: list | None = None) -> torch.Tensor:
         """K draft tokens [B, K] (int32, a view) from the verifier's hidden
@@ -68,9 +66,8 @@ class DraftHead:
             ops.moe_expert_down(x, off, self.w_proj, self.h0[:B], max_rows=B)
             ops.moe_rmsnorm(self.h0[:B], self.z[:B], eps=self.eps)
             ops.moe_expert_gate_up(self.z[:B], None, off, self.w_gate_up, self.act[:B], max_rows=B)
-            ops.moe_expert_down(self.act[:B], off, self.w_down, self.f[:B], max_rows=B)
             h1 = self.h1[i & 1][:B]
-            ops.moe_combine(None, None, self.no_w[:B], self.f[:B], 1, self.h0[:B], h1)
+            ops.moe_expert_down_residual(self.act[:B], off, self.w_down, self.h0[:B], h1, max_rows=B)
             ops.lmhead_argmax(h1, self.w_lm, self.drafts[i, :B], self.max_logit[:B], self.lws)
             if record is not None:
                 record.append({"h": cur_h.clone(), "tok": cur_t.clone(), "h0": self.h0[:B].clone(),

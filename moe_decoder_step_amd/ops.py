@@ -15,8 +15,8 @@ import torch
 from . import _lib as L
 
 __all__ = [
-    "Packed", "pack_weights", "packed_weights_bytes", "moe_route", "moe_rmsnorm", "moe_combine_route", "moe_permute", "moe_grouped_swiglu", "moe_combine", "lmhead_argmax",
-    "moe_expert_gate_up", "moe_expert_gate_up_routed", "moe_expert_down", "ROUTED_MAX_PAIRS", "spec_verify", "spec_plant_drafts", "spec_advance",
+    "Packed", "pack_weights", "packed_weights_bytes", "moe_route", "moe_rmsnorm", "moe_combine_route", "moe_permute", "moe_grouped_swiglu", "moe_combine", "moe_combine_rmsnorm", "lmhead_argmax",
+    "moe_expert_gate_up", "moe_expert_gate_up_routed", "moe_expert_down", "moe_expert_down_residual", "ROUTED_MAX_PAIRS", "spec_verify", "spec_plant_drafts", "spec_advance",
     "spec_gather_rows", "moe_attn_rope_cache", "moe_attention", "attention_workspace_bytes", "kv_cache_alloc", "spec_commit",
     "permute_workspace_bytes", "swiglu_workspace_bytes",
     "lmhead_workspace_bytes", "dtype_code", "expert_weights", "lm_weights", "router_weights", "route_alloc", "permute_alloc", "swiglu_alloc",
@@ -258,6 +258,22 @@ def moe_expert_down(act, offsets, w_down, y, max_rows=None):
         dtype_code(act), _p(y), _stream(act)))
 
 
+def moe_expert_down_residual(act, offsets, w_down, residual, y, max_rows=None):
+    """y[r] = residual[r] + round(W_d act[r]) per group (y may be residual)."""
+    n_rows, I = act.shape
+    G, H, _ = w_down.shape
+    if act.dtype == torch.bfloat16 and not (isinstance(w_down, Packed) and w_down.kind == L.PACK_ROWS):
+        raise TypeError("bf16 expert weights must be packed (expert_weights / pack_weights)")
+    for t, d, n in ((act, None, "act"), (offsets, torch.int32, "offsets"), (w_down, act.dtype, "w_down"),
+                    (residual, act.dtype, "residual"), (y, act.dtype, "y")):
+        _need(t, d, n)
+    if residual is None:
+        raise ValueError("residual is required")
+    L.check("moe_expert_down_residual", L.load().moe_expert_down_residual(
+        _p(act), _p(offsets), G, n_rows, _p(w_down), H, I, n_rows if max_rows is None else int(max_rows),
+        dtype_code(act), _p(residual), _p(y), _stream(act)))
+
+
 def moe_combine(y, inv, topk_w, y_shared, S, residual, out, combined=None):
     """out = residual + sum_j w_j y[inv] + sum_s y_shared (fixed order, fp32)."""
     T, k = topk_w.shape
@@ -269,6 +285,21 @@ def moe_combine(y, inv, topk_w, y_shared, S, residual, out, combined=None):
     L.check("moe_combine", L.load().moe_combine(
         _p(y), _p(inv), _p(topk_w), _p(y_shared), S, _p(residual), T, H, k, 0 if y is None else y.shape[0],
         dtype_code(out), _p(out), _p(combined), _stream(out)))
+
+
+def moe_combine_rmsnorm(y, inv, topk_w, y_shared, S, residual, out, xn, gain=None, eps=1e-6):
+    """moe_combine, then xn = RMSNorm(out) (* gain), in one launch."""
+    T, k = topk_w.shape
+    H = out.shape[1]
+    for t, d, n in ((y, out.dtype, "y"), (inv, torch.int32, "inv"), (topk_w, torch.float32, "topk_w"),
+                    (y_shared, out.dtype, "y_shared"), (residual, out.dtype, "residual"), (out, None, "out"),
+                    (xn, out.dtype, "xn"), (gain, torch.float32, "gain")):
+        _need(t, d, n)
+    if xn is None:
+        raise ValueError("xn is required")
+    L.check("moe_combine_rmsnorm", L.load().moe_combine_rmsnorm(
+        _p(y), _p(inv), _p(topk_w), _p(y_shared), S, _p(residual), T, H, k, 0 if y is None else y.shape[0],
+        _p(gain), float(eps), dtype_code(out), _p(out), _p(xn), _stream(out)))
 
 
 def lmhead_argmax(h, w_lm, argmax_ids, max_logit, ws):

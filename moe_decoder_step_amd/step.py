@@ -189,18 +189,23 @@ class VerifyStack:
         return self.h[:T]
 
     def _forward_attn(self, T: int, record: list | None) -> torch.Tensor:
-        """Attention block then MoE block per layer, in place on self.h[:T]
-        (the combine cannot fuse with the next routing: attention sits
-        between them)."""
+        """Attention block then MoE block per layer, in place on self.h[:T].
+        Attention sits between a combine and the next routing, so the combine
+        fuses with the attention's input norm instead (moe_combine_rmsnorm
+        writes the block's xa)."""
         B = T // self.attn[0].P
         lengths = self.lengths[:B]
         for li, blk in enumerate(self.attn):
             if li > 0:
-                self._combine(T)
+                k, S = self.k, self.S
+                y = self.y[:T * k + S * T]
+                h = self.h[:T]
+                ops.moe_combine_rmsnorm(y[:T * k], self.inv[:T * k], self.tw[:T], y[T * k:] if S else None, S,
+                                        h, h, blk.xa[:T], eps=blk.eps)
             rec = None if record is None else {}
             if record is not None and li > 0:
                 record[-1]["output"] = self.h[:T].clone()
-            blk.forward(self.h[:T], lengths, self.max_keys, rec)
+            blk.forward(self.h[:T], lengths, self.max_keys, rec, normed=li > 0)
             self._route(li, T, False)
             if record is not None:
                 rec.update({"input": self.h[:T].clone(), "ids": self.ids[:T].clone(), "w": self.tw[:T].clone()})

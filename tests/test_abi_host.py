@@ -21,7 +21,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = L.header_functions()
-    assert len(names) == 25
+    assert len(names) == 27
     assert set(names) == set(L.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
@@ -129,6 +129,12 @@ def test_expert_halves_checks(lib):
     assert dn(A, A, 0, 40, A, 1280, 896, 4, m.BF16, A, None) == L.ERR_SHAPE
     assert dn(MIS, A, 66, 40, A, 1280, 896, 4, m.BF16, A, None) == L.ERR_ALIGN
     assert dn(None, None, 66, 0, None, 1280, 896, 4, m.BF16, None, None) == L.OK
+    dr = lib.moe_expert_down_residual
+    assert dr(A, A, 1, 40, A, 1280, 1280, 40, m.BF16, None, A, None) == L.ERR_NULL
+    assert dr(A, A, 1, 40, A, 1280, 1280, 40, m.BF16, MIS, A, None) == L.ERR_ALIGN
+    assert dr(A, A, 1, 40, A, 1280, 1280, 40, m.BF16, A, None, None) == L.ERR_NULL
+    assert dr(A, A, 0, 40, A, 1280, 1280, 40, m.BF16, A, A, None) == L.ERR_SHAPE
+    assert dr(None, None, 1, 0, None, 1280, 1280, 40, m.BF16, None, None, None) == L.OK
 
 
 def test_rmsnorm_checks(lib):
@@ -227,6 +233,15 @@ def test_combine_lmhead_verify_plant_checks(lib):
     assert lib.moe_combine(A, A, A, A, 2, A, 4, 1280, 6, 40, m.BF16, MIS, None, None) == L.ERR_ALIGN
     assert lib.moe_combine(A, A, A, A, 2, A, 4, 1280, 65, 40, m.BF16, A, None, None) == L.ERR_UNSUPPORTED
     assert lib.moe_combine(A, A, A, A, 2, A, 0, 1280, 6, 40, m.BF16, A, None, None) == L.OK
+    cn = lib.moe_combine_rmsnorm
+    B = P(0x200000)
+    assert cn(A, A, A, A, 2, A, 4, 1280, 6, 40, None, 1e-6, m.BF16, A, None, None) == L.ERR_NULL
+    assert cn(A, A, A, A, 2, A, 4, 1280, 6, 40, None, 1e-6, m.BF16, A, A, None) == L.ERR_SHAPE     # xn == out
+    assert cn(A, A, A, A, 2, B, 4, 1280, 6, 40, None, 1e-6, m.BF16, A, B, None) == L.ERR_SHAPE     # xn == residual
+    assert cn(A, A, A, A, 2, A, 4, 1280, 6, 40, None, 1e-6, m.BF16, A, MIS, None) == L.ERR_ALIGN
+    assert cn(A, A, A, A, 2, A, 4, 2056, 6, 40, None, 1e-6, m.BF16, A, B, None) == L.ERR_UNSUPPORTED
+    assert cn(A, A, A, None, 2, A, 4, 1280, 6, 40, None, 1e-6, m.BF16, A, B, None) == L.ERR_NULL
+    assert cn(None, None, None, None, 0, None, 0, 1280, 6, 40, None, 1e-6, m.BF16, None, None, None) == L.OK
     need = lib.lmhead_argmax_workspace_bytes(4, 129280, m.BF16)
     assert lib.lmhead_argmax(A, A, 4, 1280, 129280, m.BF16, A, None, A, need - 8, None) == L.ERR_WORKSPACE
     assert lib.lmhead_argmax(A, None, 4, 1280, 129280, m.BF16, A, None, A, need, None) == L.ERR_NULL

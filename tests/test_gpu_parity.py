@@ -300,6 +300,43 @@ def test_combine(m, dtype, T, k, S):
     assert torch.equal(res2, out)
 
 
+@pytest.mark.parametrize("dtype,T,H,k,S,gain,resid", [
+    (torch.bfloat16, 128, 1280, 6, 2, False, True), (torch.bfloat16, 37, 1280, 0, 1, True, True),
+    (torch.bfloat16, 5, 2048, 6, 2, True, False), (torch.float32, 16, 128, 2, 2, True, True),
+    (torch.bfloat16, 3, 136, 1, 0, False, True)])
+def test_combine_rmsnorm(m, dtype, T, H, k, S, gain, resid):
+    """The fused combine + RMSNorm gives the bits of moe_combine followed by
+    moe_rmsnorm of its output, and xn matches the oracle's RMSNorm of the
+    stored row; also in place (out is the residual)."""
+    mode = "bf16" if dtype == torch.bfloat16 else "f32"
+    gen = torch.Generator(device=DEV).manual_seed(13)
+    y = torch.randn(T * k + S * T, H, generator=gen, device=DEV).to(dtype)
+    inv = torch.randperm(T * k, generator=gen, device=DEV).to(torch.int32)
+    tw = torch.rand(T, k, generator=gen, device=DEV)
+    res = torch.randn(T, H, generator=gen, device=DEV).to(dtype) if resid else None
+    g = (torch.rand(H, generator=gen, device=DEV) + 0.5) if gain else None
+    yk, ys = (y[:T * k] if k else None), (y[T * k:] if S else None)
+    ref_out = torch.empty((T, H), dtype=dtype, device=DEV)
+    ref_xn = torch.empty_like(ref_out)
+    m.moe_combine(yk, inv if k else None, tw, ys, S, res, ref_out)
+    m.moe_rmsnorm(ref_out, ref_xn, gain=g)
+    out = torch.full_like(ref_out, float("nan"))
+    xn = torch.full_like(ref_out, float("nan"))
+    m.moe_combine_rmsnorm(yk, inv if k else None, tw, ys, S, res, out, xn, gain=g)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out)
+    assert torch.equal(xn, ref_xn)
+    gh = None if g is None else g.cpu().numpy().astype(np.float64)
+    assert_close(as_f64(xn), O.store(O.rmsnorm(as_f64(out), 1e-6, gh), mode),
+                 BF16_TOL if dtype == torch.bfloat16 else F32_TOL, "xn")
+    if resid:
+        h = res.clone()
+        xn2 = torch.empty_like(xn)
+        m.moe_combine_rmsnorm(yk, inv if k else None, tw, ys, S, h, h, xn2, gain=g)
+        torch.cuda.synchronize()
+        assert torch.equal(h, ref_out) and torch.equal(xn2, ref_xn)
+
+
 # --------------------------------------------------------------------------- LM head
 
 @pytest.mark.parametrize("dtype,T,H,V", [(torch.float32, 16, 128, 512), (torch.bfloat16, 4, 1280, 129280),
@@ -392,3 +429,36 @@ def test_one_group_dense_launches(m, gated, N, K):
             first = out[0].clone()
         else:
             assert torch.equal(out[0], first), f"row 0 depends on the number of rows ({rows})"
+
+
+@pytest.mark.parametrize("dtype,G,N,K,rows", [
+    (torch.bfloat16, 1, 1280, 1280, 1), (torch.bfloat16, 1, 1280, 1280, 130), (torch.bfloat16, 1, 1280, 896, 37),
+    (torch.bfloat16, 3, 1280, 896, 77), (torch.float32, 2, 128, 96, 40)])
+def test_expert_down_residual(m, dtype, G, N, K, rows):
+    """moe_expert_down_residual gives the bits of moe_expert_down followed by
+    moe_combine with the product as its one shared row; also in place."""
+    w = synth.normal(23, (G, N, K), 0.02, dtype, DEV)
+    wp = m.pack_weights(w, m._lib.PACK_ROWS) if dtype == torch.bfloat16 else w
+    x = synth.normal(24, (rows, K), 1.0, dtype, DEV)
+    res = synth.normal(25, (rows, N), 1.0, dtype, DEV)
+    cuts = np.sort(np.random.default_rng(26).integers(0, rows + 1, G - 1))
+    off = torch.tensor([0, *cuts, rows], dtype=torch.int32, device=DEV)
+    prod = torch.empty((rows, N), dtype=dtype, device=DEV)
+    m.moe_expert_down(x, off, wp, prod, max_rows=rows)
+    ref = torch.empty_like(prod)
+    m.moe_combine(None, None, torch.empty((rows, 0), device=DEV), prod, 1, res, ref)
+    y = torch.full_like(prod, float("nan"))
+    m.moe_expert_down_residual(x, off, wp, res, y, max_rows=rows)
+    h = res.clone()
+    m.moe_expert_down_residual(x, off, wp, h, h, max_rows=rows)
+    torch.cuda.synchronize()
+    assert torch.equal(y, ref)
+    assert torch.equal(h, ref)
+    # and against the oracle: residual + the product rounded to the storage type
+    mode = "bf16" if dtype == torch.bfloat16 else "f32"
+    xh, wh, offh = O.f64(host(x)), O.f64(host(w)), off.cpu().numpy()
+    pr = np.zeros((rows, N))
+    for g in range(G):
+        pr[offh[g]:offh[g + 1]] = xh[offh[g]:offh[g + 1]] @ wh[g].T
+    assert_close(as_f64(y), O.store(O.f64(host(res)) + O.store(pr, mode), mode),
+                 BF16_TOL if dtype == torch.bfloat16 else F32_TOL, "y")
