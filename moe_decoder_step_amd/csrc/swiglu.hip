@@ -14,6 +14,9 @@
 //   * the block's activation rows (up to 16 gathered tokens, the B operand)
 //     are staged once into LDS for the whole reduction length: one barrier,
 //     then every wavefront streams on its own with no activation traffic;
+//     in the gated stage, groups of more than 16 rows (the shared experts
+//     see every token) take items of 32 or 64 rows, staged in K-chunks, so
+//     each weight fragment is streamed once per 64 rows instead of per 16;
 //   * each block finds its (group, column tile, 16-row range) from the group
 //     offsets on the device, so untouched experts are never read and the
 //     launch holds few empty blocks; the ranges of one group and tile run
@@ -23,6 +26,8 @@
 //
 // fp32 path (the tiny fp32 configuration): one thread per output element,
 // plain sequential fp32 dot products.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "validate.hpp"
@@ -93,6 +98,96 @@ __device__ __forceinline__ void stream_rows(const bf16_t* wa, const bf16_t* wb, 
     if (d < rem) mma(d, nfull * D + d);
 }
 
+// The multi-row form of stream_rows for items of RB 16-row blocks: one
+// chunk of k-steps [s0, s0 + cl) against the chunk's activation columns in
+// LDS (row stride ldr, the chunk's first k-step at column 0), each weight
+// fragment feeding 2*RB MFMAs.  The weight pipeline runs on across chunks:
+// chunks start at multiples of D, so slot d always holds a step s with
+// s % D == d, and the loads issued by a chunk's last D steps are the next
+// chunk's first steps.
+template <int D, int RB, bool NT>
+__device__ __forceinline__ void stream_chunk(const bf16_t* wa, const bf16_t* wb, const bf16_t* xs, int ldr,
+                                             int s0, int cl, int nK, uint4* ra, uint4* rb, f32x4_t* acc_a,
+                                             f32x4_t* acc_b) {
+  auto mma = [&](int d, int lk) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const bf16x8_t bx = as_bf16x8(*reinterpret_cast<const uint4*>(xs + r * kRows * ldr + lk * 32));
+      acc_a[r] = mfma16x16x32(as_bf16x8(ra[d]), bx, acc_a[r]);
+      acc_b[r] = mfma16x16x32(as_bf16x8(rb[d]), bx, acc_b[r]);
+    }
+  };
+  const int nfull = cl / D;
+  for (int g = 0; g < nfull; ++g) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      mma(d, g * D + d);
+      const int kk = min(s0 + (g + 1) * D + d, nK - 1);
+      ra[d] = wload<NT>(wa + kk * 1024);
+      rb[d] = wload<NT>(wb + kk * 1024);
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      __builtin_amdgcn_sched_group_barrier(0x100, RB, 0);      // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * RB, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);       // VMEM read
+    }
+  }
+  const int rem = cl - nfull * D;
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (d < rem) mma(d, nfull * D + d);
+}
+
+// Items of more than 16 rows (groups with more than 16 rows: a shared
+// expert sees every token): an item of RB = 2 or 4 row blocks streams each
+// weight fragment once for 32 or 64 rows, where 16-row items would stream
+// it once per 16 rows -- the bytes moved to the CUs, not the HBM bytes, are
+// what the weight stream pays for.  The rows do not fit LDS for the whole
+// reduction, so they pass through it in chunks of chunk_steps(RB) k-steps:
+// each thread holds its share of the next chunk in a few registers, loaded
+// while the current chunk streams, and writes it to LDS between two
+// barriers.  A full chunk is straight-line code (stream_chunk_fixed), so
+// the compiler's waits on the weight slots stay exact around the prefetch.
+// A row's fp32 sums run over the same k-steps in the same order whatever
+// its item, so results do not depend on RB.
+constexpr int chunk_steps(int RB) { return RB == 4 ? 6 : 12; }
+constexpr int chunk_regs(int RB) { return (RB * kRows * chunk_steps(RB) * 4 + kBlockThreads - 1) / kBlockThreads; }
+// LDS bytes of a chunk of RB row blocks (rows padded by 8 elements)
+constexpr size_t chunk_lds(int RB) { return (size_t)RB * kRows * (chunk_steps(RB) * 32 + 8) * sizeof(bf16_t); }
+
+// A full chunk of CL k-steps [s0, s0 + CL), unrolled; `prefetch` (the next
+// chunk's activation loads) is issued after the first D steps' weight loads.
+template <int D, int RB, int CL, int NPF, bool NT, typename F>
+__device__ __forceinline__ void stream_chunk_fixed(const bf16_t* wa, const bf16_t* wb, const bf16_t* xs, int ldr,
+                                                   int s0, int nK, uint4* ra, uint4* rb, f32x4_t* acc_a,
+                                                   f32x4_t* acc_b, F&& prefetch) {
+  static_assert(CL % D == 0 && CL >= 2 * D, "a full chunk is at least two pipeline groups");
+#pragma unroll
+  for (int g = 0; g < CL / D; ++g) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        const bf16x8_t bx = as_bf16x8(*reinterpret_cast<const uint4*>(xs + r * kRows * ldr + (g * D + d) * 32));
+        acc_a[r] = mfma16x16x32(as_bf16x8(ra[d]), bx, acc_a[r]);
+        acc_b[r] = mfma16x16x32(as_bf16x8(rb[d]), bx, acc_b[r]);
+      }
+      const int kk = min(s0 + (g + 1) * D + d, nK - 1);
+      ra[d] = wload<NT>(wa + kk * 1024);
+      rb[d] = wload<NT>(wb + kk * 1024);
+    }
+    if (g == 0) prefetch();
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      __builtin_amdgcn_sched_group_barrier(0x100, RB, 0);      // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * RB, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);       // VMEM read
+    }
+    if (g == 0) __builtin_amdgcn_sched_group_barrier(0x020, NPF, 0);   // the prefetch
+  }
+}
+
 // GATED: x = token rows [T,K] read through gather, W = [G, 2N, K] packed as
 //        gate/up pairs (gate rows 16p.., up rows N+16p..), out = a [n_rows, N]; wavefront w owns output
 //        columns 16w..16w+15 of a 128-column block tile (its 16 gate rows and
@@ -118,8 +213,8 @@ template <bool GATED, bool ROUTED>
 __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
     const bf16_t* __restrict__ x, const int32_t* __restrict__ gather,
     const int32_t* __restrict__ offsets, int G, int n_rows, int T,
-    const bf16_t* __restrict__ W, int K, int N, int n_ctiles, int ks_log2, bf16_t* out, const bf16_t* res,
-    RoutedArgs rt) {
+    const bf16_t* __restrict__ W, int K, int N, int n_ctiles, int ks_log2, int chunk_cfg, bf16_t* out,
+    const bf16_t* res, RoutedArgs rt) {
   static_assert(!ROUTED || GATED, "only the gate/up stage derives its rows from the expert ids");
   constexpr int D = 3;                    // k-steps of weights in flight per wavefront
   constexpr int WCOLS = GATED ? 16 : 32;  // output columns per wavefront
@@ -134,9 +229,11 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
   // items per XCD and the surplus blocks, last in every XCD's list, exit.
   // Wavefront 0 finds the item: lane l handles groups l and l+64 (G <= 128),
   // counts its items on this XCD, and a wavefront prefix sum places them.
-  __shared__ int item_g, item_ct, item_r0, item_r1, item_gs;
+  __shared__ int item_g, item_ct, item_r0, item_r1, item_gs, item_rb;
   __shared__ int s_cnt[2 * kWave];   // ROUTED: rows per group
-  __shared__ int s_tok[kRows];       // ROUTED: tokens of the block's rows (routed groups)
+  __shared__ int s_tok[4 * kRows];   // ROUTED: tokens of the block's rows (routed groups)
+  // row blocks per item allowed (chunk_cfg: 0 = 16-row items only)
+  const int rb_max = (chunk_cfg >> 16) ? 4 : (chunk_cfg & 0xffff) ? 2 : 1;
   const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
   if (ROUTED) {
     // rows per group: a histogram of the (token, slot) expert ids; each
@@ -148,7 +245,7 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
   }
   if (threadIdx.x < kWave) {
     const int l = threadIdx.x;
-    int r0[2], r1[2], nr[2], nc[2];
+    int r0[2], r1[2], nr[2], nc[2], rbs[2];
     if (ROUTED) {
       // group row ranges: an exclusive scan of the counts (routed groups in
       // expert order, then the shared groups), as moe_permute lays them out
@@ -183,7 +280,9 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
         r0[h] = g < G ? clampi(offsets[g], 0, n_rows) : 0;
         r1[h] = g < G ? clampi(offsets[g + 1], r0[h], n_rows) : 0;
       }
-      nr[h] = (r1[h] - r0[h] + kRows - 1) / kRows;
+      const int rows = r1[h] - r0[h];
+      rbs[h] = rows > 2 * kRows && rb_max >= 4 ? 4 : rows > kRows && rb_max >= 2 ? 2 : 1;
+      nr[h] = (rows + rbs[h] * kRows - 1) / (rbs[h] * kRows);
       // tiles of group g on this XCD: ct = c0, c0+8, ... < n_ctiles
       const int c0 = ((xcd - g * n_ctiles) % 8 + 8) % 8;
       nc[h] = g < G && c0 < n_ctiles ? (n_ctiles - c0 + 7) / 8 : 0;
@@ -210,9 +309,10 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
         const int c0 = ((xcd - g * n_ctiles) % 8 + 8) % 8;
         item_g = g;
         item_ct = c0 + 8 * (li / nr[h]);
-        item_r0 = r0[h] + (li % nr[h]) * kRows;
+        item_r0 = r0[h] + (li % nr[h]) * rbs[h] * kRows;
         item_r1 = r1[h];
         item_gs = r0[h];
+        item_rb = rbs[h];
       }
     }
   }
@@ -221,7 +321,8 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
   if (g < 0) return;
   const int ct = item_ct;
   const int mstart = item_r0;
-  const int mr = min(kRows, item_r1 - mstart);
+  const int irb = item_rb;
+  const int mr = min(kRows * irb, item_r1 - mstart);
   const int r_begin = ROUTED ? item_gs : clampi(offsets[g], 0, n_rows);
   if (ROUTED && g < rt.E) {
     // the tokens of this block's rows: the group's (token, slot) pairs in
@@ -263,6 +364,48 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
   const int ldr = lds_row(K);
   const int nseg = K / 8;                 // 16-byte segments per activation row
 
+  // lane holds D[col 4*(lane/16)+v][row lane%16]: 4 consecutive output columns of one row
+  auto emit = [&](f32x4_t acc_a, f32x4_t acc_b, int row) __attribute__((always_inline)) {
+    if (row >= mr) return;
+    bf16_t* orow = out + (size_t)(mstart + row) * N + col0 + 4 * (lane >> 4);
+    if (GATED) {
+      uint2 pk;
+      pk.x = pack2(f32_to_bf16(silu(acc_a[0]) * acc_b[0]), f32_to_bf16(silu(acc_a[1]) * acc_b[1]));
+      pk.y = pack2(f32_to_bf16(silu(acc_a[2]) * acc_b[2]), f32_to_bf16(silu(acc_a[3]) * acc_b[3]));
+      *reinterpret_cast<uint2*>(orow) = pk;
+    } else {
+      if (res) {
+        // out = residual + y: y rounded to bf16 first, then the fp32 sum
+        // rounded once (the same bits as moe_combine adding y as a shared row)
+        const bf16_t* rrow = res + (size_t)(mstart + row) * N + col0 + 4 * (lane >> 4);
+        auto add = [](float a, uint32_t r16) {
+          return __uint_as_float(r16 << 16) + __uint_as_float((uint32_t)f32_to_bf16(a) << 16);
+        };
+        const uint2 ra2 = *reinterpret_cast<const uint2*>(rrow);
+        uint2 rb2 = ra2;
+        if (col0 + 16 < N) rb2 = *reinterpret_cast<const uint2*>(rrow + 16);
+        acc_a[0] = add(acc_a[0], ra2.x & 0xffffu); acc_a[1] = add(acc_a[1], ra2.x >> 16);
+        acc_a[2] = add(acc_a[2], ra2.y & 0xffffu); acc_a[3] = add(acc_a[3], ra2.y >> 16);
+        acc_b[0] = add(acc_b[0], rb2.x & 0xffffu); acc_b[1] = add(acc_b[1], rb2.x >> 16);
+        acc_b[2] = add(acc_b[2], rb2.y & 0xffffu); acc_b[3] = add(acc_b[3], rb2.y >> 16);
+      }
+      uint2 pa, pb;
+      pa.x = pack2(f32_to_bf16(acc_a[0]), f32_to_bf16(acc_a[1]));
+      pa.y = pack2(f32_to_bf16(acc_a[2]), f32_to_bf16(acc_a[3]));
+      pb.x = pack2(f32_to_bf16(acc_b[0]), f32_to_bf16(acc_b[1]));
+      pb.y = pack2(f32_to_bf16(acc_b[2]), f32_to_bf16(acc_b[3]));
+      *reinterpret_cast<uint2*>(orow) = pa;
+      if (col0 + 16 < N) *reinterpret_cast<uint2*>(orow + 16) = pb;
+    }
+  };
+  // the token (or activation row) of item row `row` (rows past the item repeat a valid row)
+  auto src_row = [&](int row) __attribute__((always_inline)) {
+    const int r = mstart + min(row, mr - 1);
+    if (ROUTED) return g < rt.E ? s_tok[min(row, mr - 1)] : clampi(r - r_begin, 0, T - 1);
+    if (GATED) return gather ? clampi(gather[r], 0, T - 1) : clampi(r - r_begin, 0, T - 1);
+    return r;
+  };
+
   auto body = [&](auto nt) __attribute__((always_inline)) {
     constexpr bool NT = decltype(nt)::value;
     // weights of the first D steps go out before the activation staging
@@ -281,12 +424,7 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
       for (int u = 0; u < 4; ++u) {
         const int idx = min(i + u * kBlockThreads, kRows * nseg - 1);
         const int row = idx / nseg, seg = idx % nseg;
-        const int r = mstart + min(row, mr - 1);
-        int s;
-        if (ROUTED) s = g < rt.E ? s_tok[min(row, mr - 1)] : clampi(r - r_begin, 0, T - 1);
-        else if (GATED) s = gather ? clampi(gather[r], 0, T - 1) : clampi(r - r_begin, 0, T - 1);
-        else s = r;
-        v[u] = ldg16(x + (size_t)s * K + seg * 8);
+        v[u] = ldg16(x + (size_t)src_row(row) * K + seg * 8);
         dst[u] = row * ldr + seg * 8;
       }
 #pragma unroll
@@ -314,45 +452,92 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
           acc_b += *reinterpret_cast<const f32x4_t*>(red + ((cg + q * CG) * kWave + lane) * 8 + 4);
         }
     }
-    if (active && ks == 0) {
-      // lane holds D[col 4*(lane/16)+v][row lane%16]: 4 consecutive output columns of one row
-      const int row = lane & 15;
-      if (row < mr) {
-        bf16_t* orow = out + (size_t)(mstart + row) * N + col0 + 4 * (lane >> 4);
-        if (GATED) {
-          uint2 pk;
-          pk.x = pack2(f32_to_bf16(silu(acc_a[0]) * acc_b[0]), f32_to_bf16(silu(acc_a[1]) * acc_b[1]));
-          pk.y = pack2(f32_to_bf16(silu(acc_a[2]) * acc_b[2]), f32_to_bf16(silu(acc_a[3]) * acc_b[3]));
-          *reinterpret_cast<uint2*>(orow) = pk;
-        } else {
-          if (res) {
-            // out = residual + y: y rounded to bf16 first, then the fp32 sum
-            // rounded once (the same bits as moe_combine adding y as a shared row)
-            const bf16_t* rrow = res + (size_t)(mstart + row) * N + col0 + 4 * (lane >> 4);
-            auto add = [](float a, uint32_t r16) {
-              return __uint_as_float(r16 << 16) + __uint_as_float((uint32_t)f32_to_bf16(a) << 16);
-            };
-            const uint2 ra2 = *reinterpret_cast<const uint2*>(rrow);
-            uint2 rb2 = ra2;
-            if (col0 + 16 < N) rb2 = *reinterpret_cast<const uint2*>(rrow + 16);
-            acc_a[0] = add(acc_a[0], ra2.x & 0xffffu); acc_a[1] = add(acc_a[1], ra2.x >> 16);
-            acc_a[2] = add(acc_a[2], ra2.y & 0xffffu); acc_a[3] = add(acc_a[3], ra2.y >> 16);
-            acc_b[0] = add(acc_b[0], rb2.x & 0xffffu); acc_b[1] = add(acc_b[1], rb2.x >> 16);
-            acc_b[2] = add(acc_b[2], rb2.y & 0xffffu); acc_b[3] = add(acc_b[3], rb2.y >> 16);
-          }
-          uint2 pa, pb;
-          pa.x = pack2(f32_to_bf16(acc_a[0]), f32_to_bf16(acc_a[1]));
-          pa.y = pack2(f32_to_bf16(acc_a[2]), f32_to_bf16(acc_a[3]));
-          pb.x = pack2(f32_to_bf16(acc_b[0]), f32_to_bf16(acc_b[1]));
-          pb.y = pack2(f32_to_bf16(acc_b[2]), f32_to_bf16(acc_b[3]));
-          *reinterpret_cast<uint2*>(orow) = pa;
-          if (col0 + 16 < N) *reinterpret_cast<uint2*>(orow + 16) = pb;
-        }
-      }
-    }
+    if (active && ks == 0) emit(acc_a, acc_b, lane & 15);
   };
-  if (GATED && item_r1 - r_begin > kRows) body(std::false_type{});
-  else body(std::true_type{});
+
+  // items of RB > 1 row blocks: the activations pass through LDS in chunks
+  // (K split off: ks == 0, k0 == 0)
+  auto chunked = [&](auto rbc, auto nt) __attribute__((always_inline)) {
+    constexpr int RB = decltype(rbc)::value;
+    constexpr bool NT = decltype(nt)::value;
+    constexpr int RR = RB * kRows;
+    constexpr int CL = chunk_steps(RB);
+    constexpr int NSC = CL * 4;          // 16-byte segments of a row in one chunk
+    constexpr int NPF = chunk_regs(RB);  // of them, per thread
+    constexpr int LDC = CL * 32 + 8;     // LDS row stride of a chunk (padded)
+    // every thread holds exactly NPF segments: no conditional store for the
+    // compiler to sink a prefetch load into
+    static_assert(RR * NSC == NPF * kBlockThreads, "a chunk is a whole number of segments per thread");
+    uint4 ra[D], rb[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int kk = min(d, nK - 1);
+      ra[d] = wload<NT>(wa + kk * 1024);
+      rb[d] = wload<NT>(wb + kk * 1024);
+    }
+    // this thread's segments u of a chunk: row offsets in x and segment numbers
+    int srow[NPF], sseg[NPF];
+#pragma unroll
+    for (int u = 0; u < NPF; ++u) {
+      const int idx = threadIdx.x + u * kBlockThreads;
+      srow[u] = src_row(idx / NSC) * K;
+      sseg[u] = idx % NSC;
+    }
+    uint4 pf[NPF];
+    // the chunk starting at k-step c0 (segments past the end of K repeat the
+    // row's last valid segment, never read)
+    auto ld_chunk = [&](int c0) __attribute__((always_inline)) {
+      const int last = (nK - c0) * 4 - 1;
+#pragma unroll
+      for (int u = 0; u < NPF; ++u) pf[u] = ldg16(x + srow[u] + c0 * 32 + min(sseg[u], last) * 8);
+    };
+    auto st_chunk = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < NPF; ++u) {
+        const int idx = threadIdx.x + u * kBlockThreads;
+        *reinterpret_cast<uint4*>(xl + (idx / NSC) * LDC + (idx % NSC) * 8) = pf[u];
+      }
+    };
+    ld_chunk(0);
+    st_chunk();
+    lds_barrier();
+    f32x4_t acc_a[RB], acc_b[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) acc_a[r] = acc_b[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const bf16_t* xs = xl + (lane & 15) * LDC + (lane >> 4) * 8;
+    int c0 = 0;
+    for (; c0 + CL < nK; c0 += CL) {    // full chunks with a successor
+      stream_chunk_fixed<D, RB, CL, NPF, NT>(wa, wb, xs, LDC, c0, nK, ra, rb, acc_a, acc_b,
+                                             [&]() __attribute__((always_inline)) { ld_chunk(c0 + CL); });
+      lds_barrier();                    // every wavefront is done with this chunk
+      st_chunk();
+      lds_barrier();
+    }
+    stream_chunk<D, RB, NT>(wa, wb, xs, LDC, c0, nK - c0, nK, ra, rb, acc_a, acc_b);   // the last chunk
+    if (active)
+#pragma unroll
+      for (int r = 0; r < RB; ++r) emit(acc_a[r], acc_b[r], r * kRows + (lane & 15));
+  };
+
+  // ordinary weight loads where several items read a gate/up tile (see wload)
+  const bool shared_tile = GATED && item_r1 - r_begin > kRows * irb;
+  if constexpr (GATED) {
+    if (irb == 4) {
+      if (shared_tile) chunked(std::integral_constant<int, 4>{}, std::false_type{});
+      else chunked(std::integral_constant<int, 4>{}, std::true_type{});
+      return;
+    }
+    if (irb == 2) {
+      if (shared_tile) chunked(std::integral_constant<int, 2>{}, std::false_type{});
+      else chunked(std::integral_constant<int, 2>{}, std::true_type{});
+      return;
+    }
+  }
+  if (shared_tile) {
+    body(std::false_type{});
+  } else {
+    body(std::true_type{});
+  }
 }
 
 template <bool GATED, bool ROUTED = false>
@@ -374,14 +559,21 @@ hipError_t launch_skinny(const bf16_t* x, const int32_t* gather, const int32_t* 
   //                  <= ceil(n_ctiles / 8) * (n_rows / 16 + G)
   const int per_xcd = (n_ctiles + 7) / 8 * ((n_rows + kRows - 1) / kRows + G);
   const int blocks = 8 * per_xcd;
-  const size_t lds = (size_t)kRows * lds_row(K) * sizeof(bf16_t);
+  // items of 32 / 64 rows for groups of more than 16 rows (not with a K
+  // split)
+  size_t lds = (size_t)kRows * lds_row(K) * sizeof(bf16_t);
+  int chunk_cfg = 0;
+  if (GATED && ks_log2 == 0) {
+    chunk_cfg = 2 | (4 << 16);
+    lds = std::max(lds, std::max(chunk_lds(2), chunk_lds(4)));
+  }
   if (lds > 64 * 1024) {  // K > 2040: allow up to the CU's 160 KB of LDS
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&skinny_kernel<GATED, ROUTED>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((skinny_kernel<GATED, ROUTED>), dim3(blocks), dim3(kBlockThreads), lds, s, x, gather, offsets,
-                     G, n_rows, T, W, K, N, n_ctiles, ks_log2, out, res, ra);
+                     G, n_rows, T, W, K, N, n_ctiles, ks_log2, chunk_cfg, out, res, ra);
   return hipGetLastError();
 }
 
