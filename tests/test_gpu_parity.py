@@ -341,7 +341,8 @@ def test_combine_rmsnorm(m, dtype, T, H, k, S, gain, resid):
 
 @pytest.mark.parametrize("dtype,T,H,V", [(torch.float32, 16, 128, 512), (torch.bfloat16, 4, 1280, 129280),
                                          (torch.bfloat16, 128, 1280, 20000), (torch.bfloat16, 37, 1280, 1003),
-                                         (torch.bfloat16, 1, 64, 77), (torch.bfloat16, 200, 256, 5000)])
+                                         (torch.bfloat16, 1, 64, 77), (torch.bfloat16, 200, 256, 5000),
+                                         (torch.bfloat16, 65, 512, 4099)])
 def test_lmhead_argmax(m, dtype, T, H, V):
     gen = torch.Generator(device=DEV).manual_seed(T + V)
     h = torch.randn(T, H, generator=gen, device=DEV).to(dtype)
