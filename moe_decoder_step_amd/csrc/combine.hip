@@ -122,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void combine_norm_kernel(
   if (threadIdx.x < kWave) {
     double ss = 0.0;
     for (int sg = threadIdx.x; sg < H / 8; sg += kWave) ss += ssp[sg];
-    ss = __shfl(wave_sum_f64(ss), 0, kWave);
+    ss = wave_sum_f64(ss);
     if (threadIdx.x == 0) s_scale = 1.0 / sqrt(ss / (double)H + (double)eps);
   }
   __syncthreads();

