@@ -13,8 +13,10 @@
 //      DPP wavefront max followed by a ballot: the lowest lane holding the
 //      maximum wins, which is the lower-id rule for equal logits; then the
 //      softmax weights.
-// Decode batches use 2 tokens per block so that a 128-token batch spreads
-// over 64 blocks; larger batches use 8, and prefill-sized ones 32 to
+// Decode batches (up to 256 tokens) use one token per block: the block's
+// work is a latency chain and the logits loop is VALU-bound, so 128 blocks
+// of one token beat 64 of two (measured 10 us per 12-layer step at 128
+// tokens); larger batches use 8, and prefill-sized ones 32 to
 // amortise the router reads (then the normed rows and the slice partials
 // share one LDS region, the rows being dead once the partials exist, and the
 // router slice is read in the loop rather than held in registers).  The
@@ -37,9 +39,9 @@ template <int TPB> constexpr int pre_count() { return TPB <= 16 ? 20 : 0; }
 // copies of the stored values, converted once instead of at every use)
 template <int TPB> constexpr bool lds_union() { return TPB > 16; }
 // normed rows in LDS as fp32 where they fit: the logits loop then reads them
-// with no unpacking (at 2 tokens per block the bf16 unpacking was half of
-// that loop's VALU work); bf16 rows at 8 and 16 tokens keep the LDS small
-template <int TPB> constexpr bool lds_f32() { return lds_union<TPB>() || TPB <= 2; }
+// with no unpacking (at decode sizes the bf16 unpacking was half of that
+// loop's VALU work); bf16 rows at 8 and 16 tokens keep the LDS small
+template <int TPB> constexpr bool lds_f32() { return lds_union<TPB>() || TPB <= 2; }   // 1 token per block at decode sizes
 template <typename St, int TPB> using lds_row_t = typename std::conditional<lds_f32<TPB>(), float, St>::type;
 
 __device__ __forceinline__ void load8(const bf16_t* p, float* f) { unpack8(ldg16(p), f); }
@@ -319,7 +321,7 @@ hipError_t launch_st(const void* h, void* hout, const CombineArgs* ca, const flo
     return launch_tpb<St, 16>(h, hout, ca, gain, eps, wr, bias, T, H, E, k, flags, xn, ids, w, logits, s);
   if (T > 256 && lds_bytes<St, 8>(H) <= kLds)
     return launch_tpb<St, 8>(h, hout, ca, gain, eps, wr, bias, T, H, E, k, flags, xn, ids, w, logits, s);
-  return launch_tpb<St, 2>(h, hout, ca, gain, eps, wr, bias, T, H, E, k, flags, xn, ids, w, logits, s);
+  return launch_tpb<St, 1>(h, hout, ca, gain, eps, wr, bias, T, H, E, k, flags, xn, ids, w, logits, s);
 }
 
 // RMSNorm of rows (the draft block's inputs): one wavefront per output row,
