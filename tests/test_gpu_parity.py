@@ -70,7 +70,8 @@ def test_pack_weights_layout(m, kind, shape):
 # --------------------------------------------------------------------------- route
 
 @pytest.mark.parametrize("shape,T", [("tiny", 16), ("layer128", 128), ("layer128", 1), ("layer128", 37),
-                                     ("layer128", 300), ("layer128", 4100), ("tiny", 4100)])
+                                     ("layer128", 256), ("layer128", 257), ("layer128", 300), ("layer128", 4100),
+                                     ("tiny", 4100)])
 @pytest.mark.parametrize("packed", [False, True])
 def test_route(m, shape, T, packed):
     sh = synth.SHAPES[shape]
@@ -90,6 +91,23 @@ def test_route(m, shape, T, packed):
     nflag, flagged = compare_ids(ids.cpu().numpy(), ref["ids"], ref["gap"], "topk ids")
     ok = ~flagged
     assert_close(tw.cpu().numpy()[ok], ref["w"][ok], F32_TOL, "topk weights")
+
+
+def test_route_batch_invariance(m):
+    """The same rows routed inside batches tiled 1, 8 and 32 tokens per block
+    give the same normed rows, logits, ids and weights, bit for bit (one
+    summation order for every tiling)."""
+    sh = synth.SHAPES["layer128"]
+    w = _layer(sh, 3)
+    wr = m.router_weights(w["w_router"])
+    h = synth.hidden(9, 4100, sh.H, torch.bfloat16, DEV)
+    outs = {}
+    for T in (37, 256, 300, 4100):
+        outs[T] = m.route_alloc(h[:T].contiguous(), wr, None, sh.k)
+    torch.cuda.synchronize()
+    for T in (256, 300, 4100):
+        for a, b in zip(outs[37], outs[T]):
+            assert torch.equal(a, b[:37]), T
 
 
 def test_route_full_softmax_and_no_norm(m):

@@ -155,7 +155,8 @@ def test_determinism_and_batch_invariance(m):
         assert torch.equal(st.argmax[:n], ids1[sub])
 
 
-@pytest.mark.parametrize("shape,T,L", [("step128", 128, 3), ("step128", 4, 2), ("tiny", 16, 1), ("step128", 300, 2)])
+@pytest.mark.parametrize("shape,T,L", [("step128", 128, 3), ("step128", 4, 2), ("tiny", 16, 1), ("step128", 256, 2),
+                                       ("step128", 300, 2)])
 def test_fused_combine_route_matches_separate_calls(m, shape, T, L):
     """moe_combine_route (each block's combine fused with the next block's
     routing) gives the same hidden states, ids and weights as moe_combine
