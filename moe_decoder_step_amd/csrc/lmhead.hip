@@ -325,9 +325,17 @@ __global__ __launch_bounds__(64) void lm_reduce_kernel(const unsigned long long*
                                                        int32_t* __restrict__ ids, float* __restrict__ max_logit) {
   const int t = blockIdx.x;
   unsigned long long best = 0ull;
-  for (int i = threadIdx.x; i < nblk; i += kWave) {
-    const unsigned long long k = part[(size_t)t * nblk + i];
-    best = k > best ? k : best;
+  // 8 keys per lane in flight at once (a loop of single loads waits out one
+  // round trip per key)
+  for (int i0 = threadIdx.x; i0 < nblk; i0 += 8 * kWave) {
+    unsigned long long k[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * kWave;
+      k[u] = i < nblk ? part[(size_t)t * nblk + i] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) best = k[u] > best ? k[u] : best;
   }
   best = wave_max_u64(best);
   if (threadIdx.x == 0) {

@@ -17,10 +17,21 @@ __global__ __launch_bounds__(64) void verify_kernel(const int32_t* __restrict__ 
   if (b >= B) return;
   const int32_t* db = d + (size_t)b * K;
   const int32_t* gb = g + (size_t)b * (K + 1);
-  int n = 0;
-  while (n < K && db[n] == gb[n]) ++n;
+  // every draft and target token loaded at once, then compared in registers
+  // (a compare-as-you-load loop waits out one round trip per position)
+  int32_t dv[kMaxDrafts], gv[kMaxDrafts + 1];
+#pragma unroll
+  for (int i = 0; i < kMaxDrafts; ++i) dv[i] = i < K ? db[i] : 0;
+#pragma unroll
+  for (int i = 0; i <= kMaxDrafts; ++i) gv[i] = i <= K ? gb[i] : -1;
+  int n = K;
+#pragma unroll
+  for (int i = kMaxDrafts - 1; i >= 0; --i)
+    if (i < K && dv[i] != gv[i]) n = i;       // the first mismatch
   int32_t* cb = committed + (size_t)b * (K + 1);
-  for (int i = 0; i <= K; ++i) cb[i] = i < n ? db[i] : (i == n ? gb[n] : -1);
+#pragma unroll
+  for (int i = 0; i <= kMaxDrafts; ++i)
+    if (i <= K) cb[i] = i < n ? dv[i] : (i == n ? gv[i] : -1);
   accepted[b] = n;
   n_commit[b] = n + 1;
 }
