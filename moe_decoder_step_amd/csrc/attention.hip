@@ -6,9 +6,10 @@
 //                      rotation in fp64, one rounding to bf16); k and v go
 //                      into the cache at [b][head][L_b + i][0 / 1][d];
 //   attn_split_kernel  flash-decoding: block (b, head, split) scores its span
-//                      of cached keys for the P queries, with an online fp32
-//                      softmax, and writes (max, sum, unnormalised output);
-//                      keys and values pass through LDS in 64-key tiles;
+//                      of cached keys for the P queries (q k^T on MFMA), with
+//                      an online fp32 softmax, and writes (max, sum,
+//                      unnormalised output); keys and values pass through LDS
+//                      in 64-key tiles;
 //   attn_merge_kernel  merges the splits of each (b, head, query), one
 //                      rounding to bf16.
 // Query i of sequence b sees keys 0 .. L_b + i: entries past that (drafts a
@@ -66,6 +67,12 @@ __global__ __launch_bounds__(256) void rope_cache_kernel(const bf16_t* __restric
 // block (b, head, split): keys [k0, k1) of sequence b, all P queries (P <= 16);
 // wavefront w handles queries w, w+4, ...  Partials: ws[((b*nh + head)*nsplit
 // + split)*P + i] = {max, sum, out[128]} (fp32).
+// Scores: every wavefront computes the tile's 64 keys x 16 query slots with
+// 16 v_mfma_f32_16x16x32_bf16 (keys the A operand from LDS, the queries the
+// B operand held in registers for the whole span; bf16 products, fp32 sums
+// in k-step order) and parks them in its own LDS rows, so that lane = key
+// for the softmax and the value sums.  On the VALU the dot products were
+// most of the kernel's instructions.
 __global__ __launch_bounds__(256) void attn_split_kernel(const bf16_t* __restrict__ q,
                                                          const bf16_t* __restrict__ kv,
                                                          const int32_t* __restrict__ lengths, int P, int n_heads,
@@ -73,7 +80,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(const bf16_t* __restric
                                                          float scale, float* __restrict__ ws) {
   __shared__ __align__(16) bf16_t ks[kTile][kRowPad];
   __shared__ __align__(16) bf16_t vs[kTile][kD];
-  __shared__ float qs[kMaxAttnP][kD];
+  __shared__ __align__(16) float sc[4][kMaxAttnP][kTile + 4];   // per wavefront: scores [query][key], padded rows
   __shared__ float ps[4][kTile];
   const int split = blockIdx.x % nsplit;
   const int hd = (blockIdx.x / nsplit) % n_heads;
@@ -85,12 +92,17 @@ __global__ __launch_bounds__(256) void attn_split_kernel(const bf16_t* __restric
   const int k0 = split * split_keys, k1 = min(k0 + split_keys, L + P);
   const size_t base = ((size_t)b * n_heads + hd) * max_len;
 
-  if (threadIdx.x < P * (kD / 8)) {   // P <= 16 queries: one 16-byte segment per thread
-    const int i = threadIdx.x >> 4, sg = (threadIdx.x & 15) * 8;
-    float f[8];
-    unpack8(ldg16(q + (size_t)(b * P + i) * H + hd * kD + sg), f);
+  // the MFMA B operand: lane l holds query slot l%16 (zero past P), dims
+  // 32 kk + 8 (l/16) .. +7 of k-step kk
+  bf16x8_t qf[kD / 32];
+  {
+    const int j = lane & 15;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qs[i][sg + e] = f[e];
+    for (int kk = 0; kk < kD / 32; ++kk) {
+      const uint4 v = j < P ? ldg16(q + (size_t)(b * P + j) * H + hd * kD + 32 * kk + 8 * (lane >> 4))
+                            : make_uint4(0u, 0u, 0u, 0u);
+      qf[kk] = as_bf16x8(v);
+    }
   }
   // per query this wavefront owns: running max, sum and 2 output dims per lane
   float m[4], l[4], o0[4], o1[4];
@@ -123,21 +135,34 @@ __global__ __launch_bounds__(256) void attn_split_kernel(const bf16_t* __restric
     }
     lds_barrier();
     if (t0 + kTile < k1) fetch(t0 + kTile);
+    {
+      // S[key][slot] for the tile: lane l ends with keys 16 kb + 4 (l/16) + v
+      // of query slot l%16; 16-byte key-row reads, rows 272 bytes apart
+      f32x4_t d[kTile / 16];
+#pragma unroll
+      for (int kb = 0; kb < kTile / 16; ++kb) d[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < kD / 32; ++kk)
+#pragma unroll
+        for (int kb = 0; kb < kTile / 16; ++kb) {
+          const uint4 a = *reinterpret_cast<const uint4*>(&ks[16 * kb + (lane & 15)][32 * kk + 8 * (lane >> 4)]);
+          d[kb] = mfma16x16x32(as_bf16x8(a), qf[kk], d[kb]);
+        }
+#pragma unroll
+      for (int kb = 0; kb < kTile / 16; ++kb)
+        *reinterpret_cast<f32x4_t*>(&sc[wave][lane & 15][16 * kb + 4 * (lane >> 4)]) = d[kb];
+      // the wavefront's own LDS rows: only its lanes wrote them
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int i = wave + 4 * u;
       if (i >= P) break;
       // lane = key of the tile
       const int key = t0 + lane;
-      // 16-byte reads of the key row: lanes 272 bytes apart cover all banks
-      float s = 0.f;
-#pragma unroll 4
-      for (int dd = 0; dd < kD; dd += 8) {
-        float kf[8];
-        unpack8(*reinterpret_cast<const uint4*>(&ks[lane][dd]), kf);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s = fmaf(qs[i][dd + e], kf[e], s);
-      }
+      float s = sc[wave][i][lane];
       const bool vis = lane < nk && key <= L + i;
       s = vis ? s * scale : -INFINITY;
       const float mt = wave_max_dpp(s);
