@@ -65,23 +65,32 @@ __global__ __launch_bounds__(256) void rope_cache_kernel(const bf16_t* __restric
 }
 
 // block (b, head, split): keys [k0, k1) of sequence b, all P queries (P <= 16);
-// wavefront w handles queries w, w+4, ...  Partials: ws[((b*nh + head)*nsplit
-// + split)*P + i] = {max, sum, out[128]} (fp32).
-// Scores: every wavefront computes the tile's 64 keys x 16 query slots with
-// 16 v_mfma_f32_16x16x32_bf16 (keys the A operand from LDS, the queries the
-// B operand held in registers for the whole span; bf16 products, fp32 sums
-// in k-step order) and parks them in its own LDS rows, so that lane = key
-// for the softmax and the value sums.  On the VALU the dot products were
-// most of the kernel's instructions.
+// wavefront w owns the softmax state of queries w, w+4, ...  Partials:
+// ws[((b*nh + head)*nsplit + split)*P + i] = {max, sum, out[128]} (fp32).
+// Both products run on v_mfma_f32_16x16x32_bf16 with 16 query slots:
+//   scores: every wavefront computes the tile's 64 keys x 16 slots (keys the
+//     A operand from LDS, the queries the B operand held in registers; bf16
+//     products, fp32 sums in k-step order) and parks them in its own padded
+//     LDS rows, so that lane = key for the online softmax;
+//   values: the probabilities go to LDS in bf16 [slot][key], the value tile
+//     sits in LDS transposed [dim][key], and wavefront w accumulates output
+//     dims 32 w .. 32 w + 31 of every slot (the running sums rescaled by each
+//     slot's correction first).
+// Staging: wavefronts 0-1 copy the tile's key rows (8 16-byte segments per
+// thread); wavefronts 2-3 each load an 8-key x 8-dim block of values and
+// transpose it in registers into 8 16-byte dim rows.  The next tile's loads
+// are in flight while the current one is scored.
 __global__ __launch_bounds__(256) void attn_split_kernel(const bf16_t* __restrict__ q,
                                                          const bf16_t* __restrict__ kv,
                                                          const int32_t* __restrict__ lengths, int P, int n_heads,
                                                          int max_len, int max_keys, int split_keys, int nsplit,
                                                          float scale, float* __restrict__ ws) {
-  __shared__ __align__(16) bf16_t ks[kTile][kRowPad];
-  __shared__ __align__(16) bf16_t vs[kTile][kD];
-  __shared__ __align__(16) float sc[4][kMaxAttnP][kTile + 4];   // per wavefront: scores [query][key], padded rows
-  __shared__ float ps[4][kTile];
+  constexpr int kVRow = kTile + 8;                                // bf16 per transposed value / probability row
+  __shared__ __align__(16) bf16_t ks[kTile][kRowPad];             // keys [key][dim]
+  __shared__ __align__(16) bf16_t vt[kD][kVRow];                  // values [dim][key]
+  __shared__ __align__(16) float sc[4][kMaxAttnP / 4][kTile + 4]; // per wavefront: scores of its slots [u][key]
+  __shared__ __align__(16) bf16_t pb[kMaxAttnP][kVRow];           // probabilities [slot][key]
+  __shared__ float cs[kMaxAttnP];                                 // per slot: the running sums' rescale
   const int split = blockIdx.x % nsplit;
   const int hd = (blockIdx.x / nsplit) % n_heads;
   const int b = blockIdx.x / (nsplit * n_heads);
@@ -92,7 +101,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(const bf16_t* __restric
   const int k0 = split * split_keys, k1 = min(k0 + split_keys, L + P);
   const size_t base = ((size_t)b * n_heads + hd) * max_len;
 
-  // the MFMA B operand: lane l holds query slot l%16 (zero past P), dims
+  // the scores' B operand: lane l holds query slot l%16 (zero past P), dims
   // 32 kk + 8 (l/16) .. +7 of k-step kk
   bf16x8_t qf[kD / 32];
   {
@@ -104,40 +113,70 @@ __global__ __launch_bounds__(256) void attn_split_kernel(const bf16_t* __restric
       qf[kk] = as_bf16x8(v);
     }
   }
-  // per query this wavefront owns: running max, sum and 2 output dims per lane
-  float m[4], l[4], o0[4], o1[4];
+  // slots past P: zero probabilities and unit rescale (their outputs are never written)
+  for (int idx = threadIdx.x; idx < kMaxAttnP * kVRow; idx += 256) (&pb[0][0])[idx] = (bf16_t)0;
+  if (threadIdx.x < kMaxAttnP) cs[threadIdx.x] = 1.f;
+  // softmax state of this wavefront's queries
+  float m[4], l[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) { m[u] = -INFINITY; l[u] = 0.f; o0[u] = 0.f; o1[u] = 0.f; }
+  for (int u = 0; u < 4; ++u) { m[u] = -INFINITY; l[u] = 0.f; }
+  // output dims 32 wave + 16 db + 4 (lane/16) + v of slot lane%16
+  f32x4_t o[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
 
-  // staging: thread owns the 16-byte segment sg of rows tid/16 + 16 s (s < 4)
-  // of each 64-key tile; the next tile's loads are in flight while the
-  // current one is scored
-  const int sg = (threadIdx.x & 15) * 8;
-  uint4 kr[4], vr[4];
-  auto fetch = [&](int t0) {
-    const int nk = min(kTile, k1 - t0);
+  const bool stage_k = threadIdx.x < 128;                 // wavefronts 0-1 (uniform per wavefront)
+  const int kt = threadIdx.x & 127;
+  const int ksg = kt & 15, krow = kt >> 4;                 // keys: segment ksg of rows krow + 8 j
+  const int vqb = kt & 7, vdb = kt >> 3;                   // values: keys 8 vqb .. +7, dims 8 vdb .. +7
+  uint4 r8[8];
+  auto fetch = [&](int t0) __attribute__((always_inline)) {
+    const int nk = min(kTile, k1 - t0);                    // rows past the span repeat a valid key
+    if (stage_k) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int key = t0 + min((threadIdx.x >> 4) + 16 * s, nk - 1);
-      kr[s] = ldg16(kv + (base + key) * (2 * kD) + sg);
-      vr[s] = ldg16(kv + (base + key) * (2 * kD) + kD + sg);
+      for (int j = 0; j < 8; ++j) {
+        const int key = t0 + min(krow + 8 * j, nk - 1);
+        r8[j] = ldg16(kv + (base + key) * (2 * kD) + 8 * ksg);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int key = t0 + min(8 * vqb + j, nk - 1);
+        r8[j] = ldg16(kv + (base + key) * (2 * kD) + kD + 8 * vdb);
+      }
+    }
+  };
+  auto store = [&]() __attribute__((always_inline)) {
+    if (stage_k) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4*>(&ks[krow + 8 * j][8 * ksg]) = r8[j];
+    } else {
+      // r8[j] holds dims 8 vdb .. +7 of key 8 vqb + j, two dims per word (even
+      // dim low); row e of the transpose holds keys 8 vqb .. +7 of dim 8 vdb + e
+      uint32_t w[8][4];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) { w[j][0] = r8[j].x; w[j][1] = r8[j].y; w[j][2] = r8[j].z; w[j][3] = r8[j].w; }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int wi = e >> 1;
+        uint32_t t[4];
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) {
+          const uint32_t a = w[2 * mm][wi], c = w[2 * mm + 1][wi];
+          t[mm] = (e & 1) ? ((a >> 16) | (c & 0xffff0000u)) : ((a & 0xffffu) | (c << 16));
+        }
+        *reinterpret_cast<uint4*>(&vt[8 * vdb + e][8 * vqb]) = make_uint4(t[0], t[1], t[2], t[3]);
+      }
     }
   };
   if (k0 < k1) fetch(k0);
 
   for (int t0 = k0; t0 < k1; t0 += kTile) {
     const int nk = min(kTile, k1 - t0);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int r = (threadIdx.x >> 4) + 16 * s;
-      *reinterpret_cast<uint4*>(&ks[r][sg]) = kr[s];
-      *reinterpret_cast<uint4*>(&vs[r][sg]) = vr[s];
-    }
+    store();
     lds_barrier();
     if (t0 + kTile < k1) fetch(t0 + kTile);
     {
-      // S[key][slot] for the tile: lane l ends with keys 16 kb + 4 (l/16) + v
-      // of query slot l%16; 16-byte key-row reads, rows 272 bytes apart
+      // S[key][slot]: lane l ends with keys 16 kb + 4 (l/16) + v of slot l%16;
+      // 16-byte key-row reads, rows 272 bytes apart
       f32x4_t d[kTile / 16];
 #pragma unroll
       for (int kb = 0; kb < kTile / 16; ++kb) d[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -148,9 +187,11 @@ __global__ __launch_bounds__(256) void attn_split_kernel(const bf16_t* __restric
           const uint4 a = *reinterpret_cast<const uint4*>(&ks[16 * kb + (lane & 15)][32 * kk + 8 * (lane >> 4)]);
           d[kb] = mfma16x16x32(as_bf16x8(a), qf[kk], d[kb]);
         }
+      // keep the slots this wavefront owns (slot = wave + 4 u)
+      if ((lane & 3) == wave)
 #pragma unroll
-      for (int kb = 0; kb < kTile / 16; ++kb)
-        *reinterpret_cast<f32x4_t*>(&sc[wave][lane & 15][16 * kb + 4 * (lane >> 4)]) = d[kb];
+        for (int kb = 0; kb < kTile / 16; ++kb)
+          *reinterpret_cast<f32x4_t*>(&sc[wave][(lane & 15) >> 2][16 * kb + 4 * (lane >> 4)]) = d[kb];
       // the wavefront's own LDS rows: only its lanes wrote them
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
       __builtin_amdgcn_wave_barrier();
@@ -162,7 +203,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(const bf16_t* __restric
       if (i >= P) break;
       // lane = key of the tile
       const int key = t0 + lane;
-      float s = sc[wave][i][lane];
+      float s = sc[wave][u][lane];
       const bool vis = lane < nk && key <= L + i;
       s = vis ? s * scale : -INFINITY;
       const float mt = wave_max_dpp(s);
@@ -171,36 +212,44 @@ __global__ __launch_bounds__(256) void attn_split_kernel(const bf16_t* __restric
       const float corr = m[u] == -INFINITY ? 0.f : expf(m[u] - mn);
       l[u] = l[u] * corr + wave_sum_dpp(p);
       m[u] = mn;
-      ps[wave][lane] = p;
-      // the wavefront's own LDS row: only its lanes wrote it
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-      float a0 = o0[u] * corr, a1 = o1[u] * corr;
-#pragma unroll 8
-      for (int jj = 0; jj < nk; ++jj) {
-        const float pj = ps[wave][jj];
-        const uint32_t vv = *reinterpret_cast<const uint32_t*>(&vs[jj][2 * lane]);
-        a0 = fmaf(pj, __uint_as_float(vv << 16), a0);
-        a1 = fmaf(pj, __uint_as_float(vv & 0xffff0000u), a1);
-      }
-      o0[u] = a0;
-      o1[u] = a1;
-      __builtin_amdgcn_wave_barrier();
+      pb[i][lane] = f32_to_bf16(p);
+      if (lane == 0) cs[i] = corr;
     }
-    lds_barrier();
+    lds_barrier();   // every slot's probabilities and rescale
+    {
+      const float c = cs[lane & 15];
+#pragma unroll
+      for (int db = 0; db < 2; ++db) o[db] *= c;
+#pragma unroll
+      for (int kk = 0; kk < kTile / 32; ++kk) {
+        const uint4 pf = *reinterpret_cast<const uint4*>(&pb[lane & 15][32 * kk + 8 * (lane >> 4)]);
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          const uint4 a =
+              *reinterpret_cast<const uint4*>(&vt[32 * wave + 16 * db + (lane & 15)][32 * kk + 8 * (lane >> 4)]);
+          o[db] = mfma16x16x32(as_bf16x8(a), as_bf16x8(pf), o[db]);
+        }
+      }
+    }
+    lds_barrier();   // the tile's buffers are free for the next one
   }
+  const size_t wbase = (((size_t)b * n_heads + hd) * nsplit + split) * P;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int i = wave + 4 * u;
     if (i >= P) break;
-    float* w = ws + ((((size_t)b * n_heads + hd) * nsplit + split) * P + i) * (kD + 2);
     if (lane == 0) {
-      w[0] = m[u];
-      w[1] = l[u];
+      ws[(wbase + i) * (kD + 2)] = m[u];
+      ws[(wbase + i) * (kD + 2) + 1] = l[u];
     }
-    w[2 + 2 * lane] = o0[u];
-    w[3 + 2 * lane] = o1[u];
+  }
+  const int slot = lane & 15;
+  if (slot < P) {
+    float* w = ws + (wbase + slot) * (kD + 2) + 2 + 32 * wave + 4 * (lane >> 4);
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) w[16 * db + v] = o[db][v];
   }
 }
 
