@@ -232,8 +232,11 @@ int moe_expert_down(const void* act, const int32_t* offsets, int G, int n_rows,
  * epilogue: y[r] = residual[r] + round(W_d[g] act[r]), the product rounded to
  * dtype first and the sum rounded once (the same bits as moe_expert_down
  * followed by moe_combine with y as its one shared row and k = 0).  For the
- * dense layers around the MoE blocks (the attention output projection, the
- * draft block's FFN).  residual [n_rows, H] dtype, 16-byte aligned; it may
+ * dense layers around the MoE blocks: the draft block's FFN ("Jina AI's 3.4B
+ * OCR model targets faster page parsing", section "FastMTP cuts decoding
+ * work": one dense block) and the attention output projection (the
+ * decoder's attention, jina.ai/ko model card, architecture paragraph, read
+ * as a pre-norm residual block).  residual [n_rows, H] dtype, 16-byte aligned; it may
  * be y itself (in place).  Errors as moe_expert_down, plus MOE_ERR_NULL for
  * a NULL residual. */
 int moe_expert_down_residual(const void* act, const int32_t* offsets, int G, int n_rows,
@@ -266,8 +269,9 @@ int moe_combine(const void* y, const int32_t* inv, const float* topk_w,
  * RMSNorm of each output row, in one launch: xn[t] = out[t] /
  * sqrt(mean(out[t]^2) + eps) (* gain), normalised from the stored (rounded)
  * out row, with the same bits as moe_combine then moe_rmsnorm.  For the
- * block that follows a combine and starts with a norm (the attention of the
- * next layer, the final norm before the LM head).  Arguments as moe_combine,
+ * block that follows a combine and starts with a norm: the next layer's
+ * attention (the MoE layers and attention of the decoder: jina.ai/ko model
+ * card, architecture paragraph; pre-norm blocks).  Arguments as moe_combine,
  * plus gain [H] fp32 or NULL and xn [T, H] dtype (16-byte aligned, distinct
  * from out and residual; MOE_ERR_SHAPE otherwise).  out == residual is
  * allowed.  Limits: H % 8 == 0, H <= 2048, 0 <= k <= 64. */
