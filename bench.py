@@ -285,6 +285,18 @@ def main() -> int:
                       "committed_tokens_per_s": commit_mean * sh.B / (ms * 1e-3),
                       "keep_probability": P_KEEP, "planted_steps": int(keep_d.shape[0])}
 
+    # per-step distribution (a separate pass, events around every step; the
+    # headline above is the bracketed mean)
+    pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in pev:
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    per_step = np.array([a.elapsed_time(b) for a, b in pev]) / cycle
+    dist = {"p10": float(np.percentile(per_step, 10)), "p50": float(np.percentile(per_step, 50)),
+            "p90": float(np.percentile(per_step, 90)), "steps": int(per_step.size), "launch": "eager"}
+
     # dominant kernel (expert gate/up, routed + shared experts): HIP events
     # around each launch on the stream it runs on, over a second timed pass
     st.ffn_events = ev = []
@@ -350,6 +362,7 @@ def main() -> int:
     }
     if graph_info is not None:
         out["batch1"] = graph_info
+    out["ms_per_step_distribution"] = dist
     if prefill:
         out["layer_mfma"] = {"algorithmic_flops": layer_flops,
                              "achieved_TFLOPs": layer_flops / (ms * 1e-3) / 1e12,
