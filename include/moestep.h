@@ -379,15 +379,19 @@ int spec_plant_drafts(const int32_t* argmax_ids, const uint8_t* keep, const int3
  * spec_advance appends each one's committed tokens to its stream, stops a
  * sequence at `target` tokens (the excess of its last pass is dropped) and
  * compacts the still-active sequence ids in their order.  The caller reads
- * n_active (one 4-byte copy per pass) to size the next pass.
+ * n_active (one 4-byte copy per pass) to size a later pass; a pass may be
+ * launched before that copy arrives, with the previous batch size: the slots
+ * past n_active hold -1 and every call skips them.
  *
  * spec_advance:
  *   n_commit  [B] int32, committed [B,K+1] int32   in  (spec_verify's outputs)
- *   seq_ids   [B] int32                            in  sequence of each slot, in [0,S)
+ *   seq_ids   [B] int32                            in  sequence of each slot, in [0,S);
+ *                                                      a negative id is an empty slot (skipped)
  *   total     [S] int32                            in/out tokens committed so far
  *   steps     [S] int32                            in/out passes taken so far
  *   tokens    [S,target] int32                     out committed streams
- *   seq_ids_out [<= B] int32                       out active sequences, in slot order
+ *   seq_ids_out [B] int32                          out active sequences, in slot order,
+ *                                                      then -1 up to slot B-1
  *   n_active  [1] int32                            out number of them
  *   Limits: 0 <= B <= min(S, 1024), 0 <= K <= 15, target >= 1.  The ids in
  *   seq_ids are distinct; seq_ids_out must not alias seq_ids.  B = 0 writes
@@ -396,7 +400,8 @@ int spec_plant_drafts(const int32_t* argmax_ids, const uint8_t* keep, const int3
  * spec_gather_rows: the per-pass inputs of the active sequences from pools
  * laid out [S, J, R] rows of row_bytes bytes (J passes per sequence, R rows
  * per pass):  out row i*R + r = pool row (seq_ids[i] * J + min(steps[s], J-1))
- * * R + r, with s = seq_ids[i].  Used for the hidden states of the verify
+ * * R + r, with s = seq_ids[i] (an empty slot, id < 0, reads sequence 0's
+ * row: its pass result is skipped).  Used for the hidden states of the verify
  * positions (R = K+1 rows of H bf16) and the planting draws (R = 1 row of K
  * bytes or K int32).  row_bytes = 0 (K = 0 drafts) is a no-op.
  * ------------------------------------------------------------------------- */

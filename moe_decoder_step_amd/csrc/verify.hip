@@ -60,7 +60,7 @@ __global__ __launch_bounds__(1024) void advance_kernel(const int32_t* __restrict
   const int i = threadIdx.x, wave = i >> 6, lane = i & 63;
   bool alive = false;
   int seq = 0;
-  if (i < B) {
+  if (i < B && seq_ids[i] >= 0) {   // a negative id is an empty slot
     seq = clampi(seq_ids[i], 0, S - 1);
     const int before = clampi(total[seq], 0, target);
     const int take = min(clampi(n_commit[i], 0, K + 1), target - before);
@@ -76,11 +76,12 @@ __global__ __launch_bounds__(1024) void advance_kernel(const int32_t* __restrict
   for (int w = 0; w < wave; ++w) base += wave_count[w];
   const int rank = __popcll(mask & ((1ull << lane) - 1ull));
   if (alive) seq_out[base + rank] = seq;
-  if (i == blockDim.x - 1) {
-    int n = 0;
-    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) n += wave_count[w];
-    n_active[0] = n;
-  }
+  int n = 0;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) n += wave_count[w];
+  // slots n .. B-1 of the new list are empty: a pass launched before n is
+  // known (with the previous batch size) skips them
+  if (i >= n && i < B) seq_out[i] = -1;
+  if (i == blockDim.x - 1) n_active[0] = n;
 }
 
 // out row i*R + r = pool row (seq_ids[i] * J + min(steps[seq], J - 1)) * R + r,

@@ -93,3 +93,30 @@ def test_decode_loop_matches_cpu_rerun(m, S, target, K):
     np.testing.assert_array_equal(loop.tokens.cpu().numpy(), np.array(streams))
     np.testing.assert_array_equal(loop.total.cpu().numpy(), np.full(S, target))
     np.testing.assert_array_equal(loop.steps.cpu().numpy(), np.array(ref_steps))
+
+
+@pytest.mark.parametrize("S,target,K", [(6, 20, 3), (7, 11, 1), (4, 9, 0)])
+def test_lagged_loop_matches_waiting_loop(m, S, target, K):
+    """The loop that queues pass j + 1 before pass j's count is back (empty
+    slots marked -1) commits the same streams in the same passes as the loop
+    that waits after every pass; it launches at most one extra pass."""
+    import dataclasses
+    sh = dataclasses.replace(synth.SHAPES["tiny"], B=S, P=K + 1)
+    layers = [synth.layer_weights(5, l, sh, DEV) for l in range(sh.L)]
+    w_lm = synth.lm_weight(5, sh, DEV)
+    st = m.VerifyStack(layers, w_lm, sh.E, sh.k, sh.S, max_tokens=sh.T, max_seqs=S, K=K)
+    h_pool = synth.normal(13, (S, target, K + 1, sh.H), 1.0, torch.float32, DEV)
+    keep, repl = synth.plant_schedule(14, target, S, K, sh.V, 0.576)
+    loop = m.DecodeLoop(st, h_pool, keep.permute(1, 0, 2).contiguous().to(DEV),
+                        repl.permute(1, 0, 2).contiguous().to(DEV), target)
+    rec = []
+    want = loop.run(rec)
+    tok, tot, stp = (host(t).copy() for t in (loop.tokens, loop.total, loop.steps))
+    for _ in range(2):   # twice: the second run reuses the pinned counts
+        got = loop.run()
+        assert got["passes"] == want["passes"] and got["batch_sizes"] == want["batch_sizes"]
+        assert len(got["launched"]) <= want["passes"] + 1
+        assert all(a >= b for a, b in zip(got["launched"], want["batch_sizes"]))
+        np.testing.assert_array_equal(host(loop.tokens), tok)
+        np.testing.assert_array_equal(host(loop.total), tot)
+        np.testing.assert_array_equal(host(loop.steps), stp)
