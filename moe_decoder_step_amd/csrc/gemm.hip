@@ -6,18 +6,25 @@
 // tile of 256 rows (tokens of one group) by 8 weight-row pairs:
 //   gated stage: 8 (gate 16-row, up 16-row) pairs = 128 activation columns;
 //   down stage:  8 pairs of 16 weight rows = 256 output columns.
-// The reduction runs in stages of 32 (one MFMA k-step).  A stage is 16 KB of
-// activation rows and 16 KB of weights in LDS, both in fragment order: a 1 KB
-// fragment holds, in lane order, the 16 rows x 32 k-elements one wavefront
-// feeds to v_mfma_f32_16x16x32_bf16, so every LDS read is 1 KB of
-// consecutive bytes (no bank conflicts).  Stages are loaded straight from
-// global memory into LDS (global_load_lds_dwordx4: lane l's 16 bytes land at
-// fragment offset 16 l), into a ring of 4 stage buffers, 3 stages ahead of
-// the multiply; the packed weights (moe_pack_weights) copy as they lie in
-// memory, activation rows are gathered per lane.  Per stage: wait for this
-// wavefront's loads of the stage, one barrier (after it every wavefront's
-// loads of the stage have landed and every wavefront has finished the stage
-// whose buffer is refilled next), issue the loads 3 stages ahead, multiply.
+// The reduction runs in stages of 32 (one MFMA k-step).  A stage's 16
+// activation fragments (16 KB) go through LDS, its weight fragments straight
+// into registers.  A 1 KB fragment holds, in lane order, the 16 rows x 32
+// k-elements one wavefront feeds to v_mfma_f32_16x16x32_bf16, so every LDS
+// read is 1 KB of consecutive bytes (no bank conflicts).  Activation
+// fragments are loaded from global memory straight into LDS
+// (global_load_lds_dwordx4: lane l's 16 bytes land at fragment offset 16 l),
+// rows gathered per lane, into a ring of kGAhead + 1 stage buffers; each
+// wavefront loads the 4 packed weight fragments it multiplies (1 KB each, as
+// they lie in memory, moe_pack_weights) into a register ring of kGAhead
+// stages.  Both run kGAhead stages ahead of the multiply.  Per stage: wait
+// for this wavefront's loads of the stage, one barrier (after it every
+// wavefront's activation loads of the stage have landed and every wavefront
+// has finished the stage whose buffer is refilled next), issue the
+// activation loads kGAhead stages ahead, multiply, then refill the register
+// slot just used with the weights kGAhead stages ahead.  Keeping the weights
+// out of LDS cuts its traffic per stage from 96 KB of reads and 32 KB of
+// writes to 64 KB and 16 KB; each weight fragment is fetched by the two
+// wavefronts that use it (the second read hits in cache).
 //
 // Wavefront (wm, wn) = (w / 4, w % 4) computes rows 128 wm .. +127 (8 MFMA
 // row blocks) by pairs 2 wn, 2 wn + 1 (4 weight fragments): 32 MFMAs per
@@ -41,10 +48,12 @@ namespace {
 constexpr int kGM = 256;                  // rows per tile
 constexpr int kGPairs = 8;                // weight-row pairs per tile
 constexpr int kGK = 32;                   // reduction elements per stage
-constexpr int kGRing = 4;                 // stage buffers (3 stages in flight)
+constexpr int kGAhead = 4;                // stages in flight (weights and activations)
+constexpr int kGRing = kGAhead + 1;       // activation stage buffers
 constexpr int kGWaves = 8;
 constexpr int kGThreads = kGWaves * 64;
-constexpr int kGStage = 2 * 16384;        // bytes per stage: A 16 KB + B 16 KB
+constexpr int kGStage = 16384;            // activation bytes per stage
+constexpr int kGLoads = 6;                // loads per wavefront and stage: 2 activation + 4 weight fragments
 constexpr size_t kGLds = (size_t)kGRing * kGStage;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -59,7 +68,9 @@ __device__ __forceinline__ void load_lds16(const bf16_t* g, char* base) {
 // loads of later stages stay in flight
 template <int N>
 __device__ __forceinline__ void wait_barrier() {
-  __builtin_amdgcn_s_waitcnt(0x0070 | N);  // vmcnt(N) expcnt(7) lgkmcnt(0)
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  // vmcnt(N) (bits 3:0 and 15:14) expcnt(7) lgkmcnt(0)
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
   asm volatile("s_barrier" ::: "memory");
 }
 
@@ -67,31 +78,43 @@ __device__ __forceinline__ float silu_g(float z) { return z / (1.0f + expf(-z));
 
 __device__ __forceinline__ uint4 lds16(const char* p) { return *reinterpret_cast<const uint4*>(p); }
 
-// One stage: issue this wavefront's loads of a later stage into `nxt` (when
-// `issue`), then multiply the stage in `cur`.  The two buffers are distinct;
-// saying so (restrict) lets the compiler see that the reads of `cur` do not
-// depend on the loads into `nxt` still in flight, so it adds no wait for them.
-__device__ __forceinline__ void gemm_stage(const char* __restrict__ cur, char* __restrict__ nxt, bool issue,
-                                           const bf16_t* const (&src)[4], size_t step, f32x4_t (&acc)[8][2][2],
-                                           int wm, int wn, int lane) {
-  if (issue) {
+// Row blocks i0 .. i0 + 3 of one stage: multiply the stage in `cur` with the
+// weight fragments `bw`.
+__device__ __forceinline__ void gemm_half(const char* cur, int i0, const uint4 (&bw)[2][2],
+                                          f32x4_t (&acc)[8][2][2], int wm, int lane) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) load_lds16(src[u] + step, nxt + u * 1024);
-  }
-  bf16x8_t bw[2][2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q)
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      bw[q][h] = as_bf16x8(lds16(cur + 16384 + ((wn * 2 + q) * 2 + h) * 1024 + lane * 16));
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = i0; i < i0 + 4; ++i) {
     const bf16x8_t xa = as_bf16x8(lds16(cur + (wm * 8 + i) * 1024 + lane * 16));
 #pragma unroll
     for (int q = 0; q < 2; ++q)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) acc[i][q][h] = mfma16x16x32(bw[q][h], xa, acc[i][q][h]);
+      for (int h = 0; h < 2; ++h) acc[i][q][h] = mfma16x16x32(as_bf16x8(bw[q][h]), xa, acc[i][q][h]);
   }
+}
+
+// One stage that refills: row blocks 0-3 of the stage in `cur`, the barrier
+// (N loads may stay outstanding), this wavefront's activation loads of a later
+// stage into `nxt`, row blocks 4-7.  The two buffers are distinct; saying so
+// (restrict) lets the compiler see that the reads of `cur` do not depend on
+// the loads into `nxt` still in flight, so it adds no wait for them.
+template <int N>
+__device__ __forceinline__ void gemm_stage(const char* __restrict__ cur, char* __restrict__ nxt,
+                                           const bf16_t* const (&src)[2], size_t step, const uint4 (&bw)[2][2],
+                                           f32x4_t (&acc)[8][2][2], int wm, int lane) {
+  gemm_half(cur, 0, bw, acc, wm, lane);
+  wait_barrier<N>();
+#pragma unroll
+  for (int u = 0; u < 2; ++u) load_lds16(src[u] + step, nxt + u * 1024);
+  gemm_half(cur, 4, bw, acc, wm, lane);
+}
+
+// this wavefront's 4 weight fragments of stage s: pairs 2 wn + q, sets h
+__device__ __forceinline__ void load_weights(uint4 (&bw)[2][2], const bf16_t* const (&wsrc)[2], int s) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      bw[q][h] = *reinterpret_cast<const uint4*>(wsrc[q] + (size_t)s * 1024 + h * 512);
 }
 
 template <bool GATED>
@@ -144,30 +167,25 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nS = K / kGK;                 // stages = MFMA k-steps
 
-  // loads: wavefronts 0-3 fetch the stage's 16 activation fragments (row
-  // block 4w + u), wavefronts 4-7 its 16 weight fragments (pair 2(w-4) + u/2,
-  // set u%2); 4 fragments per wavefront and stage
-  const bf16_t* src[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int f = wave * 4 + u;
-    if (f < 16) {
-      const int r = min(m0 + 16 * f + (lane & 15), m1 - 1);  // rows past the group repeat a valid row
-      int t;
-      if (GATED) t = gather ? clampi(gather[r], 0, T - 1) : clampi(r - r_begin, 0, T - 1);
-      else t = r;
-      src[u] = x + (size_t)t * K + 8 * (lane >> 4);
-    } else {
-      const int b = f - 16;
-      const int pair = min(nt * kGPairs + (b >> 1), n_pairs - 1);  // clamped pairs: loaded, never stored
-      src[u] = W + ((size_t)g * n_pairs + pair) * nS * 1024 + (b & 1) * 512 + lane * 8;
-    }
-  }
-  // per stage, an activation fragment advances 32 elements along its row, a
-  // weight fragment one packed k-step (1024 elements)
-  const size_t step = wave < 4 ? kGK : 1024;
-
+  // activation loads: wavefront w fetches row blocks 2 w and 2 w + 1 of each
+  // stage; weight loads: wavefront (wm, wn) fetches the fragments it uses
   const int wm = wave >> 2, wn = wave & 3;
+  const bf16_t* src[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int r = min(m0 + 16 * (wave * 2 + u) + (lane & 15), m1 - 1);  // rows past the group repeat a valid row
+    int t;
+    if (GATED) t = gather ? clampi(gather[r], 0, T - 1) : clampi(r - r_begin, 0, T - 1);
+    else t = r;
+    src[u] = x + (size_t)t * K + 8 * (lane >> 4);
+  }
+  const bf16_t* wsrc[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int pair = min(nt * kGPairs + wn * 2 + q, n_pairs - 1);  // clamped pairs: loaded, never stored
+    wsrc[q] = W + ((size_t)g * n_pairs + pair) * nS * 1024 + lane * 8;
+  }
+
   f32x4_t acc[8][2][2];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
@@ -176,22 +194,54 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(
 #pragma unroll
       for (int h = 0; h < 2; ++h) acc[i][q][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  char* const mine = lds + wave * 4 * 1024;  // this wavefront's 4 fragments of a stage buffer
+  // Stage s multiplies row blocks 0-3, waits at a barrier until stage s + 1
+  // has landed, issues the activation loads of stage s + kGAhead into the
+  // buffer of stage s - 1 (every wavefront is past it), multiplies row blocks
+  // 4-7, and refills its weight slot with stage s + kGAhead.  So no barrier
+  // sits between two stages: the LDS reads of stage s + 1 start while the
+  // last MFMAs of stage s run.  The loads of stage s + kGAhead (act, w) form
+  // one group, the groups issued in stage order (the prologue's kept apart by
+  // compiler fences; inside a group the compiler may reorder).  Halfway
+  // through stage s, waiting until at most kGLoads (kGAhead - 2) of this
+  // wavefront's loads are outstanding leaves only the groups of stages
+  // s+2 .. s+kGAhead-1.  nS is a multiple of kGAhead, at least 2 kGAhead.
+  static_assert(kGAhead >= 2, "the half-stage wait needs stage s + 1 issued");
+  char* const mine = lds + wave * 2 * 1024;  // this wavefront's 2 fragments of a stage buffer
+  uint4 bw[kGAhead][2][2];
 #pragma unroll
-  for (int s = 0; s < kGRing - 1; ++s)
-    if (s < nS) {
+  for (int t = 0; t < kGAhead; ++t) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) load_lds16(src[u] + s * step, mine + s * kGStage + u * 1024);
+    for (int u = 0; u < 2; ++u) load_lds16(src[u] + t * kGK, mine + t * kGStage + u * 1024);
+    load_weights(bw[t], wsrc, t);
+    asm volatile("" ::: "memory");
+  }
+  wait_barrier<kGLoads * (kGAhead - 1)>();  // stage 0
+  int s0 = 0;
+  do {  // nS >= 2 kGAhead: at least one trip
+#pragma unroll
+    for (int t = 0; t < kGAhead; ++t) {
+      const int s = s0 + t, sn = s + kGAhead;
+      // sn % kGRing is the buffer of stage s - 1
+      gemm_stage<kGLoads * (kGAhead - 2)>(lds + (s % kGRing) * kGStage, mine + (sn % kGRing) * kGStage, src,
+                                          (size_t)sn * kGK, bw[t], acc, wm, lane);
+      load_weights(bw[t], wsrc, sn);
     }
-  for (int s = 0; s < nS; ++s) {
-    // this wavefront's loads of stage s are done once at most those of the
-    // (up to two) later stages are outstanding
-    if (s + 2 < nS) wait_barrier<8>();
-    else if (s + 1 < nS) wait_barrier<4>();
-    else wait_barrier<0>();
-    const int sn = s + kGRing - 1;  // refills the buffer of stage s-1, which every wavefront has finished
-    gemm_stage(lds + (s % kGRing) * kGStage, mine + (sn % kGRing) * kGStage, sn < nS, src, sn * step, acc, wm,
-               wn, lane);
+    s0 += kGAhead;
+  } while (s0 < nS - kGAhead);
+  // the last kGAhead stages issue nothing; halfway through stage
+  // nS - kGAhead + t the groups of the stages after s + 1 are outstanding
+#pragma unroll
+  for (int t = 0; t < kGAhead; ++t) {
+    const char* cur = lds + ((nS - kGAhead + t) % kGRing) * kGStage;
+    gemm_half(cur, 0, bw[t], acc, wm, lane);
+    if (t + 2 < kGAhead) {
+      if (t == 0) wait_barrier<kGLoads * (kGAhead - 2)>();
+      else if (t == 1) wait_barrier<kGLoads * (kGAhead - 3 > 0 ? kGAhead - 3 : 0)>();
+      else wait_barrier<0>();
+    } else if (t + 2 == kGAhead) {
+      wait_barrier<0>();
+    }
+    gemm_half(cur, 4, bw[t], acc, wm, lane);
   }
 
   // lane holds D[4 (lane/16) + v][lane % 16]: weight rows (output columns)
@@ -229,7 +279,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(
 }  // namespace
 
 bool gemm_path_ok(int K, int N, int max_rows) {
-  return max_rows >= kGemmMinRows && K % kGK == 0 && N % 16 == 0;
+  return max_rows >= kGemmMinRows && K >= 2 * kGK * kGAhead && K % (kGK * kGAhead) == 0 && N % 16 == 0;
 }
 
 template <bool GATED>
