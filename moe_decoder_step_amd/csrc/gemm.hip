@@ -74,7 +74,13 @@ __device__ __forceinline__ void wait_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
-__device__ __forceinline__ float silu_g(float z) { return z / (1.0f + expf(-z)); }
+// silu(z) = z / (1 + e^-z) from the hardware exp2 and reciprocal (v_exp_f32,
+// v_rcp_f32, about 1 ulp each; the result is then rounded to bf16).  The
+// epilogue evaluates 64 per lane: with libm's expf and an IEEE division it
+// took 8 us of a 48 us block.
+__device__ __forceinline__ float silu_g(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.44269504088896341f));
+}
 
 __device__ __forceinline__ uint4 lds16(const char* p) { return *reinterpret_cast<const uint4*>(p); }
 
