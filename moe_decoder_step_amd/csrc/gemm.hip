@@ -123,25 +123,63 @@ __device__ __forceinline__ void load_weights(uint4 (&bw)[2][2], const bf16_t* co
       bw[q][h] = *reinterpret_cast<const uint4*>(wsrc[q] + (size_t)s * 1024 + h * 512);
 }
 
+// A tile: an M-tile (rows m0 .. m1-1 of group g, which starts at row rb; up
+// to 256) by column tile nt.  g < 0: the tile index is past the last M-tile.
+struct GTile {
+  int g, m0, m1, rb, nt;
+};
+
+// Tile index jt -> tile.  M-tile m runs on XCD m % 8 (tile jt runs on XCD
+// jt % 8) and its column tiles are consecutive tile indices of that XCD, so
+// they share the XCD's L2 copy of the activation rows, and neighbouring
+// M-tiles of one group share the weight tiles.  s_first[g] counts the
+// M-tiles of the groups before g (s_first[G]: all of them); s_r0, s_r1 are
+// the groups' row ranges.  Every lane returns the same tile.
+__device__ __forceinline__ GTile find_tile(int jt, int n_ntiles, int G, const int* s_first, const int* s_r0,
+                                           const int* s_r1, int lane) {
+  GTile tl;
+  const int j = jt >> 3;
+  tl.nt = j % n_ntiles;
+  const int m = (j / n_ntiles) * 8 + (jt & 7);
+  tl.g = -1;
+  tl.m0 = tl.m1 = tl.rb = 0;
+  if (m >= s_first[G]) return tl;
+  int hit = -1;  // the one group with s_first[g] <= m < s_first[g + 1]
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int g = lane + h * kWave;
+    if (g < G && m >= s_first[g] && m < s_first[g + 1]) hit = g;
+  }
+  const unsigned long long bal = __ballot(hit >= 0);
+  const int g = __builtin_amdgcn_readlane(hit, __ffsll((long long)bal) - 1);
+  tl.g = g;
+  tl.rb = s_r0[g];
+  tl.m0 = tl.rb + (m - s_first[g]) * kGM;
+  tl.m1 = s_r1[g];
+  return tl;
+}
+
+// Persistent: block b takes tiles b, b + gridDim.x, ... (gridDim.x a
+// multiple of 8, so every tile keeps its XCD).  The stages of a block's
+// tiles form one stream: the last kGAhead stages of a tile issue the first
+// kGAhead stages of the next, so the pipeline never drains between tiles and
+// the epilogue of one tile overlaps the loads of the next.
 template <bool GATED>
 __global__ __launch_bounds__(kGThreads) void gemm_kernel(
     const bf16_t* __restrict__ x, const int32_t* __restrict__ gather, const int32_t* __restrict__ offsets,
     int G, int n_rows, int T, const bf16_t* __restrict__ W, int K, int N, int n_pairs, int n_ntiles,
     bf16_t* __restrict__ out) {
   extern __shared__ __align__(16) char lds[];
-  __shared__ int s_g, s_m0, s_m1, s_rb;
+  __shared__ int s_first[2 * kWave + 1], s_r0[2 * kWave], s_r1[2 * kWave];
 
-  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
-  const int nt = j % n_ntiles;
-  const int m = (j / n_ntiles) * 8 + xcd;  // M-tile index, counted group by group
-  if (threadIdx.x < kWave) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (wave == 0) {
     // lane l counts the M-tiles of groups l and l + 64 (G <= 128); a prefix
-    // sum over the wavefront finds the group that holds M-tile m
-    const int l = threadIdx.x;
+    // sum over the wavefront numbers them
     int r0[2], r1[2], cnt[2], incl[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int g = l + h * kWave;
+      const int g = lane + h * kWave;
       r0[h] = g < G ? clampi(offsets[g], 0, n_rows) : 0;
       r1[h] = g < G ? clampi(offsets[g + 1], r0[h], n_rows) : 0;
       cnt[h] = (r1[h] - r0[h] + kGM - 1) / kGM;
@@ -149,48 +187,49 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(
 #pragma unroll
       for (int o = 1; o < kWave; o <<= 1) {
         const int v = __shfl_up(incl[h], o, kWave);
-        if (l >= o) incl[h] += v;
+        if (lane >= o) incl[h] += v;
       }
     }
     incl[1] += __shfl(incl[0], kWave - 1, kWave);
-    if (l == 0) s_g = -1;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int first = incl[h] - cnt[h];
-      if (m >= first && m < incl[h]) {
-        s_g = l + h * kWave;
-        s_m0 = r0[h] + (m - first) * kGM;
-        s_m1 = r1[h];
-        s_rb = r0[h];
-      }
+      const int g = lane + h * kWave;
+      s_first[g] = incl[h] - cnt[h];
+      s_r0[g] = r0[h];
+      s_r1[g] = r1[h];
     }
+    // groups from G on count no M-tiles: s_first[G .. 128] hold the total
+    if (lane == kWave - 1) s_first[2 * kWave] = incl[1];
   }
   __syncthreads();
-  const int g = s_g;
-  if (g < 0) return;
-  const int m0 = s_m0, m1 = s_m1, r_begin = s_rb;
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int nS = K / kGK;                 // stages = MFMA k-steps
+  int jt = blockIdx.x;
+  GTile cur = find_tile(jt, n_ntiles, G, s_first, s_r0, s_r1, lane);
+  if (cur.g < 0) return;
+
+  const int nS = K / kGK;  // stages = MFMA k-steps
+  const int wm = wave >> 2, wn = wave & 3;
 
   // activation loads: wavefront w fetches row blocks 2 w and 2 w + 1 of each
-  // stage; weight loads: wavefront (wm, wn) fetches the fragments it uses
-  const int wm = wave >> 2, wn = wave & 3;
-  const bf16_t* src[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int r = min(m0 + 16 * (wave * 2 + u) + (lane & 15), m1 - 1);  // rows past the group repeat a valid row
+  // stage (rows past the group repeat a valid row); weight loads: wavefront
+  // (wm, wn) fetches the fragments it uses (clamped pairs: loaded, never stored)
+  auto act_row = [&](const GTile& tl, int u) { return min(tl.m0 + 16 * (wave * 2 + u) + (lane & 15), tl.m1 - 1); };
+  auto act_src = [&](const GTile& tl, int u, int gv) {
     int t;
-    if (GATED) t = gather ? clampi(gather[r], 0, T - 1) : clampi(r - r_begin, 0, T - 1);
-    else t = r;
-    src[u] = x + (size_t)t * K + 8 * (lane >> 4);
-  }
+    if (GATED) t = gather ? clampi(gv, 0, T - 1) : clampi(act_row(tl, u) - tl.rb, 0, T - 1);
+    else t = act_row(tl, u);
+    return x + (size_t)t * K + 8 * (lane >> 4);
+  };
+  auto w_src = [&](const GTile& tl, int q) {
+    const int pair = min(tl.nt * kGPairs + wn * 2 + q, n_pairs - 1);
+    return W + ((size_t)tl.g * n_pairs + pair) * nS * 1024 + lane * 8;
+  };
+  const bf16_t* src[2];
   const bf16_t* wsrc[2];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int pair = min(nt * kGPairs + wn * 2 + q, n_pairs - 1);  // clamped pairs: loaded, never stored
-    wsrc[q] = W + ((size_t)g * n_pairs + pair) * nS * 1024 + lane * 8;
-  }
+  for (int u = 0; u < 2; ++u) src[u] = act_src(cur, u, GATED && gather ? gather[act_row(cur, u)] : 0);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) wsrc[q] = w_src(cur, q);
 
   f32x4_t acc[8][2][2];
 #pragma unroll
@@ -200,18 +239,21 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(
 #pragma unroll
       for (int h = 0; h < 2; ++h) acc[i][q][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Stage s multiplies row blocks 0-3, waits at a barrier until stage s + 1
-  // has landed, issues the activation loads of stage s + kGAhead into the
-  // buffer of stage s - 1 (every wavefront is past it), multiplies row blocks
-  // 4-7, and refills its weight slot with stage s + kGAhead.  So no barrier
-  // sits between two stages: the LDS reads of stage s + 1 start while the
-  // last MFMAs of stage s run.  The loads of stage s + kGAhead (act, w) form
-  // one group, the groups issued in stage order (the prologue's kept apart by
-  // compiler fences; inside a group the compiler may reorder).  Halfway
-  // through stage s, waiting until at most kGLoads (kGAhead - 2) of this
-  // wavefront's loads are outstanding leaves only the groups of stages
-  // s+2 .. s+kGAhead-1.  nS is a multiple of kGAhead, at least 2 kGAhead.
-  static_assert(kGAhead >= 2, "the half-stage wait needs stage s + 1 issued");
+  // Stage s multiplies row blocks 0-3, waits at a barrier until the next
+  // stage of the stream has landed, issues the activation loads kGAhead
+  // stages ahead into the buffer of the previous stage (every wavefront is
+  // past it), multiplies row blocks 4-7, and refills its weight slot kGAhead
+  // stages ahead.  So no barrier sits between two stages: the LDS reads of
+  // the next stage start while the last MFMAs of this one run.  The loads
+  // issued in one stage (act, w) form one group, the groups in stream order
+  // (the prologue's kept apart by compiler fences; inside a group the
+  // compiler may reorder).  Halfway through a stage, waiting until at most
+  // kGLoads (kGAhead - 2) of this wavefront's loads are outstanding leaves
+  // only the groups of the stages 2 .. kGAhead-1 ahead; other loads in the
+  // stream (the gathered row numbers of the next tile) only make that wait
+  // stricter.  nS is a multiple of kGAhead, at least 2 kGAhead, so a tile's
+  // stages use the weight slots 0 .. kGAhead-1 in turn.
+  static_assert(kGAhead >= 2, "the half-stage wait needs the next stage issued");
   char* const mine = lds + wave * 2 * 1024;  // this wavefront's 2 fragments of a stage buffer
   uint4 bw[kGAhead][2][2];
 #pragma unroll
@@ -221,71 +263,107 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(
     load_weights(bw[t], wsrc, t);
     asm volatile("" ::: "memory");
   }
-  wait_barrier<kGLoads * (kGAhead - 1)>();  // stage 0
-  int s0 = 0;
-  do {  // nS >= 2 kGAhead: at least one trip
+  wait_barrier<kGLoads * (kGAhead - 1)>();  // the first stage
+  int gb = 0;                               // stage buffer of the current stage
+  for (;;) {
+    const GTile nxt = find_tile(jt + (int)gridDim.x, n_ntiles, G, s_first, s_r0, s_r1, lane);
+    int gv[2] = {0, 0};  // the next tile's gathered row numbers
+    int sn_off = 0;
+    int s0 = 0;
+    do {
+      if (s0 == nS - kGAhead && nxt.g >= 0) {
+        // from here the loads kGAhead stages ahead are the next tile's
 #pragma unroll
-    for (int t = 0; t < kGAhead; ++t) {
-      const int s = s0 + t, sn = s + kGAhead;
-      // sn % kGRing is the buffer of stage s - 1
-      gemm_stage<kGLoads * (kGAhead - 2)>(lds + (s % kGRing) * kGStage, mine + (sn % kGRing) * kGStage, src,
-                                          (size_t)sn * kGK, bw[t], acc, wm, lane);
-      load_weights(bw[t], wsrc, sn);
-    }
-    s0 += kGAhead;
-  } while (s0 < nS - kGAhead);
-  // the last kGAhead stages issue nothing; halfway through stage
-  // nS - kGAhead + t the groups of the stages after s + 1 are outstanding
+        for (int u = 0; u < 2; ++u) src[u] = act_src(nxt, u, gv[u]);
 #pragma unroll
-  for (int t = 0; t < kGAhead; ++t) {
-    const char* cur = lds + ((nS - kGAhead + t) % kGRing) * kGStage;
-    gemm_half(cur, 0, bw[t], acc, wm, lane);
-    if (t + 2 < kGAhead) {
-      if (t == 0) wait_barrier<kGLoads * (kGAhead - 2)>();
-      else if (t == 1) wait_barrier<kGLoads * (kGAhead - 3 > 0 ? kGAhead - 3 : 0)>();
-      else wait_barrier<0>();
-    } else if (t + 2 == kGAhead) {
-      wait_barrier<0>();
-    }
-    gemm_half(cur, 4, bw[t], acc, wm, lane);
-  }
+        for (int q = 0; q < 2; ++q) wsrc[q] = w_src(nxt, q);
+        sn_off = -nS;
+      }
+      // Loaded in the tile's first pass of this loop and read at the switch
+      // above in a later pass (nS >= 2 kGAhead): the half-stage waits in
+      // between retire them, so the compiler adds no wait at the switch (a
+      // wait there for a load issued just before would drain every load in
+      // flight).
+      if (GATED && gather && s0 == 0 && nxt.g >= 0) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) gv[u] = gather[act_row(nxt, u)];
+      }
+#pragma unroll
+      for (int t = 0; t < kGAhead; ++t) {
+        // the stage kGAhead ahead in the stream; after the last tile, stage
+        // nS - 1 of this one again (loaded, never read)
+        const int sn = min(s0 + t + kGAhead + sn_off, nS - 1);
+        const int nb = gb == 0 ? kGRing - 1 : gb - 1;  // the previous stage's buffer
+        gemm_stage<kGLoads * (kGAhead - 2)>(lds + gb * kGStage, mine + nb * kGStage, src, (size_t)sn * kGK, bw[t],
+                                            acc, wm, lane);
+        load_weights(bw[t], wsrc, sn);
+        gb = gb == kGRing - 1 ? 0 : gb + 1;
+      }
+      s0 += kGAhead;
+    } while (s0 < nS);
 
-  // lane holds D[4 (lane/16) + v][lane % 16]: weight rows (output columns)
-  // 4 (lane/16) .. +3 of its fragment, for row lane % 16 of the row block
+    // lane holds D[4 (lane/16) + v][lane % 16]: weight rows (output columns)
+    // 4 (lane/16) .. +3 of its fragment, for row lane % 16 of the row block
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = m0 + (wm * 8 + i) * 16 + (lane & 15);
-    if (row >= m1) continue;
+    for (int i = 0; i < 8; ++i) {
+      const int row = cur.m0 + (wm * 8 + i) * 16 + (lane & 15);
+      if (row >= cur.m1) continue;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int pair = nt * kGPairs + wn * 2 + q;
-      if (GATED) {
-        if (pair >= n_pairs) continue;
-        const f32x4_t a = acc[i][q][0], b = acc[i][q][1];
-        uint2 pk;
-        pk.x = pack2(f32_to_bf16(silu_g(a[0]) * b[0]), f32_to_bf16(silu_g(a[1]) * b[1]));
-        pk.y = pack2(f32_to_bf16(silu_g(a[2]) * b[2]), f32_to_bf16(silu_g(a[3]) * b[3]));
-        *reinterpret_cast<uint2*>(out + (size_t)row * N + pair * 16 + 4 * (lane >> 4)) = pk;
-      } else {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int col = pair * 32 + h * 16 + 4 * (lane >> 4);
-          if (col >= N) continue;
-          const f32x4_t a = acc[i][q][h];
+      for (int q = 0; q < 2; ++q) {
+        const int pair = cur.nt * kGPairs + wn * 2 + q;
+        if (GATED) {
+          if (pair >= n_pairs) continue;
+          const f32x4_t a = acc[i][q][0], b = acc[i][q][1];
           uint2 pk;
-          pk.x = pack2(f32_to_bf16(a[0]), f32_to_bf16(a[1]));
-          pk.y = pack2(f32_to_bf16(a[2]), f32_to_bf16(a[3]));
-          *reinterpret_cast<uint2*>(out + (size_t)row * N + col) = pk;
+          pk.x = pack2(f32_to_bf16(silu_g(a[0]) * b[0]), f32_to_bf16(silu_g(a[1]) * b[1]));
+          pk.y = pack2(f32_to_bf16(silu_g(a[2]) * b[2]), f32_to_bf16(silu_g(a[3]) * b[3]));
+          *reinterpret_cast<uint2*>(out + (size_t)row * N + pair * 16 + 4 * (lane >> 4)) = pk;
+        } else {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int col = pair * 32 + h * 16 + 4 * (lane >> 4);
+            if (col >= N) continue;
+            const f32x4_t a = acc[i][q][h];
+            uint2 pk;
+            pk.x = pack2(f32_to_bf16(a[0]), f32_to_bf16(a[1]));
+            pk.y = pack2(f32_to_bf16(a[2]), f32_to_bf16(a[3]));
+            *reinterpret_cast<uint2*>(out + (size_t)row * N + col) = pk;
+          }
         }
       }
     }
+    if (nxt.g < 0) break;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) acc[i][q][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    cur = nxt;
+    jt += gridDim.x;
   }
+  // the LDS must not be released with loads into it in flight
+  __builtin_amdgcn_s_waitcnt(0);
 }
 
 }  // namespace
 
 bool gemm_path_ok(int K, int N, int max_rows) {
   return max_rows >= kGemmMinRows && K >= 2 * kGK * kGAhead && K % (kGK * kGAhead) == 0 && N % 16 == 0;
+}
+
+// blocks of the persistent grid: one per CU (one 8-wavefront block fills a
+// CU's registers), a multiple of 8 so that every tile keeps its XCD
+static int persistent_blocks() {
+  static int cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8) cus = 256;
+    cache[dev] = cus / 8 * 8;
+  }
+  return cache[dev];
 }
 
 template <bool GATED>
@@ -295,7 +373,8 @@ hipError_t launch_gemm_t(const bf16_t* x, const int32_t* gather, const int32_t* 
   const int n_ntiles = (n_pairs + kGPairs - 1) / kGPairs;
   // M-tiles <= sum over groups of ceil(rows / 256) <= n_rows / 256 + G
   const int mtiles = n_rows / kGM + G;
-  const long long blocks = 8LL * ((mtiles + 7) / 8) * n_ntiles;
+  const long long tiles = 8LL * ((mtiles + 7) / 8) * n_ntiles;
+  const long long blocks = std::min<long long>(tiles, persistent_blocks());
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<GATED>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGLds);
   if (e != hipSuccess) return e;
