@@ -7,35 +7,25 @@
 //   gated stage: 8 (gate 16-row, up 16-row) pairs = 128 activation columns;
 //   down stage:  8 pairs of 16 weight rows = 256 output columns.
 // The reduction runs in stages of 32 (one MFMA k-step).  A stage's 16
-// activation fragments (16 KB) go through LDS, its weight fragments straight
-// into registers.  A 1 KB fragment holds, in lane order, the 16 rows x 32
-// k-elements one wavefront feeds to v_mfma_f32_16x16x32_bf16, so every LDS
-// read is 1 KB of consecutive bytes (no bank conflicts).  Activation
+// activation fragments (16 KB) go through LDS, its 16 weight fragments
+// straight into registers.  A 1 KB fragment holds, in lane order, the 16 rows
+// x 32 k-elements one wavefront feeds to v_mfma_f32_16x16x32_bf16, so every
+// LDS read is 1 KB of consecutive bytes (no bank conflicts).  Activation
 // fragments are loaded from global memory straight into LDS
 // (global_load_lds_dwordx4: lane l's 16 bytes land at fragment offset 16 l),
-// rows gathered per lane, into a ring of kGAhead + 1 stage buffers; each
-// wavefront loads the 4 packed weight fragments it multiplies (1 KB each, as
-// they lie in memory, moe_pack_weights) into a register ring of kGAhead
-// stages.  Both run kGAhead stages ahead of the multiply.  Per stage: wait
-// for this wavefront's loads of the stage, one barrier (after it every
-// wavefront's activation loads of the stage have landed and every wavefront
-// has finished the stage whose buffer is refilled next), issue the
-// activation loads kGAhead stages ahead, multiply, then refill the register
-// slot just used with the weights kGAhead stages ahead.  Keeping the weights
-// out of LDS cuts its traffic per stage from 96 KB of reads and 32 KB of
-// writes to 64 KB and 16 KB; each weight fragment is fetched by the two
-// wavefronts that use it (the second read hits in cache).
+// rows gathered per lane, into a ring of kGAheadA + 1 stage buffers, kGAheadA
+// stages ahead of the multiply; each wavefront loads the 2 packed weight
+// fragments it multiplies (1 KB each, as they lie in memory,
+// moe_pack_weights) into a register ring, kGAhead stages ahead.
 //
-// Wavefront (wm, wn) = (w / 4, w % 4) computes rows 128 wm .. +127 (8 MFMA
-// row blocks) by pairs 2 wn, 2 wn + 1 (4 weight fragments): 32 MFMAs per
-// stage, 128 fp32 accumulators per lane.  The weights are the MFMA A operand
-// and the activations the B operand, so a lane ends with 4 consecutive output
-// columns of one row (8-byte stores).
+// Wavefront w computes all 256 rows (16 MFMA row blocks) by pair w (2 weight
+// fragments): 32 MFMAs per stage, 128 fp32 accumulators per lane.  So every
+// weight fragment is fetched once per block (32 KB per stage from memory in
+// all), and every wavefront reads all 16 activation fragments of a stage
+// from LDS.  The weights are the MFMA A operand and the activations the B
+// operand, so a lane ends with 4 consecutive output columns of one row
+// (8-byte stores).
 //
-// M-tiles are numbered group by group; M-tile m runs on XCD m % 8 (block b
-// runs on XCD b % 8) and its column tiles are consecutive blocks of that XCD,
-// so they share the XCD's L2 copy of the activation rows, and neighbouring
-// M-tiles of one group share the weight tiles.
 // The fp32 accumulation order along K is fixed: 32 elements per MFMA, in
 // increasing k.
 #include "common.hpp"
@@ -48,12 +38,13 @@ namespace {
 constexpr int kGM = 256;                  // rows per tile
 constexpr int kGPairs = 8;                // weight-row pairs per tile
 constexpr int kGK = 32;                   // reduction elements per stage
-constexpr int kGAhead = 4;                // stages in flight (weights and activations)
-constexpr int kGRing = kGAhead + 1;       // activation stage buffers
+constexpr int kGAhead = 4;                // weight stages in flight (register ring)
+constexpr int kGAheadA = 4;               // activation stages in flight (LDS ring), a multiple of kGAhead
+constexpr int kGRing = kGAheadA + 1;      // activation stage buffers
 constexpr int kGWaves = 8;
 constexpr int kGThreads = kGWaves * 64;
 constexpr int kGStage = 16384;            // activation bytes per stage
-constexpr int kGLoads = 6;                // loads per wavefront and stage: 2 activation + 4 weight fragments
+constexpr int kGLoads = 4;                // loads per wavefront and stage: 2 activation + 2 weight fragments
 constexpr size_t kGLds = (size_t)kGRing * kGStage;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -86,15 +77,13 @@ __device__ __forceinline__ uint4 lds16(const char* p) { return *reinterpret_cast
 
 // Row blocks i0 .. i0 + 3 of one stage: multiply the stage in `cur` with the
 // weight fragments `bw`.
-__device__ __forceinline__ void gemm_half(const char* cur, int i0, const uint4 (&bw)[2][2],
-                                          f32x4_t (&acc)[8][2][2], int wm, int lane) {
+__device__ __forceinline__ void gemm_half(const char* cur, int i0, const uint4 (&bw)[2],
+                                          f32x4_t (&acc)[16][2], int lane) {
 #pragma unroll
-  for (int i = i0; i < i0 + 4; ++i) {
-    const bf16x8_t xa = as_bf16x8(lds16(cur + (wm * 8 + i) * 1024 + lane * 16));
+  for (int i = i0; i < i0 + 8; ++i) {
+    const bf16x8_t xa = as_bf16x8(lds16(cur + i * 1024 + lane * 16));
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) acc[i][q][h] = mfma16x16x32(as_bf16x8(bw[q][h]), xa, acc[i][q][h]);
+    for (int h = 0; h < 2; ++h) acc[i][h] = mfma16x16x32(as_bf16x8(bw[h]), xa, acc[i][h]);
   }
 }
 
@@ -105,22 +94,19 @@ __device__ __forceinline__ void gemm_half(const char* cur, int i0, const uint4 (
 // the loads into `nxt` still in flight, so it adds no wait for them.
 template <int N>
 __device__ __forceinline__ void gemm_stage(const char* __restrict__ cur, char* __restrict__ nxt,
-                                           const bf16_t* const (&src)[2], size_t step, const uint4 (&bw)[2][2],
-                                           f32x4_t (&acc)[8][2][2], int wm, int lane) {
-  gemm_half(cur, 0, bw, acc, wm, lane);
+                                           const bf16_t* const (&src)[2], size_t step, const uint4 (&bw)[2],
+                                           f32x4_t (&acc)[16][2], int lane) {
+  gemm_half(cur, 0, bw, acc, lane);
   wait_barrier<N>();
 #pragma unroll
   for (int u = 0; u < 2; ++u) load_lds16(src[u] + step, nxt + u * 1024);
-  gemm_half(cur, 4, bw, acc, wm, lane);
+  gemm_half(cur, 8, bw, acc, lane);
 }
 
-// this wavefront's 4 weight fragments of stage s: pairs 2 wn + q, sets h
-__device__ __forceinline__ void load_weights(uint4 (&bw)[2][2], const bf16_t* const (&wsrc)[2], int s) {
+// this wavefront's 2 weight fragments of stage s (its pair; sets h = 0, 1)
+__device__ __forceinline__ void load_weights(uint4 (&bw)[2], const bf16_t* wsrc, int s) {
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      bw[q][h] = *reinterpret_cast<const uint4*>(wsrc[q] + (size_t)s * 1024 + h * 512);
+  for (int h = 0; h < 2; ++h) bw[h] = *reinterpret_cast<const uint4*>(wsrc + (size_t)s * 1024 + h * 512);
 }
 
 // A tile: an M-tile (rows m0 .. m1-1 of group g, which starts at row rb; up
@@ -208,11 +194,10 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(
   if (cur.g < 0) return;
 
   const int nS = K / kGK;  // stages = MFMA k-steps
-  const int wm = wave >> 2, wn = wave & 3;
 
   // activation loads: wavefront w fetches row blocks 2 w and 2 w + 1 of each
   // stage (rows past the group repeat a valid row); weight loads: wavefront
-  // (wm, wn) fetches the fragments it uses (clamped pairs: loaded, never stored)
+  // w fetches pair w of the tile (clamped pairs: loaded, never stored)
   auto act_row = [&](const GTile& tl, int u) { return min(tl.m0 + 16 * (wave * 2 + u) + (lane & 15), tl.m1 - 1); };
   auto act_src = [&](const GTile& tl, int u, int gv) {
     int t;
@@ -220,24 +205,21 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(
     else t = act_row(tl, u);
     return x + (size_t)t * K + 8 * (lane >> 4);
   };
-  auto w_src = [&](const GTile& tl, int q) {
-    const int pair = min(tl.nt * kGPairs + wn * 2 + q, n_pairs - 1);
+  auto w_src = [&](const GTile& tl) {
+    const int pair = min(tl.nt * kGPairs + wave, n_pairs - 1);
     return W + ((size_t)tl.g * n_pairs + pair) * nS * 1024 + lane * 8;
   };
   const bf16_t* src[2];
-  const bf16_t* wsrc[2];
+  const bf16_t* wsrc;
 #pragma unroll
   for (int u = 0; u < 2; ++u) src[u] = act_src(cur, u, GATED && gather ? gather[act_row(cur, u)] : 0);
-#pragma unroll
-  for (int q = 0; q < 2; ++q) wsrc[q] = w_src(cur, q);
+  wsrc = w_src(cur);
 
-  f32x4_t acc[8][2][2];
+  f32x4_t acc[16][2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 16; ++i)
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) acc[i][q][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < 2; ++h) acc[i][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // Stage s multiplies row blocks 0-3, waits at a barrier until the next
   // stage of the stream has landed, issues the activation loads kGAhead
@@ -255,32 +237,38 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(
   // stages use the weight slots 0 .. kGAhead-1 in turn.
   static_assert(kGAhead >= 2, "the half-stage wait needs the next stage issued");
   char* const mine = lds + wave * 2 * 1024;  // this wavefront's 2 fragments of a stage buffer
-  uint4 bw[kGAhead][2][2];
+  static_assert(kGAheadA >= kGAhead && kGAheadA % kGAhead == 0, "activations run at least as far ahead");
+  uint4 bw[kGAhead][2];
 #pragma unroll
-  for (int t = 0; t < kGAhead; ++t) {
+  for (int t = 0; t < kGAheadA; ++t) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) load_lds16(src[u] + t * kGK, mine + t * kGStage + u * 1024);
-    load_weights(bw[t], wsrc, t);
+    if (t < kGAhead) load_weights(bw[t], wsrc, t);
     asm volatile("" ::: "memory");
   }
-  wait_barrier<kGLoads * (kGAhead - 1)>();  // the first stage
+  // the first stage: after its weights come kGAhead - 1 groups of both and
+  // kGAheadA - kGAhead activation-only groups
+  wait_barrier<kGLoads * (kGAhead - 1) + 2 * (kGAheadA - kGAhead)>();
   int gb = 0;                               // stage buffer of the current stage
   for (;;) {
     const GTile nxt = find_tile(jt + (int)gridDim.x, n_ntiles, G, s_first, s_r0, s_r1, lane);
     int gv[2] = {0, 0};  // the next tile's gathered row numbers
-    int sn_off = 0;
+    int sa_off = 0, sw_off = 0;
     int s0 = 0;
     do {
-      if (s0 == nS - kGAhead && nxt.g >= 0) {
-        // from here the loads kGAhead stages ahead are the next tile's
+      if (s0 == nS - kGAheadA && nxt.g >= 0) {
+        // from here the activation loads kGAheadA stages ahead are the next tile's
 #pragma unroll
         for (int u = 0; u < 2; ++u) src[u] = act_src(nxt, u, gv[u]);
-#pragma unroll
-        for (int q = 0; q < 2; ++q) wsrc[q] = w_src(nxt, q);
-        sn_off = -nS;
+        sa_off = -nS;
+      }
+      if (s0 == nS - kGAhead && nxt.g >= 0) {
+        // and from here the weight loads kGAhead stages ahead
+        wsrc = w_src(nxt);
+        sw_off = -nS;
       }
       // Loaded in the tile's first pass of this loop and read at the switch
-      // above in a later pass (nS >= 2 kGAhead): the half-stage waits in
+      // above in a later pass (nS >= kGAheadA + kGAhead): the half-stage waits in
       // between retire them, so the compiler adds no wait at the switch (a
       // wait there for a load issued just before would drain every load in
       // flight).
@@ -290,13 +278,14 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(
       }
 #pragma unroll
       for (int t = 0; t < kGAhead; ++t) {
-        // the stage kGAhead ahead in the stream; after the last tile, stage
-        // nS - 1 of this one again (loaded, never read)
-        const int sn = min(s0 + t + kGAhead + sn_off, nS - 1);
+        // the stages kGAheadA and kGAhead ahead in the stream; after the last
+        // tile, stage nS - 1 of this one again (loaded, never read)
+        const int sna = min(s0 + t + kGAheadA + sa_off, nS - 1);
+        const int snw = min(s0 + t + kGAhead + sw_off, nS - 1);
         const int nb = gb == 0 ? kGRing - 1 : gb - 1;  // the previous stage's buffer
-        gemm_stage<kGLoads * (kGAhead - 2)>(lds + gb * kGStage, mine + nb * kGStage, src, (size_t)sn * kGK, bw[t],
-                                            acc, wm, lane);
-        load_weights(bw[t], wsrc, sn);
+        gemm_stage<kGLoads * (kGAhead - 2)>(lds + gb * kGStage, mine + nb * kGStage, src, (size_t)sna * kGK, bw[t],
+                                            acc, lane);
+        load_weights(bw[t], wsrc, snw);
         gb = gb == kGRing - 1 ? 0 : gb + 1;
       }
       s0 += kGAhead;
@@ -304,41 +293,36 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(
 
     // lane holds D[4 (lane/16) + v][lane % 16]: weight rows (output columns)
     // 4 (lane/16) .. +3 of its fragment, for row lane % 16 of the row block
+    const int pair = cur.nt * kGPairs + wave;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = cur.m0 + (wm * 8 + i) * 16 + (lane & 15);
+    for (int i = 0; i < 16; ++i) {
+      const int row = cur.m0 + i * 16 + (lane & 15);
       if (row >= cur.m1) continue;
+      if (GATED) {
+        if (pair >= n_pairs) continue;
+        const f32x4_t a = acc[i][0], b = acc[i][1];
+        uint2 pk;
+        pk.x = pack2(f32_to_bf16(silu_g(a[0]) * b[0]), f32_to_bf16(silu_g(a[1]) * b[1]));
+        pk.y = pack2(f32_to_bf16(silu_g(a[2]) * b[2]), f32_to_bf16(silu_g(a[3]) * b[3]));
+        *reinterpret_cast<uint2*>(out + (size_t)row * N + pair * 16 + 4 * (lane >> 4)) = pk;
+      } else {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int pair = cur.nt * kGPairs + wn * 2 + q;
-        if (GATED) {
-          if (pair >= n_pairs) continue;
-          const f32x4_t a = acc[i][q][0], b = acc[i][q][1];
+        for (int h = 0; h < 2; ++h) {
+          const int col = pair * 32 + h * 16 + 4 * (lane >> 4);
+          if (col >= N) continue;
+          const f32x4_t a = acc[i][h];
           uint2 pk;
-          pk.x = pack2(f32_to_bf16(silu_g(a[0]) * b[0]), f32_to_bf16(silu_g(a[1]) * b[1]));
-          pk.y = pack2(f32_to_bf16(silu_g(a[2]) * b[2]), f32_to_bf16(silu_g(a[3]) * b[3]));
-          *reinterpret_cast<uint2*>(out + (size_t)row * N + pair * 16 + 4 * (lane >> 4)) = pk;
-        } else {
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int col = pair * 32 + h * 16 + 4 * (lane >> 4);
-            if (col >= N) continue;
-            const f32x4_t a = acc[i][q][h];
-            uint2 pk;
-            pk.x = pack2(f32_to_bf16(a[0]), f32_to_bf16(a[1]));
-            pk.y = pack2(f32_to_bf16(a[2]), f32_to_bf16(a[3]));
-            *reinterpret_cast<uint2*>(out + (size_t)row * N + col) = pk;
-          }
+          pk.x = pack2(f32_to_bf16(a[0]), f32_to_bf16(a[1]));
+          pk.y = pack2(f32_to_bf16(a[2]), f32_to_bf16(a[3]));
+          *reinterpret_cast<uint2*>(out + (size_t)row * N + col) = pk;
         }
       }
     }
     if (nxt.g < 0) break;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 16; ++i)
 #pragma unroll
-      for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) acc[i][q][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int h = 0; h < 2; ++h) acc[i][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     cur = nxt;
     jt += gridDim.x;
   }
@@ -349,7 +333,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(
 }  // namespace
 
 bool gemm_path_ok(int K, int N, int max_rows) {
-  return max_rows >= kGemmMinRows && K >= 2 * kGK * kGAhead && K % (kGK * kGAhead) == 0 && N % 16 == 0;
+  return max_rows >= kGemmMinRows && K >= kGK * (kGAheadA + kGAhead) && K % (kGK * kGAhead) == 0 && N % 16 == 0;
 }
 
 // blocks of the persistent grid: one per CU (one 8-wavefront block fills a
