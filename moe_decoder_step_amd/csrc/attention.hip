@@ -282,7 +282,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
   }
   const int H = n_heads * kD;
   bf16_t* out = o + (size_t)(b * P + i) * H + hd * kD + 2 * lane;
-  *reinterpret_cast<uint32_t*>(out) = pack2(f32_to_bf16(a0 / Ls), f32_to_bf16(a1 / Ls));
+  *reinterpret_cast<uint32_t*>(out) = pack_bf16x2(a0 / Ls, a1 / Ls);
 }
 
 __global__ void commit_kernel(const int32_t* __restrict__ n_commit, int B, int32_t* __restrict__ lengths) {

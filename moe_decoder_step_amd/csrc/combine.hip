@@ -20,10 +20,10 @@ __device__ __forceinline__ void load8(const float* p, float* f) {
 }
 __device__ __forceinline__ void store8(bf16_t* p, const float* f) {
   uint4 o;
-  o.x = pack2(f32_to_bf16(f[0]), f32_to_bf16(f[1]));
-  o.y = pack2(f32_to_bf16(f[2]), f32_to_bf16(f[3]));
-  o.z = pack2(f32_to_bf16(f[4]), f32_to_bf16(f[5]));
-  o.w = pack2(f32_to_bf16(f[6]), f32_to_bf16(f[7]));
+  o.x = pack_bf16x2(f[0], f[1]);
+  o.y = pack_bf16x2(f[2], f[3]);
+  o.z = pack_bf16x2(f[4], f[5]);
+  o.w = pack_bf16x2(f[6], f[7]);
   *reinterpret_cast<uint4*>(p) = o;
 }
 __device__ __forceinline__ void store8(float* p, const float* f) {

@@ -18,13 +18,18 @@ typedef uint16_t bf16_t;
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+// fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.  One
+// v_cvt_pk_bf16_f32 (gfx950); over random, denormal, tie and near-tie bit
+// patterns it gives the same bits as the rounding done on the integer bits
+// (add 0x7fff plus the lowest kept bit, keep the high half; NaN: set the
+// quiet bit).
+typedef float f32x2_cvt_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_cvt_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_cvt_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_cvt_t));
 }
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) { return (bf16_t)(pack_bf16x2(f, 0.f) & 0xffffu); }
 
 // fp64 -> bf16 in a single rounding step (nearest, ties to even): the 45 low
 // mantissa bits of the double are rounded away by an integer add, then the

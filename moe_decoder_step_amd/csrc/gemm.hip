@@ -302,8 +302,8 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(
         if (pair >= n_pairs) continue;
         const f32x4_t a = acc[i][0], b = acc[i][1];
         uint2 pk;
-        pk.x = pack2(f32_to_bf16(silu_g(a[0]) * b[0]), f32_to_bf16(silu_g(a[1]) * b[1]));
-        pk.y = pack2(f32_to_bf16(silu_g(a[2]) * b[2]), f32_to_bf16(silu_g(a[3]) * b[3]));
+        pk.x = pack_bf16x2(silu_g(a[0]) * b[0], silu_g(a[1]) * b[1]);
+        pk.y = pack_bf16x2(silu_g(a[2]) * b[2], silu_g(a[3]) * b[3]);
         *reinterpret_cast<uint2*>(out + (size_t)row * N + pair * 16 + 4 * (lane >> 4)) = pk;
       } else {
 #pragma unroll
@@ -312,8 +312,8 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(
           if (col >= N) continue;
           const f32x4_t a = acc[i][h];
           uint2 pk;
-          pk.x = pack2(f32_to_bf16(a[0]), f32_to_bf16(a[1]));
-          pk.y = pack2(f32_to_bf16(a[2]), f32_to_bf16(a[3]));
+          pk.x = pack_bf16x2(a[0], a[1]);
+          pk.y = pack_bf16x2(a[2], a[3]);
           *reinterpret_cast<uint2*>(out + (size_t)row * N + col) = pk;
         }
       }

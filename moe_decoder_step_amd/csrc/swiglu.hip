@@ -370,8 +370,8 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
     bf16_t* orow = out + (size_t)(mstart + row) * N + col0 + 4 * (lane >> 4);
     if (GATED) {
       uint2 pk;
-      pk.x = pack2(f32_to_bf16(silu(acc_a[0]) * acc_b[0]), f32_to_bf16(silu(acc_a[1]) * acc_b[1]));
-      pk.y = pack2(f32_to_bf16(silu(acc_a[2]) * acc_b[2]), f32_to_bf16(silu(acc_a[3]) * acc_b[3]));
+      pk.x = pack_bf16x2(silu(acc_a[0]) * acc_b[0], silu(acc_a[1]) * acc_b[1]);
+      pk.y = pack_bf16x2(silu(acc_a[2]) * acc_b[2], silu(acc_a[3]) * acc_b[3]);
       *reinterpret_cast<uint2*>(orow) = pk;
     } else {
       if (res) {
@@ -390,10 +390,10 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
         acc_b[2] = add(acc_b[2], rb2.y & 0xffffu); acc_b[3] = add(acc_b[3], rb2.y >> 16);
       }
       uint2 pa, pb;
-      pa.x = pack2(f32_to_bf16(acc_a[0]), f32_to_bf16(acc_a[1]));
-      pa.y = pack2(f32_to_bf16(acc_a[2]), f32_to_bf16(acc_a[3]));
-      pb.x = pack2(f32_to_bf16(acc_b[0]), f32_to_bf16(acc_b[1]));
-      pb.y = pack2(f32_to_bf16(acc_b[2]), f32_to_bf16(acc_b[3]));
+      pa.x = pack_bf16x2(acc_a[0], acc_a[1]);
+      pa.y = pack_bf16x2(acc_a[2], acc_a[3]);
+      pb.x = pack_bf16x2(acc_b[0], acc_b[1]);
+      pb.y = pack_bf16x2(acc_b[2], acc_b[3]);
       *reinterpret_cast<uint2*>(orow) = pa;
       if (col0 + 16 < N) *reinterpret_cast<uint2*>(orow + 16) = pb;
     }
