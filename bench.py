@@ -371,6 +371,9 @@ def main() -> int:
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, sh, layers, w_lm, h_in, T)
+        one = cpu_baseline_1core(args, sh, layers, w_lm, h_in, T)
+        if one is not None:
+            out["cpu_baseline_1core"] = one
     print(json.dumps(out), flush=True)
     return 0
 
@@ -784,6 +787,24 @@ def cpu_baseline(args, sh, layers, w_lm, h_in, T) -> dict:
             "sample": f"{nl} of {sh.L} MoE layers on {nt} of {T} tokens ({t_layers:.1f}s) + LM head over "
                       f"{vs} of {sh.V} vocabulary rows ({t_lm:.1f}s), mean of {reps} runs, scaled to the full "
                       f"step ({t_step:.1f}s per step)"}
+
+
+def cpu_baseline_1core(args, sh, layers, w_lm, h_in, T):
+    """The same oracle with its BLAS pools held to one thread, on a smaller
+    sample (one MoE layer and an eighth of the LM head), scaled to the full
+    step; None when the thread pools cannot be limited."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:
+        return None
+    import copy
+    a = copy.copy(args)
+    a.cpu_layers, a.cpu_reps = 1, 1
+    a.cpu_vocab = max(1, min(args.cpu_vocab, sh.V) // 8)
+    with threadpool_limits(limits=1):
+        r = cpu_baseline(a, sh, layers, w_lm, h_in, T)
+    r["cores"] = 1
+    return r
 
 
 if __name__ == "__main__":
