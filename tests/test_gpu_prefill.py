@@ -63,6 +63,40 @@ def test_gemm_path_ragged_groups(m):
             assert_close(yg[a:a + c], ref, BF16_TOL, f"group {g} ({c} rows)")
 
 
+def test_gemm_path_shortest_k_gathered(m):
+    """The GEMM path at its shortest reduction (K = 256 for gate/up and down:
+    8 stages, where the next tile's gathered row numbers are loaded in one
+    pass of the stage loop and used in the next), rows gathered from a
+    random map, groups of 0, 1, 300, 1100, 7, 0 and 513 rows: every row of
+    both outputs against the oracle."""
+    H, I, T = 256, 256, 1500
+    counts = [0, 1, 300, 1100, 7, 0, 513]
+    G = len(counts)
+    n_rows = int(sum(counts))
+    assert max(counts) >= GEMM_MIN_ROWS
+    gen = torch.Generator().manual_seed(31)
+    x = torch.randn(T, H, generator=gen).to(torch.bfloat16).to(DEV)
+    wgu = (torch.randn(G, 2 * I, H, generator=gen) * 0.05).to(torch.bfloat16).to(DEV)
+    wd = (torch.randn(G, H, I, generator=gen) * 0.05).to(torch.bfloat16).to(DEV)
+    gat = torch.randint(0, T, (n_rows,), generator=gen, dtype=torch.int32).to(DEV)
+    off = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32, device=DEV)
+    wgu_p, wd_p = m.expert_weights(wgu, wd)
+    act = torch.empty((n_rows, I), dtype=torch.bfloat16, device=DEV)
+    y = torch.empty((n_rows, H), dtype=torch.bfloat16, device=DEV)
+    m.moe_expert_gate_up(x, gat, off, wgu_p, act, max_rows=max(counts))
+    m.moe_expert_down(act, off, wd_p, y, max_rows=max(counts))
+    torch.cuda.synchronize()
+    xh, gath = O.f64(host(x)), gat.cpu().numpy()
+    wguh, wdh = host(wgu), host(wd)
+    ag, yg = as_f64(act), as_f64(y)
+    for g, c in enumerate(counts):
+        a = int(sum(counts[:g]))
+        if c:
+            xa = xh[gath[a:a + c]]
+            assert_close(ag[a:a + c], O.swiglu(xa, wguh[g], np.eye(I), "bf16"), BF16_TOL, f"act group {g} ({c} rows)")
+            assert_close(yg[a:a + c], O.swiglu(xa, wguh[g], wdh[g], "bf16"), BF16_TOL, f"y group {g} ({c} rows)")
+
+
 def test_gemm_path_routed_zipf_1024_tokens(m):
     """Route -> permute -> gate/up -> down at 1,024 tokens with the Zipf
     router bias (max_rows = T selects the GEMM path): activation rows and
