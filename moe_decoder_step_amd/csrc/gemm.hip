@@ -87,9 +87,9 @@ __device__ __forceinline__ void gemm_half(const char* cur, int i0, const uint4 (
   }
 }
 
-// One stage that refills: row blocks 0-3 of the stage in `cur`, the barrier
+// One stage that refills: row blocks 0-7 of the stage in `cur`, the barrier
 // (N loads may stay outstanding), this wavefront's activation loads of a later
-// stage into `nxt`, row blocks 4-7.  The two buffers are distinct; saying so
+// stage into `nxt`, row blocks 8-15.  The two buffers are distinct; saying so
 // (restrict) lets the compiler see that the reads of `cur` do not depend on
 // the loads into `nxt` still in flight, so it adds no wait for them.
 template <int N>
@@ -221,10 +221,10 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(
 #pragma unroll
     for (int h = 0; h < 2; ++h) acc[i][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Stage s multiplies row blocks 0-3, waits at a barrier until the next
+  // Stage s multiplies row blocks 0-7, waits at a barrier until the next
   // stage of the stream has landed, issues the activation loads kGAhead
   // stages ahead into the buffer of the previous stage (every wavefront is
-  // past it), multiplies row blocks 4-7, and refills its weight slot kGAhead
+  // past it), multiplies row blocks 8-15, and refills its weight slot kGAhead
   // stages ahead.  So no barrier sits between two stages: the LDS reads of
   // the next stage start while the last MFMAs of this one run.  The loads
   // issued in one stage (act, w) form one group, the groups in stream order
