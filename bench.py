@@ -90,33 +90,40 @@ def ffn_roofline(st, h_in, sh, steps: int) -> dict:
 # HBM traffic of the gate/up kernel per launch, from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE runs scaled by the same counters on a plain copy of known size;
 # valid only while the kernel's sources are the ones that were measured
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "expert_gate_up_step128_traffic.txt")
-KERNEL_SOURCES = ["moe_decoder_step_amd/csrc/swiglu.hip", "moe_decoder_step_amd/csrc/common.hpp"]
+TRAFFIC = {
+    "step128": (os.path.join(ROOT, "profiles", "expert_gate_up_step128_traffic.txt"),
+                ["moe_decoder_step_amd/csrc/swiglu.hip", "moe_decoder_step_amd/csrc/common.hpp"]),
+    "prefill": (os.path.join(ROOT, "profiles", "gemm_gate_up_prefill_traffic.txt"),
+                ["moe_decoder_step_amd/csrc/gemm.hip", "moe_decoder_step_amd/csrc/common.hpp"]),
+}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(workload: str = "step128") -> str:
     import hashlib
     d = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in TRAFFIC[workload][1]:
         with open(os.path.join(ROOT, f), "rb") as fh:
             d.update(fh.read())
     return d.hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(workload: str = "step128"):
     """(fetch + write bytes per launch, note) or (None, reason)."""
-    if not os.path.exists(TRAFFIC_FILE):
+    if workload not in TRAFFIC:
+        return None, "no counter run recorded for this workload"
+    path = TRAFFIC[workload][0]
+    if not os.path.exists(path):
         return None, "no counter run recorded"
     kv = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("source_sha256") != kernel_source_hash():
+    if kv.get("source_sha256") != kernel_source_hash(workload):
         return None, "kernel changed since the counters were taken"
     return (float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"]),
-            os.path.relpath(TRAFFIC_FILE, ROOT))
+            os.path.relpath(path, ROOT))
 
 
 def copy_calibration(args) -> int:
@@ -308,13 +315,13 @@ def main() -> int:
     gu_b = float(np.mean(gu_bytes))
     achieved = gu_b / (gu_ms * 1e-3) / 1e9
     log(f"expert gate/up: {gu_ms * 1e3:.1f} us/launch, {achieved:.0f} GB/s")
-    traffic, traffic_src = measured_traffic() if sh.name == "step128" else (None, "counters taken on step128")
+    traffic, traffic_src = measured_traffic(sh.name)
     if prefill:
         tflops = gu_flops / (gu_ms * 1e-3) / 1e12
         log(f"expert gate/up: {gu_ms * 1e3:.1f} us/launch, {tflops:.0f} TFLOP/s")
         roofline = {"kernel": "moe_expert_gate_up (gemm_kernel<true>)", "bound": "mfma", "achieved": tflops,
                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tflops / BF16_PEAK_TFLOPS,
-                    "traffic": None, "traffic_source": "no counter run recorded for this kernel",
+                    "traffic": traffic, "traffic_source": traffic_src,
                     "us_per_launch": gu_ms * 1e3, "algorithmic_flops_per_launch": gu_flops}
     else:
         roofline = {"kernel": "moe_expert_gate_up_routed (skinny_kernel<true, true>)" if T * sh.k <= 4096
