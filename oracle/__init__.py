@@ -48,6 +48,17 @@ Pin status (what fixes each function other than itself; tests/test_oracle_*):
   speculative loop ... token-identical to step-by-step greedy decoding
   plant_drafts ....... accepted count = leading keeps; E[n+1] = 1+p+p^2+p^3
   active_params ...... the pages' ~570M active per token and 3.4B total
+  verify_step ........ rows chained through the blocks one token at a time, a
+                       linear argmax scan and acceptance walked per sequence
+  rope ............... hand rotations of unit vectors at d = 4 (angles 1, 0.01)
+                       and at d = 128 (pos * 10000^(-j/64)); position 0 is the
+                       identity; norms kept; scores depend on distance only
+  causal_attention ... two and three visible keys with scores set by hand
+                       (softmax weights in closed form, scale 1/sqrt(d));
+                       causality; zero queries average the values
+  draft_step ......... every weight non-zero, recomputed with loops (FFN on
+                       z = rmsnorm(h0), residual h0); identity and token
+                       projections reduce to the greedy head / copy the token
 Numerical values at the real shapes are otherwise parity unpinned: the pages
 print no tensors, logits or token ids.
 """

@@ -419,6 +419,49 @@ def test_speculative_equals_greedy(K):
     assert seq == ref and all(c == K + 1 for c in commits[:-1])
 
 
+def test_verify_step_composition_by_hand():
+    """verify_step chains L blocks, takes the LM-head argmax of every row and
+    judges each sequence's drafts against its own K+1 rows (sequence-major).
+    Recomputed here per row: the blocks as loops over tokens, the full logits
+    with a linear scan, and acceptance by walking each sequence; drafts are
+    planted from that scan so that some sequences accept 0, some 1..K."""
+    rng = np.random.default_rng(41)
+    B, K, H, I, E, k, V = 4, 3, 16, 8, 4, 2, 37
+    layers = [{"w_router": rng.standard_normal((E, H)) * 0.3, "bias": np.zeros(E),
+               "w_gate_up": rng.standard_normal((E + 1, 2 * I, H)) * 0.3,
+               "w_down": rng.standard_normal((E + 1, H, I)) * 0.3} for _ in range(2)]
+    w_lm = rng.standard_normal((V, H))
+    h = rng.standard_normal((B * (K + 1), H))
+    # per-row reference: each token alone through the two blocks
+    cur = h.copy()
+    for wts in layers:
+        cur = np.stack([O.moe_layer(cur[[t]], wts, k, 1e-6, "exact")["h_out"][0] for t in range(B * (K + 1))])
+    g = []
+    for t in range(B * (K + 1)):
+        lg = [float(w_lm[v] @ cur[t]) for v in range(V)]
+        g.append(max(range(V), key=lambda v: (lg[v], -v)))
+    g = np.array(g).reshape(B, K + 1)
+    n_keep = [0, 1, 3, 2]
+    drafts = np.zeros((B, K), dtype=np.int64)
+    for b in range(B):
+        for i in range(K):
+            drafts[b, i] = g[b, i] if i < n_keep[b] else (g[b, i] + 1) % V
+    out = O.verify_step(h, layers, w_lm, drafts, k, 1e-6, "exact")
+    np.testing.assert_allclose(out["layers"][-1]["h_out"], cur, rtol=1e-12, atol=1e-13)
+    np.testing.assert_array_equal(out["argmax"], g.reshape(-1))
+    np.testing.assert_array_equal(out["accepted"], n_keep)
+    np.testing.assert_array_equal(out["n_commit"], np.array(n_keep) + 1)
+    for b in range(B):
+        n = n_keep[b]
+        want = list(drafts[b, :n]) + [g[b, n]] + [-1] * (K - n)
+        assert list(out["committed"][b]) == want
+    # teacher forcing with the free-running inputs reproduces the free run
+    ins = [h] + [o["h_out"] for o in out["layers"][:-1]]
+    tf = O.verify_step(h, layers, w_lm, drafts, k, 1e-6, "exact", layer_inputs=ins,
+                       lm_input=out["layers"][-1]["h_out"])
+    np.testing.assert_array_equal(tf["argmax"], out["argmax"])
+
+
 # --------------------------------------------------------------------------
 # attention over a KV cache
 # --------------------------------------------------------------------------
@@ -441,6 +484,35 @@ def test_rope_scores_depend_only_on_the_position_difference():
             a = (O.rope(q, [dp + 5]) * O.rope(k, [5])).sum(-1)
             b = (O.rope(q, [dp + 5 + shift]) * O.rope(k, [5 + shift])).sum(-1)
             np.testing.assert_allclose(a, b, rtol=1e-9, atol=1e-9)
+
+
+def test_rope_closed_form_d4_position_1():
+    """d = 4 (m = 2) at position 1: the angles are 1 * 10000^(-j/2), i.e. 1 and
+    0.01.  Unit vectors rotate by hand: e0 -> (cos 1, 0, sin 1, 0),
+    e1 -> (0, cos .01, 0, sin .01), e2 -> (-sin 1, 0, cos 1, 0),
+    e3 -> (0, -sin .01, 0, cos .01).  A wrong frequency schedule or a reversed
+    rotation fails it."""
+    c1, s1, c2, s2 = math.cos(1.0), math.sin(1.0), math.cos(0.01), math.sin(0.01)
+    want = np.array([[c1, 0, s1, 0], [0, c2, 0, s2], [-s1, 0, c1, 0], [0, -s2, 0, c2]])
+    got = O.rope(np.eye(4)[:, None, :], np.ones(4))[:, 0, :]
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-15)
+
+
+def test_rope_closed_form_head_128_far_position():
+    """The decoder's head of 128 dims (m = 64): component j pairs with j + 64 and
+    turns by pos * 10000^(-j/64).  Checked for a few j at position 20,000 by
+    direct cos/sin of the angle written out."""
+    pos = 20000
+    for j in (0, 1, 17, 63):
+        x = np.zeros((1, 1, 128))
+        x[0, 0, j] = 2.0
+        x[0, 0, j + 64] = -0.5
+        a = pos * 10000.0 ** (-j / 64.0)
+        got = O.rope(x, [pos])[0, 0]
+        want = np.zeros(128)
+        want[j] = 2.0 * math.cos(a) + 0.5 * math.sin(a)
+        want[j + 64] = 2.0 * math.sin(a) - 0.5 * math.cos(a)
+        np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
 
 
 def _attn_weights(rng, H, n_heads):
@@ -473,6 +545,50 @@ def test_attention_zero_queries_average_the_values():
     for i in range(P):
         vis = np.concatenate([cv0[0, :, :5], np.moveaxis(v[:i + 1], 0, 1)], axis=1)   # [nh, 5+i+1, d]
         np.testing.assert_allclose(out["o"][i].reshape(nh, 16), vis.mean(axis=1), rtol=1e-10, atol=1e-12)
+
+
+def test_attention_two_keys_closed_form():
+    """One head, d = 4, one cached key k1 = e0 with value v1, and the pass's own
+    position with key k2 = 0 and value v2.  A query (a, 0, 0, 0) scores a/sqrt(4)
+    and 0, so o = sigmoid(a/2) v1 + (1 - sigmoid(a/2)) v2.  A missing or wrong
+    score scale fails it."""
+    rng = np.random.default_rng(37)
+    for a in (-3.0, 0.7, 5.0):
+        ck, cv = np.zeros((1, 1, 4, 4)), np.zeros((1, 1, 4, 4))
+        ck[0, 0, 0] = [1.0, 0, 0, 0]
+        v1, v2 = rng.standard_normal(4), rng.standard_normal(4)
+        cv[0, 0, 0], cv[0, 0, 1] = v1, v2        # row 1 is the pass's own position (L = 1)
+        q = np.array([[[a, 0.0, 0.0, 0.0]]])
+        o = O.causal_attention(q, ck, cv, [1], 1)[0, 0]
+        w = 1.0 / (1.0 + math.exp(-a / 2.0))
+        np.testing.assert_allclose(o, w * v1 + (1 - w) * v2, rtol=1e-13, atol=1e-15)
+
+
+def test_attention_three_keys_d16_closed_form():
+    """d = 16 (scale 1/4): three visible keys with scores s_j = q . k_j / 4 set by
+    hand, two heads with different queries, two positions of one pass.  The
+    weights are exp(s_j) / sum exp(s), written out per key."""
+    d, nh = 16, 2
+    ck, cv = np.zeros((1, nh, 8, d)), np.zeros((1, nh, 8, d))
+    rng = np.random.default_rng(38)
+    ck[0, :, 0, 0] = 1.0          # key 0 = e0
+    ck[0, :, 1, 1] = 2.0          # key 1 = 2 e1
+    ck[0, :, 2, 0] = -1.0         # key 2 = -e0 + e2 (the pass's first position)
+    ck[0, :, 2, 2] = 1.0
+    ck[0, :, 3, 3] = 1.0          # key 3 = e3 (the pass's second position)
+    cv[0, :, :4] = rng.standard_normal((nh, 4, d))
+    q = np.zeros((2, nh, d))
+    q[:, 0, :4] = [2.0, 1.0, 3.0, 0.5]
+    q[:, 1, :4] = [-1.0, 0.0, 0.5, 4.0]
+    o = O.causal_attention(q, ck, cv, [2], 2)
+    for i in range(2):
+        for hd in range(nh):
+            qq = q[i, hd]
+            n_vis = 3 + i
+            s = [float(qq @ ck[0, hd, j]) / 4.0 for j in range(n_vis)]
+            z = [math.exp(x) for x in s]
+            want = sum(z[j] / sum(z) * cv[0, hd, j] for j in range(n_vis))
+            np.testing.assert_allclose(o[i, hd], want, rtol=1e-12, atol=1e-14)
 
 
 def test_attention_ignores_cache_entries_past_each_position():
@@ -577,6 +693,47 @@ def test_draft_block_ffn_is_the_residual_swiglu():
                        1e-6, "bf16")
     assert not out["h1"].any()
     np.testing.assert_array_equal(out["ids"], [0, 0, 0])
+
+
+def _rms_loop(v, eps):
+    ms = sum(float(x) * float(x) for x in v) / len(v)
+    return [float(x) / math.sqrt(ms + eps) for x in v]
+
+
+def test_draft_step_nonzero_ffn_written_as_loops():
+    """A draft step with every weight non-zero, recomputed with plain loops:
+    x = [rmsnorm(h); rmsnorm(E[tok])], h0 = W_p x, z = rmsnorm(h0),
+    f = W_d (silu(W_g z) * W_u z), h1 = h0 + f, draft = argmax of W_lm h1.
+    W_p is small, so h0 is far from unit RMS and the FFN fed h0 (or x) instead
+    of z fails; so does a dropped residual."""
+    rng = np.random.default_rng(24)
+    V, H, I = 23, 12, 10
+    w = _draft_tiny(rng, V, H, I)
+    w["w_gate_up"] = w["w_gate_up"] * 40.0     # make the FFN term comparable to h0
+    w["w_down"] = w["w_down"] * 40.0
+    w_lm = rng.standard_normal((V, H))
+    h = rng.standard_normal((3, H)) * 2.0
+    tok = np.array([4, 0, 22])
+    eps = 1e-6
+    out = O.draft_step(h, tok, w, w_lm, eps, "exact")
+    for t in range(3):
+        x = _rms_loop(h[t], eps) + _rms_loop(w["emb"][tok[t]], eps)
+        h0 = [sum(w["w_proj"][r][c] * x[c] for c in range(2 * H)) for r in range(H)]
+        z = _rms_loop(h0, eps)
+        g = [sum(w["w_gate_up"][r][c] * z[c] for c in range(H)) for r in range(I)]
+        u = [sum(w["w_gate_up"][I + r][c] * z[c] for c in range(H)) for r in range(I)]
+        a = [g[r] / (1.0 + math.exp(-g[r])) * u[r] for r in range(I)]
+        f = [sum(w["w_down"][r][c] * a[c] for c in range(I)) for r in range(H)]
+        h1 = [h0[r] + f[r] for r in range(H)]
+        np.testing.assert_allclose(out["x"][t], x, rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(out["h0"][t], h0, rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(out["z"][t], z, rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(out["h1"][t], h1, rtol=1e-12, atol=1e-14)
+        logits = [sum(w_lm[v][c] * h1[c] for c in range(H)) for v in range(V)]
+        best = max(range(V), key=lambda v: (logits[v], -v))
+        assert out["ids"][t] == best
+        # the FFN contributes: h1 differs from h0 by more than rounding
+        assert max(abs(f[r]) for r in range(H)) > 0.05 * max(abs(v) for v in h0)
 
 
 @pytest.mark.parametrize("K", [1, 3])
