@@ -31,8 +31,10 @@
  *   are clamped into range (memory-safe, the mistake is not reported).
  * - Outputs are fully overwritten.  The only aliasing allowed is
  *   out == residual in moe_combine.
- * - No global mutable state: calls on different streams may run concurrently
- *   as long as they do not share output or workspace buffers.
+ * - The only process-wide state is a per-device cache of the compute-unit
+ *   count (atomics; racing threads store the same value).  Calls on different
+ *   streams may run concurrently as long as they do not share output or
+ *   workspace buffers.
  */
 #ifndef MOESTEP_H
 #define MOESTEP_H
@@ -133,6 +135,14 @@ int moe_route(const void* h, const float* gain, float eps,
 
 /* ---------------------------------------------------------------------------
  * moe_permute -- group the T*k (token, slot) pairs by expert.
+ *
+ * Why the step needs it: every token is sent to 6 of 64 routed experts and
+ * to the 2 shared experts ("Jina AI's 3.4B OCR model targets faster page
+ * parsing", section "A compressed visual front end"; jina.ai/ko model card
+ * "jina-ocr-v1", architecture paragraph), so the rows an expert multiplies
+ * are scattered over the batch; grouping them lets each expert's weights be
+ * read once per call.  How the pairs are grouped is not on the pages: a
+ * stable counting sort, so the order is unique.
  *
  * Slot s = t*k + j.  Routed expert e owns rows offsets[e] .. offsets[e+1]-1,
  * holding its slots in ascending token order (a stable counting sort).
@@ -245,6 +255,14 @@ int moe_expert_down_residual(const void* act, const int32_t* offsets, int G, int
 
 /* ---------------------------------------------------------------------------
  * moe_combine -- weighted sum of the expert outputs plus the residual.
+ *
+ * Why the step needs it: a token's layer output joins its 6 routed experts
+ * (top-6 of 64), weighted by the router, and its 2 shared experts ("Jina
+ * AI's 3.4B OCR model targets faster page parsing", section "A compressed
+ * visual front end"; jina.ai/ko model card "jina-ocr-v1", architecture
+ * paragraph).  The pages do not give the weighting; the reading taken is
+ * the router's softmax over the selected logits for routed experts, weight
+ * 1 for shared ones, added to the block's input (a residual block).
  *
  *   c[t]   = sum_{j<k} topk_w[t,j] * y[inv[t*k+j]] + sum_{s<S} y_shared[s*T+t]
  *   out[t] = residual[t] + c[t]          (out = c[t] when residual is NULL)

@@ -10,7 +10,9 @@ import os
 import re
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmoestep.so")
+# MOESTEP_LIB names another build of the same library (the host-sanitizer
+# build of the host checks); by default the in-tree one.
+LIB_PATH = os.environ.get("MOESTEP_LIB") or os.path.join(HERE, "libmoestep.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "moestep.h")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP = range(7)

@@ -1,6 +1,7 @@
 """Build libmoestep.so (the HIP kernels and the C ABI) for gfx950, in-tree.
 
-    python -m moe_decoder_step_amd.build
+    python -m moe_decoder_step_amd.build            # the library
+    python -m moe_decoder_step_amd.build sanitize   # host ASan + UBSan build
 
 Each source compiles to an object under moe_decoder_step_amd/_build/ (in
 parallel), then one link produces moe_decoder_step_amd/libmoestep.so.
@@ -43,6 +44,52 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
+# Host-sanitizer build: the host side of every source with AddressSanitizer
+# and UndefinedBehaviorSanitizer (device code unchanged), for running the
+# host-side checks of the ABI on the CPU.  Linked with the LLVM driver against
+# its shared sanitizer runtime, which the Python process preloads.
+SAN_BUILD = os.path.join(HERE, "_build_san")
+SAN_LIB = os.path.join(SAN_BUILD, "libmoestep_san.so")
+CLANGXX = "/opt/rocm/llvm/bin/clang++"
+SAN_HOST = ["-fsanitize=address", "-fsanitize=undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer"]
+
+
+def _compile_san(src: str) -> str:
+    obj = os.path.join(SAN_BUILD, os.path.splitext(src)[0] + ".o")
+    path = os.path.join(CSRC, src)
+    if src.endswith(".hip"):
+        host = [f for flag in SAN_HOST for f in ("-Xarch_host", flag)]
+        cmd = [HIPCC, f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, *host, "-c", path, "-o", obj]
+    else:
+        cmd = [CLANGXX, *COMMON, *SAN_HOST, "-c", path, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return obj
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """Compile the host side of every source with ASan + UBSan into
+    _build_san/libmoestep_san.so; returns its path."""
+    os.makedirs(SAN_BUILD, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(_compile_san, SOURCES))
+    cmd = [CLANGXX, "-shared", "-fPIC", *SAN_HOST, "-shared-libsan", *objs, "-L/opt/rocm/lib", "-lamdhip64",
+           "-Wl,-rpath,/opt/rocm/lib", "-o", SAN_LIB]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {SAN_LIB}")
+    return SAN_LIB
+
+
+def sanitizer_runtime() -> str:
+    """Path of the LLVM shared ASan runtime the sanitized library needs preloaded."""
+    r = subprocess.run([CLANGXX, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    return r.stdout.strip()
+
+
 def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     """Compile every source for gfx950 and link libmoestep.so; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
@@ -61,5 +108,8 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    if len(sys.argv) > 1 and sys.argv[1] == "sanitize":
+        build_sanitized(verbose=True)
+    else:
+        build(verbose=True)
     sys.exit(0)

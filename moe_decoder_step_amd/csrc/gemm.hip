@@ -28,6 +28,7 @@
 //
 // The fp32 accumulation order along K is fixed: 32 elements per MFMA, in
 // increasing k.
+#include <atomic>
 #include "common.hpp"
 #include "kernels.hpp"
 #include "validate.hpp"
@@ -337,17 +338,21 @@ bool gemm_path_ok(int K, int N, int max_rows) {
 }
 
 // blocks of the persistent grid: one per CU (one 8-wavefront block fills a
-// CU's registers), a multiple of 8 so that every tile keeps its XCD
+// CU's registers), a multiple of 8 so that every tile keeps its XCD.  The CU
+// count is cached per device in atomics: threads that race store the same
+// value.
 static int persistent_blocks() {
-  static int cache[64] = {};
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8) cus = 256;
-    cache[dev] = cus / 8 * 8;
+    n = cus / 8 * 8;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
 template <bool GATED>
