@@ -31,6 +31,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) { return (bf16_t)(pack_bf16x2(f, 0.f) & 0xffffu); }
 
+// silu(z) = z / (1 + e^-z) from the hardware exp2 and reciprocal (v_exp_f32,
+// v_rcp_f32, about 1 ulp each; the product with the up projection is then
+// rounded to bf16).  Every bf16 SwiGLU path uses this one function -- the
+// weight-streaming kernel for decode-sized groups and the tiled GEMM for
+// prefill-sized ones -- so, with the same MFMA k-order in both, a token row's
+// activation does not depend on which path its batch size selects.
+__device__ __forceinline__ float silu_bf16path(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.44269504088896341f));
+}
+
 // fp64 -> bf16 in a single rounding step (nearest, ties to even): the 45 low
 // mantissa bits of the double are rounded away by an integer add, then the
 // (now 8-significant-bit) value converts to fp32 exactly.  Normal range only.

@@ -66,13 +66,10 @@ __device__ __forceinline__ void wait_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
-// silu(z) = z / (1 + e^-z) from the hardware exp2 and reciprocal (v_exp_f32,
-// v_rcp_f32, about 1 ulp each; the result is then rounded to bf16).  The
-// epilogue evaluates 64 per lane: with libm's expf and an IEEE division it
-// took 8 us of a 48 us block.
-__device__ __forceinline__ float silu_g(float z) {
-  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.44269504088896341f));
-}
+// The epilogue's SiLU is silu_bf16path (hardware exp2 and reciprocal), the
+// same function as the weight-streaming kernel's.  The epilogue evaluates 64
+// per lane: with libm's expf and an IEEE division it took 8 us of a 48 us
+// block.
 
 __device__ __forceinline__ uint4 lds16(const char* p) { return *reinterpret_cast<const uint4*>(p); }
 
@@ -303,8 +300,8 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(
         if (pair >= n_pairs) continue;
         const f32x4_t a = acc[i][0], b = acc[i][1];
         uint2 pk;
-        pk.x = pack_bf16x2(silu_g(a[0]) * b[0], silu_g(a[1]) * b[1]);
-        pk.y = pack_bf16x2(silu_g(a[2]) * b[2], silu_g(a[3]) * b[3]);
+        pk.x = pack_bf16x2(silu_bf16path(a[0]) * b[0], silu_bf16path(a[1]) * b[1]);
+        pk.y = pack_bf16x2(silu_bf16path(a[2]) * b[2], silu_bf16path(a[3]) * b[3]);
         *reinterpret_cast<uint2*>(out + (size_t)row * N + pair * 16 + 4 * (lane >> 4)) = pk;
       } else {
 #pragma unroll

@@ -36,7 +36,9 @@ namespace moe {
 namespace {
 
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// fp32 path (the tiny fp32 configuration, one code path at every size):
+// libm's expf and an IEEE division.  The bf16 paths use silu_bf16path.
+__device__ __forceinline__ float silu_f32path(float z) { return z / (1.0f + expf(-z)); }
 
 constexpr int kWaves = 8;                 // wavefronts per block
 constexpr int kBlockThreads = kWaves * 64;
@@ -370,8 +372,8 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
     bf16_t* orow = out + (size_t)(mstart + row) * N + col0 + 4 * (lane >> 4);
     if (GATED) {
       uint2 pk;
-      pk.x = pack_bf16x2(silu(acc_a[0]) * acc_b[0], silu(acc_a[1]) * acc_b[1]);
-      pk.y = pack_bf16x2(silu(acc_a[2]) * acc_b[2], silu(acc_a[3]) * acc_b[3]);
+      pk.x = pack_bf16x2(silu_bf16path(acc_a[0]) * acc_b[0], silu_bf16path(acc_a[1]) * acc_b[1]);
+      pk.y = pack_bf16x2(silu_bf16path(acc_a[2]) * acc_b[2], silu_bf16path(acc_a[3]) * acc_b[3]);
       *reinterpret_cast<uint2*>(orow) = pk;
     } else {
       if (res) {
@@ -609,7 +611,7 @@ __global__ __launch_bounds__(256) void f32_gate_up_kernel(const float* __restric
       a = fmaf(wg[h], xr[h], a);
       u = fmaf(wu[h], xr[h], u);
     }
-    act[(size_t)r * I + c] = silu(a) * u;
+    act[(size_t)r * I + c] = silu_f32path(a) * u;
   }
 }
 

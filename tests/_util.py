@@ -2,6 +2,8 @@
 
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import torch
 
@@ -26,6 +28,12 @@ def tol_for(t: torch.Tensor) -> float:
     return BF16_TOL if t.dtype == torch.bfloat16 else F32_TOL
 
 
+# (test, what, elementwise error, max|d| / max|ref|, tolerance) of every float
+# comparison, printed at the end of the run so that the headroom under each
+# tolerance is visible, not only pass / fail
+ACHIEVED: list = []
+
+
 def assert_close(got, ref, tol, what=""):
     """max|d|/max(1,|ref|) <= tol elementwise, and max|d| <= tol * max|ref|."""
     got = np.asarray(got, np.float64)
@@ -35,6 +43,9 @@ def assert_close(got, ref, tol, what=""):
         return
     d = np.abs(got - ref)
     rel = (d / np.maximum(1.0, np.abs(ref))).max()
+    scale0 = np.abs(ref).max()
+    ACHIEVED.append((os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0], what, float(rel),
+                     float(d.max() / scale0) if scale0 > 0 else 0.0, tol))
     assert rel <= tol, f"{what}: max|d|/max(1,|ref|) = {rel:.3e} > {tol:.1e}"
     scale = np.abs(ref).max()
     assert d.max() <= tol * max(scale, 1e-30), f"{what}: max|d| = {d.max():.3e} > {tol:.1e} * max|ref| ({scale:.3e})"
