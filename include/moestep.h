@@ -31,10 +31,12 @@
  *   are clamped into range (memory-safe, the mistake is not reported).
  * - Outputs are fully overwritten.  The only aliasing allowed is
  *   out == residual in moe_combine.
- * - The only process-wide state is a per-device cache of the compute-unit
- *   count (atomics; racing threads store the same value).  Calls on different
- *   streams may run concurrently as long as they do not share output or
- *   workspace buffers.
+ * - Process-wide state: a per-device cache of the compute-unit count
+ *   (atomics; racing threads store the same value), and for
+ *   lmhead_argmax_noalloc a static device array per GPU and a per-device
+ *   cache of its address (under a mutex).  Calls on different streams may
+ *   run concurrently as long as they do not share output or workspace
+ *   buffers (lmhead_argmax_noalloc calls share that array).
  */
 #ifndef MOESTEP_H
 #define MOESTEP_H
@@ -353,6 +355,27 @@ size_t lmhead_argmax_workspace_bytes(int T, int V, int dtype);
 int lmhead_argmax(const void* h, const void* w_lm, int T, int H, int V, int dtype,
                   int32_t* argmax_ids, float* max_logit,
                   void* ws, size_t ws_bytes, void* stream);
+
+/* lmhead_argmax_noalloc -- lmhead_argmax for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid allocation.  Same kernels and results, bit for bit;
+ * the workspace is a static device array of the library instead of `ws`.
+ *
+ * Each GPU holds its own copy of that array (MOE_NOALLOC_SCRATCH_BYTES) until
+ * the process ends.  Its device address is looked up on the first call on a
+ * device (the stream's device; hipGetSymbolAddress with that device current)
+ * and cached.  Calls that overlap on one GPU (several streams or host
+ * threads) share the array and race: serialise them.  Nothing is allocated,
+ * freed or cleared.
+ *
+ * Arguments as lmhead_argmax without ws / ws_bytes.  Errors as
+ * lmhead_argmax, plus MOE_ERR_WORKSPACE when
+ * lmhead_argmax_workspace_bytes(T, V, dtype) > MOE_NOALLOC_SCRATCH_BYTES
+ * (e.g. more than 519 rows at V = 129,280 in bf16), and MOE_ERR_HIP if the
+ * array's address cannot be looked up or the launch fails. */
+#define MOE_NOALLOC_SCRATCH_BYTES (4u << 20)
+int lmhead_argmax_noalloc(const void* h, const void* w_lm, int T, int H, int V, int dtype,
+                          int32_t* argmax_ids, float* max_logit, void* stream);
 
 /* ---------------------------------------------------------------------------
  * spec_verify -- greedy longest-prefix acceptance plus the bonus token.

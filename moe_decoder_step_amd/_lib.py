@@ -19,6 +19,7 @@ OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP = ra
 BF16, F32 = 0, 1
 ROUTE_NORM, ROUTE_RENORM, ROUTE_WPACKED = 1, 2, 4
 PACK_GATE_UP, PACK_ROWS, PACK_ROUTER = 0, 1, 2
+NOALLOC_SCRATCH_BYTES = 4 << 20   # MOE_NOALLOC_SCRATCH_BYTES
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -47,6 +48,7 @@ SIGNATURES = {
     "moe_combine_route": (_I, [_P, _P, _P, _P, _I, _I, _I, _P, _I, _I, _P, _F, _P, _P, _I, _I, _I, _I,
                                _P, _P, _P, _P, _P]),
     "lmhead_argmax": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _Z, _P]),
+    "lmhead_argmax_noalloc": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P]),
     "spec_verify": (_I, [_P, _P, _I, _I, _P, _P, _P, _P]),
     "spec_plant_drafts": (_I, [_P, _P, _P, _I, _I, _I, _P, _P]),
     "spec_advance": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),

@@ -19,7 +19,7 @@ __all__ = [
     "moe_expert_gate_up", "moe_expert_gate_up_routed", "moe_expert_down", "moe_expert_down_residual", "ROUTED_MAX_PAIRS", "spec_verify", "spec_plant_drafts", "spec_advance",
     "spec_gather_rows", "moe_attn_rope_cache", "moe_attention", "attention_workspace_bytes", "kv_cache_alloc", "spec_commit",
     "permute_workspace_bytes", "swiglu_workspace_bytes",
-    "lmhead_workspace_bytes", "dtype_code", "expert_weights", "lm_weights", "router_weights", "route_alloc", "permute_alloc", "swiglu_alloc",
+    "lmhead_workspace_bytes", "lmhead_argmax_noalloc", "dtype_code", "expert_weights", "lm_weights", "router_weights", "route_alloc", "permute_alloc", "swiglu_alloc",
     "combine_alloc", "lmhead_alloc", "verify_alloc",
 ]
 
@@ -314,6 +314,20 @@ def lmhead_argmax(h, w_lm, argmax_ids, max_logit, ws):
     L.check("lmhead_argmax", L.load().lmhead_argmax(
         _p(h), _p(w_lm), T, H, V, dtype_code(h), _p(argmax_ids), _p(max_logit), _p(ws),
         ws.numel() * ws.element_size(), _stream(h)))
+
+
+def lmhead_argmax_noalloc(h, w_lm, argmax_ids, max_logit):
+    """lmhead_argmax with the library's static per-GPU workspace (no caller
+    buffer, nothing allocated); concurrent calls on one GPU race on it."""
+    T, H = h.shape
+    V = w_lm.shape[0]
+    if h.dtype == torch.bfloat16 and not (isinstance(w_lm, Packed) and w_lm.kind == L.PACK_ROWS):
+        raise TypeError("a bf16 LM head must be packed (lm_weights / pack_weights)")
+    for t, d, n in ((h, None, "h"), (w_lm, h.dtype, "w_lm"), (argmax_ids, torch.int32, "argmax_ids"),
+                    (max_logit, torch.float32, "max_logit")):
+        _need(t, d, n)
+    L.check("lmhead_argmax_noalloc", L.load().lmhead_argmax_noalloc(
+        _p(h), _p(w_lm), T, H, V, dtype_code(h), _p(argmax_ids), _p(max_logit), _stream(h)))
 
 
 def spec_verify(drafts, argmax_ids, accepted, committed, n_commit):

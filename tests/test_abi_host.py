@@ -21,7 +21,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = L.header_functions()
-    assert len(names) == 27
+    assert len(names) == 28
     assert set(names) == set(L.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
@@ -260,3 +260,19 @@ def test_binding_raises_without_gpu_tensors():
     with pytest.raises(ValueError):
         m.moe_route(h, torch.zeros(8, 128), None, 2, torch.zeros_like(h), torch.zeros(4, 2, dtype=torch.int32),
                     torch.zeros(4, 2))
+
+
+def test_lmhead_noalloc_checks(lib):
+    """The allocation-free LM head: argument checks as lmhead_argmax, and a
+    batch whose workspace would exceed the static array is rejected."""
+    f = lib.lmhead_argmax_noalloc
+    V = 129280
+    assert f(None, A, 4, 1280, V, m.BF16, A, None, None) == L.ERR_NULL
+    assert f(A, A, 4, 1280, V, m.BF16, None, None, None) == L.ERR_NULL
+    assert f(MIS, A, 4, 1280, V, m.BF16, A, None, None) == L.ERR_ALIGN
+    assert f(A, A, 4, 1290, V, m.BF16, A, None, None) == L.ERR_UNSUPPORTED
+    assert f(A, A, -1, 1280, V, m.BF16, A, None, None) == L.ERR_SHAPE
+    assert f(A, A, 0, 1280, V, m.BF16, A, None, None) == L.OK
+    assert lib.lmhead_argmax_workspace_bytes(519, V, m.BF16) <= L.NOALLOC_SCRATCH_BYTES
+    assert lib.lmhead_argmax_workspace_bytes(520, V, m.BF16) > L.NOALLOC_SCRATCH_BYTES
+    assert f(A, A, 520, 1280, V, m.BF16, A, None, None) == L.ERR_WORKSPACE
