@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--cpu-layers", type=int, default=12, help="layers of the oracle sample")
     ap.add_argument("--cpu-vocab", type=int, default=129280, help="LM-head rows of the oracle sample")
     ap.add_argument("--cpu-reps", type=int, default=3, help="repetitions of the oracle sample")
+    ap.add_argument("--cpu-steps", type=int, default=4,
+                    help="decode32: full-batch passes the oracle runs for the extrapolated loop figure")
     ap.add_argument("--cpu-tokens", type=int, default=512, help="tokens of the oracle sample (at most T)")
     ap.add_argument("--drafts", type=int, default=None, help="drafts K per sequence (positions = K + 1)")
     ap.add_argument("--no-graph", action="store_true", help="batch1: time eager launches only")
@@ -64,16 +66,16 @@ def expert_bytes(sh) -> int:
 def ffn_roofline(st, h_in, sh, steps: int) -> dict:
     """The routed gate/up kernel of a verify pass over h_in: algorithmic
     bytes from the pass's own routing (gate and up rows of every touched
-    expert and the shared ones, the normed tokens in, the SwiGLU rows out)
-    over its mean launch duration, HIP events on its stream."""
+    expert and the shared ones, the normed tokens in; the SwiGLU rows it
+    writes are an intermediate and not counted) over its mean launch
+    duration, HIP events on its stream."""
     import numpy as np
     import torch
     T = h_in.shape[0]
     rec = []
     st.forward(h_in, rec)
     touched = [int(np.unique(r["ids"].cpu().numpy()).size) for r in rec]
-    n_rows = T * sh.k + sh.S * T
-    gu_b = float(np.mean([(t + sh.S) * 2 * sh.I * sh.H * 2 + T * sh.H * 2 + n_rows * sh.I * 2 for t in touched]))
+    gu_b = float(np.mean([(t + sh.S) * 2 * sh.I * sh.H * 2 + T * sh.H * 2 for t in touched]))
     st.ffn_events = ev = []
     for _ in range(steps):
         st.forward(h_in)
@@ -231,10 +233,11 @@ def main() -> int:
     del rec
     layer_bytes = [(t + sh.S) * expert_bytes(sh) + sh.E * sh.H * 4 + 2 * T * sh.H * 2 for t in touched]
     step_bytes = sum(layer_bytes) / cycle + (sh.V * sh.H * 2 if sh.V else 0)
-    # gate/up kernel per launch: gate and up rows of every touched expert, the
-    # normed tokens in, the SwiGLU activation rows out
+    # gate/up kernel per launch: gate and up rows of every touched expert and
+    # the normed tokens in (the SwiGLU activation rows it writes are an
+    # intermediate, left out of the algorithmic bytes)
     n_rows = T * sh.k + sh.S * T
-    gu_bytes = [(t + sh.S) * 2 * sh.I * sh.H * 2 + T * sh.H * 2 + n_rows * sh.I * 2 for t in touched]
+    gu_bytes = [(t + sh.S) * 2 * sh.I * sh.H * 2 + T * sh.H * 2 for t in touched]
     gu_flops = n_rows * 2 * (2 * sh.I) * sh.H
     layer_flops = 2 * T * sh.H * sh.E + n_rows * 6 * sh.H * sh.I      # router + experts
 
@@ -405,7 +408,6 @@ def decode_loop_bench(args) -> int:
     layers = [synth.layer_weights(0, l, sh, dev) for l in range(sh.L)]
     w_lm = synth.lm_weight(0, sh, dev)
     st = m.VerifyStack(layers, w_lm, sh.E, sh.k, sh.S, max_tokens=S * P, max_seqs=S, K=K)
-    del layers, w_lm
     h_pool = synth.normal(synth.subseed(4, "decode_hidden"), (S, target, P, sh.H), 1.0, torch.bfloat16, dev)
     keep, repl = synth.plant_schedule(4, target, S, K, sh.V, P_KEEP)
     loop = m.DecodeLoop(st, h_pool, keep.permute(1, 0, 2).contiguous().to(dev),
@@ -438,6 +440,22 @@ def decode_loop_bench(args) -> int:
                  "committed_per_pass_per_seq": committed / float(np.sum(sizes)),
                  "expected_committed_per_pass": sum(P_KEEP ** i for i in range(K + 1))},
     }
+    if not args.no_cpu_baseline:
+        # the oracle over the loop's first full-batch passes (12 layers + LM
+        # head + acceptance on 32 x 4 positions each), extrapolated per verify
+        # position to every pass the GPU loop ran
+        import copy
+        a = copy.copy(args)
+        a.cpu_layers, a.cpu_tokens, a.cpu_vocab, a.cpu_reps = sh.L, S * P, sh.V, max(1, args.cpu_steps)
+        first = h_pool[:, 0].reshape(S * P, sh.H)
+        cb = cpu_baseline(a, sh, layers, w_lm, first, S * P)
+        positions = float(np.sum(sizes)) * P
+        t_loop = positions / cb["value"]
+        cb.update({"value": committed / t_loop, "unit": "tokens/s", "extrapolated": True,
+                   "sample": f"{a.cpu_reps} full-batch passes of the oracle ({S} x {P} positions, {sh.L} layers + "
+                             f"LM head {sh.V} rows), {cb['value']:.1f} verify positions/s, extrapolated to the "
+                             f"loop's {res['passes']} passes ({positions:.0f} positions): {t_loop:.0f} s per loop"})
+        out["cpu_baseline"] = cb
     print(json.dumps(out), flush=True)
     return 0
 
@@ -750,6 +768,25 @@ def attention_step_bench(args) -> int:
     return 0
 
 
+def host_cpu() -> dict:
+    """The host's CPU model (lscpu) and the cores this process may use."""
+    model = None
+    try:
+        import subprocess
+        r = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10)
+        for line in r.stdout.splitlines():
+            if line.startswith("Model name:"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except Exception:
+        pass
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except Exception:
+        nproc = os.cpu_count()
+    return {"cpu_model": model, "nproc": nproc}
+
+
 def cpu_baseline(args, sh, layers, w_lm, h_in, T) -> dict:
     """The fp64 oracle on the host cores over a bounded sample of the same
     step: `cpu_layers` MoE layers on `cpu_tokens` tokens plus the LM head over
@@ -790,7 +827,7 @@ def cpu_baseline(args, sh, layers, w_lm, h_in, T) -> dict:
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         cores = os.cpu_count() or 1
-    return {"value": T / t_step, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": T / t_step, "unit": "tokens/s", "cores": cores, "kind": "oracle", **host_cpu(),
             "sample": f"{nl} of {sh.L} MoE layers on {nt} of {T} tokens ({t_layers:.1f}s) + LM head over "
                       f"{vs} of {sh.V} vocabulary rows ({t_lm:.1f}s), mean of {reps} runs, scaled to the full "
                       f"step ({t_step:.1f}s per step)"}
