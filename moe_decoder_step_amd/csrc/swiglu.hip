@@ -40,8 +40,15 @@ namespace {
 // libm's expf and an IEEE division.  The bf16 paths use silu_bf16path.
 __device__ __forceinline__ float silu_f32path(float z) { return z / (1.0f + expf(-z)); }
 
+#ifndef MOE_DEEP_MAX_ITEMS
+#define MOE_DEEP_MAX_ITEMS 256
+#endif
+constexpr int kDeepMaxItems = MOE_DEEP_MAX_ITEMS;   // launches of at most this many items use the deep ring
+
+constexpr int kRoutedMaxPairs = kPermuteChunk;   // (token, slot) pairs of one routed launch (host-checked)
 constexpr int kWaves = 8;                 // wavefronts per block
 constexpr int kBlockThreads = kWaves * 64;
+constexpr int kStage1 = 5;                // 16-byte activation segments per thread staged before the weights
 constexpr int kRows = 16;                 // activation rows per block (one MFMA block)
 
 __host__ __device__ constexpr int lds_row(int K) { return K + 8; }  // padded LDS row (bf16): conflict-free
@@ -211,14 +218,21 @@ __device__ __forceinline__ void stream_chunk_fixed(const bf16_t* wa, const bf16_
 // expert and tile; the split multiplies the blocks by KS.  KS depends on
 // the weight shape only, never on the number of rows, so a row's result
 // does not depend on the batch.
-template <bool GATED, bool ROUTED>
+// DEEP: 6 k-steps of weights in flight per wavefront instead of 3 in the
+// 16-row item form.  A launch with few work items (batch 1: ~20 touched
+// experts) has too few bytes in flight to cover the memory latency at 3
+// (bandwidth ~ bytes in flight / latency); with many items 3 suffice and
+// the smaller register ring keeps more blocks per CU.  The depth does not
+// change any row's k-order, so results are the same bits either way.
+template <bool GATED, bool ROUTED, bool DEEP>
 __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
     const bf16_t* __restrict__ x, const int32_t* __restrict__ gather,
     const int32_t* __restrict__ offsets, int G, int n_rows, int T,
     const bf16_t* __restrict__ W, int K, int N, int n_ctiles, int ks_log2, int chunk_cfg, bf16_t* out,
     const bf16_t* res, RoutedArgs rt) {
   static_assert(!ROUTED || GATED, "only the gate/up stage derives its rows from the expert ids");
-  constexpr int D = 3;                    // k-steps of weights in flight per wavefront
+  constexpr int D = 3;                    // k-steps of weights in flight per wavefront (multi-row items)
+  constexpr int DB = DEEP ? 6 : 3;        // the same for 16-row items
   constexpr int WCOLS = GATED ? 16 : 32;  // output columns per wavefront
   extern __shared__ __align__(16) bf16_t xl[];   // [kRows][lds_row(K)]
 
@@ -234,15 +248,31 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
   __shared__ int item_g, item_ct, item_r0, item_r1, item_gs, item_rb;
   __shared__ int s_cnt[2 * kWave];   // ROUTED: rows per group
   __shared__ int s_tok[4 * kRows];   // ROUTED: tokens of the block's rows (routed groups)
+  __shared__ int s_ids[ROUTED ? kRoutedMaxPairs : 1];   // ROUTED: the (token, slot) expert ids, clamped
   // row blocks per item allowed (chunk_cfg: 0 = 16-row items only)
   const int rb_max = (chunk_cfg >> 16) ? 4 : (chunk_cfg & 0xffff) ? 2 : 1;
   const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
   if (ROUTED) {
     // rows per group: a histogram of the (token, slot) expert ids; each
-    // shared group holds every token
+    // shared group holds every token.  The ids stay in LDS for the token
+    // scan below.  Every thread loads all its ids (at most 8) before using
+    // any, so the loads overlap.
+    static_assert(kRoutedMaxPairs <= 8 * kBlockThreads, "8 ids per thread");
     for (int g = threadIdx.x; g < G; g += kBlockThreads) s_cnt[g] = g < rt.E ? 0 : T;
+    const int np = T * rt.k;
+    int idv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) idv[u] = rt.ids[min((int)threadIdx.x + u * kBlockThreads, np - 1)];
     lds_barrier();
-    for (int p = threadIdx.x; p < T * rt.k; p += kBlockThreads) atomicAdd(&s_cnt[clampi(rt.ids[p], 0, rt.E - 1)], 1);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int p = threadIdx.x + u * kBlockThreads;
+      if (p < np) {
+        const int e = clampi(idv[u], 0, rt.E - 1);
+        s_ids[p] = e;
+        atomicAdd(&s_cnt[e], 1);
+      }
+    }
     lds_barrier();
   }
   if (threadIdx.x < kWave) {
@@ -337,7 +367,7 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
       int base = 0;
       for (int c0 = 0; c0 < T * rt.k && base < want1; c0 += kWave) {
         const int p = c0 + lane;
-        const bool f = p < T * rt.k && clampi(rt.ids[p], 0, rt.E - 1) == g;
+        const bool f = p < T * rt.k && s_ids[p] == g;
         const unsigned long long m = __ballot(f);
         const int rank = base + __popcll(m & ((1ull << lane) - 1ull));
         if (f && rank >= want0 && rank < want1) {
@@ -410,34 +440,41 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
 
   auto body = [&](auto nt) __attribute__((always_inline)) {
     constexpr bool NT = decltype(nt)::value;
-    // weights of the first D steps go out before the activation staging
-    uint4 ra[D], rb[D];
+    // Stage the range's activation rows (rows past the group repeat a valid
+    // row).  Their loads go out first, then the weights of the first DB
+    // steps: loads retire in issue order, so the LDS stores below wait for
+    // the activation rows only and the weight latency overlaps the staging.
+    // The first round covers kStage1 segments per thread (K <= 1280 in one
+    // round); longer rows stage the rest after it.
+    const int nstg = kRows * nseg;
+    uint4 v[kStage1];
+    int dst[kStage1];
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
+    for (int u = 0; u < kStage1; ++u) {
+      const int idx = min((int)threadIdx.x + u * kBlockThreads, nstg - 1);
+      const int row = idx / nseg, seg = idx % nseg;
+      v[u] = ldg16(x + (size_t)src_row(row) * K + seg * 8);
+      dst[u] = row * ldr + seg * 8;
+    }
+    uint4 ra[DB], rb[DB];
+#pragma unroll
+    for (int d = 0; d < DB; ++d) {
       const int kk = min(d, nKs - 1);
       ra[d] = wload<NT>(wa + kk * 1024);
       rb[d] = wload<NT>(wb + kk * 1024);
     }
-    // stage the range's activation rows (rows past the group repeat a valid row)
-    for (int i = threadIdx.x; i < kRows * nseg; i += kBlockThreads * 4) {
-      uint4 v[4];
-      int dst[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int idx = min(i + u * kBlockThreads, kRows * nseg - 1);
-        const int row = idx / nseg, seg = idx % nseg;
-        v[u] = ldg16(x + (size_t)src_row(row) * K + seg * 8);
-        dst[u] = row * ldr + seg * 8;
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (i + u * kBlockThreads < kRows * nseg) *reinterpret_cast<uint4*>(xl + dst[u]) = v[u];
+    for (int u = 0; u < kStage1; ++u)
+      if ((int)threadIdx.x + u * kBlockThreads < nstg) *reinterpret_cast<uint4*>(xl + dst[u]) = v[u];
+    for (int i = threadIdx.x + kStage1 * kBlockThreads; i < nstg; i += kBlockThreads) {
+      const int row = i / nseg, seg = i % nseg;
+      *reinterpret_cast<uint4*>(xl + row * ldr + seg * 8) = ldg16(x + (size_t)src_row(row) * K + seg * 8);
     }
     lds_barrier();
 
     f32x4_t acc_a = f32x4_t{0.f, 0.f, 0.f, 0.f}, acc_b = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (active || KS > 1)   // with a K split every wavefront streams (inactive ones a valid pair) to reach the barriers
-      stream_rows<D, NT>(wa, wb, xl + (lane & 15) * ldr + (lane >> 4) * 8 + k0 * 32, nKs, ra, rb, acc_a, acc_b);
+      stream_rows<DB, NT>(wa, wb, xl + (lane & 15) * ldr + (lane >> 4) * 8 + k0 * 32, nKs, ra, rb, acc_a, acc_b);
     if (KS > 1) {
       // partial sums of the slices, added in slice order; the staged rows are
       // dead, their LDS holds the partials [wavefront][lane][8]
@@ -470,13 +507,6 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
     // every thread holds exactly NPF segments: no conditional store for the
     // compiler to sink a prefetch load into
     static_assert(RR * NSC == NPF * kBlockThreads, "a chunk is a whole number of segments per thread");
-    uint4 ra[D], rb[D];
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-      const int kk = min(d, nK - 1);
-      ra[d] = wload<NT>(wa + kk * 1024);
-      rb[d] = wload<NT>(wb + kk * 1024);
-    }
     // this thread's segments u of a chunk: row offsets in x and segment numbers
     int srow[NPF], sseg[NPF];
 #pragma unroll
@@ -500,7 +530,16 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
         *reinterpret_cast<uint4*>(xl + (idx / NSC) * LDC + (idx % NSC) * 8) = pf[u];
       }
     };
+    // the first chunk's loads go out before the weights of the first D
+    // steps, so its LDS stores wait for the activation rows only
     ld_chunk(0);
+    uint4 ra[D], rb[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int kk = min(d, nK - 1);
+      ra[d] = wload<NT>(wa + kk * 1024);
+      rb[d] = wload<NT>(wb + kk * 1024);
+    }
     st_chunk();
     lds_barrier();
     f32x4_t acc_a[RB], acc_b[RB];
@@ -569,13 +608,18 @@ hipError_t launch_skinny(const bf16_t* x, const int32_t* gather, const int32_t* 
     chunk_cfg = 2 | (4 << 16);
     lds = std::max(lds, std::max(chunk_lds(2), chunk_lds(4)));
   }
+  // few work items (an upper bound: non-empty groups x column tiles x K
+  // slices): the deep weight ring
+  const long long items_ub = (long long)std::min(G, n_rows) * n_ctiles << ks_log2;
+  const bool deep = items_ub <= kDeepMaxItems;
+  auto kern = deep ? &skinny_kernel<GATED, ROUTED, true> : &skinny_kernel<GATED, ROUTED, false>;
   if (lds > 64 * 1024) {  // K > 2040: allow up to the CU's 160 KB of LDS
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&skinny_kernel<GATED, ROUTED>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((skinny_kernel<GATED, ROUTED>), dim3(blocks), dim3(kBlockThreads), lds, s, x, gather, offsets,
-                     G, n_rows, T, W, K, N, n_ctiles, ks_log2, chunk_cfg, out, res, ra);
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(kBlockThreads), lds, s, x, gather, offsets, G, n_rows, T, W, K, N,
+                     n_ctiles, ks_log2, chunk_cfg, out, res, ra);
   return hipGetLastError();
 }
 
