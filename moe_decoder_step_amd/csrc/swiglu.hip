@@ -249,9 +249,17 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
   __shared__ int s_cnt[2 * kWave];   // ROUTED: rows per group
   __shared__ int s_tok[4 * kRows];   // ROUTED: tokens of the block's rows (routed groups)
   __shared__ int s_ids[ROUTED ? kRoutedMaxPairs : 1];   // ROUTED: the (token, slot) expert ids, clamped
+  __shared__ __align__(16) int s_chunk[ROUTED ? kRoutedMaxPairs / kWave : 4];   // ROUTED: the group's pairs per 64-pair chunk
   // row blocks per item allowed (chunk_cfg: 0 = 16-row items only)
   const int rb_max = (chunk_cfg >> 16) ? 4 : (chunk_cfg & 0xffff) ? 2 : 1;
   const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  // Where a CU holds two blocks, the one that starts streaming first takes
+  // nearly all of the CU's memory issue and the other's staging loads wait
+  // behind its weight stream (measured per block: the second block's staging
+  // took 3-4x as long).  The set-up and staging run at raised wave priority
+  // so that both blocks reach the stream early; streaming runs at the
+  // normal priority.
+  __builtin_amdgcn_s_setprio(3);
   if (ROUTED) {
     // rows per group: a histogram of the (token, slot) expert ids; each
     // shared group holds every token.  The ids stay in LDS for the token
@@ -356,30 +364,6 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
   const int irb = item_rb;
   const int mr = min(kRows * irb, item_r1 - mstart);
   const int r_begin = ROUTED ? item_gs : clampi(offsets[g], 0, n_rows);
-  if (ROUTED && g < rt.E) {
-    // the tokens of this block's rows: the group's (token, slot) pairs in
-    // ascending order, ranks mstart - r_begin .. +mr; the blocks of the first
-    // column tile also record each pair's row (inv) for the combine
-    if (threadIdx.x < kWave) {
-      const int lane = threadIdx.x;
-      const int want0 = mstart - r_begin, want1 = want0 + mr;
-      const bool owner = ct == 0;
-      int base = 0;
-      for (int c0 = 0; c0 < T * rt.k && base < want1; c0 += kWave) {
-        const int p = c0 + lane;
-        const bool f = p < T * rt.k && s_ids[p] == g;
-        const unsigned long long m = __ballot(f);
-        const int rank = base + __popcll(m & ((1ull << lane) - 1ull));
-        if (f && rank >= want0 && rank < want1) {
-          s_tok[rank - want0] = p / rt.k;
-          if (owner) rt.inv[p] = r_begin + rank;
-        }
-        base += __popcll(m);
-      }
-    }
-    lds_barrier();
-  }
-
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int KS = 1 << ks_log2, CG = kWaves >> ks_log2;
   const int cg = wave & (CG - 1), ks = wave >> (3 - ks_log2);
@@ -395,6 +379,49 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
   const bf16_t* wb = wa + 512;
   const int ldr = lds_row(K);
   const int nseg = K / 8;                 // 16-byte segments per activation row
+
+  // ordinary weight loads where several items read a gate/up tile (see wload)
+  const bool shared_tile = GATED && item_r1 - r_begin > kRows * irb;
+  const bool pre = ROUTED && g < rt.E;   // a routed group: rows from the token scan
+  auto token_scan = [&]() __attribute__((always_inline)) {
+    // the tokens of this block's rows: the group's (token, slot) pairs in
+    // ascending order, ranks mstart - r_begin .. +mr; the blocks of the first
+    // column tile also record each pair's row (inv) for the combine.
+    // Wavefront w takes the 64-pair chunks w, w + 8, ...: it counts the
+    // group's pairs in each, the counts of the chunks before a chunk give
+    // its first rank, and the pairs of the wanted ranks are written.
+    const int np = T * rt.k, nch = (np + kWave - 1) / kWave;
+    const int want0 = mstart - r_begin, want1 = want0 + mr;
+#pragma unroll 1
+    for (int c = wave; c < nch; c += kWaves) {
+      const int p = c * kWave + lane;
+      const unsigned long long m = __ballot(p < np && s_ids[p] == g);
+      if (lane == 0) s_chunk[c] = __popcll(m);
+    }
+    lds_barrier();
+    const bool owner = ct == 0;
+    const int4* cnt4 = reinterpret_cast<const int4*>(s_chunk);
+    int base4 = 0, c4 = 0;   // pairs of the group in chunks [0, c4), c4 a multiple of 4
+#pragma unroll 1
+    for (int c = wave; c < nch; c += kWaves) {
+      for (; c4 + 4 <= c; c4 += 4) {
+        const int4 q = cnt4[c4 >> 2];
+        base4 += q.x + q.y + q.z + q.w;
+      }
+      int base = base4;   // pairs of the group in chunks [0, c)
+      for (int cc = c4; cc < c; ++cc) base += s_chunk[cc];
+      if (base >= want1) break;
+      const int p = c * kWave + lane;
+      const bool f = p < np && s_ids[p] == g;
+      const unsigned long long m = __ballot(f);
+      const int rank = base + __popcll(m & ((1ull << lane) - 1ull));
+      if (f && rank >= want0 && rank < want1) {
+        s_tok[rank - want0] = p / rt.k;
+        if (owner) rt.inv[p] = r_begin + rank;
+      }
+    }
+    lds_barrier();
+  };
 
   // lane holds D[col 4*(lane/16)+v][row lane%16]: 4 consecutive output columns of one row
   auto emit = [&](f32x4_t acc_a, f32x4_t acc_b, int row) __attribute__((always_inline)) {
@@ -433,17 +460,31 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
   // the token (or activation row) of item row `row` (rows past the item repeat a valid row)
   auto src_row = [&](int row) __attribute__((always_inline)) {
     const int r = mstart + min(row, mr - 1);
-    if (ROUTED) return g < rt.E ? s_tok[min(row, mr - 1)] : clampi(r - r_begin, 0, T - 1);
+    if (ROUTED) return clampi(g < rt.E ? s_tok[min(row, mr - 1)] : r - r_begin, 0, T - 1);
     if (GATED) return gather ? clampi(gather[r], 0, T - 1) : clampi(r - r_begin, 0, T - 1);
     return r;
   };
 
   auto body = [&](auto nt) __attribute__((always_inline)) {
     constexpr bool NT = decltype(nt)::value;
+    uint4 ra[DB], rb[DB];
+    if constexpr (ROUTED) {
+      // The first weight steps depend on the item only: they go out before
+      // the token scan that finds a routed group's rows, so their latency
+      // overlaps the scan and the staging.
+#pragma unroll
+      for (int d = 0; d < DB; ++d) {
+        const int kk = min(d, nKs - 1);
+        ra[d] = wload<NT>(wa + kk * 1024);
+        rb[d] = wload<NT>(wb + kk * 1024);
+      }
+      if (pre) token_scan();
+    }
     // Stage the range's activation rows (rows past the group repeat a valid
-    // row).  Their loads go out first, then the weights of the first DB
-    // steps: loads retire in issue order, so the LDS stores below wait for
-    // the activation rows only and the weight latency overlaps the staging.
+    // row).  Without a token scan their loads go out first, then the weights
+    // of the first DB steps: loads retire in issue order, so the LDS stores
+    // below wait for the activation rows only and the weight latency
+    // overlaps the staging.
     // The first round covers kStage1 segments per thread (K <= 1280 in one
     // round); longer rows stage the rest after it.
     const int nstg = kRows * nseg;
@@ -456,12 +497,13 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
       v[u] = ldg16(x + (size_t)src_row(row) * K + seg * 8);
       dst[u] = row * ldr + seg * 8;
     }
-    uint4 ra[DB], rb[DB];
+    if constexpr (!ROUTED) {
 #pragma unroll
-    for (int d = 0; d < DB; ++d) {
-      const int kk = min(d, nKs - 1);
-      ra[d] = wload<NT>(wa + kk * 1024);
-      rb[d] = wload<NT>(wb + kk * 1024);
+      for (int d = 0; d < DB; ++d) {
+        const int kk = min(d, nKs - 1);
+        ra[d] = wload<NT>(wa + kk * 1024);
+        rb[d] = wload<NT>(wb + kk * 1024);
+      }
     }
 #pragma unroll
     for (int u = 0; u < kStage1; ++u)
@@ -472,6 +514,7 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
     }
     lds_barrier();
 
+    __builtin_amdgcn_s_setprio(0);
     f32x4_t acc_a = f32x4_t{0.f, 0.f, 0.f, 0.f}, acc_b = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (active || KS > 1)   // with a K split every wavefront streams (inactive ones a valid pair) to reach the barriers
       stream_rows<DB, NT>(wa, wb, xl + (lane & 15) * ldr + (lane >> 4) * 8 + k0 * 32, nKs, ra, rb, acc_a, acc_b);
@@ -507,6 +550,10 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
     // every thread holds exactly NPF segments: no conditional store for the
     // compiler to sink a prefetch load into
     static_assert(RR * NSC == NPF * kBlockThreads, "a chunk is a whole number of segments per thread");
+    // a routed group's token scan comes first here (issuing the weights
+    // before it, as the 16-row form does, took the kernel to 140 VGPRs: one
+    // block per CU)
+    if (pre) token_scan();
     // this thread's segments u of a chunk: row offsets in x and segment numbers
     int srow[NPF], sseg[NPF];
 #pragma unroll
@@ -542,6 +589,7 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
     }
     st_chunk();
     lds_barrier();
+    __builtin_amdgcn_s_setprio(0);
     f32x4_t acc_a[RB], acc_b[RB];
 #pragma unroll
     for (int r = 0; r < RB; ++r) acc_a[r] = acc_b[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -560,8 +608,6 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
       for (int r = 0; r < RB; ++r) emit(acc_a[r], acc_b[r], r * kRows + (lane & 15));
   };
 
-  // ordinary weight loads where several items read a gate/up tile (see wload)
-  const bool shared_tile = GATED && item_r1 - r_begin > kRows * irb;
   if constexpr (GATED) {
     if (irb == 4) {
       if (shared_tile) chunked(std::integral_constant<int, 4>{}, std::false_type{});
