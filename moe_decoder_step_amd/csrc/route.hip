@@ -103,12 +103,19 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     return *reinterpret_cast<const float4*>(wr + (size_t)min(e, E - 1) * H + hh);
   };
   // the fused form holds only the first kPreA of them in registers during
-  // the combine (the combine's row loads need registers too), the rest go out
-  // right after it
+  // the combine (the combine's row loads need registers too), up to kPreB
+  // go out as soon as the combine's rows are summed and the rest after the
+  // norm (issuing all of them after the sums spilled registers)
   constexpr int kPreA = COMBINE ? (kPre < 8 ? kPre : 8) : kPre;
+  constexpr int kPreB = COMBINE ? (kPre < 16 ? kPre : 16) : kPre;
   float4 wpre[kPre > 0 ? kPre : 1];
 #pragma unroll
   for (int u = 0; u < kPreA; ++u) wpre[u] = wload(min(h_lo + 4 * u, H - 4));
+  // up to 8 tokens per block the expert's bias is read here, not at the
+  // top-k, and the fused norm's gain is staged through LDS (at 16 tokens the
+  // extra live registers spilled)
+  constexpr bool kEarly = TPB <= 8;
+  const float bias_e = kEarly && bias && e < E ? bias[e] : 0.f;
 
   // ---- 0. (fused) the previous layer's combine: h' = h + sum_j w_j y[inv] + sum_s ys,
   //         the same fixed-order fp32 sums as moe_combine, into h and the LDS rows ----
@@ -116,6 +123,16 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     __shared__ int crow[TPB][kMaxExperts];
     __shared__ float cwt[TPB][kMaxExperts];
     __shared__ double s_scale[TPB];
+    // the norm gain staged once into LDS, its loads issued with the router
+    // weights' (H <= 2 x kThreads)
+    __shared__ float s_gain[kEarly ? kMaxHidden : 1];
+    static_assert(kMaxHidden <= 2 * kThreads, "two gain values per thread");
+    const bool use_gain = kEarly && (flags & 1) && gain;
+    float gv0 = 0.f, gv1 = 0.f;
+    if (use_gain) {
+      if ((int)threadIdx.x < H) gv0 = gain[threadIdx.x];
+      if ((int)threadIdx.x + kThreads < H) gv1 = gain[threadIdx.x + kThreads];
+    }
     double* ssp = reinterpret_cast<double*>(part);  // [TPB][H/8] segment sums (part is free until the logits)
     const St* y = static_cast<const St*>(ca.y);
     const St* ys = static_cast<const St*>(ca.ys);
@@ -123,6 +140,10 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
       const int i = idx / ca.k, j = idx % ca.k, t = min(t0 + i, T - 1);
       crow[i][j] = clampi(ca.inv[(size_t)t * ca.k + j], 0, ca.n_rows - 1);
       cwt[i][j] = ca.w[(size_t)t * ca.k + j];
+    }
+    if (use_gain) {
+      if ((int)threadIdx.x < H) s_gain[threadIdx.x] = gv0;
+      if ((int)threadIdx.x + kThreads < H) s_gain[threadIdx.x + kThreads] = gv1;
     }
     lds_barrier();
     const int nseg = H / 8;
@@ -142,6 +163,8 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
       load8(o, g);
       ssp[idx] = seg_sumsq(g);   // this 8-element segment's sum of squares
     }
+#pragma unroll
+    for (int u = kPreA; u < kPreB; ++u) wpre[u] = wload(min(h_lo + 4 * u, H - 4));
     lds_barrier();
     // scale per token from its segment sums, in the order the unfused norm uses
     for (int i = wave; i < TPB; i += kWaves) {
@@ -158,15 +181,13 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
       float f[8];
       St o[8];
       load8(xs + i * H + c, f);
-      norm8(f, s_scale[i], (flags & 1) ? gain : nullptr, c, o);
+      norm8(f, s_scale[i], use_gain ? s_gain : (flags & 1) ? gain : nullptr, c, o);
       store8(xn + (size_t)t * H + c, o);
       store8(xs + i * H + c, o);
     }
   }
-
-
 #pragma unroll
-  for (int u = kPreA; u < kPre; ++u) wpre[u] = wload(min(h_lo + 4 * u, H - 4));
+  for (int u = kPreB; u < kPre; ++u) wpre[u] = wload(min(h_lo + 4 * u, H - 4));
 
   // ---- 1. RMSNorm: xn = h / sqrt(mean(h^2) + eps) * gain, scale in fp64, one rounding ----
   // (the fused form did this above with the whole block).  The sum of squares
@@ -233,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     float l = part[i * kWave + e];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) l += part[(w * TPB + i) * kWave + e];
-    if (bias && valid) l += bias[e];
+    if (bias && valid) l += kEarly ? bias_e : bias[e];
     if (logits && valid) logits[(size_t)t * E + e] = l;
     // k rounds: the largest remaining logit, then the lowest lane holding it
     float cur = valid ? l : -INFINITY;

@@ -40,11 +40,6 @@ namespace {
 // libm's expf and an IEEE division.  The bf16 paths use silu_bf16path.
 __device__ __forceinline__ float silu_f32path(float z) { return z / (1.0f + expf(-z)); }
 
-#ifndef MOE_DEEP_MAX_ITEMS
-#define MOE_DEEP_MAX_ITEMS 256
-#endif
-constexpr int kDeepMaxItems = MOE_DEEP_MAX_ITEMS;   // launches of at most this many items use the deep ring
-
 constexpr int kRoutedMaxPairs = kPermuteChunk;   // (token, slot) pairs of one routed launch (host-checked)
 constexpr int kWaves = 8;                 // wavefronts per block
 constexpr int kBlockThreads = kWaves * 64;
@@ -218,13 +213,15 @@ __device__ __forceinline__ void stream_chunk_fixed(const bf16_t* wa, const bf16_
 // expert and tile; the split multiplies the blocks by KS.  KS depends on
 // the weight shape only, never on the number of rows, so a row's result
 // does not depend on the batch.
-// DEEP: 6 k-steps of weights in flight per wavefront instead of 3 in the
-// 16-row item form.  A launch with few work items (batch 1: ~20 touched
-// experts) has too few bytes in flight to cover the memory latency at 3
-// (bandwidth ~ bytes in flight / latency); with many items 3 suffice and
-// the smaller register ring keeps more blocks per CU.  The depth does not
-// change any row's k-order, so results are the same bits either way.
-template <bool GATED, bool ROUTED, bool DEEP>
+// The 16-row item form keeps 6 k-steps of weights in flight per wavefront
+// (the multi-row forms 3).  Bandwidth per block is about its bytes in
+// flight over the memory latency: a launch with few items (batch 1: ~20
+// touched experts) needs the depth to cover the latency at all, and in a
+// launch of many items it shortens the tail where the last blocks stream
+// alone.  Measured against a 3-deep ring from 1 to 1,000 tokens it was as
+// fast or faster at every size, although the down kernel then holds 2
+// blocks per CU instead of 3.  The depth does not change any row's k-order.
+template <bool GATED, bool ROUTED>
 __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
     const bf16_t* __restrict__ x, const int32_t* __restrict__ gather,
     const int32_t* __restrict__ offsets, int G, int n_rows, int T,
@@ -232,7 +229,7 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
     const bf16_t* res, RoutedArgs rt) {
   static_assert(!ROUTED || GATED, "only the gate/up stage derives its rows from the expert ids");
   constexpr int D = 3;                    // k-steps of weights in flight per wavefront (multi-row items)
-  constexpr int DB = DEEP ? 6 : 3;        // the same for 16-row items
+  constexpr int DB = 6;                   // the same for 16-row items
   constexpr int WCOLS = GATED ? 16 : 32;  // output columns per wavefront
   extern __shared__ __align__(16) bf16_t xl[];   // [kRows][lds_row(K)]
 
@@ -654,11 +651,7 @@ hipError_t launch_skinny(const bf16_t* x, const int32_t* gather, const int32_t* 
     chunk_cfg = 2 | (4 << 16);
     lds = std::max(lds, std::max(chunk_lds(2), chunk_lds(4)));
   }
-  // few work items (an upper bound: non-empty groups x column tiles x K
-  // slices): the deep weight ring
-  const long long items_ub = (long long)std::min(G, n_rows) * n_ctiles << ks_log2;
-  const bool deep = items_ub <= kDeepMaxItems;
-  auto kern = deep ? &skinny_kernel<GATED, ROUTED, true> : &skinny_kernel<GATED, ROUTED, false>;
+  auto kern = &skinny_kernel<GATED, ROUTED>;
   if (lds > 64 * 1024) {  // K > 2040: allow up to the CU's 160 KB of LDS
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
