@@ -9,7 +9,8 @@
 // (ascending token inside an expert) and deterministic, with no atomics.
 // One chunk (every decode batch) is a single block; larger inputs take a
 // count pass, a one-block scan over (chunk, expert) and a scatter pass that
-// re-ranks its chunk.
+// re-ranks its chunk, with chunks of 1024 slots there (one piece per
+// wavefront: 217 blocks at 36,992 x 6 slots, where 4096-slot chunks gave 55).
 #include "common.hpp"
 #include "kernels.hpp"
 #include "validate.hpp"
@@ -21,15 +22,17 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;                // 16
 constexpr int kPieces = kPermuteChunk / kWave;          // 64 pieces per chunk
 constexpr int kPiecesPerWave = kPieces / kWaves;        // 4
+static_assert(kPermuteChunkM == kWaves * kWave, "multi-block chunks: one piece per wavefront");
 
 // Rank the slots of one chunk.  Fills pcount[p][e] (count of expert e in
 // piece p; lanes >= E write nothing) and, per pass pi, the lane's expert and
 // rank inside its piece.
+template <int PPW>
 __device__ __forceinline__ void rank_chunk(const int32_t* __restrict__ ids, int s0, int n, int E,
                                            int (*pcount)[kMaxExperts], int* my_e, int* my_rank) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
-  for (int pi = 0; pi < kPiecesPerWave; ++pi) {
+  for (int pi = 0; pi < PPW; ++pi) {
     const int p = wave + kWaves * pi;
     const int s = p * kWave + lane;
     const int e = s < n ? clampi(ids[s0 + s], 0, E - 1) : -1;
@@ -60,12 +63,13 @@ __device__ __forceinline__ int scan_pieces(int (*pcount)[kMaxExperts], int n_pie
   return run;
 }
 
+template <int PPW>
 __device__ __forceinline__ void scatter_chunk(int s0, int n, int k, const int* base,
                                               int (*pcount)[kMaxExperts], const int* my_e, const int* my_rank,
                                               int32_t* __restrict__ gather, int32_t* __restrict__ inv) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
-  for (int pi = 0; pi < kPiecesPerWave; ++pi) {
+  for (int pi = 0; pi < PPW; ++pi) {
     const int p = wave + kWaves * pi;
     const int s = p * kWave + lane;
     if (s < n) {
@@ -112,68 +116,94 @@ __global__ __launch_bounds__(kThreads) void permute_one_block(const int32_t* __r
   const int n = T * k;
   const int n_pieces = (n + kWave - 1) / kWave;
   int my_e[kPiecesPerWave], my_rank[kPiecesPerWave];
-  rank_chunk(ids, 0, n, E, pcount, my_e, my_rank);
+  rank_chunk<kPiecesPerWave>(ids, 0, n, E, pcount, my_e, my_rank);
   __syncthreads();
   if (threadIdx.x < E) tot[threadIdx.x] = scan_pieces(pcount, n_pieces, threadIdx.x);
   __syncthreads();
   if (threadIdx.x < kWave) scan_experts(tot, E, S, T, base, offsets);
   __syncthreads();
-  scatter_chunk(0, n, k, base, pcount, my_e, my_rank, gather, inv);
+  scatter_chunk<kPiecesPerWave>(0, n, k, base, pcount, my_e, my_rank, gather, inv);
   fill_shared_rows(T, k, S, gather, threadIdx.x, kThreads);
 }
 
 // count pass: per-chunk expert totals
 __global__ __launch_bounds__(kThreads) void permute_count(const int32_t* __restrict__ ids, int n_slots, int E,
                                                           int32_t* __restrict__ counts) {
-  __shared__ int pcount[kPieces][kMaxExperts];
-  const int s0 = blockIdx.x * kPermuteChunk;
-  const int n = min(kPermuteChunk, n_slots - s0);
+  __shared__ int pcount[kWaves][kMaxExperts];
+  const int s0 = blockIdx.x * kPermuteChunkM;
+  const int n = min(kPermuteChunkM, n_slots - s0);
   const int n_pieces = (n + kWave - 1) / kWave;
-  int my_e[kPiecesPerWave], my_rank[kPiecesPerWave];
-  rank_chunk(ids, s0, n, E, pcount, my_e, my_rank);
+  int my_e[1], my_rank[1];
+  rank_chunk<1>(ids, s0, n, E, pcount, my_e, my_rank);
   __syncthreads();
   if (threadIdx.x < E) counts[blockIdx.x * E + threadIdx.x] = scan_pieces(pcount, n_pieces, threadIdx.x);
 }
 
-// One block of 64 threads: thread e walks the chunks in order.
-__global__ __launch_bounds__(64) void permute_scan(const int32_t* __restrict__ counts, int n_chunks, int E,
-                                                   int S, int T, int32_t* __restrict__ bases,
-                                                   int32_t* __restrict__ offsets) {
+// One block, 16 threads per expert: thread j of expert e owns the chunks
+// [j per, (j+1) per).  Pass 1 sums its chunks' counts (loads issued 8 at a
+// time), a 16-lane prefix sum gives each run's start, and the experts'
+// totals are scanned into their first rows; pass 2 writes each chunk's base
+// (first row + the counts of the expert's earlier chunks).  Integer sums:
+// the same bases as a sequential walk over the chunks.
+__global__ __launch_bounds__(kThreads) void permute_scan(const int32_t* __restrict__ counts, int n_chunks, int E,
+                                                         int S, int T, int32_t* __restrict__ bases,
+                                                         int32_t* __restrict__ offsets) {
   __shared__ int tot[kMaxExperts];
   __shared__ int first[kMaxExperts];
-  const int e = threadIdx.x;
-  if (e < E) {
-    int run = 0;
-    for (int c = 0; c < n_chunks; ++c) {
-      bases[c * E + e] = run;
-      run += counts[c * E + e];
-    }
-    tot[e] = run;
+  static_assert(kThreads == 16 * kMaxExperts, "16 threads per expert");
+  const int e = threadIdx.x >> 4, j = threadIdx.x & 15;
+  const int per = (n_chunks + 15) / 16, c0 = min(j * per, n_chunks), c1 = min(c0 + per, n_chunks);
+  const bool act = e < E;
+  int sum = 0;
+  for (int c = c0; c < c1; c += 8) {
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = act && c + u < c1 ? counts[(size_t)(c + u) * E + e] : 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sum += v[u];
   }
+  int incl = sum;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) {
+    const int x = __shfl_up(incl, o, 16);
+    if (j >= o) incl += x;
+  }
+  if (act && j == 15) tot[e] = incl;
   __syncthreads();
-  scan_experts(tot, E, S, T, first, offsets);
+  if (threadIdx.x < kWave) scan_experts(tot, E, S, T, first, offsets);
   __syncthreads();
-  if (e < E)
-    for (int c = 0; c < n_chunks; ++c) bases[c * E + e] += first[e];
+  if (!act) return;
+  int run = first[e] + incl - sum;
+  for (int c = c0; c < c1; c += 8) {
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = c + u < c1 ? counts[(size_t)(c + u) * E + e] : 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (c + u < c1) {
+        bases[(size_t)(c + u) * E + e] = run;
+        run += v[u];
+      }
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void permute_scatter(const int32_t* __restrict__ ids, int T, int k,
                                                             int E, int S, const int32_t* __restrict__ bases,
                                                             int32_t* __restrict__ gather,
                                                             int32_t* __restrict__ inv) {
-  __shared__ int pcount[kPieces][kMaxExperts];
+  __shared__ int pcount[kWaves][kMaxExperts];
   __shared__ int base[kMaxExperts];
   const int n_slots = T * k;
-  const int s0 = blockIdx.x * kPermuteChunk;
-  const int n = min(kPermuteChunk, n_slots - s0);
+  const int s0 = blockIdx.x * kPermuteChunkM;
+  const int n = min(kPermuteChunkM, n_slots - s0);
   const int n_pieces = (n + kWave - 1) / kWave;
-  int my_e[kPiecesPerWave], my_rank[kPiecesPerWave];
-  rank_chunk(ids, s0, n, E, pcount, my_e, my_rank);
+  int my_e[1], my_rank[1];
+  rank_chunk<1>(ids, s0, n, E, pcount, my_e, my_rank);
   if (threadIdx.x < E) base[threadIdx.x] = bases[blockIdx.x * E + threadIdx.x];
   __syncthreads();
   if (threadIdx.x < E) scan_pieces(pcount, n_pieces, threadIdx.x);
   __syncthreads();
-  scatter_chunk(s0, n, k, base, pcount, my_e, my_rank, gather, inv);
+  scatter_chunk<1>(s0, n, k, base, pcount, my_e, my_rank, gather, inv);
   fill_shared_rows(T, k, S, gather, blockIdx.x * kThreads + threadIdx.x, gridDim.x * kThreads);
 }
 
@@ -182,15 +212,15 @@ __global__ __launch_bounds__(kThreads) void permute_scatter(const int32_t* __res
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int S, int32_t* offsets,
                           int32_t* gather, int32_t* inv, void* ws, hipStream_t s) {
   const int n_slots = T * k;
-  const int n_chunks = (n_slots + kPermuteChunk - 1) / kPermuteChunk;
-  if (n_chunks <= 1) {
+  if (n_slots <= kPermuteChunk) {
     hipLaunchKernelGGL(permute_one_block, dim3(1), dim3(kThreads), 0, s, ids, T, k, E, S, offsets, gather, inv);
     return hipGetLastError();
   }
+  const int n_chunks = (n_slots + kPermuteChunkM - 1) / kPermuteChunkM;
   int32_t* counts = static_cast<int32_t*>(ws);
   int32_t* bases = counts + (size_t)n_chunks * E;
   hipLaunchKernelGGL(permute_count, dim3(n_chunks), dim3(kThreads), 0, s, ids, n_slots, E, counts);
-  hipLaunchKernelGGL(permute_scan, dim3(1), dim3(64), 0, s, counts, n_chunks, E, S, T, bases, offsets);
+  hipLaunchKernelGGL(permute_scan, dim3(1), dim3(kThreads), 0, s, counts, n_chunks, E, S, T, bases, offsets);
   hipLaunchKernelGGL(permute_scatter, dim3(n_chunks), dim3(kThreads), 0, s, ids, T, k, E, S, bases, gather, inv);
   return hipGetLastError();
 }

@@ -42,8 +42,8 @@ int check_pack(const void* src, const void* dst, int G, int N, int K, int kind, 
 size_t permute_ws_bytes(int T, int k, int E) {
   if (T <= 0 || k <= 0 || E <= 0) return 0;
   long long slots = (long long)T * k;
-  long long chunks = (slots + kPermuteChunk - 1) / kPermuteChunk;
-  if (chunks <= 1) return 0;
+  if (slots <= kPermuteChunk) return 0;   // one block, no workspace
+  long long chunks = (slots + kPermuteChunkM - 1) / kPermuteChunkM;
   // per-chunk expert counts and per-chunk scatter bases
   return align256((size_t)(2 * chunks * E) * sizeof(int32_t));
 }

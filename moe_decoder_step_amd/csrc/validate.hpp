@@ -15,7 +15,8 @@ constexpr int kMaxExperts = 64;      // one router lane per expert in a wavefron
 constexpr int kMaxHidden = 2048;     // route kernel keeps a block's normed rows in LDS
 constexpr int kMaxShared = 8;
 constexpr int kMaxDrafts = 15;
-constexpr int kPermuteChunk = 4096;  // slots per block of the permutation kernels
+constexpr int kPermuteChunk = 4096;  // slots of the one-block permutation (every decode batch)
+constexpr int kPermuteChunkM = 1024; // slots per block of the multi-block permutation passes
 constexpr int kAdvanceMaxB = 1024;   // sequences of one spec_advance call (one block)
 constexpr int kAttnHeadDim = 128;    // attention head size
 constexpr int kMaxAttnP = 16;        // verify positions per sequence in one attention call
