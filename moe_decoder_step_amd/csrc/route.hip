@@ -111,6 +111,15 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   float4 wpre[kPre > 0 ? kPre : 1];
 #pragma unroll
   for (int u = 0; u < kPreA; ++u) wpre[u] = wload(min(h_lo + 4 * u, H - 4));
+  // larger blocks stream the slice through a ring of kRing float4 loads, the
+  // first ones issued here so that they land while the norm runs (a single
+  // load in flight made every 128 FMAs wait out an L2 round trip)
+  constexpr int kRing = kPre > 0 ? 1 : 8;
+  float4 wring[kRing];
+  if constexpr (kPre == 0) {
+#pragma unroll
+    for (int d = 0; d < kRing; ++d) wring[d] = wload(min(h_lo + 4 * d, H - 4));
+  }
   // up to 8 tokens per block the expert's bias is read here, not at the
   // top-k, and the fused norm's gain is staged through LDS (at 16 tokens the
   // extra live registers spilled)
@@ -200,24 +209,60 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
       if (t >= T) break;
       const St* hrow = h + (size_t)t * H;
       Xs* xrow = xs + i * H;
-      double scale = 1.0;
-      if (norm) {
-        double ss = 0.0;
+      if constexpr (kPre == 0) {
+        // (blocks of 32 tokens, no router registers held) the row's segments
+        // of this lane (l, l + 64, ...): all loads in flight at once, kept
+        // for the normalising pass
+        constexpr int kSegs = (kMaxHidden + 8 * kWave - 1) / (8 * kWave);
+        typename Row8<St>::raw rr[kSegs];
+#pragma unroll
+        for (int q = 0; q < kSegs; ++q) rr[q] = Row8<St>::load(hrow + min(lane * 8 + q * 8 * kWave, H - 8));
+        double scale = 1.0;
+        if (norm) {
+          double ss = 0.0;
+#pragma unroll
+          for (int q = 0; q < kSegs; ++q) {
+            if (lane * 8 + q * 8 * kWave < H) {
+              float f[8];
+              Row8<St>::unpack(rr[q], f);
+              ss += seg_sumsq(f);
+            }
+          }
+          ss = wave_sum_f64(ss);
+          scale = 1.0 / sqrt(ss / (double)H + (double)eps);
+        }
+#pragma unroll
+        for (int q = 0; q < kSegs; ++q) {
+          const int c = lane * 8 + q * 8 * kWave;
+          if (c < H) {
+            float f[8];
+            St o[8];
+            Row8<St>::unpack(rr[q], f);
+            norm8(f, scale, norm ? gain : nullptr, c, o);
+            store8(xn + (size_t)t * H + c, o);
+            store8(xrow + c, o);
+          }
+        }
+      } else {
+        double scale = 1.0;
+        if (norm) {
+          double ss = 0.0;
+          for (int c = lane * 8; c < H; c += 8 * kWave) {
+            float f[8];
+            load8(hrow + c, f);
+            ss += seg_sumsq(f);
+          }
+          ss = wave_sum_f64(ss);
+          scale = 1.0 / sqrt(ss / (double)H + (double)eps);
+        }
         for (int c = lane * 8; c < H; c += 8 * kWave) {
           float f[8];
+          St o[8];
           load8(hrow + c, f);
-          ss += seg_sumsq(f);
+          norm8(f, scale, norm ? gain : nullptr, c, o);
+          store8(xn + (size_t)t * H + c, o);
+          store8(xrow + c, o);
         }
-        ss = wave_sum_f64(ss);
-        scale = 1.0 / sqrt(ss / (double)H + (double)eps);
-      }
-      for (int c = lane * 8; c < H; c += 8 * kWave) {
-        float f[8];
-        St o[8];
-        load8(hrow + c, f);
-        norm8(f, scale, norm ? gain : nullptr, c, o);
-        store8(xn + (size_t)t * H + c, o);
-        store8(xrow + c, o);
       }
     }
   }
@@ -237,10 +282,23 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
       acc[i] = fmaf(x.w, w.w, acc[i]);
     }
   };
+  if constexpr (kPre > 0) {
 #pragma unroll
-  for (int u = 0; u < kPre; ++u)
-    if (h_lo + 4 * u < h_hi) fma4(wpre[u], h_lo + 4 * u);
-  for (int hh = h_lo + 4 * kPre; hh < h_hi; hh += 4) fma4(wload(hh), hh);
+    for (int u = 0; u < kPre; ++u)
+      if (h_lo + 4 * u < h_hi) fma4(wpre[u], h_lo + 4 * u);
+    for (int hh = h_lo + 4 * kPre; hh < h_hi; hh += 4) fma4(wload(hh), hh);
+  } else {
+    // slot d holds the step s with s % kRing == d; the refill kRing steps
+    // ahead is unconditional (past the slice: a valid address, never used)
+    for (int s0 = 0; h_lo + 4 * s0 < h_hi; s0 += kRing) {
+#pragma unroll
+      for (int d = 0; d < kRing; ++d) {
+        const int hh = h_lo + 4 * (s0 + d);
+        if (hh < h_hi) fma4(wring[d], hh);
+        wring[d] = wload(min(h_lo + 4 * (s0 + d + kRing), H - 4));
+      }
+    }
+  }
   if (lds_union<TPB>()) lds_barrier();  // every wavefront is done with the normed rows
 #pragma unroll
   for (int i = 0; i < TPB; ++i) part[(wave * TPB + i) * kWave + e] = acc[i];
