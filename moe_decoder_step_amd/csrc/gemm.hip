@@ -6,28 +6,38 @@
 // tile of 256 rows (tokens of one group) by 8 weight-row pairs:
 //   gated stage: 8 (gate 16-row, up 16-row) pairs = 128 activation columns;
 //   down stage:  8 pairs of 16 weight rows = 256 output columns.
-// The reduction runs in stages of 32 (one MFMA k-step).  A stage's 16
-// activation fragments (16 KB) go through LDS, its 16 weight fragments
-// straight into registers.  A 1 KB fragment holds, in lane order, the 16 rows
-// x 32 k-elements one wavefront feeds to v_mfma_f32_16x16x32_bf16, so every
-// LDS read is 1 KB of consecutive bytes (no bank conflicts).  Activation
-// fragments are loaded from global memory straight into LDS
-// (global_load_lds_dwordx4: lane l's 16 bytes land at fragment offset 16 l),
-// rows gathered per lane, into a ring of kGAheadA + 1 stage buffers, kGAheadA
-// stages ahead of the multiply; each wavefront loads the 2 packed weight
-// fragments it multiplies (1 KB each, as they lie in memory,
-// moe_pack_weights) into a register ring, kGAhead stages ahead.
+// The reduction runs in stages of 32.  A stage's activations (16 KB) go
+// through LDS, its weights (the pair's two packed 16 x 32 fragments,
+// moe_pack_weights) straight into registers.  Wavefront w computes all 256
+// rows by pair w, 128 fp32 accumulators per lane, so every weight byte is
+// fetched once per block (32 KB per stage from memory in all) and every
+// wavefront reads all 16 KB of a stage's activations from LDS.
 //
-// Wavefront w computes all 256 rows (16 MFMA row blocks) by pair w (2 weight
-// fragments): 32 MFMAs per stage, 128 fp32 accumulators per lane.  So every
-// weight fragment is fetched once per block (32 KB per stage from memory in
-// all), and every wavefront reads all 16 activation fragments of a stage
-// from LDS.  The weights are the MFMA A operand and the activations the B
-// operand, so a lane ends with 4 consecutive output columns of one row
-// (8-byte stores).
+// The multiply:
+//   gated: v_mfma_f32_16x16x32_bf16, the fragments as they lie in memory
+//          (lane l: row l % 16, k-elements 8 (l / 16) .. +7) as the A
+//          operand, 16 token rows as the B operand, 32 MFMAs per stage;
+//   down:  v_mfma_f32_32x32x16_bf16, the pair's 32 weight rows as one A
+//          operand, 32 token rows as the B operand, 2 MFMAs (k-halves) per
+//          row block, 16 per stage.
+// On the same data one 16x16x32 MFMA and the two 32x32x16 MFMAs of its
+// k-halves give the same bits (an in-bounds probe over 4.2M outputs --
+// random, wide-exponent, cancelling and large-accumulator inputs -- found no
+// difference), so both stages, and the weight-streaming kernel, sum a row's
+// products identically.  The larger shape ran the LDS-fed stage loop alone at
+// 0.94 of the MFMA peak against 0.74, and the down GEMM 8% faster; the gate/up
+// GEMM measured 5% slower with it (stores, load lane order and LDS read
+// schedule ruled out) and keeps the smaller one.
 //
-// The fp32 accumulation order along K is fixed: 32 elements per MFMA, in
-// increasing k.
+// Activations are loaded from global memory straight into LDS
+// (global_load_lds_dwordx4: lane l's 16 bytes land at offset 16 l of a 1 KB
+// block, one load covering the 64-byte stage segments of 16 token rows),
+// rows gathered per lane, into a ring of kGAheadA + 1 stage buffers,
+// kGAheadA stages ahead of the multiply; the block layout is per shape
+// (act_slot).  The weights go into a register ring, kGAhead stages ahead.
+//
+// The fp32 accumulation order along K is fixed: 32 elements per 16x16x32
+// MFMA (16 per 32x32x16 MFMA, the same sums), in increasing k.
 #include <atomic>
 #include "common.hpp"
 #include "kernels.hpp"
@@ -73,38 +83,124 @@ __device__ __forceinline__ void wait_barrier() {
 
 __device__ __forceinline__ uint4 lds16(const char* p) { return *reinterpret_cast<const uint4*>(p); }
 
-// Row blocks i0 .. i0 + 3 of one stage: multiply the stage in `cur` with the
-// weight fragments `bw`.
-__device__ __forceinline__ void gemm_half(const char* cur, int i0, const uint4 (&bw)[2],
-                                          f32x4_t (&acc)[16][2], int lane) {
-#pragma unroll
-  for (int i = i0; i < i0 + 8; ++i) {
-    const bf16x8_t xa = as_bf16x8(lds16(cur + i * 1024 + lane * 16));
-#pragma unroll
-    for (int h = 0; h < 2; ++h) acc[i][h] = mfma16x16x32(as_bf16x8(bw[h]), xa, acc[i][h]);
-  }
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+
+__device__ __forceinline__ f32x16_t mfma32x32x16(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// One stage that refills: row blocks 0-7 of the stage in `cur`, the barrier
+// A stage's 16 KB of activations: 16 blocks of 1 KB, block b = token rows
+// 16 b .. 16 b + 15 of the tile; the place of row q's chunk c (k-elements
+// 8 c .. 8 c + 7) in a block:
+//   16x16x32: 16 (16 c + q), lane order of the B operand (lane 16 c + q);
+//   32x32x16: 64 q + 16 (c ^ (q / 4 mod 4)): the whole 64-byte row segment
+//     comes from one load (4 lanes per row, one request per segment), and
+//     the swizzle keeps the operand reads (16 rows, one chunk) free of bank
+//     conflicts.  (The 16x16x32 gate/up GEMM measured 2% slower with it.)
+template <bool M32>
+__device__ __forceinline__ int act_slot(int q, int c) {
+  return M32 ? q * 64 + ((c ^ ((q >> 2) & 3)) << 4) : (16 * c + q) * 16;
+}
+
+// The accumulators of a wavefront (256 rows by its pair) and the stage
+// multiply, by MFMA shape.
+template <bool M32>
+struct Mma;
+
+// 16x16x32: row block i (16 rows) by fragment h; B operand lane l = row
+// l % 16, chunk l / 16.
+template <>
+struct Mma<false> {
+  f32x4_t acc[16][2];
+  int boff;
+  __device__ __forceinline__ void init(int lane) {
+    boff = act_slot<false>(lane & 15, lane >> 4);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) acc[i][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  // half 0 or 1 of a stage: row blocks 8 half .. 8 half + 7
+  __device__ __forceinline__ void half(const char* cur, int hf, const uint4 (&bw)[2]) {
+#pragma unroll
+    for (int i = 8 * hf; i < 8 * hf + 8; ++i) {
+      const bf16x8_t xa = as_bf16x8(lds16(cur + i * 1024 + boff));
+#pragma unroll
+      for (int h = 0; h < 2; ++h) acc[i][h] = mfma16x16x32(as_bf16x8(bw[h]), xa, acc[i][h]);
+    }
+  }
+};
+
+// 32x32x16: row block i (32 rows) by the pair's 32 weight rows, k-halves
+// h = 0, 1; B operand lane l = row l % 32 (block 2 i + (l % 32) / 16), chunk
+// 2 h + l / 32.
+template <>
+struct Mma<true> {
+  f32x16_t acc[8];
+  int boff[2];
+  __device__ __forceinline__ void init(int lane) {
+    const int q = lane & 31;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) boff[h] = (q >> 4) * 1024 + act_slot<true>(q & 15, 2 * h + (lane >> 5));
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
+  }
+  // half 0 or 1 of a stage: row blocks 4 half .. 4 half + 3, k-half 0 of
+  // all four, then k-half 1
+  __device__ __forceinline__ void half(const char* cur, int hf, const uint4 (&bw)[2]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 4 * hf; i < 4 * hf + 4; ++i) {
+        const bf16x8_t xa = as_bf16x8(lds16(cur + i * 2048 + boff[h]));
+        acc[i] = mfma32x32x16(as_bf16x8(bw[h]), xa, acc[i]);
+      }
+  }
+};
+
+// One stage that refills: the first half of the stage in `cur`, the barrier
 // (N loads may stay outstanding), this wavefront's activation loads of a later
-// stage into `nxt`, row blocks 8-15.  The two buffers are distinct; saying so
+// stage into `nxt`, the second half.  The two buffers are distinct; saying so
 // (restrict) lets the compiler see that the reads of `cur` do not depend on
 // the loads into `nxt` still in flight, so it adds no wait for them.
-template <int N>
+template <int N, bool M32>
 __device__ __forceinline__ void gemm_stage(const char* __restrict__ cur, char* __restrict__ nxt,
                                            const bf16_t* const (&src)[2], size_t step, const uint4 (&bw)[2],
-                                           f32x4_t (&acc)[16][2], int lane) {
-  gemm_half(cur, 0, bw, acc, lane);
+                                           Mma<M32>& mma) {
+  mma.half(cur, 0, bw);
   wait_barrier<N>();
 #pragma unroll
   for (int u = 0; u < 2; ++u) load_lds16(src[u] + step, nxt + u * 1024);
-  gemm_half(cur, 8, bw, acc, lane);
+  mma.half(cur, 1, bw);
 }
 
-// this wavefront's 2 weight fragments of stage s (its pair; sets h = 0, 1)
+// This wavefront's 2 weight operands of stage s (its pair), lane l's 16 bytes
+// each, wsrc being the lane's place in the stage's 2 KB:
+//   16x16x32: fragments h = 0, 1 as they lie (wsrc = 8 l elements on);
+//   32x32x16: k-halves h = 0, 1 of the 32 x 32 pair, 256 elements apart.
+template <bool M32>
 __device__ __forceinline__ void load_weights(uint4 (&bw)[2], const bf16_t* wsrc, int s) {
 #pragma unroll
-  for (int h = 0; h < 2; ++h) bw[h] = *reinterpret_cast<const uint4*>(wsrc + (size_t)s * 1024 + h * 512);
+  for (int h = 0; h < 2; ++h)
+    bw[h] = *reinterpret_cast<const uint4*>(wsrc + (size_t)s * 1024 + h * (M32 ? 256 : 512));
+}
+
+// The place of lane l's 16 weight bytes in a stage, in elements.
+//   16x16x32: 8 l.
+//   32x32x16: A-operand row i = l % 32 stands for row r of fragment f,
+//     f = (i / 4) mod 2, r = 4 (i / 8) + i mod 4.  Accumulator v of lane l
+//     holds operand row 8 (v / 4) + 4 (l / 32) + v % 4, which this map makes
+//     output column 16 (l / 32) + v of the pair: 16 consecutive columns per
+//     lane.  Its k-half-0 chunk (k-elements 8 (l / 32) .. +7) is the one lane
+//     16 (l / 32) + r of fragment f holds: 512 f + 8 (16 (l / 32) + r).
+template <bool M32>
+__device__ __forceinline__ int wlane_offset(int lane) {
+  if (!M32) return 8 * lane;
+  const int i = lane & 31;
+  const int f = (i >> 2) & 1, r = 4 * (i >> 3) + (i & 3);
+  return 512 * f + 8 * (16 * (lane >> 5) + r);
 }
 
 // A tile: an M-tile (rows m0 .. m1-1 of group g, which starts at row rb; up
@@ -193,19 +289,27 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(
 
   const int nS = K / kGK;  // stages = MFMA k-steps
 
-  // activation loads: wavefront w fetches row blocks 2 w and 2 w + 1 of each
-  // stage (rows past the group repeat a valid row); weight loads: wavefront
-  // w fetches pair w of the tile (clamped pairs: loaded, never stored)
-  auto act_row = [&](const GTile& tl, int u) { return min(tl.m0 + 16 * (wave * 2 + u) + (lane & 15), tl.m1 - 1); };
+  constexpr bool M32 = !GATED;  // the MFMA shape: 32x32x16 for down, 16x16x32 for gate/up
+
+  // activation loads: wavefront w fetches blocks 2 w and 2 w + 1 of each
+  // stage (token rows 32 w + 16 u .. +15, load u = 0, 1), lane l the (row,
+  // chunk) that act_slot places at 16 l: 16x16x32 row l % 16, chunk l / 16;
+  // 32x32x16 row l / 4, chunk (l % 4) ^ (l / 16 mod 4) (rows past the group
+  // repeat a valid row); weight loads: wavefront w fetches pair w of the tile
+  // (clamped pairs: loaded, never stored)
+  const int lrow = M32 ? lane >> 2 : lane & 15;
+  const int chunk = M32 ? (lane & 3) ^ ((lane >> 4) & 3) : lane >> 4;
+  auto act_row = [&](const GTile& tl, int u) { return min(tl.m0 + 32 * wave + 16 * u + lrow, tl.m1 - 1); };
   auto act_src = [&](const GTile& tl, int u, int gv) {
     int t;
     if (GATED) t = gather ? clampi(gv, 0, T - 1) : clampi(act_row(tl, u) - tl.rb, 0, T - 1);
     else t = act_row(tl, u);
-    return x + (size_t)t * K + 8 * (lane >> 4);
+    return x + (size_t)t * K + 8 * chunk;
   };
+  const int wlane = wlane_offset<M32>(lane);
   auto w_src = [&](const GTile& tl) {
     const int pair = min(tl.nt * kGPairs + wave, n_pairs - 1);
-    return W + ((size_t)tl.g * n_pairs + pair) * nS * 1024 + lane * 8;
+    return W + ((size_t)tl.g * n_pairs + pair) * nS * 1024 + wlane;
   };
   const bf16_t* src[2];
   const bf16_t* wsrc;
@@ -213,16 +317,13 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(
   for (int u = 0; u < 2; ++u) src[u] = act_src(cur, u, GATED && gather ? gather[act_row(cur, u)] : 0);
   wsrc = w_src(cur);
 
-  f32x4_t acc[16][2];
-#pragma unroll
-  for (int i = 0; i < 16; ++i)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) acc[i][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  Mma<M32> mma;
+  mma.init(lane);
 
-  // Stage s multiplies row blocks 0-7, waits at a barrier until the next
+  // Stage s multiplies its first half, waits at a barrier until the next
   // stage of the stream has landed, issues the activation loads kGAhead
   // stages ahead into the buffer of the previous stage (every wavefront is
-  // past it), multiplies row blocks 8-15, and refills its weight slot kGAhead
+  // past it), multiplies its second half, and refills its weight slot kGAhead
   // stages ahead.  So no barrier sits between two stages: the LDS reads of
   // the next stage start while the last MFMAs of this one run.  The loads
   // issued in one stage (act, w) form one group, the groups in stream order
@@ -241,7 +342,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(
   for (int t = 0; t < kGAheadA; ++t) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) load_lds16(src[u] + t * kGK, mine + t * kGStage + u * 1024);
-    if (t < kGAhead) load_weights(bw[t], wsrc, t);
+    if (t < kGAhead) load_weights<M32>(bw[t], wsrc, t);
     asm volatile("" ::: "memory");
   }
   // the first stage: after its weights come kGAhead - 1 groups of both and
@@ -281,46 +382,54 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(
         const int sna = min(s0 + t + kGAheadA + sa_off, nS - 1);
         const int snw = min(s0 + t + kGAhead + sw_off, nS - 1);
         const int nb = gb == 0 ? kGRing - 1 : gb - 1;  // the previous stage's buffer
-        gemm_stage<kGLoads * (kGAhead - 2)>(lds + gb * kGStage, mine + nb * kGStage, src, (size_t)sna * kGK, bw[t],
-                                            acc, lane);
-        load_weights(bw[t], wsrc, snw);
+        gemm_stage<kGLoads * (kGAhead - 2), M32>(lds + gb * kGStage, mine + nb * kGStage, src, (size_t)sna * kGK,
+                                                 bw[t], mma);
+        load_weights<M32>(bw[t], wsrc, snw);
         gb = gb == kGRing - 1 ? 0 : gb + 1;
       }
       s0 += kGAhead;
     } while (s0 < nS);
 
-    // lane holds D[4 (lane/16) + v][lane % 16]: weight rows (output columns)
-    // 4 (lane/16) .. +3 of its fragment, for row lane % 16 of the row block
     const int pair = cur.nt * kGPairs + wave;
+    if constexpr (!M32) {
+      // lane holds D[4 (lane/16) + v][lane % 16]: weight rows (columns of the
+      // pair) 4 (lane/16) .. +3 of its fragments, for row lane % 16 of the
+      // row block; SiLU(gate) * up pairs fragment 0 with fragment 1
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = cur.m0 + i * 16 + (lane & 15);
-      if (row >= cur.m1) continue;
-      if (GATED) {
-        if (pair >= n_pairs) continue;
-        const f32x4_t a = acc[i][0], b = acc[i][1];
+      for (int i = 0; i < 16; ++i) {
+        const int row = cur.m0 + i * 16 + (lane & 15);
+        if (row >= cur.m1 || pair >= n_pairs) continue;
+        const f32x4_t a = mma.acc[i][0], b = mma.acc[i][1];
         uint2 pk;
         pk.x = pack_bf16x2(silu_bf16path(a[0]) * b[0], silu_bf16path(a[1]) * b[1]);
         pk.y = pack_bf16x2(silu_bf16path(a[2]) * b[2], silu_bf16path(a[3]) * b[3]);
         *reinterpret_cast<uint2*>(out + (size_t)row * N + pair * 16 + 4 * (lane >> 4)) = pk;
-      } else {
+      }
+    } else {
+      // lane holds output columns pair * 32 + 16 (lane/32) .. +15 of token
+      // row 32 i + lane % 32 (wlane_offset)
+      const int col = pair * 32 + 16 * (lane >> 5);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int col = pair * 32 + h * 16 + 4 * (lane >> 4);
-          if (col >= N) continue;
-          const f32x4_t a = acc[i][h];
-          uint2 pk;
-          pk.x = pack_bf16x2(a[0], a[1]);
-          pk.y = pack_bf16x2(a[2], a[3]);
-          *reinterpret_cast<uint2*>(out + (size_t)row * N + col) = pk;
-        }
+      for (int i = 0; i < 8; ++i) {
+        const int row = cur.m0 + i * 32 + (lane & 31);
+        if (row >= cur.m1 || col >= N) continue;
+        const f32x16_t a = mma.acc[i];
+        uint4 p0, p1;
+        p0.x = pack_bf16x2(a[0], a[1]);
+        p0.y = pack_bf16x2(a[2], a[3]);
+        p0.z = pack_bf16x2(a[4], a[5]);
+        p0.w = pack_bf16x2(a[6], a[7]);
+        p1.x = pack_bf16x2(a[8], a[9]);
+        p1.y = pack_bf16x2(a[10], a[11]);
+        p1.z = pack_bf16x2(a[12], a[13]);
+        p1.w = pack_bf16x2(a[14], a[15]);
+        uint4* o = reinterpret_cast<uint4*>(out + (size_t)row * N + col);
+        o[0] = p0;
+        o[1] = p1;
       }
     }
     if (nxt.g < 0) break;
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) acc[i][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    mma.init(lane);
     cur = nxt;
     jt += gridDim.x;
   }
