@@ -42,72 +42,6 @@ __device__ __forceinline__ void store8s(bf16_t* p, const bf16_t* v) {
 }
 __device__ __forceinline__ void store8s(float* p, const float* v) { store8(p, v); }
 
-// combine8 (the fixed-order sums) with every row load of the first batch in
-// flight at once: the shared rows go out with the first routed rows instead
-// of after their sums, so a token costs one memory round trip, not two.  The
-// expert rows are read once: non-temporal loads.  The sums are combine8's,
-// in its order.
-template <typename St> struct RowNT;
-template <> struct RowNT<bf16_t> {
-  typedef uint4 raw;
-  static __device__ __forceinline__ raw load(const bf16_t* p) { return ldg16_stream(p); }
-};
-template <> struct RowNT<float> {
-  typedef Row8<float>::raw raw;
-  static __device__ __forceinline__ raw load(const float* p) { return Row8<float>::load(p); }
-};
-
-template <typename St>
-__device__ __forceinline__ void combine8_ahead(const St* y, const int* rows, const float* wk, int k, const St* ys,
-                                               int S, int T, int t, int H, int c, float* acc) {
-  constexpr int kEarly = 4;   // shared rows loaded with the first routed batch
-  typename Row8<St>::raw rs[kEarly];
-  if (S > 0) {
-#pragma unroll
-    for (int u = 0; u < kEarly; ++u) rs[u] = RowNT<St>::load(ys + ((size_t)min(u, S - 1) * T + t) * H + c);
-  }
-#pragma unroll
-  for (int q = 0; q < 8; ++q) acc[q] = 0.f;
-  for (int j0 = 0; j0 < k; j0 += 8) {
-    typename Row8<St>::raw r[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) r[u] = RowNT<St>::load(y + (size_t)rows[min(j0 + u, k - 1)] * H + c);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (j0 + u < k) {
-        float f[8];
-        Row8<St>::unpack(r[u], f);
-        const float wj = wk[j0 + u];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) acc[q] = fmaf(wj, f[q], acc[q]);
-      }
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < kEarly; ++u) {
-    if (u < S) {
-      float f[8];
-      Row8<St>::unpack(rs[u], f);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] += f[q];
-    }
-  }
-  for (int s0 = kEarly; s0 < S; s0 += 4) {
-    typename Row8<St>::raw r[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) r[u] = RowNT<St>::load(ys + ((size_t)min(s0 + u, S - 1) * T + t) * H + c);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (s0 + u < S) {
-        float f[8];
-        Row8<St>::unpack(r[u], f);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) acc[q] += f[q];
-      }
-    }
-  }
-}
-
 template <typename St>
 __global__ __launch_bounds__(kThreads) void combine_kernel(
     const St* __restrict__ y, const int32_t* __restrict__ inv, const float* __restrict__ w,
@@ -125,7 +59,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
     float acc[8], f[8];
     typename Row8<St>::raw rres{};
     if (res) rres = Row8<St>::load(res + (size_t)t * H + c);   // in flight with the expert rows
-    combine8_ahead(y, rows, wk, k, ys, S, T, t, H, c, acc);
+    combine8(y, rows, wk, k, ys, S, T, t, H, c, acc);
     if (combined) store8(combined + (size_t)t * H + c, acc);
     if (res) {
       Row8<St>::unpack(rres, f);
@@ -166,7 +100,7 @@ __global__ __launch_bounds__(kThreads) void combine_norm_kernel(
     float acc[8];
     typename Row8<St>::raw rres{};
     if (res) rres = Row8<St>::load(res + (size_t)t * H + c);
-    combine8_ahead(y, rows, wk, k, ys, S, T, t, H, c, acc);
+    combine8(y, rows, wk, k, ys, S, T, t, H, c, acc);
     if (res) {
       Row8<St>::unpack(rres, f);
 #pragma unroll

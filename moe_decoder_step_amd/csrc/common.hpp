@@ -201,8 +201,10 @@ __device__ __forceinline__ void lds_barrier() {
 
 // ---- the weighted combine of one token's expert rows, 8 hidden elements ----
 // acc[q] = sum_j w[j] * y[rows[j]][c+q] (j ascending, fmaf) + sum_s ys[s*T+t][c+q]
-// (s ascending), in fp32.  Every row load of a batch of 8 is issued before
-// any of the sums, so the k rows cost one memory round trip, not k.
+// (s ascending), in fp32.  Every row load of the first batch of 8 routed rows
+// and of the first 4 shared rows (1 for fp32 rows) is issued before any of
+// the sums, so a bf16 token's rows cost one memory round trip (k <= 8,
+// S <= 4), not one per row or per kind.  The expert rows are read once: non-temporal loads.
 template <typename St> struct Row8;
 template <> struct Row8<bf16_t> {
   typedef uint4 raw;
@@ -219,15 +221,33 @@ template <> struct Row8<float> {
   }
 };
 
+template <typename St> struct RowNT;
+template <> struct RowNT<bf16_t> {
+  typedef uint4 raw;
+  static __device__ __forceinline__ raw load(const bf16_t* p) { return ldg16_stream(p); }
+};
+template <> struct RowNT<float> {
+  typedef Row8<float>::raw raw;
+  static __device__ __forceinline__ raw load(const float* p) { return Row8<float>::load(p); }
+};
+
 template <typename St>
 __device__ __forceinline__ void combine8(const St* y, const int* rows, const float* wk, int k, const St* ys, int S,
                                          int T, int t, int H, int c, float* acc) {
+  // shared rows loaded with the first routed batch (1 for fp32 rows, which
+  // take twice the registers)
+  constexpr int kEarly = sizeof(St) == 2 ? 4 : 1;
+  typename Row8<St>::raw rs[kEarly];
+  if (S > 0) {
+#pragma unroll
+    for (int u = 0; u < kEarly; ++u) rs[u] = RowNT<St>::load(ys + ((size_t)min(u, S - 1) * T + t) * H + c);
+  }
 #pragma unroll
   for (int q = 0; q < 8; ++q) acc[q] = 0.f;
   for (int j0 = 0; j0 < k; j0 += 8) {
     typename Row8<St>::raw r[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) r[u] = Row8<St>::load(y + (size_t)rows[min(j0 + u, k - 1)] * H + c);
+    for (int u = 0; u < 8; ++u) r[u] = RowNT<St>::load(y + (size_t)rows[min(j0 + u, k - 1)] * H + c);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (j0 + u < k) {
@@ -239,10 +259,19 @@ __device__ __forceinline__ void combine8(const St* y, const int* rows, const flo
       }
     }
   }
-  for (int s0 = 0; s0 < S; s0 += 4) {
+#pragma unroll
+  for (int u = 0; u < kEarly; ++u) {
+    if (u < S) {
+      float f[8];
+      Row8<St>::unpack(rs[u], f);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] += f[q];
+    }
+  }
+  for (int s0 = kEarly; s0 < S; s0 += 4) {
     typename Row8<St>::raw r[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) r[u] = Row8<St>::load(ys + ((size_t)min(s0 + u, S - 1) * T + t) * H + c);
+    for (int u = 0; u < 4; ++u) r[u] = RowNT<St>::load(ys + ((size_t)min(s0 + u, S - 1) * T + t) * H + c);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       if (s0 + u < S) {

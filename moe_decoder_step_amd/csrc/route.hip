@@ -92,7 +92,30 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   const int t0 = blockIdx.x * TPB;
   const int e = lane;
 
-  // this wavefront's slice of the hidden dim; its router weights go out first
+  // (fused) the token's expert row numbers and weights go out before the
+  // router weights: loads retire in issue order, so behind the router loads
+  // their wait would include the router loads' latency
+  // (so are the norm gain's, staged through LDS before the first barrier)
+  constexpr bool kEarly = TPB <= 8;
+  int crow_g = 0;
+  float cwt_g = 0.f, gv0 = 0.f, gv1 = 0.f;
+  const bool use_gain = COMBINE && kEarly && (flags & 1) && gain;
+  if constexpr (COMBINE) {
+    static_assert(TPB * kMaxExperts <= kThreads, "one (token, slot) per thread");
+    static_assert(kMaxHidden <= 2 * kThreads, "two gain values per thread");
+    if ((int)threadIdx.x < TPB * ca.k) {
+      const int t = min(t0 + (int)threadIdx.x / ca.k, T - 1), j = (int)threadIdx.x % ca.k;
+      crow_g = ca.inv[(size_t)t * ca.k + j];
+      cwt_g = ca.w[(size_t)t * ca.k + j];
+    }
+    if (use_gain) {
+      if ((int)threadIdx.x < H) gv0 = gain[threadIdx.x];
+      if ((int)threadIdx.x + kThreads < H) gv1 = gain[threadIdx.x + kThreads];
+    }
+    asm volatile("" ::: "memory");
+  }
+
+  // this wavefront's slice of the hidden dim; its router weights go out next
   // (they depend on nothing) and land while the combine and the norm run
   const int hq = ((H / kWaves + 3) / 4) * 4;
   const int h_lo = min(H, wave * hq), h_hi = min(H, h_lo + hq);
@@ -123,7 +146,6 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   // up to 8 tokens per block the expert's bias is read here, not at the
   // top-k, and the fused norm's gain is staged through LDS (at 16 tokens the
   // extra live registers spilled)
-  constexpr bool kEarly = TPB <= 8;
   const float bias_e = kEarly && bias && e < E ? bias[e] : 0.f;
 
   // ---- 0. (fused) the previous layer's combine: h' = h + sum_j w_j y[inv] + sum_s ys,
@@ -132,23 +154,16 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     __shared__ int crow[TPB][kMaxExperts];
     __shared__ float cwt[TPB][kMaxExperts];
     __shared__ double s_scale[TPB];
-    // the norm gain staged once into LDS, its loads issued with the router
-    // weights' (H <= 2 x kThreads)
+    // the norm gain staged once into LDS (H <= 2 x kThreads), its loads
+    // issued at entry
     __shared__ float s_gain[kEarly ? kMaxHidden : 1];
-    static_assert(kMaxHidden <= 2 * kThreads, "two gain values per thread");
-    const bool use_gain = kEarly && (flags & 1) && gain;
-    float gv0 = 0.f, gv1 = 0.f;
-    if (use_gain) {
-      if ((int)threadIdx.x < H) gv0 = gain[threadIdx.x];
-      if ((int)threadIdx.x + kThreads < H) gv1 = gain[threadIdx.x + kThreads];
-    }
     double* ssp = reinterpret_cast<double*>(part);  // [TPB][H/8] segment sums (part is free until the logits)
     const St* y = static_cast<const St*>(ca.y);
     const St* ys = static_cast<const St*>(ca.ys);
-    for (int idx = threadIdx.x; idx < TPB * ca.k; idx += kThreads) {
-      const int i = idx / ca.k, j = idx % ca.k, t = min(t0 + i, T - 1);
-      crow[i][j] = clampi(ca.inv[(size_t)t * ca.k + j], 0, ca.n_rows - 1);
-      cwt[i][j] = ca.w[(size_t)t * ca.k + j];
+    if ((int)threadIdx.x < TPB * ca.k) {
+      const int i = (int)threadIdx.x / ca.k, j = (int)threadIdx.x % ca.k;
+      crow[i][j] = clampi(crow_g, 0, ca.n_rows - 1);
+      cwt[i][j] = cwt_g;
     }
     if (use_gain) {
       if ((int)threadIdx.x < H) s_gain[threadIdx.x] = gv0;
@@ -190,7 +205,11 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
       float f[8];
       St o[8];
       load8(xs + i * H + c, f);
-      norm8(f, s_scale[i], use_gain ? s_gain : (flags & 1) ? gain : nullptr, c, o);
+      // the gain from LDS through an LDS pointer: a pointer that may point to
+      // either LDS or global memory compiles to flat loads, and each of
+      // those waits for every global load in flight (the router weights)
+      if (use_gain) norm8(f, s_scale[i], s_gain, c, o);
+      else norm8(f, s_scale[i], (flags & 1) ? gain : nullptr, c, o);
       store8(xn + (size_t)t * H + c, o);
       store8(xs + i * H + c, o);
     }
