@@ -237,9 +237,13 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
   // ranges.  Pair (g, ct) belongs to XCD (g*n_ctiles + ct) % 8 (block b runs
   // on XCD b % 8); on each XCD the items are ordered by group, tile, range,
   // so the ranges of one large group (a shared expert sees every token) run
-  // back to back on one XCD and share its L2 copy of the weights.  Block b
-  // takes the (b/8)-th item of XCD b%8; the launch holds an upper bound of
-  // items per XCD and the surplus blocks, last in every XCD's list, exit.
+  // back to back on one XCD and share its L2 copy of the weights.  The
+  // groups go in reverse order: the shared experts, last in group order,
+  // have the most rows and the longest items, and their blocks, dispatched
+  // first, no longer end the launch (128-token step: 1.153 -> 1.124 ms).
+  // Block b takes the (b/8)-th item of XCD b%8; the launch holds an upper
+  // bound of items per XCD and the surplus blocks, last in every XCD's list,
+  // exit.
   // Wavefront 0 finds the item: lane l handles groups l and l+64 (G <= 128),
   // counts its items on this XCD, and a wavefront prefix sum places them.
   __shared__ int item_g, item_ct, item_r0, item_r1, item_gs, item_rb;
@@ -309,20 +313,36 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
         for (int h = 0; h < 2; ++h)
           if (l + h * kWave <= G) rt.offsets[l + h * kWave] = l + h * kWave < G ? r0[h] : n_rows;
       }
+      // the items run in reverse group order (below): lane l, half h takes
+      // group G - 1 - (l + 64 h), whose range another lane holds
+      int q0[2], q1[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int gg = max(G - 1 - (l + h * kWave), 0), sl = gg & (kWave - 1);
+        const int a0 = __shfl(r0[0], sl, kWave), a1 = __shfl(r0[1], sl, kWave);
+        const int b0 = __shfl(r1[0], sl, kWave), b1 = __shfl(r1[1], sl, kWave);
+        q0[h] = gg >= kWave ? a1 : a0;
+        q1[h] = gg >= kWave ? b1 : b0;
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        r0[h] = q0[h];
+        r1[h] = q1[h];
+      }
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int g = l + h * kWave;
+      const int g = G - 1 - (l + h * kWave);   // groups in reverse order
       if (!ROUTED) {
-        r0[h] = g < G ? clampi(offsets[g], 0, n_rows) : 0;
-        r1[h] = g < G ? clampi(offsets[g + 1], r0[h], n_rows) : 0;
+        r0[h] = g >= 0 ? clampi(offsets[g], 0, n_rows) : 0;
+        r1[h] = g >= 0 ? clampi(offsets[g + 1], r0[h], n_rows) : 0;
       }
       const int rows = r1[h] - r0[h];
       rbs[h] = rows > 2 * kRows && rb_max >= 4 ? 4 : rows > kRows && rb_max >= 2 ? 2 : 1;
       nr[h] = (rows + rbs[h] * kRows - 1) / (rbs[h] * kRows);
       // tiles of group g on this XCD: ct = c0, c0+8, ... < n_ctiles
       const int c0 = ((xcd - g * n_ctiles) % 8 + 8) % 8;
-      nc[h] = g < G && c0 < n_ctiles ? (n_ctiles - c0 + 7) / 8 : 0;
+      nc[h] = g >= 0 && g < G && c0 < n_ctiles ? (n_ctiles - c0 + 7) / 8 : 0;
     }
     int cnt[2] = {nr[0] * nc[0], nr[1] * nc[1]};
     int incl[2];
@@ -341,7 +361,7 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
     for (int h = 0; h < 2; ++h) {
       const int first = incl[h] - cnt[h];
       if (j >= first && j < incl[h]) {
-        const int g = l + h * kWave;
+        const int g = G - 1 - (l + h * kWave);
         const int li = j - first;              // ordered by tile, then range
         const int c0 = ((xcd - g * n_ctiles) % 8 + 8) % 8;
         item_g = g;
