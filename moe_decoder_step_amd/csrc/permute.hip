@@ -139,41 +139,65 @@ __global__ __launch_bounds__(kThreads) void permute_count(const int32_t* __restr
   if (threadIdx.x < E) counts[blockIdx.x * E + threadIdx.x] = scan_pieces(pcount, n_pieces, threadIdx.x);
 }
 
-// One block, 16 threads per expert: thread j of expert e owns the chunks
-// [j per, (j+1) per).  Pass 1 sums its chunks' counts (loads issued 8 at a
-// time), a 16-lane prefix sum gives each run's start, and the experts'
+// One block: wavefront j owns the chunks [j per, (j+1) per), lane e the
+// expert.  Pass 1 sums the lane's counts over the wavefront's chunks, the
+// wavefronts' sums (through LDS) give each run's start, and the experts'
 // totals are scanned into their first rows; pass 2 writes each chunk's base
 // (first row + the counts of the expert's earlier chunks).  Integer sums:
 // the same bases as a sequential walk over the chunks.
 __global__ __launch_bounds__(kThreads) void permute_scan(const int32_t* __restrict__ counts, int n_chunks, int E,
                                                          int S, int T, int32_t* __restrict__ bases,
                                                          int32_t* __restrict__ offsets) {
+  __shared__ int part[kWaves][kMaxExperts];   // per wavefront's chunk range and expert: its pairs
   __shared__ int tot[kMaxExperts];
   __shared__ int first[kMaxExperts];
-  static_assert(kThreads == 16 * kMaxExperts, "16 threads per expert");
-  const int e = threadIdx.x >> 4, j = threadIdx.x & 15;
-  const int per = (n_chunks + 15) / 16, c0 = min(j * per, n_chunks), c1 = min(c0 + per, n_chunks);
+  static_assert(kThreads == kWaves * kMaxExperts && kMaxExperts == kWave, "a wavefront covers every expert");
+  // lane = expert, wavefront j = chunks [j per, (j + 1) per): every load and
+  // store of a wavefront is one row of 64 experts, 256 contiguous bytes
+  const int e = threadIdx.x & (kWave - 1), j = threadIdx.x >> 6;
+  const int per = (n_chunks + kWaves - 1) / kWaves, c0 = min(j * per, n_chunks), c1 = min(c0 + per, n_chunks);
   const bool act = e < E;
+  // up to kRegChunks chunks per wavefront (every layer of up to 16 x 16 x
+  // 1024 slots): all counts loaded at once and kept in registers for the
+  // second pass, so the kernel waits for one memory round trip instead of
+  // four
+  constexpr int kRegChunks = 16;
+  const bool in_regs = per <= kRegChunks;
+  int vr[kRegChunks];
   int sum = 0;
-  for (int c = c0; c < c1; c += 8) {
-    int v[8];
+  if (in_regs) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = act && c + u < c1 ? counts[(size_t)(c + u) * E + e] : 0;
+    for (int u = 0; u < kRegChunks; ++u) vr[u] = act && c0 + u < c1 ? counts[(size_t)(c0 + u) * E + e] : 0;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) sum += v[u];
+    for (int u = 0; u < kRegChunks; ++u) sum += vr[u];
+  } else {
+    for (int c = c0; c < c1; c += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = act && c + u < c1 ? counts[(size_t)(c + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sum += v[u];
+    }
   }
-  int incl = sum;
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) {
-    const int x = __shfl_up(incl, o, 16);
-    if (j >= o) incl += x;
-  }
-  if (act && j == 15) tot[e] = incl;
+  part[j][e] = sum;
+  __syncthreads();
+  int before = 0;   // pairs of expert e in the chunks of wavefronts 0 .. j-1
+  for (int jj = 0; jj < j; ++jj) before += part[jj][e];
+  if (j == kWaves - 1) tot[e] = act ? before + sum : 0;
   __syncthreads();
   if (threadIdx.x < kWave) scan_experts(tot, E, S, T, first, offsets);
   __syncthreads();
   if (!act) return;
-  int run = first[e] + incl - sum;
+  int run = first[e] + before;
+  if (in_regs) {
+#pragma unroll
+    for (int u = 0; u < kRegChunks; ++u)
+      if (c0 + u < c1) {
+        bases[(size_t)(c0 + u) * E + e] = run;
+        run += vr[u];
+      }
+    return;
+  }
   for (int c = c0; c < c1; c += 8) {
     int v[8];
 #pragma unroll
