@@ -4,10 +4,12 @@
 //   1. norm: wavefront w normalises tokens w, w+16, ... (fp64 scale, one
 //      rounding to the storage type) into LDS and to xn;
 //   2. logits: the hidden dimension is split in sixteen slices, one per
-//      wavefront; lane e (= expert e, E <= 64) accumulates its slice of
-//      l[t,e] for all TPB tokens in fp32, its router row slice having been
-//      loaded into registers at kernel entry (it does not depend on the norm),
-//      the normed tokens read from LDS (broadcast);
+//      wavefront, and each slice in two halves; lane l accumulates experts
+//      l % 32 and l % 32 + 32 (E <= 64) over half l / 32 of its wavefront's
+//      slice for all TPB tokens in fp32, so every normed value read from LDS
+//      (a broadcast) feeds two experts' FMAs; the router weights were loaded
+//      into registers at kernel entry (they do not depend on the norm); the
+//      two halves of an expert's slice are then added, half 0 + half 1;
 //   3. top-k: wavefront w sums the sixteen slices in order (a fixed order that
 //      does not depend on the batch), adds the bias and runs k rounds of a
 //      DPP wavefront max followed by a ballot: the lowest lane holding the
@@ -33,8 +35,10 @@ namespace {
 constexpr int kWaves = 16;     // wavefronts per block (hidden split in 16 slices)
 constexpr int kThreads = kWaves * 64;
 
-// router-weight float4 per lane loaded at kernel entry
-template <int TPB> constexpr int pre_count() { return TPB <= 16 ? 20 : 0; }
+// router-weight float4 per lane loaded at kernel entry (two per step of 4
+// hidden elements: the lane's two experts); 16 tokens per block hold fewer,
+// their accumulators taking the registers
+template <int TPB> constexpr int pre_count() { return TPB <= 8 ? 20 : TPB <= 16 ? 8 : 0; }
 // the slice partials reuse the normed rows' LDS, which then hold fp32 (exact
 // copies of the stored values, converted once instead of at every use)
 template <int TPB> constexpr bool lds_union() { return TPB > 16; }
@@ -119,11 +123,20 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   // (they depend on nothing) and land while the combine and the norm run
   const int hq = ((H / kWaves + 3) / 4) * 4;
   const int h_lo = min(H, wave * hq), h_hi = min(H, h_lo + hq);
-  // router weights of hidden elements hh..hh+3 for this lane's expert: packed,
-  // a wavefront load is 1 KB of consecutive bytes; row-major, it touches 64 rows
-  auto wload = [&](int hh) __attribute__((always_inline)) -> float4 {
-    if (PACKED) return *reinterpret_cast<const float4*>(wr + ((size_t)(hh >> 2) * kWave + e) * 4);
-    return *reinterpret_cast<const float4*>(wr + (size_t)min(e, E - 1) * H + hh);
+  // lane l: experts ea = l % 32 and ea + 32 over half hb = l / 32 of the
+  // slice, [my_lo, my_hi) (the halves split at a multiple of 4)
+  const int hb = lane >> 5, ea = lane & 31;
+  const int h_mid = min(h_hi, h_lo + ((((h_hi - h_lo) >> 1) + 3) & ~3));
+  const int my_lo = hb ? h_mid : h_lo, my_hi = hb ? h_hi : h_mid;
+  // router weights of hidden elements hh..hh+3 for expert ex: packed, a
+  // wavefront load is 2 x 512 consecutive bytes; row-major, it touches 32 rows
+  auto wload = [&](int ex, int hh) __attribute__((always_inline)) -> float4 {
+    if (PACKED) return *reinterpret_cast<const float4*>(wr + ((size_t)(hh >> 2) * kWave + ex) * 4);
+    return *reinterpret_cast<const float4*>(wr + (size_t)min(ex, E - 1) * H + hh);
+  };
+  // float4 slot u of the prefetch: step u / 2, expert ea (+ 32 if u is odd)
+  auto wpre_load = [&](int u) __attribute__((always_inline)) -> float4 {
+    return wload(ea + 32 * (u & 1), min(my_lo + 4 * (u >> 1), H - 4));
   };
   // the fused form holds only the first kPreA of them in registers during
   // the combine (the combine's row loads need registers too), up to kPreB
@@ -133,15 +146,17 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   constexpr int kPreB = COMBINE ? (kPre < 16 ? kPre : 16) : kPre;
   float4 wpre[kPre > 0 ? kPre : 1];
 #pragma unroll
-  for (int u = 0; u < kPreA; ++u) wpre[u] = wload(min(h_lo + 4 * u, H - 4));
-  // larger blocks stream the slice through a ring of kRing float4 loads, the
-  // first ones issued here so that they land while the norm runs (a single
-  // load in flight made every 128 FMAs wait out an L2 round trip)
-  constexpr int kRing = kPre > 0 ? 1 : 8;
-  float4 wring[kRing];
+  for (int u = 0; u < kPreA; ++u) wpre[u] = wpre_load(u);
+  // larger blocks stream the slice through a ring of kRing steps (2 float4
+  // each), the first ones issued here so that they land while the norm runs
+  // (a single load in flight made every 128 FMAs wait out an L2 round trip)
+  constexpr int kRing = kPre > 0 ? 1 : 2;
+  float4 wring[kRing][2];
   if constexpr (kPre == 0) {
 #pragma unroll
-    for (int d = 0; d < kRing; ++d) wring[d] = wload(min(h_lo + 4 * d, H - 4));
+    for (int d = 0; d < kRing; ++d)
+#pragma unroll
+      for (int x = 0; x < 2; ++x) wring[d][x] = wload(ea + 32 * x, min(my_lo + 4 * d, H - 4));
   }
   // up to 8 tokens per block the expert's bias is read here, not at the
   // top-k, and the fused norm's gain is staged through LDS (at 16 tokens the
@@ -188,7 +203,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
       ssp[idx] = seg_sumsq(g);   // this 8-element segment's sum of squares
     }
 #pragma unroll
-    for (int u = kPreA; u < kPreB; ++u) wpre[u] = wload(min(h_lo + 4 * u, H - 4));
+    for (int u = kPreA; u < kPreB; ++u) wpre[u] = wpre_load(u);
     lds_barrier();
     // scale per token from its segment sums, in the order the unfused norm uses
     for (int i = wave; i < TPB; i += kWaves) {
@@ -215,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     }
   }
 #pragma unroll
-  for (int u = kPreB; u < kPre; ++u) wpre[u] = wload(min(h_lo + 4 * u, H - 4));
+  for (int u = kPreB; u < kPre; ++u) wpre[u] = wpre_load(u);
 
   // ---- 1. RMSNorm: xn = h / sqrt(mean(h^2) + eps) * gain, scale in fp64, one rounding ----
   // (the fused form did this above with the whole block).  The sum of squares
@@ -287,40 +302,54 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   }
   lds_barrier();
 
-  // ---- 2. partial logits over this wavefront's slice, fp32, ascending h ----
-  float acc[TPB];
+  // ---- 2. partial logits: per expert and half slice, fp32, ascending h ----
+  float acc[2][TPB];   // [expert ea, ea + 32][token]
 #pragma unroll
-  for (int i = 0; i < TPB; ++i) acc[i] = 0.f;
-  auto fma4 = [&](const float4& w, int hh) __attribute__((always_inline)) {
+  for (int i = 0; i < TPB; ++i) acc[0][i] = acc[1][i] = 0.f;
+  auto fma4 = [&](const float4& w0, const float4& w1, int hh) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < TPB; ++i) {
       const float4 x = lds4(xs + i * H + hh);
-      acc[i] = fmaf(x.x, w.x, acc[i]);
-      acc[i] = fmaf(x.y, w.y, acc[i]);
-      acc[i] = fmaf(x.z, w.z, acc[i]);
-      acc[i] = fmaf(x.w, w.w, acc[i]);
+      acc[0][i] = fmaf(x.x, w0.x, acc[0][i]);
+      acc[0][i] = fmaf(x.y, w0.y, acc[0][i]);
+      acc[0][i] = fmaf(x.z, w0.z, acc[0][i]);
+      acc[0][i] = fmaf(x.w, w0.w, acc[0][i]);
+      acc[1][i] = fmaf(x.x, w1.x, acc[1][i]);
+      acc[1][i] = fmaf(x.y, w1.y, acc[1][i]);
+      acc[1][i] = fmaf(x.z, w1.z, acc[1][i]);
+      acc[1][i] = fmaf(x.w, w1.w, acc[1][i]);
     }
   };
   if constexpr (kPre > 0) {
+    constexpr int kPreSteps = kPre / 2;
 #pragma unroll
-    for (int u = 0; u < kPre; ++u)
-      if (h_lo + 4 * u < h_hi) fma4(wpre[u], h_lo + 4 * u);
-    for (int hh = h_lo + 4 * kPre; hh < h_hi; hh += 4) fma4(wload(hh), hh);
+    for (int u = 0; u < kPreSteps; ++u)
+      if (my_lo + 4 * u < my_hi) fma4(wpre[2 * u], wpre[2 * u + 1], my_lo + 4 * u);
+    for (int hh = my_lo + 4 * kPreSteps; hh < my_hi; hh += 4) fma4(wload(ea, hh), wload(ea + 32, hh), hh);
   } else {
     // slot d holds the step s with s % kRing == d; the refill kRing steps
-    // ahead is unconditional (past the slice: a valid address, never used)
-    for (int s0 = 0; h_lo + 4 * s0 < h_hi; s0 += kRing) {
+    // ahead is unconditional (past the half: a valid address, never used)
+    for (int s0 = 0; my_lo + 4 * s0 < my_hi; s0 += kRing) {
 #pragma unroll
       for (int d = 0; d < kRing; ++d) {
-        const int hh = h_lo + 4 * (s0 + d);
-        if (hh < h_hi) fma4(wring[d], hh);
-        wring[d] = wload(min(h_lo + 4 * (s0 + d + kRing), H - 4));
+        const int hh = my_lo + 4 * (s0 + d);
+        if (hh < my_hi) fma4(wring[d][0], wring[d][1], hh);
+#pragma unroll
+        for (int x = 0; x < 2; ++x) wring[d][x] = wload(ea + 32 * x, min(my_lo + 4 * (s0 + d + kRing), H - 4));
       }
     }
   }
+  // lane l ends with expert l's slice: half 0 (lane l % 32) + half 1 (lane
+  // l % 32 + 32), the other half from lane l ^ 32
+  float lsl[TPB];
+#pragma unroll
+  for (int i = 0; i < TPB; ++i) {
+    const float o0 = __shfl_xor(acc[0][i], 32, kWave), o1 = __shfl_xor(acc[1][i], 32, kWave);
+    lsl[i] = hb == 0 ? acc[0][i] + o0 : o1 + acc[1][i];
+  }
   if (lds_union<TPB>()) lds_barrier();  // every wavefront is done with the normed rows
 #pragma unroll
-  for (int i = 0; i < TPB; ++i) part[(wave * TPB + i) * kWave + e] = acc[i];
+  for (int i = 0; i < TPB; ++i) part[(wave * TPB + i) * kWave + e] = lsl[i];
   lds_barrier();
 
   // ---- 3. top-k by (logit desc, expert id asc), then softmax weights ----
