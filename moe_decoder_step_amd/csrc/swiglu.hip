@@ -228,7 +228,7 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
     const bf16_t* __restrict__ W, int K, int N, int n_ctiles, int ks_log2, int chunk_cfg, bf16_t* out,
     const bf16_t* res, RoutedArgs rt) {
   static_assert(!ROUTED || GATED, "only the gate/up stage derives its rows from the expert ids");
-  constexpr int D = 3;                    // k-steps of weights in flight per wavefront (multi-row items)
+  constexpr int D = 3;                    // k-steps of weights in flight per wavefront (64-row items)
   constexpr int DB = 6;                   // the same for 16-row items
   constexpr int WCOLS = GATED ? 16 : 32;  // output columns per wavefront
   extern __shared__ __align__(16) bf16_t xl[];   // [kRows][lds_row(K)]
@@ -560,6 +560,10 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
     constexpr int RB = decltype(rbc)::value;
     constexpr bool NT = decltype(nt)::value;
     constexpr int RR = RB * kRows;
+    // weight k-steps in flight: 32-row items take the 16-row items' 6-deep
+    // ring (they had ended the launch at half the 16-row items' stream rate;
+    // 6 deep, 118 VGPRs, still two blocks per CU); 64-row items stay at 3
+    constexpr int DR = RB == 2 ? DB : D;
     constexpr int CL = chunk_steps(RB);
     constexpr int NSC = CL * 4;          // 16-byte segments of a row in one chunk
     constexpr int NPF = chunk_regs(RB);  // of them, per thread
@@ -597,9 +601,9 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
     // the first chunk's loads go out before the weights of the first D
     // steps, so its LDS stores wait for the activation rows only
     ld_chunk(0);
-    uint4 ra[D], rb[D];
+    uint4 ra[DR], rb[DR];
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
+    for (int d = 0; d < DR; ++d) {
       const int kk = min(d, nK - 1);
       ra[d] = wload<NT>(wa + kk * 1024);
       rb[d] = wload<NT>(wb + kk * 1024);
@@ -613,13 +617,13 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
     const bf16_t* xs = xl + (lane & 15) * LDC + (lane >> 4) * 8;
     int c0 = 0;
     for (; c0 + CL < nK; c0 += CL) {    // full chunks with a successor
-      stream_chunk_fixed<D, RB, CL, NPF, NT>(wa, wb, xs, LDC, c0, nK, ra, rb, acc_a, acc_b,
+      stream_chunk_fixed<DR, RB, CL, NPF, NT>(wa, wb, xs, LDC, c0, nK, ra, rb, acc_a, acc_b,
                                              [&]() __attribute__((always_inline)) { ld_chunk(c0 + CL); });
       lds_barrier();                    // every wavefront is done with this chunk
       st_chunk();
       lds_barrier();
     }
-    stream_chunk<D, RB, NT>(wa, wb, xs, LDC, c0, nK - c0, nK, ra, rb, acc_a, acc_b);   // the last chunk
+    stream_chunk<DR, RB, NT>(wa, wb, xs, LDC, c0, nK - c0, nK, ra, rb, acc_a, acc_b);   // the last chunk
     if (active)
 #pragma unroll
       for (int r = 0; r < RB; ++r) emit(acc_a[r], acc_b[r], r * kRows + (lane & 15));
