@@ -27,14 +27,17 @@
  * - A size of 0 tokens (or sequences) is a no-op that returns MOE_OK.
  * - The return value is a moe_status.  Host-side argument checks run before
  *   anything is enqueued; a failed launch returns MOE_ERR_HIP.  Device-side
- *   data is never trusted for memory addressing: out-of-range ids and offsets
- *   are clamped into range (memory-safe, the mistake is not reported).
+ *   data is never trusted for memory addressing: out-of-range ids, row
+ *   indices, offsets and lengths are clamped into range (memory-safe), and
+ *   the kernel that clamped also sets the matching MOE_DATA_ERR_* bit in a
+ *   per-GPU word that moe_data_errors reads back (see there).
  * - Outputs are fully overwritten.  The only aliasing allowed is
  *   out == residual in moe_combine.
  * - Process-wide state: a per-device cache of the compute-unit count
- *   (atomics; racing threads store the same value), and for
- *   lmhead_argmax_noalloc a static device array per GPU and a per-device
- *   cache of its address (under a mutex).  Calls on different streams may
+ *   (atomics; racing threads store the same value); the data-error word, a
+ *   static device variable per GPU, and a per-device cache of its address;
+ *   for lmhead_argmax_noalloc a static device array per GPU and a per-device
+ *   cache of its address (the address caches fill under a mutex).  Calls on different streams may
  *   run concurrently as long as they do not share output or workspace
  *   buffers (lmhead_argmax_noalloc calls share that array).
  */
@@ -152,7 +155,8 @@ int moe_route(const void* h, const float* gain, float eps,
  * T*k + s*T .. T*k + (s+1)*T - 1, one per token in order, so one grouped
  * SwiGLU call covers routed and shared experts.
  *
- * topk_ids [T,k] int32     in  (ids outside [0,E) are clamped into it)
+ * topk_ids [T,k] int32     in  (ids outside [0,E) are clamped into it and
+ *                                reported: MOE_DATA_ERR_EXPERT_ID)
  * offsets  [E+S+1] int32   out (offsets[E+s] = T*k + s*T)
  * gather   [T*k + S*T] int32 out: token read by each row
  * inv      [T*k] int32     out: row of each slot
@@ -177,9 +181,10 @@ int moe_permute(const int32_t* topk_ids, int T, int k, int E, int S,
  * paragraph; the SwiGLU form is a reading, the pages do not give it).
  *
  * x         [T,H] dtype                 in
- * gather    [n_rows] int32 or NULL      in  (clamped into [0,T))
+ * gather    [n_rows] int32 or NULL      in  (clamped into [0,T); MOE_DATA_ERR_ROW_INDEX)
  * offsets   [G+1] int32 (device)        in  (nondecreasing, offsets[G] <= n_rows;
- *                                            clamped into [0,n_rows])
+ *                                            clamped into [0,n_rows];
+ *                                            MOE_DATA_ERR_OFFSETS)
  * w_gate_up [G, 2I, H] dtype            in  rows 0..I-1 = W_g, I..2I-1 = W_u;
  *                                            MOE_BF16: packed (MOE_PACK_GATE_UP, N = I)
  * w_down    [G, H, I] dtype             in  MOE_BF16: packed (MOE_PACK_ROWS, N = H)
@@ -225,7 +230,7 @@ int moe_expert_gate_up(const void* x, const int32_t* gather, const int32_t* offs
  * produced.  offsets feeds moe_expert_down, inv feeds the combine.
  *
  * x         [T,H] bf16           in   normed tokens
- * topk_ids  [T,k] int32          in   (clamped into [0,E))
+ * topk_ids  [T,k] int32          in   (clamped into [0,E); MOE_DATA_ERR_EXPERT_ID)
  * w_gate_up [E+S, 2I, H] bf16    in   packed (MOE_PACK_GATE_UP, N = I)
  * act       [T*k + S*T, I] bf16  out
  * offsets   [E+S+1] int32        out  (written also for T = 0)
@@ -272,7 +277,7 @@ int moe_expert_down_residual(const void* act, const int32_t* offsets, int G, int
  * carry weight 1.
  *
  * y        [n_rows, H] dtype (rows in permuted order)   in
- * inv      [T*k] int32  (clamped into [0,n_rows))        in
+ * inv      [T*k] int32  (clamped into [0,n_rows); MOE_DATA_ERR_INV)  in
  * topk_w   [T,k] fp32                                    in
  * y_shared [S*T, H] dtype or NULL (then S must be 0)     in
  * residual [T,H] dtype or NULL                           in
@@ -303,7 +308,7 @@ int moe_combine_rmsnorm(const void* y, const int32_t* inv, const float* topk_w,
 /* ---------------------------------------------------------------------------
  * moe_rmsnorm -- RMSNorm of rows: out[t] = x[r] / sqrt(mean(x[r]^2) + eps)
  * (* gain), r = rows[t] (a gather, e.g. of token embeddings; clamped into
- * [0, x_rows)) or t when rows is NULL.  The scale is fp64 with one rounding
+ * [0, x_rows), MOE_DATA_ERR_ROW_INDEX) or t when rows is NULL.  The scale is fp64 with one rounding
  * to the storage type, in the same order as moe_route's norm, so a row
  * normalises to the same bits in both.  Used for the inputs of the draft
  * block ("Jina AI's 3.4B OCR model targets faster page parsing", section
@@ -427,7 +432,9 @@ int spec_plant_drafts(const int32_t* argmax_ids, const uint8_t* keep, const int3
  * spec_advance:
  *   n_commit  [B] int32, committed [B,K+1] int32   in  (spec_verify's outputs)
  *   seq_ids   [B] int32                            in  sequence of each slot, in [0,S);
- *                                                      a negative id is an empty slot (skipped)
+ *                                                      a negative id is an empty slot (skipped);
+ *                                                      ids >= S and n_commit outside [0,K+1] are
+ *                                                      clamped (MOE_DATA_ERR_SEQUENCE)
  *   total     [S] int32                            in/out tokens committed so far
  *   steps     [S] int32                            in/out passes taken so far
  *   tokens    [S,target] int32                     out committed streams
@@ -442,7 +449,8 @@ int spec_plant_drafts(const int32_t* argmax_ids, const uint8_t* keep, const int3
  * laid out [S, J, R] rows of row_bytes bytes (J passes per sequence, R rows
  * per pass):  out row i*R + r = pool row (seq_ids[i] * J + min(steps[s], J-1))
  * * R + r, with s = seq_ids[i] (an empty slot, id < 0, reads sequence 0's
- * row: its pass result is skipped).  Used for the hidden states of the verify
+ * row: its pass result is skipped; an id >= S is clamped to S-1 and reported,
+ * MOE_DATA_ERR_SEQUENCE).  Used for the hidden states of the verify
  * positions (R = K+1 rows of H bf16) and the planting draws (R = 1 row of K
  * bytes or K int32).  row_bytes = 0 (K = 0 drafts) is a no-op.
  * ------------------------------------------------------------------------- */
@@ -472,6 +480,7 @@ int spec_gather_rows(const void* pool, const int32_t* seq_ids, const int32_t* st
  *   bf16 inputs, one rounding to bf16.
  *   qkv [B*P, 3H] bf16                          in
  *   lengths [B] int32                           in   clamped to [0, max_len-P]
+ *                                                    (MOE_DATA_ERR_LENGTH)
  *   q [B*P, H] bf16                             out
  *   kv [B, n_heads, max_len, 2, 128] bf16       in/out (P positions each)
  *
@@ -481,7 +490,8 @@ int spec_gather_rows(const void* pool, const int32_t* seq_ids, const int32_t* st
  *   Cache rows past L_b + i (drafts of an earlier pass that the verifier
  *   rejected) are never read, so rejecting drafts needs no cache write.
  *   max_keys bounds lengths[b] + P for every b (it sizes the grid and the
- *   workspace; a longer length is clamped to max_keys - P).
+ *   workspace; a longer length is clamped to max_keys - P and reported,
+ *   MOE_DATA_ERR_LENGTH).
  *   q [B*P, H] bf16, kv as above                in
  *   o [B*P, H] bf16                             out
  *   ws                                          scratch of
@@ -502,6 +512,48 @@ int moe_attention(const void* q, const void* kv_cache, const int32_t* lengths, i
                   int n_heads, int head_dim, int max_len, int max_keys, int dtype, void* o,
                   void* ws, size_t ws_bytes, void* stream);
 int spec_commit(const int32_t* n_commit, int B, int32_t* lengths, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_data_errors -- device-side data errors seen since the last clear.
+ *
+ * The kernels clamp every index argument before it addresses memory; an
+ * argument that needed clamping is a caller mistake, and the kernel that saw
+ * it ORs its kind into a 32-bit word that each GPU holds for the library
+ * (a static device variable; its address is looked up once per device and
+ * cached).  The clamped call still completes and its outputs are those of
+ * the clamped data.  Bits:
+ *   MOE_DATA_ERR_EXPERT_ID  topk_ids entry outside [0, E)
+ *                           (moe_permute, moe_expert_gate_up_routed)
+ *   MOE_DATA_ERR_ROW_INDEX  gather / rows entry outside [0, T) or
+ *                           [0, x_rows) (moe_grouped_swiglu,
+ *                           moe_expert_gate_up, moe_rmsnorm)
+ *   MOE_DATA_ERR_OFFSETS    offsets outside [0, n_rows] or decreasing, or an
+ *                           identity-gathered group longer than T (the
+ *                           expert FFN calls)
+ *   MOE_DATA_ERR_INV        inv entry outside [0, n_rows) (moe_combine,
+ *                           moe_combine_rmsnorm, moe_combine_route)
+ *   MOE_DATA_ERR_LENGTH     lengths entry outside [0, max_len - P]
+ *                           (moe_attn_rope_cache) or [0, max_keys - P]
+ *                           (moe_attention)
+ *   MOE_DATA_ERR_SEQUENCE   seq_ids entry >= S, or n_commit outside
+ *                           [0, K+1] (spec_advance, spec_gather_rows)
+ * A draft id outside the vocabulary is no error (a mismatch, spec_verify).
+ *
+ * Enqueues one single-thread kernel on `stream` that writes the word to
+ * flags_out (device memory, 4-byte aligned) and, with clear != 0, clears the
+ * bits it read.  Calls on one stream see the errors of every earlier call on
+ * it; a call on another stream of the same GPU may set bits at any time
+ * (the word is per GPU).  Returns MOE_ERR_NULL / MOE_ERR_ALIGN for a bad
+ * flags_out, MOE_ERR_HIP if the word's address cannot be looked up or the
+ * launch fails.
+ * ------------------------------------------------------------------------- */
+#define MOE_DATA_ERR_EXPERT_ID 1u
+#define MOE_DATA_ERR_ROW_INDEX 2u
+#define MOE_DATA_ERR_OFFSETS 4u
+#define MOE_DATA_ERR_INV 8u
+#define MOE_DATA_ERR_LENGTH 16u
+#define MOE_DATA_ERR_SEQUENCE 32u
+int moe_data_errors(uint32_t* flags_out, int clear, void* stream);
 
 #ifdef __cplusplus
 }

@@ -20,6 +20,8 @@ BF16, F32 = 0, 1
 ROUTE_NORM, ROUTE_RENORM, ROUTE_WPACKED = 1, 2, 4
 PACK_GATE_UP, PACK_ROWS, PACK_ROUTER = 0, 1, 2
 NOALLOC_SCRATCH_BYTES = 4 << 20   # MOE_NOALLOC_SCRATCH_BYTES
+# MOE_DATA_ERR_* bits (moe_data_errors)
+ERR_EXPERT_ID, ERR_ROW_INDEX, ERR_OFFSETS, ERR_INV, ERR_LENGTH, ERR_SEQUENCE = 1, 2, 4, 8, 16, 32
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -57,6 +59,7 @@ SIGNATURES = {
     "moe_attention_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "moe_attention": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
     "spec_commit": (_I, [_P, _I, _P, _P]),
+    "moe_data_errors": (_I, [_P, _I, _P]),
 }
 
 _lib = None

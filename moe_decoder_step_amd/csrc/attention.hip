@@ -34,7 +34,8 @@ constexpr int kRowPad = kD + 8;       // bf16 per LDS row (conflict-free column 
 __global__ __launch_bounds__(256) void rope_cache_kernel(const bf16_t* __restrict__ qkv,
                                                          const int32_t* __restrict__ lengths, int B, int P,
                                                          int n_heads, int max_len, double log_base,
-                                                         bf16_t* __restrict__ q, bf16_t* __restrict__ kv) {
+                                                         bf16_t* __restrict__ q, bf16_t* __restrict__ kv,
+                                                         uint32_t* err) {
   // one thread per (token, head, rotation pair j < 64)
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const int half = kD / 2;
@@ -43,7 +44,9 @@ __global__ __launch_bounds__(256) void rope_cache_kernel(const bf16_t* __restric
   const int hd = (int)((idx / half) % n_heads);
   const int t = (int)(idx / ((long long)half * n_heads));
   const int b = t / P, i = t % P;
-  const int pos = clampi(lengths[b], 0, max_len - P) + i;
+  // (one thread per sequence reports a length outside [0, max_len - P])
+  const int pos = clamp_report(lengths[b], 0, max_len - P, i == 0 && hd == 0 && j == 0 ? err : nullptr,
+                               kDataErrLength) + i;
   const int H = n_heads * kD;
   const double ang = (double)pos * exp(-(double)j / (double)half * log_base);
   const double c = cos(ang), s = sin(ang);
@@ -84,7 +87,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(const bf16_t* __restric
                                                          const bf16_t* __restrict__ kv,
                                                          const int32_t* __restrict__ lengths, int P, int n_heads,
                                                          int max_len, int max_keys, int split_keys, int nsplit,
-                                                         float scale, float* __restrict__ ws) {
+                                                         float scale, float* __restrict__ ws, uint32_t* err) {
   constexpr int kVRow = kTile + 8;                                // bf16 per transposed value / probability row
   __shared__ __align__(16) bf16_t ks[kTile][kRowPad];             // keys [key][dim]
   __shared__ __align__(16) bf16_t vt[kD][kVRow];                  // values [dim][key]
@@ -97,7 +100,8 @@ __global__ __launch_bounds__(256) void attn_split_kernel(const bf16_t* __restric
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int H = n_heads * kD;
   // the grid covers keys < max_keys (<= max_len); a longer length is clamped
-  const int L = clampi(lengths[b], 0, max_keys - P);
+  const int L = clamp_report(lengths[b], 0, max_keys - P, threadIdx.x == 0 && split == 0 && hd == 0 ? err : nullptr,
+                             kDataErrLength);
   const int k0 = split * split_keys, k1 = min(k0 + split_keys, L + P);
   const size_t base = ((size_t)b * n_heads + hd) * max_len;
 
@@ -297,7 +301,7 @@ hipError_t launch_rope_cache(const void* qkv, const int32_t* lengths, int B, int
   const long long n = (long long)B * P * n_heads * (kD / 2);
   hipLaunchKernelGGL(rope_cache_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                      static_cast<const bf16_t*>(qkv), lengths, B, P, n_heads, max_len, log((double)rope_base),
-                     static_cast<bf16_t*>(q), static_cast<bf16_t*>(kv_cache));
+                     static_cast<bf16_t*>(q), static_cast<bf16_t*>(kv_cache), data_error_word(s));
   return hipGetLastError();
 }
 
@@ -308,7 +312,7 @@ hipError_t launch_attention(const void* q, const void* kv_cache, const int32_t* 
   float* w = static_cast<float*>(ws);
   hipLaunchKernelGGL(attn_split_kernel, dim3(B * n_heads * nsplit), dim3(256), 0, s, static_cast<const bf16_t*>(q),
                      static_cast<const bf16_t*>(kv_cache), lengths, P, n_heads,
-                     max_len, max_keys, sk, nsplit, 1.0f / sqrtf((float)kD), w);
+                     max_len, max_keys, sk, nsplit, 1.0f / sqrtf((float)kD), w, data_error_word(s));
   const int waves = B * n_heads * P;
   hipLaunchKernelGGL(attn_merge_kernel, dim3((waves + 3) / 4), dim3(256), 0, s, w, B, P, n_heads, nsplit,
                      static_cast<bf16_t*>(o));

@@ -46,12 +46,12 @@ template <typename St>
 __global__ __launch_bounds__(kThreads) void combine_kernel(
     const St* __restrict__ y, const int32_t* __restrict__ inv, const float* __restrict__ w,
     const St* __restrict__ ys, int S, const St* res, int T, int H, int k, int n_rows, St* out,
-    St* __restrict__ combined) {
+    St* __restrict__ combined, uint32_t* err) {
   const int t = blockIdx.x;
   __shared__ int rows[kMaxExperts];
   __shared__ float wk[kMaxExperts];
   if (threadIdx.x < k) {
-    rows[threadIdx.x] = clampi(inv[(size_t)t * k + threadIdx.x], 0, n_rows - 1);
+    rows[threadIdx.x] = clamp_report(inv[(size_t)t * k + threadIdx.x], 0, n_rows - 1, err, kDataErrInv);
     wk[threadIdx.x] = w[(size_t)t * k + threadIdx.x];
   }
   __syncthreads();
@@ -82,14 +82,14 @@ template <typename St>
 __global__ __launch_bounds__(kThreads) void combine_norm_kernel(
     const St* __restrict__ y, const int32_t* __restrict__ inv, const float* __restrict__ w,
     const St* __restrict__ ys, int S, const St* res, int T, int H, int k, int n_rows, const float* __restrict__ gain,
-    float eps, St* out, St* __restrict__ xn) {
+    float eps, St* out, St* __restrict__ xn, uint32_t* err) {
   const int t = blockIdx.x;
   __shared__ int rows[kMaxExperts];
   __shared__ float wk[kMaxExperts];
   __shared__ double ssp[kThreads];
   __shared__ double s_scale;
   if (threadIdx.x < k) {
-    rows[threadIdx.x] = clampi(inv[(size_t)t * k + threadIdx.x], 0, n_rows - 1);
+    rows[threadIdx.x] = clamp_report(inv[(size_t)t * k + threadIdx.x], 0, n_rows - 1, err, kDataErrInv);
     wk[threadIdx.x] = w[(size_t)t * k + threadIdx.x];
   }
   __syncthreads();
@@ -142,12 +142,12 @@ hipError_t launch_combine_norm(const void* y, const int32_t* inv, const float* t
     hipLaunchKernelGGL((combine_norm_kernel<bf16_t>), dim3(T), dim3(kThreads), 0, s,
                        static_cast<const bf16_t*>(y), inv, topk_w, static_cast<const bf16_t*>(y_shared), S,
                        static_cast<const bf16_t*>(residual), T, H, k, n_rows, gain, eps, static_cast<bf16_t*>(out),
-                       static_cast<bf16_t*>(xn));
+                       static_cast<bf16_t*>(xn), data_error_word(s));
   else
     hipLaunchKernelGGL((combine_norm_kernel<float>), dim3(T), dim3(kThreads), 0, s,
                        static_cast<const float*>(y), inv, topk_w, static_cast<const float*>(y_shared), S,
                        static_cast<const float*>(residual), T, H, k, n_rows, gain, eps, static_cast<float*>(out),
-                       static_cast<float*>(xn));
+                       static_cast<float*>(xn), data_error_word(s));
   return hipGetLastError();
 }
 
@@ -158,12 +158,12 @@ hipError_t launch_combine(const void* y, const int32_t* inv, const float* topk_w
     hipLaunchKernelGGL((combine_kernel<bf16_t>), dim3(T), dim3(kThreads), 0, s,
                        static_cast<const bf16_t*>(y), inv, topk_w, static_cast<const bf16_t*>(y_shared), S,
                        static_cast<const bf16_t*>(residual), T, H, k, n_rows, static_cast<bf16_t*>(out),
-                       static_cast<bf16_t*>(combined));
+                       static_cast<bf16_t*>(combined), data_error_word(s));
   else
     hipLaunchKernelGGL((combine_kernel<float>), dim3(T), dim3(kThreads), 0, s,
                        static_cast<const float*>(y), inv, topk_w, static_cast<const float*>(y_shared), S,
                        static_cast<const float*>(residual), T, H, k, n_rows, static_cast<float*>(out),
-                       static_cast<float*>(combined));
+                       static_cast<float*>(combined), data_error_word(s));
   return hipGetLastError();
 }
 

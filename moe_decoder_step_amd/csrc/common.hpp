@@ -169,6 +169,25 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
+// Device-side data errors (moestep.h MOE_DATA_ERR_*).  An index argument is
+// always clamped before it addresses memory; when it was out of range the
+// kernel also ORs the error's kind into the per-GPU word `err` (relaxed,
+// device scope).  In-range data issues no memory operation here.
+constexpr uint32_t kDataErrExpertId = 1u;   // MOE_DATA_ERR_EXPERT_ID
+constexpr uint32_t kDataErrRowIndex = 2u;   // MOE_DATA_ERR_ROW_INDEX
+constexpr uint32_t kDataErrOffsets = 4u;    // MOE_DATA_ERR_OFFSETS
+constexpr uint32_t kDataErrInv = 8u;        // MOE_DATA_ERR_INV
+constexpr uint32_t kDataErrLength = 16u;    // MOE_DATA_ERR_LENGTH
+constexpr uint32_t kDataErrSequence = 32u;  // MOE_DATA_ERR_SEQUENCE
+__device__ __forceinline__ void report_error(uint32_t* err, bool bad, uint32_t bit) {
+  if (__builtin_expect(bad, false) && err) __hip_atomic_fetch_or(err, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// clampi that reports an argument outside [lo, hi]
+__device__ __forceinline__ int clamp_report(int v, int lo, int hi, uint32_t* err, uint32_t bit) {
+  report_error(err, v < lo || v > hi, bit);
+  return clampi(v, lo, hi);
+}
+
 // 16x16x32 bf16 MFMA, fp32 accumulate.  Lane l supplies A[l%16][8*(l/16)+0..7]
 // and B[8*(l/16)+0..7][l%16]; it receives D[4*(l/16)+v][l%16], v = 0..3.
 __device__ __forceinline__ f32x4_t mfma16x16x32(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {

@@ -248,7 +248,7 @@ template <bool GATED>
 __global__ __launch_bounds__(kGThreads) void gemm_kernel(
     const bf16_t* __restrict__ x, const int32_t* __restrict__ gather, const int32_t* __restrict__ offsets,
     int G, int n_rows, int T, const bf16_t* __restrict__ W, int K, int N, int n_pairs, int n_ntiles,
-    bf16_t* __restrict__ out) {
+    bf16_t* __restrict__ out, uint32_t* err) {
   extern __shared__ __align__(16) char lds[];
   __shared__ int s_first[2 * kWave + 1], s_r0[2 * kWave], s_r1[2 * kWave];
 
@@ -260,8 +260,10 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int g = lane + h * kWave;
-      r0[h] = g < G ? clampi(offsets[g], 0, n_rows) : 0;
-      r1[h] = g < G ? clampi(offsets[g + 1], r0[h], n_rows) : 0;
+      // (block 0 reports ranges outside [0, n_rows] or decreasing)
+      uint32_t* const eb = blockIdx.x == 0 ? err : nullptr;
+      r0[h] = g < G ? clamp_report(offsets[g], 0, n_rows, eb, kDataErrOffsets) : 0;
+      r1[h] = g < G ? clamp_report(offsets[g + 1], r0[h], n_rows, eb, kDataErrOffsets) : 0;
       cnt[h] = (r1[h] - r0[h] + kGM - 1) / kGM;
       incl[h] = cnt[h];
 #pragma unroll
@@ -302,7 +304,9 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(
   auto act_row = [&](const GTile& tl, int u) { return min(tl.m0 + 32 * wave + 16 * u + lrow, tl.m1 - 1); };
   auto act_src = [&](const GTile& tl, int u, int gv) {
     int t;
-    if (GATED) t = gather ? clampi(gv, 0, T - 1) : clampi(act_row(tl, u) - tl.rb, 0, T - 1);
+    if (GATED)
+      t = gather ? clamp_report(gv, 0, T - 1, err, kDataErrRowIndex)
+                 : clamp_report(act_row(tl, u) - tl.rb, 0, T - 1, err, kDataErrOffsets);
     else t = act_row(tl, u);
     return x + (size_t)t * K + 8 * chunk;
   };
@@ -474,7 +478,7 @@ hipError_t launch_gemm_t(const bf16_t* x, const int32_t* gather, const int32_t* 
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGLds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((gemm_kernel<GATED>), dim3((unsigned)blocks), dim3(kGThreads), kGLds, s, x, gather, offsets,
-                     G, n_rows, T, W, K, N, n_pairs, n_ntiles, out);
+                     G, n_rows, T, W, K, N, n_pairs, n_ntiles, out, data_error_word(s));
   return hipGetLastError();
 }
 

@@ -7,6 +7,10 @@
 
 namespace moe {
 
+// This GPU's data-error word (the stream's device; NULL stream: the current
+// one), or NULL if its address cannot be found (errors then go unreported).
+uint32_t* data_error_word(hipStream_t s);
+
 hipError_t launch_pack(const void* src, void* dst, int G, int N, int K, int kind, hipStream_t s);
 hipError_t launch_pack_router(const void* src, void* dst, int G, int E, int K, hipStream_t s);
 
@@ -17,6 +21,7 @@ struct CombineArgs {
   const float* w;        // [T, k] routing weights
   const void* ys;        // [S*T, H] shared-expert outputs or NULL
   int S, n_rows, k;
+  uint32_t* err = nullptr;  // the data-error word (set by the launcher)
 };
 
 hipError_t launch_combine_route(const CombineArgs& ca, void* h, const float* gain, float eps, const float* w_router,

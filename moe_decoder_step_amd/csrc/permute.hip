@@ -26,16 +26,18 @@ static_assert(kPermuteChunkM == kWaves * kWave, "multi-block chunks: one piece p
 
 // Rank the slots of one chunk.  Fills pcount[p][e] (count of expert e in
 // piece p; lanes >= E write nothing) and, per pass pi, the lane's expert and
-// rank inside its piece.
+// rank inside its piece.  Ids outside [0, E) count as the nearest expert and,
+// with err set, are reported.
 template <int PPW>
 __device__ __forceinline__ void rank_chunk(const int32_t* __restrict__ ids, int s0, int n, int E,
-                                           int (*pcount)[kMaxExperts], int* my_e, int* my_rank) {
+                                           int (*pcount)[kMaxExperts], int* my_e, int* my_rank,
+                                           uint32_t* err) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
   for (int pi = 0; pi < PPW; ++pi) {
     const int p = wave + kWaves * pi;
     const int s = p * kWave + lane;
-    const int e = s < n ? clampi(ids[s0 + s], 0, E - 1) : -1;
+    const int e = s < n ? clamp_report(ids[s0 + s], 0, E - 1, err, kDataErrExpertId) : -1;
     int rank = 0, cnt = 0;
     if (p * kWave < n) {
       for (int ee = 0; ee < E; ++ee) {
@@ -109,14 +111,14 @@ __device__ __forceinline__ void scan_experts(const int* tot, int E, int S, int T
 __global__ __launch_bounds__(kThreads) void permute_one_block(const int32_t* __restrict__ ids, int T, int k,
                                                               int E, int S, int32_t* __restrict__ offsets,
                                                               int32_t* __restrict__ gather,
-                                                              int32_t* __restrict__ inv) {
+                                                              int32_t* __restrict__ inv, uint32_t* err) {
   __shared__ int pcount[kPieces][kMaxExperts];
   __shared__ int tot[kMaxExperts];
   __shared__ int base[kMaxExperts];
   const int n = T * k;
   const int n_pieces = (n + kWave - 1) / kWave;
   int my_e[kPiecesPerWave], my_rank[kPiecesPerWave];
-  rank_chunk<kPiecesPerWave>(ids, 0, n, E, pcount, my_e, my_rank);
+  rank_chunk<kPiecesPerWave>(ids, 0, n, E, pcount, my_e, my_rank, err);
   __syncthreads();
   if (threadIdx.x < E) tot[threadIdx.x] = scan_pieces(pcount, n_pieces, threadIdx.x);
   __syncthreads();
@@ -128,13 +130,13 @@ __global__ __launch_bounds__(kThreads) void permute_one_block(const int32_t* __r
 
 // count pass: per-chunk expert totals
 __global__ __launch_bounds__(kThreads) void permute_count(const int32_t* __restrict__ ids, int n_slots, int E,
-                                                          int32_t* __restrict__ counts) {
+                                                          int32_t* __restrict__ counts, uint32_t* err) {
   __shared__ int pcount[kWaves][kMaxExperts];
   const int s0 = blockIdx.x * kPermuteChunkM;
   const int n = min(kPermuteChunkM, n_slots - s0);
   const int n_pieces = (n + kWave - 1) / kWave;
   int my_e[1], my_rank[1];
-  rank_chunk<1>(ids, s0, n, E, pcount, my_e, my_rank);
+  rank_chunk<1>(ids, s0, n, E, pcount, my_e, my_rank, err);
   __syncthreads();
   if (threadIdx.x < E) counts[blockIdx.x * E + threadIdx.x] = scan_pieces(pcount, n_pieces, threadIdx.x);
 }
@@ -222,7 +224,7 @@ __global__ __launch_bounds__(kThreads) void permute_scatter(const int32_t* __res
   const int n = min(kPermuteChunkM, n_slots - s0);
   const int n_pieces = (n + kWave - 1) / kWave;
   int my_e[1], my_rank[1];
-  rank_chunk<1>(ids, s0, n, E, pcount, my_e, my_rank);
+  rank_chunk<1>(ids, s0, n, E, pcount, my_e, my_rank, nullptr);   // the count pass reported
   if (threadIdx.x < E) base[threadIdx.x] = bases[blockIdx.x * E + threadIdx.x];
   __syncthreads();
   if (threadIdx.x < E) scan_pieces(pcount, n_pieces, threadIdx.x);
@@ -236,14 +238,16 @@ __global__ __launch_bounds__(kThreads) void permute_scatter(const int32_t* __res
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int S, int32_t* offsets,
                           int32_t* gather, int32_t* inv, void* ws, hipStream_t s) {
   const int n_slots = T * k;
+  uint32_t* err = data_error_word(s);
   if (n_slots <= kPermuteChunk) {
-    hipLaunchKernelGGL(permute_one_block, dim3(1), dim3(kThreads), 0, s, ids, T, k, E, S, offsets, gather, inv);
+    hipLaunchKernelGGL(permute_one_block, dim3(1), dim3(kThreads), 0, s, ids, T, k, E, S, offsets, gather, inv,
+                       err);
     return hipGetLastError();
   }
   const int n_chunks = (n_slots + kPermuteChunkM - 1) / kPermuteChunkM;
   int32_t* counts = static_cast<int32_t*>(ws);
   int32_t* bases = counts + (size_t)n_chunks * E;
-  hipLaunchKernelGGL(permute_count, dim3(n_chunks), dim3(kThreads), 0, s, ids, n_slots, E, counts);
+  hipLaunchKernelGGL(permute_count, dim3(n_chunks), dim3(kThreads), 0, s, ids, n_slots, E, counts, err);
   hipLaunchKernelGGL(permute_scan, dim3(1), dim3(kThreads), 0, s, counts, n_chunks, E, S, T, bases, offsets);
   hipLaunchKernelGGL(permute_scatter, dim3(n_chunks), dim3(kThreads), 0, s, ids, T, k, E, S, bases, gather, inv);
   return hipGetLastError();

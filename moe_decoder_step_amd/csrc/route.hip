@@ -177,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     const St* ys = static_cast<const St*>(ca.ys);
     if ((int)threadIdx.x < TPB * ca.k) {
       const int i = (int)threadIdx.x / ca.k, j = (int)threadIdx.x % ca.k;
-      crow[i][j] = clampi(crow_g, 0, ca.n_rows - 1);
+      crow[i][j] = clamp_report(crow_g, 0, ca.n_rows - 1, ca.err, kDataErrInv);
       cwt[i][j] = cwt_g;
     }
     if (use_gain) {
@@ -457,10 +457,11 @@ hipError_t launch_st(const void* h, void* hout, const CombineArgs* ca, const flo
 template <typename St>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const St* __restrict__ x, const int32_t* __restrict__ rows,
                                                       int x_rows, int T, int H, const float* __restrict__ gain,
-                                                      float eps, St* __restrict__ out, int out_stride) {
+                                                      float eps, St* __restrict__ out, int out_stride,
+                                                      uint32_t* err) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (t >= T) return;
-  const int r = rows ? clampi(rows[t], 0, x_rows - 1) : t;
+  const int r = rows ? clamp_report(rows[t], 0, x_rows - 1, err, kDataErrRowIndex) : t;
   const St* xr = x + (size_t)r * H;
   double ss = 0.0;
   for (int c = lane * 8; c < H; c += 8 * kWave) {
@@ -486,10 +487,10 @@ hipError_t launch_rmsnorm(const void* x, const int32_t* rows, int x_rows, int T,
   const dim3 grid((T + 3) / 4), block(256);
   if (dtype == kBf16)
     hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, grid, block, 0, s, static_cast<const bf16_t*>(x), rows, x_rows, T, H,
-                       gain, eps, static_cast<bf16_t*>(out), out_stride);
+                       gain, eps, static_cast<bf16_t*>(out), out_stride, data_error_word(s));
   else
     hipLaunchKernelGGL(rmsnorm_kernel<float>, grid, block, 0, s, static_cast<const float*>(x), rows, x_rows, T, H,
-                       gain, eps, static_cast<float*>(out), out_stride);
+                       gain, eps, static_cast<float*>(out), out_stride, data_error_word(s));
   return hipGetLastError();
 }
 
@@ -505,9 +506,11 @@ hipError_t launch_route(const void* h, const float* gain, float eps, const float
 hipError_t launch_combine_route(const CombineArgs& ca, void* h, const float* gain, float eps, const float* w_router,
                                 const float* bias, int T, int H, int E, int k, int flags, int dtype, void* xn,
                                 int32_t* ids, float* w, float* logits, hipStream_t s) {
+  CombineArgs c = ca;
+  c.err = data_error_word(s);
   if (dtype == kBf16)
-    return launch_st<bf16_t>(h, h, &ca, gain, eps, w_router, bias, T, H, E, k, flags, xn, ids, w, logits, s);
-  return launch_st<float>(h, h, &ca, gain, eps, w_router, bias, T, H, E, k, flags, xn, ids, w, logits, s);
+    return launch_st<bf16_t>(h, h, &c, gain, eps, w_router, bias, T, H, E, k, flags, xn, ids, w, logits, s);
+  return launch_st<float>(h, h, &c, gain, eps, w_router, bias, T, H, E, k, flags, xn, ids, w, logits, s);
 }
 
 }  // namespace moe

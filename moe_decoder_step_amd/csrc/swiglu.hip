@@ -226,7 +226,7 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
     const bf16_t* __restrict__ x, const int32_t* __restrict__ gather,
     const int32_t* __restrict__ offsets, int G, int n_rows, int T,
     const bf16_t* __restrict__ W, int K, int N, int n_ctiles, int ks_log2, int chunk_cfg, bf16_t* out,
-    const bf16_t* res, RoutedArgs rt) {
+    const bf16_t* res, RoutedArgs rt, uint32_t* err) {
   static_assert(!ROUTED || GATED, "only the gate/up stage derives its rows from the expert ids");
   constexpr int D = 3;                    // k-steps of weights in flight per wavefront (64-row items)
   constexpr int DB = 6;                   // the same for 16-row items
@@ -277,7 +277,7 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
     for (int u = 0; u < 8; ++u) {
       const int p = threadIdx.x + u * kBlockThreads;
       if (p < np) {
-        const int e = clampi(idv[u], 0, rt.E - 1);
+        const int e = clamp_report(idv[u], 0, rt.E - 1, err, kDataErrExpertId);
         s_ids[p] = e;
         atomicAdd(&s_cnt[e], 1);
       }
@@ -334,8 +334,10 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
     for (int h = 0; h < 2; ++h) {
       const int g = G - 1 - (l + h * kWave);   // groups in reverse order
       if (!ROUTED) {
-        r0[h] = g >= 0 ? clampi(offsets[g], 0, n_rows) : 0;
-        r1[h] = g >= 0 ? clampi(offsets[g + 1], r0[h], n_rows) : 0;
+        // (block 0 reports ranges outside [0, n_rows] or decreasing)
+        uint32_t* const eb = blockIdx.x == 0 ? err : nullptr;
+        r0[h] = g >= 0 ? clamp_report(offsets[g], 0, n_rows, eb, kDataErrOffsets) : 0;
+        r1[h] = g >= 0 ? clamp_report(offsets[g + 1], r0[h], n_rows, eb, kDataErrOffsets) : 0;
       }
       const int rows = r1[h] - r0[h];
       rbs[h] = rows > 2 * kRows && rb_max >= 4 ? 4 : rows > kRows && rb_max >= 2 ? 2 : 1;
@@ -478,7 +480,9 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_kernel(
   auto src_row = [&](int row) __attribute__((always_inline)) {
     const int r = mstart + min(row, mr - 1);
     if (ROUTED) return clampi(g < rt.E ? s_tok[min(row, mr - 1)] : r - r_begin, 0, T - 1);
-    if (GATED) return gather ? clampi(gather[r], 0, T - 1) : clampi(r - r_begin, 0, T - 1);
+    if (GATED)
+      return gather ? clamp_report(gather[r], 0, T - 1, err, kDataErrRowIndex)
+                    : clamp_report(r - r_begin, 0, T - 1, err, kDataErrOffsets);
     return r;
   };
 
@@ -682,7 +686,7 @@ hipError_t launch_skinny(const bf16_t* x, const int32_t* gather, const int32_t* 
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(kBlockThreads), lds, s, x, gather, offsets, G, n_rows, T, W, K, N,
-                     n_ctiles, ks_log2, chunk_cfg, out, res, ra);
+                     n_ctiles, ks_log2, chunk_cfg, out, res, ra, data_error_word(s));
   return hipGetLastError();
 }
 
@@ -699,16 +703,27 @@ __device__ __forceinline__ int find_group(const int32_t* offsets, int G, int n_r
   return -1;
 }
 
+// block 0 checks the group row ranges once: within [0, n_rows], non-decreasing
+__device__ __forceinline__ void check_offsets(const int32_t* offsets, int G, int n_rows, uint32_t* err) {
+  if (blockIdx.x != 0 || !err) return;
+  for (int g = threadIdx.x; g < G; g += blockDim.x) {
+    const int a = offsets[g], b = offsets[g + 1];
+    report_error(err, a < 0 || b < a || b > n_rows, kDataErrOffsets);
+  }
+}
+
 __global__ __launch_bounds__(256) void f32_gate_up_kernel(const float* __restrict__ x,
                                                           const int32_t* __restrict__ gather,
                                                           const int32_t* __restrict__ offsets, int G,
                                                           int n_rows, int T, const float* __restrict__ wgu,
-                                                          int H, int I, float* __restrict__ act) {
+                                                          int H, int I, float* __restrict__ act, uint32_t* err) {
+  check_offsets(offsets, G, n_rows, err);
   const int r = blockIdx.x;
   int r_begin = 0;
   const int g = find_group(offsets, G, n_rows, r, &r_begin);
   if (g < 0) return;
-  const int t = gather ? clampi(gather[r], 0, T - 1) : clampi(r - r_begin, 0, T - 1);
+  const int t = gather ? clamp_report(gather[r], 0, T - 1, err, kDataErrRowIndex)
+                       : clamp_report(r - r_begin, 0, T - 1, err, kDataErrOffsets);
   const float* xr = x + (size_t)t * H;
   for (int c = threadIdx.x; c < I; c += blockDim.x) {
     const float* wg = wgu + ((size_t)g * 2 * I + c) * H;
@@ -725,7 +740,8 @@ __global__ __launch_bounds__(256) void f32_gate_up_kernel(const float* __restric
 __global__ __launch_bounds__(256) void f32_down_kernel(const float* __restrict__ act,
                                                        const int32_t* __restrict__ offsets, int G, int n_rows,
                                                        const float* __restrict__ wd, int H, int I, float* y,
-                                                       const float* res) {
+                                                       const float* res, uint32_t* err) {
+  check_offsets(offsets, G, n_rows, err);
   const int r = blockIdx.x;
   int r_begin = 0;
   const int g = find_group(offsets, G, n_rows, r, &r_begin);
@@ -747,7 +763,7 @@ hipError_t launch_gate_up(const void* x, const int32_t* gather, const int32_t* o
   if (dtype == kF32) {
     hipLaunchKernelGGL(f32_gate_up_kernel, dim3(n_rows), dim3(256), 0, s, static_cast<const float*>(x), gather,
                        offsets, G, n_rows, T, static_cast<const float*>(w_gate_up), H, I,
-                       static_cast<float*>(act));
+                       static_cast<float*>(act), data_error_word(s));
     return hipGetLastError();
   }
   if (gemm_path_ok(H, I, max_rows))
@@ -768,7 +784,7 @@ hipError_t launch_down(const void* act, const int32_t* offsets, int G, int n_row
   if (dtype == kF32) {
     hipLaunchKernelGGL(f32_down_kernel, dim3(n_rows), dim3(256), 0, s, static_cast<const float*>(act), offsets,
                        G, n_rows, static_cast<const float*>(w_down), H, I, static_cast<float*>(y),
-                       static_cast<const float*>(residual));
+                       static_cast<const float*>(residual), data_error_word(s));
     return hipGetLastError();
   }
   // the tiled GEMM has no residual epilogue: with a residual the weight-streaming form serves every size

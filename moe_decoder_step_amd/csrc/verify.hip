@@ -55,15 +55,16 @@ __global__ __launch_bounds__(1024) void advance_kernel(const int32_t* __restrict
                                                        const int32_t* __restrict__ seq_ids, int B, int K, int S,
                                                        int target, int32_t* __restrict__ total,
                                                        int32_t* __restrict__ steps, int32_t* __restrict__ tokens,
-                                                       int32_t* __restrict__ seq_out, int32_t* __restrict__ n_active) {
+                                                       int32_t* __restrict__ seq_out, int32_t* __restrict__ n_active,
+                                                       uint32_t* err) {
   __shared__ int wave_count[kAdvanceMaxB / 64];
   const int i = threadIdx.x, wave = i >> 6, lane = i & 63;
   bool alive = false;
   int seq = 0;
   if (i < B && seq_ids[i] >= 0) {   // a negative id is an empty slot
-    seq = clampi(seq_ids[i], 0, S - 1);
+    seq = clamp_report(seq_ids[i], 0, S - 1, err, kDataErrSequence);
     const int before = clampi(total[seq], 0, target);
-    const int take = min(clampi(n_commit[i], 0, K + 1), target - before);
+    const int take = min(clamp_report(n_commit[i], 0, K + 1, err, kDataErrSequence), target - before);
     for (int j = 0; j < take; ++j) tokens[(size_t)seq * target + before + j] = committed[(size_t)i * (K + 1) + j];
     total[seq] = before + take;
     steps[seq] += 1;
@@ -88,10 +89,13 @@ __global__ __launch_bounds__(1024) void advance_kernel(const int32_t* __restrict
 // row_bytes bytes each (4-byte words when aligned, else bytes)
 __global__ __launch_bounds__(256) void gather_rows_kernel(const char* __restrict__ pool, const int32_t* __restrict__ seq_ids,
                                                           const int32_t* __restrict__ steps, int B, int R, int J, int S,
-                                                          int row_bytes, bool words, char* __restrict__ out) {
+                                                          int row_bytes, bool words, char* __restrict__ out,
+                                                          uint32_t* err) {
   const int o = blockIdx.x;  // output row
   const int i = o / R, r = o % R;
-  const int seq = clampi(seq_ids[i], 0, S - 1);
+  const int sid = seq_ids[i];   // < 0: an empty slot (reads sequence 0), >= S: reported
+  report_error(threadIdx.x == 0 ? err : nullptr, sid >= S, kDataErrSequence);
+  const int seq = clampi(sid, 0, S - 1);
   const int st = clampi(steps[seq], 0, J - 1);
   const char* src = pool + (((size_t)seq * J + st) * R + r) * row_bytes;
   char* dst = out + (size_t)o * row_bytes;
@@ -110,7 +114,7 @@ hipError_t launch_advance(const int32_t* n_commit, const int32_t* committed, con
                           int32_t* n_active, hipStream_t s) {
   const int threads = ((B + 63) / 64) * 64;
   hipLaunchKernelGGL(advance_kernel, dim3(1), dim3(threads < 64 ? 64 : threads), 0, s, n_commit, committed, seq_ids,
-                     B, K, S, target, total, steps, tokens, seq_out, n_active);
+                     B, K, S, target, total, steps, tokens, seq_out, n_active, data_error_word(s));
   return hipGetLastError();
 }
 
@@ -119,7 +123,7 @@ hipError_t launch_gather_rows(const void* pool, const int32_t* seq_ids, const in
   const bool words = row_bytes % 4 == 0 && (reinterpret_cast<uintptr_t>(pool) & 3) == 0 &&
                      (reinterpret_cast<uintptr_t>(out) & 3) == 0;
   hipLaunchKernelGGL(gather_rows_kernel, dim3(B * R), dim3(256), 0, s, static_cast<const char*>(pool), seq_ids,
-                     steps, B, R, J, S, row_bytes, words, static_cast<char*>(out));
+                     steps, B, R, J, S, row_bytes, words, static_cast<char*>(out), data_error_word(s));
   return hipGetLastError();
 }
 

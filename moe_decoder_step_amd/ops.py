@@ -17,7 +17,7 @@ from . import _lib as L
 __all__ = [
     "Packed", "pack_weights", "packed_weights_bytes", "moe_route", "moe_rmsnorm", "moe_combine_route", "moe_permute", "moe_grouped_swiglu", "moe_combine", "moe_combine_rmsnorm", "lmhead_argmax",
     "moe_expert_gate_up", "moe_expert_gate_up_routed", "moe_expert_down", "moe_expert_down_residual", "ROUTED_MAX_PAIRS", "spec_verify", "spec_plant_drafts", "spec_advance",
-    "spec_gather_rows", "moe_attn_rope_cache", "moe_attention", "attention_workspace_bytes", "kv_cache_alloc", "spec_commit",
+    "spec_gather_rows", "moe_data_errors", "data_errors", "moe_attn_rope_cache", "moe_attention", "attention_workspace_bytes", "kv_cache_alloc", "spec_commit",
     "permute_workspace_bytes", "swiglu_workspace_bytes",
     "lmhead_workspace_bytes", "lmhead_argmax_noalloc", "dtype_code", "expert_weights", "lm_weights", "router_weights", "route_alloc", "permute_alloc", "swiglu_alloc",
     "combine_alloc", "lmhead_alloc", "verify_alloc",
@@ -437,6 +437,24 @@ def spec_commit(n_commit, lengths):
     if n_commit.shape[0] < B:
         raise ValueError("n_commit is shorter than lengths")
     L.check("spec_commit", L.load().spec_commit(_p(n_commit), B, _p(lengths), _stream(lengths)))
+
+
+def moe_data_errors(flags_out, clear=True):
+    """Write the GPU's device-side data-error bits (MOE_DATA_ERR_*) into the
+    one-element int32 tensor flags_out, on the current stream, and clear the
+    bits read if `clear`."""
+    _need(flags_out, torch.int32, "flags_out")
+    if flags_out.numel() < 1:
+        raise ValueError("flags_out needs one element")
+    L.check("moe_data_errors", L.load().moe_data_errors(_p(flags_out), 1 if clear else 0, _stream(flags_out)))
+
+
+def data_errors(device="cuda", clear=True) -> int:
+    """The data-error bits as an int (allocates one word, synchronises the
+    current stream)."""
+    out = torch.zeros(1, dtype=torch.int32, device=device)
+    moe_data_errors(out, clear)
+    return int(out.item()) & 0xFFFFFFFF
 
 
 # ------------------------------------------------------------------ allocating helpers

@@ -3,6 +3,7 @@ declares, and its argument checks return the documented status codes before
 anything reaches the GPU (no compute calls here)."""
 
 import ctypes
+import re
 
 import pytest
 
@@ -21,7 +22,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = L.header_functions()
-    assert len(names) == 28
+    assert len(names) == 29
     assert set(names) == set(L.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
@@ -32,6 +33,17 @@ def test_version_and_status_strings(lib):
     for s in range(7):
         assert lib.moe_status_str(s)
     assert lib.moe_status_str(99) == b"unknown status"
+
+
+def test_data_errors_checks(lib):
+    f = lib.moe_data_errors
+    assert f(None, 1, None) == L.ERR_NULL
+    assert f(P(0x100002), 1, None) == L.ERR_ALIGN     # the flag word is 4-byte aligned
+    # the binding's bits are the header's
+    with open(L.HEADER) as fh:
+        bits = dict((n, int(v)) for n, v in re.findall(r"#define MOE_DATA_ERR_(\w+) (\d+)u", fh.read()))
+    assert bits == {"EXPERT_ID": L.ERR_EXPERT_ID, "ROW_INDEX": L.ERR_ROW_INDEX, "OFFSETS": L.ERR_OFFSETS,
+                    "INV": L.ERR_INV, "LENGTH": L.ERR_LENGTH, "SEQUENCE": L.ERR_SEQUENCE}
 
 
 def test_workspace_queries(lib):
