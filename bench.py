@@ -42,6 +42,8 @@ def parse():
                              "pages32", "copy"],
                     help="copy: a plain 1 GiB device copy, the reference for scaling the HBM traffic counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-companions", action="store_true",
+                    help="step128: skip the batch-1, prefill and decode-loop lines run after the headline")
     ap.add_argument("--cpu-layers", type=int, default=12, help="layers of the oracle sample")
     ap.add_argument("--cpu-vocab", type=int, default=129280, help="LM-head rows of the oracle sample")
     ap.add_argument("--cpu-reps", type=int, default=3, help="repetitions of the oracle sample")
@@ -379,6 +381,8 @@ def main() -> int:
                              "frac": layer_flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                              "expert_rows_desc": np.sort(load)[::-1].tolist()}
 
+    if sh.name == "step128" and not args.no_companions:
+        out["companions"] = companions(args)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, sh, layers, w_lm, h_in, T)
         one = cpu_baseline_1core(args, sh, layers, w_lm, h_in, T)
@@ -386,6 +390,42 @@ def main() -> int:
             out["cpu_baseline_1core"] = one
     print(json.dumps(out), flush=True)
     return 0
+
+
+COMPANION_KEYS = {
+    "batch1": ("step_hbm", "batch1", "roofline"),
+    "prefill": ("layer_mfma", "roofline", "step_hbm"),
+    "decode32": ("loop", "roofline"),
+}
+
+
+def companions(args) -> dict:
+    """The other configurations, measured in the same run: batch-1 verify
+    (graph replay, K = 3), the 36,992-token prefill layer and the
+    concurrency-32 decode loop, each by this script in a child process of its
+    own (--workload W, no oracle); their lines, trimmed, under their names.
+    The headline's timed region is over before the first child starts."""
+    import subprocess
+    out = {}
+    for w in COMPANION_KEYS:
+        cmd = [sys.executable, "-u", os.path.abspath(__file__), "--workload", w, "--no-cpu-baseline",
+               "--steps", str(args.steps), "--warmup", str(args.warmup)]
+        log(f"companion line: {' '.join(cmd[2:])}")
+        try:
+            r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True, timeout=600)
+        except subprocess.TimeoutExpired:
+            out[w] = {"error": "timed out"}
+            continue
+        lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
+        if r.returncode != 0 or not lines:
+            out[w] = {"error": f"exit status {r.returncode}"}
+            continue
+        d = json.loads(lines[-1])
+        keep = {k: d[k] for k in ("metric", "value", "unit", "ms_per_step", "config") if k in d}
+        keep.update({k: d[k] for k in COMPANION_KEYS[w] if k in d})
+        keep["command"] = "python bench.py " + " ".join(cmd[3:])
+        out[w] = keep
+    return out
 
 
 def decode_loop_bench(args) -> int:
