@@ -1,10 +1,11 @@
 """Build libmoestep.so (the HIP kernels and the C ABI) for gfx950, in-tree.
 
-    python -m moe_decoder_step_amd.build            # the library
+    python -m moe_decoder_step_amd.build            # the library (and the C client of its ABI)
     python -m moe_decoder_step_amd.build sanitize   # host ASan + UBSan build
 
 Each source compiles to an object under moe_decoder_step_amd/_build/ (in
-parallel), then one link produces moe_decoder_step_amd/libmoestep.so.
+parallel), then one link produces moe_decoder_step_amd/libmoestep.so; gcc
+then builds tests/c_client/verify_pass, a plain C client of the ABI.
 """
 
 from __future__ import annotations
@@ -90,8 +91,29 @@ def sanitizer_runtime() -> str:
     return r.stdout.strip()
 
 
+# The plain C client of the ABI (tests/c_client): C99 with HIP's C runtime
+# API, linked against the in-tree libmoestep.so (found next to it at run time).
+C_CLIENT_SRC = os.path.join(ROOT, "tests", "c_client", "verify_pass.c")
+C_CLIENT = os.path.join(ROOT, "tests", "c_client", "verify_pass")
+
+
+def build_c_client(verbose: bool = False) -> str:
+    """Compile tests/c_client/verify_pass.c with gcc; returns the binary's path."""
+    cmd = ["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-O2", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+           f"-I{os.path.join(ROOT, 'include')}", C_CLIENT_SRC, f"-L{HERE}", "-lmoestep", "-L/opt/rocm/lib",
+           "-lamdhip64", "-Wl,-rpath,$ORIGIN/../../moe_decoder_step_amd", "-Wl,-rpath,/opt/rocm/lib",
+           "-o", C_CLIENT]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"C client build failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {C_CLIENT}")
+    return C_CLIENT
+
+
 def build(verbose: bool = False, extra: list[str] | None = None) -> str:
-    """Compile every source for gfx950 and link libmoestep.so; returns its path."""
+    """Compile every source for gfx950 and link libmoestep.so, then the C
+    client of the ABI; returns the library's path."""
     os.makedirs(BUILD, exist_ok=True)
     extra = list(extra or [])
     with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
@@ -104,6 +126,7 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
+    build_c_client(verbose)
     return LIB
 
 
