@@ -97,6 +97,8 @@ def ffn_roofline(st, h_in, sh, steps: int) -> dict:
 TRAFFIC = {
     "step128": (os.path.join(ROOT, "profiles", "expert_gate_up_step128_traffic.txt"),
                 ["moe_decoder_step_amd/csrc/swiglu.hip", "moe_decoder_step_amd/csrc/common.hpp"]),
+    "batch1": (os.path.join(ROOT, "profiles", "expert_gate_up_batch1_traffic.txt"),
+               ["moe_decoder_step_amd/csrc/swiglu.hip", "moe_decoder_step_amd/csrc/common.hpp"]),
     "prefill": (os.path.join(ROOT, "profiles", "gemm_gate_up_prefill_traffic.txt"),
                 ["moe_decoder_step_amd/csrc/gemm.hip", "moe_decoder_step_amd/csrc/common.hpp"]),
 }
