@@ -156,7 +156,7 @@ def copy_calibration(args) -> int:
 def main() -> int:
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
               "(the step is sharded by design only; see the sharding notes).", file=sys.stderr)
         return 2
 

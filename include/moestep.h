@@ -57,7 +57,7 @@ typedef enum {
   MOE_OK = 0,
   MOE_ERR_NULL = 1,         /* a required pointer is NULL */
   MOE_ERR_SHAPE = 2,        /* a size is negative or inconsistent */
-  MOE_ERR_UNSUPPORTED = 3,  /* a valid shape this build does not handle (e.g. E > 64) */
+  MOE_ERR_UNSUPPORTED = 3,  /* a valid shape the library does not handle (e.g. E > 64) */
   MOE_ERR_ALIGN = 4,        /* a tensor pointer is not 16-byte aligned */
   MOE_ERR_WORKSPACE = 5,    /* workspace missing or smaller than the query says */
   MOE_ERR_HIP = 6           /* the HIP runtime reported an error at launch */

@@ -21,7 +21,7 @@ const char* moe_status_str(int status) {
     case MOE_OK: return "ok";
     case MOE_ERR_NULL: return "a required pointer is NULL";
     case MOE_ERR_SHAPE: return "a size is negative or inconsistent";
-    case MOE_ERR_UNSUPPORTED: return "shape or dtype not supported by this build";
+    case MOE_ERR_UNSUPPORTED: return "shape or dtype not supported by the library";
     case MOE_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
     case MOE_ERR_HIP: return "HIP runtime error at launch";
