@@ -1,4 +1,5 @@
-"""The batch-1 verify pass captured in a HIP graph and replayed.
+"""Verify passes (batch 1 and 32 x 4 tokens) and the prefill layer captured
+in a HIP graph and replayed.
 
 The whole pass (12 MoE layers, LM-head argmax, draft planting, acceptance)
 is captured once over static buffers.  Each replay gets new inputs copied
@@ -27,10 +28,10 @@ def m():
     return mod
 
 
-@pytest.mark.parametrize("K", [3, 1])
-def test_graph_replay_matches_eager(m, K):
+@pytest.mark.parametrize("shape,K", [("batch1", 3), ("batch1", 1), ("step128", 3)])
+def test_graph_replay_matches_eager(m, shape, K):
     import dataclasses
-    sh = dataclasses.replace(synth.SHAPES["batch1"], P=K + 1)
+    sh = dataclasses.replace(synth.SHAPES[shape], P=K + 1)
     layers = [synth.layer_weights(0, l, sh, DEV) for l in range(sh.L)]
     w_lm = synth.lm_weight(0, sh, DEV)
     st = m.VerifyStack(layers, w_lm, sh.E, sh.k, sh.S, max_tokens=sh.T, max_seqs=sh.B, K=sh.K)
@@ -75,3 +76,31 @@ def test_graph_replay_matches_eager(m, K):
         np.testing.assert_array_equal(got[5].cpu().numpy(), nc)
         lead = np.cumprod(keep_all[i].numpy().astype(bool), axis=1).sum(axis=1)
         np.testing.assert_array_equal(acc, lead)
+
+
+def test_prefill_layer_graph_replay_matches_eager(m):
+    """One 36,992-token layer (multi-pass permute, both MFMA GEMMs, 32-token
+    route, combine) captured once; three replays on new hidden states, each
+    equal bit for bit to an eager pass of the same input run between them."""
+    sh = synth.SHAPES["prefill"]
+    w = synth.layer_weights(1, 0, sh, DEV)
+    st = m.VerifyStack([w], None, sh.E, sh.k, sh.S, max_tokens=sh.T)
+    h_s = synth.hidden(300, sh.T, sh.H, torch.bfloat16, DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        st.forward(h_s)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        st.forward(h_s)
+    for i in range(3):
+        h_i = synth.hidden(301 + i, sh.T, sh.H, torch.bfloat16, DEV)
+        h_s.copy_(h_i)
+        graph.replay()
+        got = [t.clone() for t in (st.h[:sh.T], st.ids[:sh.T], st.tw[:sh.T])]
+        st.forward(h_i)
+        ref = [t.clone() for t in (st.h[:sh.T], st.ids[:sh.T], st.tw[:sh.T])]
+        torch.cuda.synchronize()
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b), f"replay {i} differs from the eager pass"
