@@ -395,23 +395,27 @@ def main() -> int:
 
 
 COMPANION_KEYS = {
-    "batch1": ("step_hbm", "batch1", "roofline"),
-    "prefill": ("layer_mfma", "roofline", "step_hbm"),
-    "decode32": ("loop", "roofline"),
+    "layer128": ("step_hbm", "roofline", "cpu_baseline", "cpu_baseline_1core"),
+    "batch1": ("step_hbm", "batch1", "roofline", "cpu_baseline", "cpu_baseline_1core"),
+    "prefill": ("layer_mfma", "roofline", "step_hbm", "cpu_baseline", "cpu_baseline_1core"),
+    "decode32": ("loop", "roofline", "cpu_baseline"),
 }
 
 
 def companions(args) -> dict:
-    """The other configurations, measured in the same run: batch-1 verify
-    (graph replay, K = 3), the 36,992-token prefill layer and the
-    concurrency-32 decode loop, each by this script in a child process of its
-    own (--workload W, no oracle); their lines, trimmed, under their names.
-    The headline's timed region is over before the first child starts."""
+    """The other configurations, measured in the same run: one real-shape
+    layer at 128 tokens, batch-1 verify (graph replay, K = 3), the
+    36,992-token prefill layer and the concurrency-32 decode loop, each by
+    this script in a child process of its own (--workload W; the oracle
+    baselines on one repetition of their samples unless --no-cpu-baseline);
+    their lines, trimmed, under their names.  The headline's timed region is
+    over before the first child starts."""
     import subprocess
     out = {}
     for w in COMPANION_KEYS:
-        cmd = [sys.executable, "-u", os.path.abspath(__file__), "--workload", w, "--no-cpu-baseline",
+        cmd = [sys.executable, "-u", os.path.abspath(__file__), "--workload", w,
                "--steps", str(args.steps), "--warmup", str(args.warmup)]
+        cmd += ["--no-cpu-baseline"] if args.no_cpu_baseline else ["--cpu-reps", "1"]
         log(f"companion line: {' '.join(cmd[2:])}")
         try:
             r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True, timeout=600)
