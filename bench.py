@@ -25,6 +25,8 @@ if ROOT not in sys.path:
 ZIPF_BIAS = os.path.join(ROOT, "tests", "golden", "zipf_bias_prefill.json")
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E, GB/s
 P_KEEP = 0.576                # per-position draft keep probability (the pages' acceptance rate)
+Q_KEEP = 0.749                # the keep probability whose mean commits per pass, 1 + q + q^2 + q^3,
+                              # equal the pages' tau of 2.73
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, TFLOP/s
 
 
@@ -42,6 +44,8 @@ def parse():
                              "pages32", "copy"],
                     help="copy: a plain 1 GiB device copy, the reference for scaling the HBM traffic counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--keep", type=float, default=None,
+                    help="batch1, decode32, pages32, spec128: draft keep probability (default 0.576)")
     ap.add_argument("--no-companions", action="store_true",
                     help="step128: skip the batch-1, prefill and decode-loop lines run after the headline")
     ap.add_argument("--cpu-layers", type=int, default=12, help="layers of the oracle sample")
@@ -155,6 +159,12 @@ def copy_calibration(args) -> int:
 
 def main() -> int:
     args = parse()
+    global P_KEEP
+    if args.keep is not None:
+        if not 0.0 <= args.keep <= 1.0:
+            print("--keep is a probability", file=sys.stderr)
+            return 2
+        P_KEEP = args.keep
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
               "(the step is sharded by design only; see the sharding notes).", file=sys.stderr)
@@ -399,23 +409,28 @@ COMPANION_KEYS = {
     "batch1": ("step_hbm", "batch1", "roofline", "cpu_baseline", "cpu_baseline_1core"),
     "prefill": ("layer_mfma", "roofline", "step_hbm", "cpu_baseline", "cpu_baseline_1core"),
     "decode32": ("loop", "roofline", "cpu_baseline"),
+    "decode32_tau": ("loop",),
 }
 
 
 def companions(args) -> dict:
     """The other configurations, measured in the same run: one real-shape
     layer at 128 tokens, batch-1 verify (graph replay, K = 3), the
-    36,992-token prefill layer and the concurrency-32 decode loop, each by
-    this script in a child process of its own (--workload W; the oracle
-    baselines on one repetition of their samples unless --no-cpu-baseline);
-    their lines, trimmed, under their names.  The headline's timed region is
-    over before the first child starts."""
+    36,992-token prefill layer and the concurrency-32 decode loop (drafts
+    kept with the pages' acceptance rate 0.576, and again with q = 0.749,
+    whose mean commits per pass equal the pages' tau of 2.73), each by this
+    script in a child process of its own (--workload W; the oracle baselines
+    on one repetition of their samples unless --no-cpu-baseline); their
+    lines, trimmed, under their names.  The headline's timed region is over
+    before the first child starts."""
     import subprocess
     out = {}
     for w in COMPANION_KEYS:
-        cmd = [sys.executable, "-u", os.path.abspath(__file__), "--workload", w,
-               "--steps", str(args.steps), "--warmup", str(args.warmup)]
-        cmd += ["--no-cpu-baseline"] if args.no_cpu_baseline else ["--cpu-reps", "1"]
+        cmd = [sys.executable, "-u", os.path.abspath(__file__), "--steps", str(args.steps), "--warmup", str(args.warmup)]
+        if w == "decode32_tau":   # the same loop with drafts kept at q: the pages' tau = 2.73 per pass
+            cmd += ["--workload", "decode32", "--keep", str(Q_KEEP), "--no-cpu-baseline"]
+        else:
+            cmd += ["--workload", w] + (["--no-cpu-baseline"] if args.no_cpu_baseline else ["--cpu-reps", "1"])
         log(f"companion line: {' '.join(cmd[2:])}")
         try:
             r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True, timeout=600)

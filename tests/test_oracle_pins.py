@@ -371,6 +371,30 @@ def test_planted_tau_closed_form():
     assert abs(f["spec_tok_s_eager"] / f["ar_tok_s_eager"] - f["speedup_eager_K3"]) < 0.01
 
 
+def test_tau_matched_keep_probability():
+    """The secondary planting: the keep probability q whose mean commits per
+    pass, 1 + q + q^2 + q^3, equal the pages' printed tau of 2.73 is 0.749
+    (to 3 decimals); planted at q, the oracle's mean n+1 matches it."""
+    f = facts()
+    K = f["draft_tokens_K"]
+    tau = f["tau_eager_K3"]
+    lo, hi = 0.0, 1.0
+    for _ in range(60):   # bisection: 1 + q + q^2 + q^3 is increasing on [0, 1]
+        mid = (lo + hi) / 2
+        lo, hi = (mid, hi) if sum(mid ** i for i in range(K + 1)) < tau else (lo, mid)
+    assert round(lo, 3) == 0.749
+    q = 0.749
+    rng = np.random.default_rng(15)
+    n_s = 200000
+    keep = rng.random((n_s, K)) < q
+    g = np.zeros((n_s, K + 1), np.int64)
+    d = O.plant_drafts(g, keep, rng.integers(0, 10, (n_s, K)))
+    _, _, nc = O.spec_verify(d, g)
+    se = nc.std() / math.sqrt(n_s)
+    assert abs(nc.mean() - sum(q ** i for i in range(K + 1))) < 4 * se
+    assert abs(sum(q ** i for i in range(K + 1)) - tau) < 0.005
+
+
 # --------------------------------------------------------------------------
 # speculative decoding is token-identical to greedy decoding
 # --------------------------------------------------------------------------
